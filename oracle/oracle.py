@@ -1,0 +1,269 @@
+"""Oracle for the score -> head-sum -> top-k -> sparse-attention path.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, CPU definition
+that the HIP path is checked against.  Only the test suite, the smoke
+check and the CPU-baseline leg of the benchmark may import it; the product
+path never calls it.  It shares no code with the HIP library.
+
+Precision: inputs are bf16, widened exactly to float64; every dot product,
+softmax and attention sum is evaluated in float64.  The one integer
+decision (which k tokens to keep) is taken on the scores rounded to
+float32, the precision the kernels decide in, with ties to the lower index.
+
+Sources (the pages' titles and sections; no formula for the score is
+printed there, the readings below are the plainest ones the text supports):
+
+* FastOCR: Dynamic Visual Fixation via KV Cache Pruning (technical summary,
+  Methodology / Focal-Guided Pruning, "Cross-Layer Propagation"): focal
+  layers attend over the full KV cache, pick the top-attended image tokens
+  at kept ratio tau, and every other layer attends only to that set.
+* same page, "Cross-Step Fixation Reuse": a non-focal first layer inherits
+  the deepest focal layer's set from the previous step; the set is refined
+  at the first focal layer.
+* same page, Methodology opening and Significance: the full cache is kept;
+  only the attended subset changes per step.
+* FastKV: Decoupling of Context Reduction and KV Cache Compression (section
+  2A, Token-Selective Propagation): saliency is attention weight from a
+  recent window of queries to all context tokens, averaged; the top-ranked
+  tokens plus the window tokens are propagated.
+* FastKV section 2B (Decoupled KV Retention): a KV budget per layer chosen
+  independently of the propagation rate.
+* HPD-Parsing wiki, method item 2 (shared-prefix KV reuse): branches read
+  the shared visual context zero-copy and attend to it, their own layout
+  prefix and their own history.
+
+Readings where the pages are silent (each also listed with its reason in
+the design notes): softmax scale 1/sqrt(d); q head h reads kv head
+h // (Hq/Hkv); focal scores are softmax over the candidate segment, summed
+over the head group (the window score instead normalises over every
+visible key); window queries are causal; the average pool is zero-padded
+and always divides by its width; ties go to the lower index; kept indices
+are returned ascending.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def widen(x) -> np.ndarray:
+    """bf16/fp32 tensor or array -> float64 ndarray (exact for bf16)."""
+    if hasattr(x, "detach"):
+        x = x.detach().float().cpu().numpy()
+    return np.asarray(x, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# KV store: logical rows of a paged cache
+# ---------------------------------------------------------------------------
+
+def logical_rows(pool, table_row, g: int, n: int, block: int = 16) -> np.ndarray:
+    """Rows [0, n) of one sequence's kv head g from a paged pool.
+
+    ``pool`` is [num_blocks][num_kv_heads][block][d]; logical row j lives in
+    physical block table_row[j // block] at offset j % block.  A shared
+    prefix is the same physical block ids in several tables, so reading it
+    through any branch's table gives the same rows (HPD wiki, method item 2).
+    """
+    j = np.arange(n)
+    tr = np.asarray(table_row, dtype=np.int64)
+    blk = tr[j // block]
+    off = j % block
+    if hasattr(pool, "index_select"):
+        import torch
+        bt = torch.from_numpy(blk).to(pool.device)
+        ot = torch.from_numpy(off).to(pool.device)
+        return widen(pool[bt, g, ot, :])
+    return widen(np.asarray(pool)[blk, g, off, :])
+
+
+# ---------------------------------------------------------------------------
+# scoring
+# ---------------------------------------------------------------------------
+
+def logits(q, K, scale) -> np.ndarray:
+    """s[..., i] = (q . K[i]) * scale, in float64."""
+    return (np.asarray(q, F64) @ np.asarray(K, F64).T) * F64(scale)
+
+
+def softmax(s) -> np.ndarray:
+    s = np.asarray(s, F64)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def focal_scores(qg, K, s0: int, s1: int, scale, norm: str = "segment") -> np.ndarray:
+    """Decode focal score of the candidate tokens [s0, s1) for one GQA group.
+
+    qg: [G, d] the group's queries; K: [N, d] the group's logical K rows.
+    For each head: softmax of its logits over the candidate segment
+    ("segment") or over all N rows read off at the segment ("context"),
+    then the probabilities are summed over the G heads of the group.
+    Result [s1 - s0], segment-relative (FastOCR, Focal-Guided Pruning).
+    """
+    s = logits(qg, K, scale)
+    if norm == "segment":
+        p = softmax(s[:, s0:s1])
+    elif norm == "context":
+        p = softmax(s)[:, s0:s1]
+    else:
+        raise ValueError(norm)
+    return p.sum(axis=0)
+
+
+def window_scores(qw, K, s0: int, s1: int, scale, causal: bool = True) -> np.ndarray:
+    """FastKV window saliency of tokens [s0, s1) for one GQA group.
+
+    qw: [W, G, d], queries of the last W positions N-W .. N-1 (FastKV 2A,
+    "a recent window of queries").  Each (window row, head) is a softmax
+    over the keys it can see -- keys at positions <= its own when causal --
+    and the probabilities are summed over the window rows and heads.
+    """
+    qw = np.asarray(qw, F64)
+    K = np.asarray(K, F64)
+    N = K.shape[0]
+    W = qw.shape[0]
+    acc = np.zeros(N, F64)
+    for r in range(W):
+        pos = N - W + r
+        vis = pos + 1 if causal else N
+        p = softmax(logits(qw[r], K[:vis], scale))      # [G, vis]
+        acc[:vis] += p.sum(axis=0)
+    return acc[s0:s1]
+
+
+def avg_pool(x, width: int) -> np.ndarray:
+    """1-D average pool, stride 1, 'same' length, zero padding; every output
+    divides by ``width`` (padding counted), width odd."""
+    assert width % 2 == 1
+    x = np.asarray(x, F64)
+    h = width // 2
+    pad = np.concatenate([np.zeros(h, F64), x, np.zeros(h, F64)])
+    out = np.empty_like(x)
+    for i in range(x.shape[0]):
+        out[i] = pad[i:i + width].sum() / width
+    return out
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def topk(scores, k: int) -> np.ndarray:
+    """The k highest scores; among equal float32 scores the lower index wins.
+
+    Full sort by (score descending, index ascending), keep the first k,
+    return those indices ascending.
+    """
+    s32 = np.asarray(scores, dtype=np.float32).astype(F64)
+    n = s32.shape[0]
+    if not 1 <= k <= n:
+        raise ValueError("need 1 <= k <= n")
+    order = np.lexsort((np.arange(n), -s32))
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def topk_warm(scores, k: int, warm) -> np.ndarray:
+    """Top-k restricted to candidates scoring at least theta, the lowest
+    current score among the k warm indices (the previous step's set,
+    FastOCR Cross-Step Fixation Reuse).  At least k candidates reach theta,
+    so the k-th best score does too and the result is the top-k of the
+    whole row."""
+    s32 = np.asarray(scores, dtype=np.float32)
+    warm = np.asarray(warm, dtype=np.int64)
+    theta = s32[warm].min()
+    cand = np.nonzero(s32 >= theta)[0]
+    return cand[topk(s32[cand], k)]
+
+
+def kept_rows(idx, s0: int, s1: int, n: int) -> np.ndarray:
+    """Rows a sparse layer attends: the selected candidates (segment-relative
+    idx shifted by s0) and every row outside the segment [s0, s1)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    return np.concatenate([s0 + idx, np.arange(0, s0), np.arange(s1, n)])
+
+
+def tie_band_check(gpu_idx, oracle_scores, k: int, rel: float = 1e-6):
+    """Accept a kept set that may differ from the oracle's only at near ties.
+
+    An index is ambiguous when its oracle score lies within ``rel`` of the
+    k-th largest oracle score.  The kept set passes when it has k distinct
+    in-range indices and every index in its symmetric difference with the
+    oracle's set is ambiguous.  Returns (ok, n_diff).
+    """
+    sc = np.asarray(oracle_scores, F64)
+    g = np.asarray(gpu_idx, dtype=np.int64)
+    if g.shape[0] != k or len(np.unique(g)) != k or g.min() < 0 or g.max() >= sc.shape[0]:
+        return False, -1
+    o = topk(sc, k)
+    sk = np.sort(sc)[::-1][k - 1]
+    diff = np.setxor1d(g, o)
+    amb = np.abs(sc[diff] - sk) <= rel * abs(sk)
+    return bool(amb.all()), int(diff.shape[0])
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def attention(qg, K, V, rows, scale):
+    """Softmax attention of each query in qg [G, d] over the given rows of
+    K, V ([N, d]).  Rows are taken as a set (ascending).  Returns
+    (out [G, d], lse [G]) with lse the natural log of the softmax
+    normaliser including the max shift."""
+    r = np.unique(np.asarray(rows, dtype=np.int64))
+    if r.shape[0] != np.asarray(rows).shape[0]:
+        raise ValueError("rows must be distinct")
+    Kr = np.asarray(K, F64)[r]
+    Vr = np.asarray(V, F64)[r]
+    s = logits(qg, Kr, scale)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    out = (e @ Vr) / z
+    return out, (m + np.log(z))[:, 0]
+
+
+def dense_attention(qg, K, V, scale):
+    return attention(qg, K, V, np.arange(np.asarray(K).shape[0]), scale)
+
+
+def gather_rows(src, idx, tail_begin: int = 0, n_tail: int = 0):
+    """Rows idx of src followed by rows [tail_begin, tail_begin + n_tail):
+    the selected tokens' hidden states, then the window tokens
+    (FastKV 2A: top-ranked tokens plus the window tokens)."""
+    rows = np.concatenate([np.asarray(idx, dtype=np.int64),
+                           np.arange(tail_begin, tail_begin + n_tail, dtype=np.int64)])
+    return np.asarray(src)[rows]
+
+
+# ---------------------------------------------------------------------------
+# layer / step schedule
+# ---------------------------------------------------------------------------
+
+def focal_layer_plan(n_layers: int, focal, t: int):
+    """What each layer does at decode step t.
+
+    ('focal', l)               full attention + scoring + top-k
+    ('sparse', l, ts, ls)      attend over the set chosen by layer ls at step ts
+    ('dense', l)               full attention, no set to reuse yet
+
+    Layers after a focal layer reuse the most recent focal layer's set of the
+    same step (Cross-Layer Propagation).  Layers before the first focal layer
+    reuse the deepest focal layer's set of step t-1 (Cross-Step Fixation
+    Reuse); at t = 0 there is no previous step and they attend densely.
+    """
+    focal = sorted(set(int(f) for f in focal))
+    first, last = focal[0], focal[-1]
+    plan = []
+    for l in range(n_layers):
+        if l in focal:
+            plan.append(("focal", l))
+        elif l < first:
+            plan.append(("dense", l) if t == 0 else ("sparse", l, t - 1, last))
+        else:
+            src = max(f for f in focal if f < l)
+            plan.append(("sparse", l, t, src))
+    return plan

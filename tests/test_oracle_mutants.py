@@ -1,0 +1,105 @@
+"""The pins catch plausible mistakes.
+
+Each case plants one slip in the oracle (on the CPU, by swapping one of its
+functions for a wrong variant) and checks that at least one pin from
+test_oracle_pins.py then fails.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests import test_oracle_pins as P
+
+F64 = np.float64
+
+
+def _no_scale(q, K, scale):
+    return np.asarray(q, F64) @ np.asarray(K, F64).T
+
+
+def _softmax_axis0(s):
+    s = np.asarray(s, F64)
+    m = s.max(axis=0, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def _topk_high_index_wins(scores, k):
+    s32 = np.asarray(scores, dtype=np.float32).astype(F64)
+    n = s32.shape[0]
+    order = np.lexsort((-np.arange(n), -s32))
+    return np.sort(order[:k])
+
+
+def _window_off_by_one(qw, K, s0, s1, scale, causal=True):
+    qw = np.asarray(qw, F64)
+    K = np.asarray(K, F64)
+    N, W = K.shape[0], qw.shape[0]
+    acc = np.zeros(N)
+    for r in range(W):
+        vis = max(N - W + r, 1)
+        acc[:vis] += O.softmax(O.logits(qw[r], K[:vis], scale)).sum(0)
+    return acc[s0:s1]
+
+
+def _attention_uses_k_for_v(qg, K, V, rows, scale):
+    r = np.unique(np.asarray(rows, dtype=np.int64))
+    s = O.logits(qg, np.asarray(K, F64)[r], scale)
+    m = s.max(1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(1, keepdims=True)
+    return (e @ np.asarray(K, F64)[r]) / z, (m + np.log(z))[:, 0]
+
+
+def _pool_excluding_pad(x, width):
+    x = np.asarray(x, F64)
+    h = width // 2
+    out = np.empty_like(x)
+    for i in range(len(x)):
+        lo, hi = max(0, i - h), min(len(x), i + h + 1)
+        out[i] = x[lo:hi].mean()
+    return out
+
+
+def _kept_rows_unshifted(idx, s0, s1, n):
+    idx = np.asarray(idx, dtype=np.int64)
+    return np.concatenate([idx, np.arange(0, s0), np.arange(s1, n)])
+
+
+def _focal_sum_over_keys(qg, K, s0, s1, scale, norm="segment"):
+    s = O.logits(qg, K, scale)
+    p = O.softmax(s[:, s0:s1])
+    return p.sum(axis=1).repeat(s1 - s0)[: s1 - s0]
+
+
+def _warm_uses_max(scores, k, warm):
+    s32 = np.asarray(scores, dtype=np.float32)
+    theta = s32[np.asarray(warm)].max()
+    cand = np.nonzero(s32 >= theta)[0]
+    if cand.shape[0] < k:
+        return cand
+    return cand[O.topk(s32[cand], k)]
+
+
+MUTANTS = [
+    ("logits", _no_scale, [P.test_attention_matches_sdpa, P.test_window_scores_scale_sensitive]),
+    ("softmax", _softmax_axis0, [lambda: P.test_score_sums(2), lambda: P.test_golden_focal_scores("softmax_three_keys")]),
+    ("topk", _topk_high_index_wins, [lambda: P.test_topk_brute_force(0), P.test_golden_topk_ties]),
+    ("window_scores", _window_off_by_one, [P.test_golden_window_causal_uniform]),
+    ("attention", _attention_uses_k_for_v, [lambda: P.test_attention_matches_sdpa(0)]),
+    ("avg_pool", _pool_excluding_pad, [lambda: P.test_pool_matches_torch(8), P.test_golden_pool]),
+    ("kept_rows", _kept_rows_unshifted, [P.test_full_budget_is_dense]),
+    ("focal_scores", _focal_sum_over_keys, [lambda: P.test_golden_focal_scores("group_sum_two_heads")]),
+    ("topk_warm", _warm_uses_max, [lambda: P.test_topk_warm_equals_cold(0)]),
+]
+
+
+@pytest.mark.parametrize("name,bad,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, bad, pins):
+    monkeypatch.setattr(O, name, bad)
+    for pin in pins:
+        fn = pin
+        if getattr(pin, "__code__", None) is not None and pin.__code__.co_argcount == 1:
+            fn = lambda p=pin: p(0)    # noqa: E731  seeded pins take a seed
+        with pytest.raises((AssertionError, ValueError, IndexError)):
+            fn()

@@ -1,0 +1,319 @@
+"""Pins of the oracle to facts outside itself.
+
+Each pin is independent of the oracle's own code: a library routine that
+computes the same quantity (torch's scaled-dot-product attention and
+average pool), hand-derived worked cases (tests/golden/hand_cases.json),
+closed forms, invariants that hold for any input, and brute force on tiny
+inputs.  A plausible slip in the oracle (a dropped scale, a wrong softmax
+axis, an off-by-one causal mask, a reversed tie-break, a transposed
+operand) fails at least one of them; test_oracle_mutants.py checks that.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLD = json.load(open(os.path.join(HERE, "golden", "hand_cases.json")))["cases"]
+D = 128
+SCALE = 1.0 / math.sqrt(D)
+
+
+def _q_for_logits(logit_rows):
+    """Queries/keys whose scaled dot products equal the given logits:
+    q_h = sqrt(d) * e_h and K[i, h] = logit_rows[h][i]."""
+    lr = np.asarray(logit_rows, dtype=np.float64)
+    G, n = lr.shape
+    q = np.zeros((G, D))
+    K = np.zeros((n, D))
+    for h in range(G):
+        q[h, h] = math.sqrt(D)
+        K[:, h] = lr[h]
+    return q, K
+
+
+def _rand(rng, *shape):
+    """bf16-representable normals as float64."""
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    return x.double().numpy()
+
+
+# --------------------------------------------------------------------------
+# golden hand-derived cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["softmax_three_keys", "group_sum_two_heads"])
+def test_golden_focal_scores(name):
+    c = GOLD[name]
+    q, K = _q_for_logits(c["logits"])
+    s0, s1 = c["segment"]
+    got = O.focal_scores(q, K, s0, s1, SCALE, "segment")
+    np.testing.assert_allclose(got, c["scores"], rtol=1e-13, atol=0)
+
+
+def test_golden_context_vs_segment():
+    c = GOLD["context_vs_segment"]
+    q, K = _q_for_logits(c["logits"])
+    s0, s1 = c["segment"]
+    np.testing.assert_allclose(O.focal_scores(q, K, s0, s1, SCALE, "segment"), c["scores_segment"], rtol=1e-13)
+    np.testing.assert_allclose(O.focal_scores(q, K, s0, s1, SCALE, "context"), c["scores_context"], rtol=1e-13)
+
+
+def test_golden_topk_ties():
+    c = GOLD["topk_ties"]
+    for k, want in c["topk"].items():
+        assert O.topk(c["scores"], int(k)).tolist() == want
+
+
+def test_golden_pool():
+    c = GOLD["pool_width7"]
+    np.testing.assert_allclose(O.avg_pool(c["x"], 7), c["pooled"], rtol=0, atol=1e-15)
+
+
+def test_golden_attention_two_rows():
+    c = GOLD["attention_two_rows"]
+    q, K = _q_for_logits(c["logits"])
+    V = np.zeros((2, D))
+    V[:, :2] = c["v01"]
+    out, lse = O.attention(q, K, V, [0, 1], SCALE)
+    np.testing.assert_allclose(out[0, :2], c["out01"], rtol=1e-14)
+    assert np.all(out[0, 2:] == 0)
+    assert abs(lse[0] - c["lse"]) < 1e-14
+
+
+def test_golden_window_causal_uniform():
+    c = GOLD["window_causal_uniform"]
+    n, W = c["n"], c["window"]
+    qw = np.zeros((W, 1, D))
+    K = np.random.default_rng(0).standard_normal((n, D))
+    got = O.window_scores(qw, K, 0, n, SCALE, causal=True)
+    np.testing.assert_allclose(got, c["scores"], rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# library routines
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_attention_matches_sdpa(seed):
+    rng = np.random.default_rng(seed)
+    G, N = int(rng.integers(1, 9)), int(rng.integers(1, 300))
+    q, K, V = _rand(rng, G, D), _rand(rng, N, D), _rand(rng, N, D)
+    rows = np.sort(rng.choice(N, size=int(rng.integers(1, N + 1)), replace=False))
+    out, _ = O.attention(q, K, V, rng.permutation(rows), SCALE)
+    tq = torch.from_numpy(q)[None, :, None, :]              # [1, G, 1, d]
+    tk = torch.from_numpy(K[rows])[None, None].expand(1, G, -1, -1)
+    tv = torch.from_numpy(V[rows])[None, None].expand(1, G, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 8, 50, 257])
+def test_pool_matches_torch(n):
+    x = np.random.default_rng(n).random(n)
+    ref = torch.nn.functional.avg_pool1d(torch.from_numpy(x)[None, None], 7, 1, 3, count_include_pad=True)[0, 0].numpy()
+    np.testing.assert_allclose(O.avg_pool(x, 7), ref, rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+def test_attention_zero_query_is_mean():
+    rng = np.random.default_rng(1)
+    K, V = _rand(rng, 40, D), _rand(rng, 40, D)
+    rows = np.array([3, 9, 17, 33])
+    out, lse = O.attention(np.zeros((2, D)), K, V, rows, SCALE)
+    np.testing.assert_allclose(out[0], V[rows].mean(0), rtol=1e-13, atol=1e-14)
+    assert abs(lse[0] - math.log(4)) < 1e-14
+
+
+def test_attention_single_row_and_constant_v():
+    rng = np.random.default_rng(2)
+    q, K, V = _rand(rng, 3, D), _rand(rng, 20, D), _rand(rng, 20, D)
+    out, lse = O.attention(q, K, V, [11], SCALE)
+    np.testing.assert_array_equal(out, np.repeat(V[11][None], 3, 0))
+    np.testing.assert_allclose(lse, (q @ K[11]) * SCALE, rtol=1e-14)
+    Vc = np.repeat(V[4][None], 20, 0)
+    out, _ = O.attention(q, K, Vc, np.arange(20), SCALE)
+    np.testing.assert_allclose(out, np.repeat(V[4][None], 3, 0), rtol=1e-13, atol=1e-14)
+
+
+def test_window_scores_scale_sensitive():
+    """A two-key case where the scale matters: one window row, one head,
+    logits 0 and ln 3 after scaling -> weights 1/4, 3/4 (causal row sees both)."""
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = math.sqrt(D)
+    K = np.zeros((2, D))
+    K[1, 0] = math.log(3)
+    np.testing.assert_allclose(O.window_scores(q, K, 0, 2, SCALE), [0.25, 0.75], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_score_sums(G):
+    rng = np.random.default_rng(G)
+    N, s0, s1 = 300, 20, 250
+    q, K = _rand(rng, G, D), _rand(rng, N, D)
+    seg = O.focal_scores(q, K, s0, s1, SCALE, "segment")
+    assert abs(seg.sum() - G) < 1e-12 and seg.shape == (s1 - s0,)
+    ctx_in = O.focal_scores(q, K, s0, s1, SCALE, "context")
+    ctx_all = O.focal_scores(q, K, 0, N, SCALE, "context")
+    assert abs(ctx_all.sum() - G) < 1e-12
+    np.testing.assert_allclose(ctx_all[s0:s1], ctx_in, rtol=1e-14)
+    assert np.all(ctx_in < seg)
+    W = 8
+    qw = _rand(rng, W, G, D)
+    ws = O.window_scores(qw, K, 0, N, SCALE, causal=True)
+    assert abs(ws.sum() - W * G) < 1e-11
+    # the causal window: key N-1 is seen only by the last window row
+    qw2 = qw.copy()
+    qw2[:-1] *= 0.0
+    ws2 = O.window_scores(qw2, K, 0, N, SCALE, causal=True)
+    assert abs(ws2.sum() - W * G) < 1e-11
+
+
+def test_score_permutation_equivariance():
+    rng = np.random.default_rng(5)
+    N = 120
+    q, K = _rand(rng, 2, D), _rand(rng, N, D)
+    perm = rng.permutation(N)
+    a = O.focal_scores(q, K, 0, N, SCALE, "segment")
+    b = O.focal_scores(q, K[perm], 0, N, SCALE, "segment")
+    np.testing.assert_allclose(b, a[perm], rtol=1e-13)
+
+
+def _brute_topk(s, k):
+    """The unique k-subset S with: for i in S, j not in S, s_i > s_j or
+    (s_i == s_j and i < j).  Enumerates every subset."""
+    n = len(s)
+    found = []
+    for S in itertools.combinations(range(n), k):
+        Sset = set(S)
+        ok = all((s[i] > s[j]) or (s[i] == s[j] and i < j)
+                 for i in S for j in range(n) if j not in Sset)
+        if ok:
+            found.append(list(S))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 11))
+    # few distinct values so that ties are common
+    s = rng.integers(0, 4, size=n).astype(np.float32) / 4
+    for k in range(1, n + 1):
+        assert O.topk(s, k).tolist() == _brute_topk(s.tolist(), k)
+
+
+def test_topk_all_equal_and_budget_count():
+    s = np.full(3584, 1.0 / 3584, dtype=np.float32)
+    assert O.topk(s, 179).tolist() == list(range(179))
+    rng = np.random.default_rng(9)
+    for cfg in (synth.C0, synth.C1, synth.C4):
+        sc = rng.random(cfg.n_visual)
+        keep = O.topk(sc, cfg.k)
+        assert keep.shape[0] == cfg.k and len(np.unique(keep)) == cfg.k
+        n = cfg.prefix_len + 5
+        R = O.kept_rows(keep, 0, cfg.n_visual, n)
+        assert len(np.unique(R)) == cfg.k + (n - cfg.n_visual)
+    assert (synth.C0.k, synth.C1.k, synth.C2.k, synth.C4.k, synth.C3.k) == (179, 320, 6554, 154, 2048)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_topk_warm_equals_cold(seed):
+    rng = np.random.default_rng(seed)
+    n, k = 500, 25
+    s = (rng.integers(0, 40, size=n) / 40).astype(np.float32)
+    cold = O.topk(s, k)
+    for _ in range(10):
+        warm = np.sort(rng.choice(n, size=k, replace=False))
+        assert O.topk_warm(s, k, warm).tolist() == cold.tolist()
+    assert O.topk_warm(s, k, cold).tolist() == cold.tolist()
+
+
+def test_full_budget_is_dense():
+    rng = np.random.default_rng(3)
+    N, s0, s1 = 200, 10, 150
+    q, K, V = _rand(rng, 2, D), _rand(rng, N, D), _rand(rng, N, D)
+    sc = O.focal_scores(q, K, s0, s1, SCALE)
+    keep = O.topk(sc, s1 - s0)
+    out_s, lse_s = O.attention(q, K, V, O.kept_rows(keep, s0, s1, N), SCALE)
+    out_d, lse_d = O.dense_attention(q, K, V, SCALE)
+    np.testing.assert_array_equal(out_s, out_d)
+    np.testing.assert_array_equal(lse_s, lse_d)
+
+
+def test_tie_band_check():
+    rng = np.random.default_rng(4)
+    sc = rng.random(100)
+    k = 10
+    o = O.topk(sc, k)
+    assert O.tie_band_check(o, sc, k) == (True, 0)
+    sc2 = sc.copy()
+    order = np.argsort(-sc2)
+    sc2[order[k]] = sc2[order[k - 1]] * (1 - 1e-7)     # a near tie at the boundary
+    o2 = O.topk(sc2, k)
+    swapped = np.sort(np.concatenate([np.setdiff1d(o2, [order[k - 1]]), [order[k]]]))
+    assert O.tie_band_check(swapped, sc2, k)[0]
+    far = np.sort(np.concatenate([o[1:], [order[-1]]]))
+    assert not O.tie_band_check(far, sc, k)[0]
+    assert not O.tie_band_check(o[:-1], sc, k)[0]
+    assert not O.tie_band_check(np.concatenate([o[:-1], o[:1]]), sc, k)[0]
+
+
+# --------------------------------------------------------------------------
+# KV store and schedule
+# --------------------------------------------------------------------------
+
+def test_logical_rows_inverts_scatter():
+    rng = np.random.default_rng(7)
+    blk, hkv, n = 16, 3, 100
+    rows = _rand(rng, hkv, n, 8)
+    nb = -(-n // blk)
+    phys = rng.permutation(nb + 4)[:nb]
+    pool = np.zeros((nb + 4, hkv, blk, 8))
+    for j in range(n):
+        pool[phys[j // blk], :, j % blk, :] = rows[:, j, :]
+    for g in range(hkv):
+        np.testing.assert_array_equal(O.logical_rows(pool, phys, g, n, blk), rows[g])
+
+
+def test_shared_prefix_table_reads_same_prefix():
+    from synth.gen import shared_prefix_table
+    table, nb = shared_prefix_table(4, np.array([2, 5, 1]))
+    rng = np.random.default_rng(8)
+    pool = rng.standard_normal((nb, 2, 16, 8))
+    a = O.logical_rows(pool, table[0], 1, 64)
+    b = O.logical_rows(pool, table[2], 1, 64)
+    np.testing.assert_array_equal(a, b)
+    c = O.logical_rows(pool, table[1], 1, 64 + 80)
+    assert not np.array_equal(c[64:80], O.logical_rows(pool, table[0], 1, 80)[64:80])
+
+
+def test_layer_plan_c1():
+    p0 = O.focal_layer_plan(28, (3, 14), 0)
+    assert [e[0] for e in p0[:3]] == ["dense"] * 3
+    assert p0[3] == ("focal", 3) and p0[14] == ("focal", 14)
+    assert all(p0[l] == ("sparse", l, 0, 3) for l in range(4, 14))
+    assert all(p0[l] == ("sparse", l, 0, 14) for l in range(15, 28))
+    p5 = O.focal_layer_plan(28, (3, 14), 5)
+    assert all(p5[l] == ("sparse", l, 4, 14) for l in range(3))
+
+
+def test_gather_rows_exact():
+    src = np.arange(40 * 6).reshape(40, 6)
+    got = O.gather_rows(src, [3, 7, 20], 36, 4)
+    np.testing.assert_array_equal(got, src[[3, 7, 20, 36, 37, 38, 39]])
