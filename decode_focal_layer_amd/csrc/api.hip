@@ -1,0 +1,389 @@
+// libkvsel C-ABI: argument validation (pure host code, before any HIP call),
+// workspace layout and launch of the kernels on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+#include "kvsel_internal.h"
+
+using namespace kvsel;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvsel_status fail(kvsel_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvsel_status ok() {
+  g_err[0] = 0;
+  return KVSEL_OK;
+}
+
+kvsel_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVSEL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+kvsel_status check_desc(const kvsel_kv_desc *kv, bool need_v) {
+  if (kv == nullptr) return fail(KVSEL_EINVAL, "kv descriptor is NULL");
+  if (kv->head_dim != kD) return fail(KVSEL_EUNSUPPORTED, "head_dim %d unsupported (128 only)", kv->head_dim);
+  if (kv->block_size != kBlk) return fail(KVSEL_EUNSUPPORTED, "block_size %d unsupported (16 only)", kv->block_size);
+  if (kv->batch < 1) return fail(KVSEL_EINVAL, "batch must be >= 1");
+  if (kv->num_kv_heads < 1) return fail(KVSEL_EINVAL, "num_kv_heads must be >= 1");
+  if ((int64_t)kv->batch * kv->num_kv_heads > kMaxPairs)
+    return fail(KVSEL_EUNSUPPORTED, "batch * num_kv_heads > %d", kMaxPairs);
+  if (kv->max_blocks_per_seq < 1) return fail(KVSEL_EINVAL, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)kv->max_blocks_per_seq * kBlk > 0x7fffffff) return fail(KVSEL_EUNSUPPORTED, "sequence too long");
+  if (kv->max_seq_len < 0 || (int64_t)kv->max_seq_len > (int64_t)kv->max_blocks_per_seq * kBlk)
+    return fail(KVSEL_EINVAL, "max_seq_len must be in [0, max_blocks_per_seq*16]");
+  if (kv->max_seg_len < 0 || kv->max_seg_len > kv->max_seq_len)
+    return fail(KVSEL_EINVAL, "max_seg_len must be in [0, max_seq_len]");
+  if (kv->min_seg_len < 0 || kv->min_seg_len > kv->max_seg_len)
+    return fail(KVSEL_EINVAL, "min_seg_len must be in [0, max_seg_len]");
+  if (kv->num_blocks < 1) return fail(KVSEL_EINVAL, "num_blocks must be >= 1");
+  if ((uint64_t)kv->num_blocks * (uint64_t)kv->num_kv_heads * kBlk >= 0xffffffffull)
+    return fail(KVSEL_EUNSUPPORTED, "pool has 2^32 or more rows");
+  if (!kv->k_pool || !kv->block_table || !kv->seq_len || !kv->seg_begin || !kv->seg_end)
+    return fail(KVSEL_EINVAL, "k_pool, block_table, seq_len, seg_begin and seg_end are required");
+  if (need_v && !kv->v_pool) return fail(KVSEL_EINVAL, "v_pool is required");
+  if (!aligned(kv->k_pool, 16) || (kv->v_pool && !aligned(kv->v_pool, 16)))
+    return fail(KVSEL_EINVAL, "k_pool and v_pool must be 16-byte aligned");
+  return KVSEL_OK;
+}
+
+kvsel_status check_heads(const kvsel_kv_desc *kv, int32_t hq, int *group) {
+  if (hq < 1 || hq % kv->num_kv_heads != 0)
+    return fail(KVSEL_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", hq,
+                kv->num_kv_heads);
+  const int G = hq / kv->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(KVSEL_EUNSUPPORTED, "group size %d unsupported (1, 2, 4 or 8)", G);
+  *group = G;
+  return KVSEL_OK;
+}
+
+kvsel_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return KVSEL_OK;
+  if (ws == nullptr) return fail(KVSEL_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, kAlign)) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(KVSEL_ENOSPC, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return KVSEL_OK;
+}
+
+int gather_rows_bound(const kvsel_kv_desc *kv, int32_t k) {
+  const int64_t r = (int64_t)k + kv->max_seq_len - kv->min_seg_len;
+  return (int)(r < 1 ? 1 : (r > 0x7fffffff ? 0x7fffffff : r));
+}
+
+int logit_mode_of(bool with_scores, int32_t norm) {
+  return with_scores ? (norm == KVSEL_NORM_SEGMENT ? 1 : 2) : 0;
+}
+
+AttnArgs attn_args(const kvsel_kv_desc *kv, const uint16_t *q, int32_t hq, float scale, const int32_t *idx,
+                   int32_t k, const AttnPlan &p, char *ws, float *out, float *lse, int logit_mode) {
+  AttnArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = kv->block_table;
+  a.seq_len = kv->seq_len;
+  a.seg_begin = kv->seg_begin;
+  a.seg_end = kv->seg_end;
+  a.num_blocks = kv->num_blocks;
+  a.max_blocks = kv->max_blocks_per_seq;
+  a.hkv = kv->num_kv_heads;
+  a.hq = hq;
+  a.k = k;
+  a.q = q;
+  a.idx = idx;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rps = p.rps;
+  a.nsplit = p.nsplit;
+  a.counters = reinterpret_cast<uint32_t *>(ws + p.off_counters);
+  a.rec = reinterpret_cast<float *>(ws + p.off_rec);
+  a.out = out;
+  a.lse = lse;
+  a.logits = logit_mode ? reinterpret_cast<float *>(ws + p.off_logits) : nullptr;
+  a.ld_logits = p.ld_logits;
+  a.logit_mode = logit_mode;
+  return a;
+}
+
+NormArgs norm_args(const kvsel_kv_desc *kv, int32_t hq, int heads_per_out, int n_out, int32_t norm, float scale,
+                   const float *logits, int64_t ld_logits) {
+  NormArgs n{};
+  n.logits = logits;
+  n.ld_logits = ld_logits;
+  n.seq_len = kv->seq_len;
+  n.seg_begin = kv->seg_begin;
+  n.seg_end = kv->seg_end;
+  n.cap_rows = kv->max_blocks_per_seq * kBlk;
+  n.hq = hq;
+  n.heads_per_out = heads_per_out;
+  n.n_out = n_out;
+  n.norm = norm;
+  n.scale = (double)scale;
+  return n;
+}
+
+// kvsel_score scratch layout
+struct ScorePlan {
+  bool window = false;
+  AttnPlan lp;      // decode: logits plan (rps, ld_logits, offsets)
+  WinPlan wp;       // window
+  size_t off_part = 0, total = 0;
+  int64_t ld64 = 0;
+};
+
+ScorePlan score_plan(const kvsel_kv_desc *kv, int32_t n_rows, int32_t hq, int32_t reduce, int32_t norm,
+                     int32_t pool_width) {
+  ScorePlan sp;
+  const int G = hq / kv->num_kv_heads;
+  if (n_rows > 1) {
+    sp.window = true;
+    sp.wp = win_plan(kv->batch, kv->num_kv_heads, G, n_rows, kv->max_seq_len, kv->max_seg_len);
+    sp.total = sp.wp.total;
+    return sp;
+  }
+  const int mode = logit_mode_of(true, norm);
+  const int rows = mode == 1 ? kv->max_seg_len : kv->max_seq_len;
+  sp.lp = attn_plan(kv->batch, kv->num_kv_heads, hq, rows > 0 ? rows : 1, mode, kv->max_seg_len, kv->max_seq_len);
+  // the logits kernel needs only the logit scratch; reuse the plan's layout from off_logits
+  size_t off = sp.lp.off_extra;
+  const bool need_part = pool_width > 1;
+  sp.ld64 = kv->max_seg_len > 0 ? kv->max_seg_len : 1;
+  if (need_part) {
+    const int n_out = reduce == KVSEL_REDUCE_GROUP ? kv->num_kv_heads : 1;
+    sp.off_part = off;
+    off = align_up(off + (size_t)kv->batch * n_out * sp.ld64 * sizeof(double));
+  }
+  sp.total = off;
+  return sp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvsel_version(void) { return KVSEL_VERSION; }
+
+const char *kvsel_status_string(kvsel_status s) {
+  switch (s) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_EINVAL: return "invalid argument";
+    case KVSEL_ENOSPC: return "workspace too small";
+    case KVSEL_EUNSUPPORTED: return "unsupported shape";
+    case KVSEL_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *kvsel_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------------
+size_t kvsel_attn_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads, int32_t k, int32_t with_scores,
+                            int32_t norm) {
+  int G;
+  if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;
+  const int rows = k < 0 ? (kv->max_seq_len > 0 ? kv->max_seq_len : 1) : gather_rows_bound(kv, k);
+  const int mode = k < 0 ? logit_mode_of(with_scores != 0, norm) : 0;
+  return attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, rows, mode, kv->max_seg_len, kv->max_seq_len).total;
+}
+
+kvsel_status kvsel_gather_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
+                               const int32_t *idx, int32_t k, float *out, float *lse, void *ws, size_t ws_bytes,
+                               kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr) return fail(KVSEL_EINVAL, "out is NULL");
+  if (k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
+  if (k > 0 && idx == nullptr) return fail(KVSEL_EINVAL, "idx is NULL with k > 0");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  const AttnPlan p = attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, gather_rows_bound(kv, k), 0,
+                               kv->max_seg_len, kv->max_seq_len);
+  if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
+  AttnArgs a = attn_args(kv, q, num_q_heads, scale, idx, k, p, (char *)ws, out, lse, 0);
+  a.dense = 0;   // k == 0: only the always-attended rows
+  return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "gather_attn launch");
+}
+
+kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale, float *out,
+                              float *lse, float *seg_scores, int64_t ld, int32_t norm, void *ws, size_t ws_bytes,
+                              kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr) return fail(KVSEL_EINVAL, "out is NULL");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (seg_scores != nullptr) {
+    if (norm != KVSEL_NORM_SEGMENT && norm != KVSEL_NORM_CONTEXT) return fail(KVSEL_EINVAL, "bad norm %d", norm);
+    if (ld < kv->max_seg_len || ld < 1) return fail(KVSEL_EINVAL, "ld must be >= max_seg_len");
+  }
+  const int mode = logit_mode_of(seg_scores != nullptr, norm);
+  const AttnPlan p = attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, kv->max_seq_len > 0 ? kv->max_seq_len : 1,
+                               mode, kv->max_seg_len, kv->max_seq_len);
+  if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
+  AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, p, (char *)ws, out, lse, mode);
+  a.dense = 1;
+  hipError_t e = launch_attn(a, kv->batch, G, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "dense_attn launch");
+  if (seg_scores == nullptr) return ok();
+  NormArgs n = norm_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, a.logits, p.ld_logits);
+  n.scores = seg_scores;
+  n.ld = ld;
+  return hip_status(launch_focal_norm(n, kv->batch, (hipStream_t)stream), "focal score launch");
+}
+
+// ------------------------------------------------------------------------
+size_t kvsel_score_workspace(const kvsel_kv_desc *kv, int32_t n_rows, int32_t num_q_heads, int32_t reduce,
+                             int32_t norm) {
+  int G;
+  if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;
+  if (n_rows < 1) return 0;
+  // the pool post-pass scratch is sized for any pool width
+  return score_plan(kv, n_rows, num_q_heads, reduce, norm, 3).total;
+}
+
+kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_rows, int32_t num_q_heads, float scale,
+                         int32_t reduce, int32_t norm, int32_t causal, int32_t pool_width, float *scores, int64_t ld,
+                         void *ws, size_t ws_bytes, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, false)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (scores == nullptr) return fail(KVSEL_EINVAL, "scores is NULL");
+  if (n_rows < 1 || n_rows > 64) return fail(KVSEL_EINVAL, "n_rows must be in [1, 64]");
+  if (reduce != KVSEL_REDUCE_GROUP && reduce != KVSEL_REDUCE_ALL) return fail(KVSEL_EINVAL, "bad reduce %d", reduce);
+  if (norm != KVSEL_NORM_SEGMENT && norm != KVSEL_NORM_CONTEXT) return fail(KVSEL_EINVAL, "bad norm %d", norm);
+  if (n_rows > 1 && norm != KVSEL_NORM_CONTEXT)
+    return fail(KVSEL_EINVAL, "a query window (n_rows > 1) is context-normalised");
+  if (n_rows > 1 && n_rows * G > 32)
+    return fail(KVSEL_EUNSUPPORTED, "n_rows * group = %d > 32", n_rows * G);
+  if (pool_width < 1 || pool_width % 2 == 0) return fail(KVSEL_EINVAL, "pool_width must be odd and >= 1");
+  if (ld < kv->max_seg_len || ld < 1) return fail(KVSEL_EINVAL, "ld must be >= max_seg_len");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  const ScorePlan sp = score_plan(kv, n_rows, num_q_heads, reduce, norm, pool_width);
+  if ((st = check_ws(ws, ws_bytes, sp.total)) != KVSEL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char *w = (char *)ws;
+  const int n_out = reduce == KVSEL_REDUCE_GROUP ? kv->num_kv_heads : 1;
+
+  if (sp.window) {
+    WinArgs a{};
+    a.k_pool = kv->k_pool;
+    a.block_table = kv->block_table;
+    a.seq_len = kv->seq_len;
+    a.seg_begin = kv->seg_begin;
+    a.seg_end = kv->seg_end;
+    a.num_blocks = kv->num_blocks;
+    a.max_blocks = kv->max_blocks_per_seq;
+    a.hkv = kv->num_kv_heads;
+    a.hq = num_q_heads;
+    a.group = G;
+    a.n_rows = n_rows;
+    a.causal = causal ? 1 : 0;
+    a.q = q;
+    a.scale = (double)scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.tile_rows = sp.wp.tile_rows;
+    a.ntiles = sp.wp.ntiles;
+    a.stat = reinterpret_cast<float *>(w + sp.wp.off_stat);
+    a.part = reinterpret_cast<double *>(w + sp.wp.off_part);
+    a.ld64 = sp.wp.ld64;
+    hipError_t e = launch_window(a, sp.wp, kv->batch, s);
+    if (e != hipSuccess) return hip_status(e, "window score launch");
+    PoolArgs pa{};
+    pa.part = a.part;
+    pa.ld64 = a.ld64;
+    pa.n_in = kv->num_kv_heads;
+    pa.n_out = n_out;
+    pa.seq_len = kv->seq_len;
+    pa.seg_begin = kv->seg_begin;
+    pa.seg_end = kv->seg_end;
+    pa.cap_rows = kv->max_blocks_per_seq * kBlk;
+    pa.width = pool_width;
+    pa.scores = scores;
+    pa.ld = ld;
+    return hip_status(launch_pool(pa, kv->batch, kv->max_seg_len, s), "pool launch");
+  }
+
+  const int mode = logit_mode_of(true, norm);
+  const int rows = mode == 1 ? kv->max_seg_len : kv->max_seq_len;
+  const AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, sp.lp, w, nullptr, nullptr, mode);
+  hipError_t e = launch_logits(a, kv->batch, G, rows, s);
+  if (e != hipSuccess) return hip_status(e, "score logits launch");
+  NormArgs n = norm_args(kv, num_q_heads, reduce == KVSEL_REDUCE_GROUP ? G : num_q_heads, n_out, norm, scale, a.logits,
+                         sp.lp.ld_logits);
+  if (pool_width == 1) {
+    n.scores = scores;
+    n.ld = ld;
+    return hip_status(launch_focal_norm(n, kv->batch, s), "score launch");
+  }
+  n.scores64 = reinterpret_cast<double *>(w + sp.off_part);
+  n.ld64 = sp.ld64;
+  e = launch_focal_norm(n, kv->batch, s);
+  if (e != hipSuccess) return hip_status(e, "score launch");
+  PoolArgs pa{};
+  pa.part = n.scores64;
+  pa.ld64 = sp.ld64;
+  pa.n_in = n_out;
+  pa.n_out = n_out;
+  pa.seq_len = kv->seq_len;
+  pa.seg_begin = kv->seg_begin;
+  pa.seg_end = kv->seg_end;
+  pa.cap_rows = kv->max_blocks_per_seq * kBlk;
+  pa.width = pool_width;
+  pa.scores = scores;
+  pa.ld = ld;
+  return hip_status(launch_pool(pa, kv->batch, kv->max_seg_len, s), "pool launch");
+}
+
+// ------------------------------------------------------------------------
+size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k) {
+  (void)rows;
+  (void)n;
+  (void)k;
+  return 0;
+}
+
+kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, int32_t n, int32_t k, const int32_t *warm_idx,
+                        int32_t *idx, void *ws, size_t ws_bytes, kvsel_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (scores == nullptr || idx == nullptr) return fail(KVSEL_EINVAL, "scores and idx are required");
+  if (rows < 1) return fail(KVSEL_EINVAL, "rows must be >= 1");
+  if (k < 1 || k > n) return fail(KVSEL_EINVAL, "need 1 <= k <= n (k=%d, n=%d)", k, n);
+  if ((int64_t)n > ld) return fail(KVSEL_EINVAL, "need n <= ld");
+  TopkArgs a{scores, ld, rows, n, k, warm_idx, idx};
+  return hip_status(launch_topk(a, (hipStream_t)stream), "topk launch");
+}
+
+// ------------------------------------------------------------------------
+kvsel_status kvsel_gather_rows(const void *src, int64_t row_bytes, int64_t n_src_rows, const int32_t *idx,
+                               int32_t n_idx, int64_t tail_begin, int32_t n_tail, void *dst, kvsel_stream stream) {
+  if (src == nullptr || dst == nullptr) return fail(KVSEL_EINVAL, "src and dst are required");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(KVSEL_EINVAL, "src and dst must be 16-byte aligned");
+  if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(KVSEL_EINVAL, "row_bytes must be a positive multiple of 16");
+  if (n_idx < 0 || n_tail < 0 || n_src_rows < 0) return fail(KVSEL_EINVAL, "negative count");
+  if (n_idx > 0 && idx == nullptr) return fail(KVSEL_EINVAL, "idx is NULL with n_idx > 0");
+  if ((int64_t)n_idx + n_tail > 0x7fffffff) return fail(KVSEL_EINVAL, "too many rows");
+  return hip_status(launch_gather_rows(src, row_bytes, n_src_rows, idx, n_idx, tail_begin, n_tail, dst,
+                                       (hipStream_t)stream),
+                    "gather_rows launch");
+}
+
+}  // extern "C"

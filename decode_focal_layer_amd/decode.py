@@ -1,0 +1,107 @@
+"""Decode-step driver: the focal-layer schedule over libkvsel calls.
+
+FastOCR (technical summary, Focal-Guided Pruning / Cross-Layer Propagation):
+only the focal layers attend over the full cache and select the top-k
+visual tokens; every later layer attends over the most recent focal layer's
+set.  Cross-Step Fixation Reuse: layers before the first focal layer reuse
+the deepest focal layer's set from the previous step (at the first step
+there is none and they attend densely); each focal layer's top-k is warm
+started from its own previous selection.
+
+This module only decides which buffer each call reads (index propagation
+moves no data) and issues the calls; the arithmetic runs in the library.
+The same driver serves the HPD-style branched decode: branches are the
+sequences of the descriptor and share their prefix blocks through the
+block table.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import kvsel
+
+
+class FocalDecoder:
+    def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, k: int, focal: Sequence[int], scale: float,
+                 seg_len: int, warm_start: bool = True, device="cuda", keep_outputs: bool = True):
+        self.kvs = list(kvs)
+        self.L = len(self.kvs)
+        self.hq = num_q_heads
+        self.k = k
+        self.focal = sorted(set(int(f) for f in focal))
+        self.scale = float(scale)
+        self.seg_len = seg_len
+        self.warm_start = warm_start
+        kv0 = self.kvs[0]
+        B, hkv = kv0.batch, kv0.hkv
+        self.B, self.hkv = B, hkv
+        self.device = device
+        self.scores = torch.empty((B, hkv, seg_len), dtype=torch.float32, device=device)
+        # two selection buffers per focal layer: this step's and the previous step's
+        self.idx = {f: [torch.zeros((B, hkv, k), dtype=torch.int32, device=device) for _ in range(2)]
+                    for f in self.focal}
+        self.cur = 0
+        self.out = torch.empty((self.L, B, num_q_heads, 128), dtype=torch.float32, device=device)
+        self.ws = kvsel.Workspace(device)
+        need = 0
+        for kv in self.kvs:
+            need = max(need, kvsel.attn_workspace(kv, num_q_heads, -1, True, kvsel.NORM_SEGMENT),
+                       kvsel.attn_workspace(kv, num_q_heads, k))
+        self.ws_ptr, self.ws_n = self.ws.ptr_and_size(need)
+        self.t = 0
+        self._lib = kvsel.lib()
+
+    def plan(self, t: int):
+        """(kind, src_step_is_previous, src_layer) per layer."""
+        first, last = self.focal[0], self.focal[-1]
+        plan = []
+        for l in range(self.L):
+            if l in self.focal:
+                plan.append(("focal", None))
+            elif l < first:
+                plan.append(("dense", None) if t == 0 else ("sparse", ("prev", last)))
+            else:
+                plan.append(("sparse", ("cur", max(f for f in self.focal if f < l))))
+        return plan
+
+    def step(self, t: int, q: torch.Tensor, seq_len: torch.Tensor, stream=None, layer_hook=None):
+        """One decode step.  q: bf16 [layers][B][hq][128]; seq_len: int32 [B]
+        (rows present, including this step's appended row)."""
+        L = self._lib
+        st = kvsel._stream(stream)
+        cur, prev = self.cur, 1 - self.cur
+        sl = seq_len.data_ptr()
+        for l, (kind, src) in enumerate(self.plan(t)):
+            kv = self.kvs[l]
+            kv.c.seq_len = sl
+            qp = ctypes.c_void_p(q[l].data_ptr())
+            op = ctypes.c_void_p(self.out[l].data_ptr())
+            if layer_hook is not None:
+                layer_hook(l, kind, "begin")
+            if kind == "focal":
+                kvsel._check(L.kvsel_dense_attn(kv.ref(), qp, self.hq, self.scale, op, None,
+                                                ctypes.c_void_p(self.scores.data_ptr()), self.seg_len,
+                                                kvsel.NORM_SEGMENT, self.ws_ptr, self.ws_n, st))
+                warm = self.idx[l][prev].data_ptr() if (self.warm_start and t > 0) else None
+                kvsel._check(L.kvsel_topk(ctypes.c_void_p(self.scores.data_ptr()), self.seg_len, self.B * self.hkv,
+                                          self.seg_len, self.k, warm, ctypes.c_void_p(self.idx[l][cur].data_ptr()),
+                                          None, 0, st))
+            elif kind == "dense":
+                kvsel._check(L.kvsel_dense_attn(kv.ref(), qp, self.hq, self.scale, op, None, None, 0,
+                                                kvsel.NORM_SEGMENT, self.ws_ptr, self.ws_n, st))
+            else:
+                which, ls = src
+                buf = self.idx[ls][cur if which == "cur" else prev]
+                kvsel._check(L.kvsel_gather_attn(kv.ref(), qp, self.hq, self.scale,
+                                                 ctypes.c_void_p(buf.data_ptr()), self.k, op, None,
+                                                 self.ws_ptr, self.ws_n, st))
+            if layer_hook is not None:
+                layer_hook(l, kind, "end")
+        self.cur = prev   # this step's selection becomes "previous"
+
+    def selection(self, layer: int, previous: bool = False) -> torch.Tensor:
+        """Kept indices of a focal layer after the last step (or the step before)."""
+        return self.idx[layer][self.cur if previous else 1 - self.cur]

@@ -1,0 +1,304 @@
+"""Python binding of libkvsel (ctypes).
+
+Argument marshalling only: tensors become raw device pointers, the current
+torch stream becomes the hipStream_t, a non-zero status becomes KvselError.
+Every step of the path runs in the library's HIP kernels; nothing here
+computes.  PyTorch supplies device memory and streams.
+
+The binding fails loudly if libkvsel.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+
+REDUCE_GROUP, REDUCE_ALL = 0, 1
+NORM_SEGMENT, NORM_CONTEXT = 0, 1
+STATUS = {0: "KVSEL_OK", -1: "KVSEL_EINVAL", -2: "KVSEL_ENOSPC", -3: "KVSEL_EUNSUPPORTED", -4: "KVSEL_EHIP"}
+
+# every symbol the public header declares
+SYMBOLS = (
+    "kvsel_version", "kvsel_status_string", "kvsel_last_error",
+    "kvsel_score", "kvsel_score_workspace",
+    "kvsel_topk", "kvsel_topk_workspace",
+    "kvsel_gather_attn", "kvsel_attn_workspace",
+    "kvsel_dense_attn", "kvsel_gather_rows",
+)
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class KvDescC(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("max_seg_len", ctypes.c_int32), ("min_seg_len", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+        ("seg_begin", ctypes.c_void_p), ("seg_end", ctypes.c_void_p),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_DP = ctypes.POINTER(KvDescC)
+_I32, _I64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvsel.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libkvsel.so not found at {LIB_PATH}: build it with "
+                           "`python -m decode_focal_layer_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.kvsel_version.restype = _I32
+    L.kvsel_status_string.restype = ctypes.c_char_p
+    L.kvsel_status_string.argtypes = [_I32]
+    L.kvsel_last_error.restype = ctypes.c_char_p
+    L.kvsel_score.restype = _I32
+    L.kvsel_score.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]
+    L.kvsel_score_workspace.restype = _SZ
+    L.kvsel_score_workspace.argtypes = [_DP, _I32, _I32, _I32, _I32]
+    L.kvsel_topk.restype = _I32
+    L.kvsel_topk.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
+    L.kvsel_topk_workspace.restype = _SZ
+    L.kvsel_topk_workspace.argtypes = [_I32, _I32, _I32]
+    L.kvsel_gather_attn.restype = _I32
+    L.kvsel_gather_attn.argtypes = [_DP, _P, _I32, _F32, _P, _I32, _P, _P, _P, _SZ, _P]
+    L.kvsel_attn_workspace.restype = _SZ
+    L.kvsel_attn_workspace.argtypes = [_DP, _I32, _I32, _I32, _I32]
+    L.kvsel_dense_attn.restype = _I32
+    L.kvsel_dense_attn.argtypes = [_DP, _P, _I32, _F32, _P, _P, _P, _I64, _I32, _P, _SZ, _P]
+    L.kvsel_gather_rows.restype = _I32
+    L.kvsel_gather_rows.argtypes = [_P, _I64, _I64, _P, _I32, _I64, _I32, _P, _P]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise KvselError(status, lib().kvsel_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# descriptor and workspace
+# ---------------------------------------------------------------------------
+
+@dataclass
+class KV:
+    """A paged KV cache view.  Keeps the tensors alive while the C struct
+    holds their addresses."""
+    k_pool: torch.Tensor
+    v_pool: Optional[torch.Tensor]
+    block_table: torch.Tensor
+    seq_len: torch.Tensor
+    seg_begin: torch.Tensor
+    seg_end: torch.Tensor
+    max_seq_len: int
+    max_seg_len: int
+    min_seg_len: int = 0
+
+    def __post_init__(self):
+        _need(self.k_pool, torch.bfloat16, "k_pool")
+        if self.v_pool is not None:
+            _need(self.v_pool, torch.bfloat16, "v_pool")
+            if self.v_pool.shape != self.k_pool.shape:
+                raise ValueError("k_pool and v_pool shapes differ")
+        for n in ("block_table", "seq_len", "seg_begin", "seg_end"):
+            _need(getattr(self, n), torch.int32, n)
+        nb, hkv, blk, d = self.k_pool.shape
+        c = KvDescC()
+        c.batch = self.block_table.shape[0]
+        c.num_kv_heads = hkv
+        c.head_dim = d
+        c.block_size = blk
+        c.max_blocks_per_seq = self.block_table.shape[1]
+        c.max_seq_len = int(self.max_seq_len)
+        c.max_seg_len = int(self.max_seg_len)
+        c.min_seg_len = int(self.min_seg_len)
+        c.num_blocks = nb
+        c.k_pool = self.k_pool.data_ptr()
+        c.v_pool = self.v_pool.data_ptr() if self.v_pool is not None else None
+        c.block_table = self.block_table.data_ptr()
+        c.seq_len = self.seq_len.data_ptr()
+        c.seg_begin = self.seg_begin.data_ptr()
+        c.seg_end = self.seg_end.data_ptr()
+        self.c = c
+
+    @property
+    def batch(self):
+        return self.c.batch
+
+    @property
+    def hkv(self):
+        return self.c.num_kv_heads
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def with_seq_len(self, seq_len: torch.Tensor, max_seq_len: Optional[int] = None) -> "KV":
+        return KV(self.k_pool, self.v_pool, self.block_table, seq_len, self.seg_begin, self.seg_end,
+                  self.max_seq_len if max_seq_len is None else max_seq_len, self.max_seg_len, self.min_seg_len)
+
+
+class Workspace:
+    """Zero-filled device scratch, grown on demand (a grown buffer is zero-filled
+    again; the library leaves its counters at zero after every call)."""
+
+    def __init__(self, device="cuda", nbytes: int = 0):
+        self.device = device
+        self.buf = None
+        if nbytes:
+            self.ensure(nbytes)
+
+    def ensure(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256) + 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def ptr_and_size(self, nbytes: int):
+        b = self.ensure(nbytes)
+        addr = b.data_ptr()
+        pad = (-addr) % 256
+        return ctypes.c_void_p(addr + pad), b.numel() - pad
+
+
+_default_ws = {}
+
+
+def _ws(ws: Optional[Workspace], device) -> Workspace:
+    if ws is not None:
+        return ws
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C calls)
+# ---------------------------------------------------------------------------
+
+def version() -> int:
+    return lib().kvsel_version()
+
+
+def score_workspace(kv: KV, n_rows: int, num_q_heads: int, reduce: int, norm: int) -> int:
+    return lib().kvsel_score_workspace(kv.ref(), n_rows, num_q_heads, reduce, norm)
+
+
+def attn_workspace(kv: KV, num_q_heads: int, k: int, with_scores: bool = False, norm: int = NORM_SEGMENT) -> int:
+    return lib().kvsel_attn_workspace(kv.ref(), num_q_heads, k, int(with_scores), norm)
+
+
+def score(kv: KV, q: torch.Tensor, n_rows: int, num_q_heads: int, scale: float, reduce: int, norm: int,
+          causal: bool, pool_width: int, scores: torch.Tensor, ws: Optional[Workspace] = None, stream=None):
+    """kvsel_score.  q: bf16 [batch][n_rows][hq][128]; scores: fp32 [batch][hkv or 1][ld]."""
+    _need(q, torch.bfloat16, "q")
+    _need(scores, torch.float32, "scores")
+    w = _ws(ws, q.device)
+    p, n = w.ptr_and_size(score_workspace(kv, n_rows, num_q_heads, reduce, norm))
+    _check(lib().kvsel_score(kv.ref(), _ptr(q), n_rows, num_q_heads, scale, reduce, norm, int(causal),
+                             pool_width, _ptr(scores), scores.shape[-1], p, n, _stream(stream)))
+    return scores
+
+
+def topk(scores: torch.Tensor, n: int, k: int, idx: torch.Tensor, warm: Optional[torch.Tensor] = None,
+         stream=None):
+    """kvsel_topk.  scores: fp32 [..., ld] viewed as rows; idx: int32 [rows][k]."""
+    _need(scores, torch.float32, "scores")
+    _need(idx, torch.int32, "idx")
+    ld = scores.shape[-1]
+    rows = scores.numel() // ld
+    if idx.numel() != rows * k:
+        raise ValueError("idx must hold rows * k entries")
+    if warm is not None:
+        _need(warm, torch.int32, "warm")
+        if warm.numel() != rows * k:
+            raise ValueError("warm must hold rows * k entries")
+    _check(lib().kvsel_topk(_ptr(scores), ld, rows, n, k, _ptr(warm), _ptr(idx), None, 0, _stream(stream)))
+    return idx
+
+
+def gather_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, idx: Optional[torch.Tensor], k: int,
+                out: torch.Tensor, lse: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
+                stream=None):
+    """kvsel_gather_attn.  q: bf16 [batch][hq][128]; idx: int32 [batch][hkv][k]; out fp32 [batch][hq][128]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+        if idx.numel() != kv.batch * kv.hkv * k:
+            raise ValueError("idx must be [batch][num_kv_heads][k]")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    w = _ws(ws, q.device)
+    p, n = w.ptr_and_size(attn_workspace(kv, num_q_heads, k))
+    _check(lib().kvsel_gather_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(idx), k, _ptr(out), _ptr(lse),
+                                   p, n, _stream(stream)))
+    return out
+
+
+def dense_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: torch.Tensor,
+               lse: Optional[torch.Tensor] = None, seg_scores: Optional[torch.Tensor] = None,
+               norm: int = NORM_SEGMENT, ws: Optional[Workspace] = None, stream=None):
+    """kvsel_dense_attn, optionally fused with the focal scores [batch][hkv][ld]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    ld = 0
+    if seg_scores is not None:
+        _need(seg_scores, torch.float32, "seg_scores")
+        ld = seg_scores.shape[-1]
+    w = _ws(ws, q.device)
+    p, n = w.ptr_and_size(attn_workspace(kv, num_q_heads, -1, seg_scores is not None, norm))
+    _check(lib().kvsel_dense_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(out), _ptr(lse), _ptr(seg_scores),
+                                  ld, norm, p, n, _stream(stream)))
+    return out
+
+
+def gather_rows(src: torch.Tensor, idx: Optional[torch.Tensor], n_idx: int, tail_begin: int, n_tail: int,
+                dst: torch.Tensor, stream=None):
+    """kvsel_gather_rows: dst = src[idx[:n_idx]] ++ src[tail_begin : tail_begin + n_tail] (rows)."""
+    if not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous")
+    row_bytes = src[0].numel() * src.element_size()
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+    _check(lib().kvsel_gather_rows(_ptr(src), row_bytes, src.shape[0], _ptr(idx), n_idx, tail_begin, n_tail,
+                                   _ptr(dst), _stream(stream)))
+    return dst

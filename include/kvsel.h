@@ -1,0 +1,240 @@
+/*
+ * kvsel.h -- libkvsel: attention-score-guided KV token selection followed by
+ * sparse decode attention, for AMD Instinct MI355X (gfx950).
+ *
+ * The path this library runs, per decode step:
+ *   1. a focal layer scores the query against the cached keys of a candidate
+ *      segment (visual tokens in FastOCR; the long prompt in FastKV) and sums
+ *      the softmax probabilities over the query heads that share a kv head;
+ *   2. the k highest-scoring tokens are kept (ties to the lower index);
+ *   3. the other layers attend only over the kept tokens plus every token
+ *      outside the candidate segment (text, layout, recent or suffix rows);
+ *      the full cache stays in memory and only the attended subset changes.
+ *
+ * Sources:
+ *   FastOCR: Dynamic Visual Fixation via KV Cache Pruning -- technical
+ *     summary, Methodology: Focal-Guided Pruning (focal-layer scoring over
+ *     the full cache, top image tokens at kept ratio tau, propagation to
+ *     non-focal layers) and Cross-Step Fixation Reuse (warm start from the
+ *     previous step's set); Significance (the full cache is retained).
+ *   FastKV: Decoupling of Context Reduction and KV Cache Compression --
+ *     section 2A Token-Selective Propagation (saliency from a recent window
+ *     of queries, averaged; top tokens plus the window tokens propagate)
+ *     and section 2B Decoupled KV Retention (a per-layer decode budget).
+ *   HPD-Parsing wiki -- method item 2, shared-prefix KV reuse and context
+ *     isolation (branches read one prefix zero-copy; each attends to the
+ *     shared context, its own prefix and its own history).
+ *
+ * Conventions (every entry point):
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains device memory; scratch comes from a
+ *     caller workspace sized by the matching kvsel_*_workspace() call.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns.  Ordering is the stream's.
+ *   - Argument errors are found on the host before any HIP call and return
+ *     KVSEL_EINVAL / KVSEL_ENOSPC / KVSEL_EUNSUPPORTED with nothing enqueued;
+ *     the text is in kvsel_last_error() (thread-local).  A failed launch
+ *     returns KVSEL_EHIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation.
+ *   - Device-resident integers (seq_len, segment bounds, block ids, kept
+ *     indices) are clamped or skipped by the kernels when out of range, so a
+ *     bad value gives a wrong result, never an out-of-bounds access.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Workspace: the byte count from kvsel_*_workspace(); the buffer must be
+ *     256-byte aligned and ZERO-FILLED ONCE before its first use.  Its first
+ *     64 KiB hold split counters that only the attention calls touch and
+ *     that every call leaves at zero when its kernels finish, so a workspace
+ *     can be reused by any later call on the same stream.  Two calls that may
+ *     run at the same time need separate workspaces.
+ *   - batch * num_kv_heads <= 16384 (KVSEL_EUNSUPPORTED otherwise).
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define KVSEL_API __attribute__((visibility("default")))
+#else
+#define KVSEL_API
+#endif
+
+typedef int32_t kvsel_status;
+#define KVSEL_OK            0
+#define KVSEL_EINVAL       (-1)  /* bad argument                                  */
+#define KVSEL_ENOSPC       (-2)  /* workspace too small                           */
+#define KVSEL_EUNSUPPORTED (-3)  /* head_dim != 128, block_size != 16, group > 8  */
+#define KVSEL_EHIP         (-4)  /* a HIP launch failed                           */
+
+#define KVSEL_VERSION 1
+
+#define KVSEL_REDUCE_GROUP 0     /* one score per (sequence, kv head)            */
+#define KVSEL_REDUCE_ALL   1     /* one score per (sequence): summed over heads  */
+
+#define KVSEL_NORM_SEGMENT 0     /* softmax over the candidate segment only      */
+#define KVSEL_NORM_CONTEXT 1     /* softmax over every row the query can see     */
+
+typedef void *kvsel_stream;      /* hipStream_t */
+
+/*
+ * Paged KV cache descriptor (non-owning).
+ *
+ * K and V pools are bf16 [num_blocks][num_kv_heads][block_size][head_dim]:
+ * one (block, kv head) is a contiguous block_size*head_dim*2 = 4 KiB run.
+ * Logical row j of sequence b is row j % block_size of physical block
+ * block_table[b * max_blocks_per_seq + j / block_size].  Rows [0, seq_len[b])
+ * are present.  Sequences that share a prefix list the same physical block
+ * ids (zero-copy; HPD wiki, method item 2).  A contiguous cache is the
+ * identity table.
+ *
+ * Candidate segment: rows [seg_begin[b], seg_end[b]) are scored and
+ * selectable; every row outside it is always attended by gather attention.
+ */
+typedef struct {
+  int32_t batch;               /* sequences (or branches)                        */
+  int32_t num_kv_heads;        /* H_kv                                           */
+  int32_t head_dim;            /* must be 128                                    */
+  int32_t block_size;          /* must be 16                                     */
+  int32_t max_blocks_per_seq;  /* row stride of block_table                      */
+  int32_t max_seq_len;         /* host upper bound of seq_len[] (grid sizing);   */
+                               /* <= max_blocks_per_seq * block_size             */
+  int32_t max_seg_len;         /* host upper bound of seg_end[] - seg_begin[]     */
+  int32_t min_seg_len;         /* host lower bound of seg_end[] - seg_begin[]     */
+                               /* (0 if unknown); sizes the gather launch        */
+  int64_t num_blocks;          /* physical blocks in each pool                   */
+  const uint16_t *k_pool;      /* bf16, device                                   */
+  const uint16_t *v_pool;      /* bf16, device (may be NULL for kvsel_score)     */
+  const int32_t *block_table;  /* [batch][max_blocks_per_seq], device            */
+  const int32_t *seq_len;      /* [batch], device                                */
+  const int32_t *seg_begin;    /* [batch], device                                */
+  const int32_t *seg_end;      /* [batch], device                                */
+} kvsel_kv_desc;
+
+/* Version of this header's ABI (KVSEL_VERSION). */
+KVSEL_API int32_t kvsel_version(void);
+/* Static text for a status code. */
+KVSEL_API const char *kvsel_status_string(kvsel_status s);
+/* Text of the last error on the calling thread ("" if none). */
+KVSEL_API const char *kvsel_last_error(void);
+
+/*
+ * kvsel_score -- token saliency over the candidate segment.
+ * (FastOCR Focal-Guided Pruning: focal-layer attention over the full cache;
+ *  FastKV 2A: attention weights from a recent window of queries, averaged.)
+ *
+ * q: bf16 [batch][n_rows][num_q_heads][128].  n_rows == 1 is a decode query
+ * at position seq_len[b]-1 (it sees every present row).  n_rows > 1 is a
+ * window: row r is the query of position seq_len[b] - n_rows + r and, when
+ * `causal`, sees rows <= its position.  Query head h reads kv head
+ * h / (num_q_heads / num_kv_heads).
+ *
+ * Each (row, head) takes a softmax of its logits (q . k) * scale over the
+ * segment (NORM_SEGMENT) or over every row it sees (NORM_CONTEXT); the
+ * probabilities of the segment tokens are summed over the rows and the heads
+ * of a kv head's group (REDUCE_GROUP) or over all heads (REDUCE_ALL).  If
+ * pool_width > 1 (odd), the sums are then averaged over a centred window of
+ * pool_width tokens, zero-padded at the segment ends, always divided by
+ * pool_width.
+ *
+ * scores: fp32 [batch][num_kv_heads or 1][ld], entry i is segment token
+ * seg_begin[b] + i; entries past the segment length are not written.
+ * Requires ld >= max_seg_len.  n_rows in [1, 64].  NORM_SEGMENT requires
+ * n_rows == 1 (a window is always context-normalised).  n_rows > 1 uses
+ * MFMA on the (n_rows x group) query rows of a kv head, which must be at
+ * most 32 (KVSEL_EUNSUPPORTED otherwise).  Workspace:
+ * kvsel_score_workspace(kv, n_rows, num_q_heads, reduce, norm).
+ */
+KVSEL_API kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_rows,
+                         int32_t num_q_heads, float scale, int32_t reduce, int32_t norm,
+                         int32_t causal, int32_t pool_width, float *scores, int64_t ld,
+                         void *ws, size_t ws_bytes, kvsel_stream stream);
+KVSEL_API size_t kvsel_score_workspace(const kvsel_kv_desc *kv, int32_t n_rows, int32_t num_q_heads,
+                             int32_t reduce, int32_t norm);
+
+/*
+ * kvsel_topk -- exact top-k per row.
+ * (FastOCR Focal-Guided Pruning: keep the top tau of image tokens; FastKV 2A:
+ *  keep the top-ranked tokens; Cross-Step Fixation Reuse: warm start.)
+ *
+ * scores: fp32 [rows][ld], the first n entries of each row are candidates.
+ * idx: int32 [rows][k], the k indices (in [0, n)) of the largest scores,
+ * ascending.  Among exactly equal scores the lower index is kept.  Scores
+ * must not be NaN.
+ *
+ * warm_idx: NULL, or int32 [rows][k], a previous selection (strictly
+ * ascending, in [0, n)).  Then theta = the lowest current score among the
+ * warm indices and only tokens scoring >= theta are ranked; at least k of
+ * them do, so the result is identical to the cold call.  A row whose warm
+ * indices are not strictly ascending and in range is ranked cold.
+ * Requires 1 <= k <= n <= ld, rows >= 1.
+ */
+KVSEL_API kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, int32_t n, int32_t k,
+                        const int32_t *warm_idx, int32_t *idx, void *ws, size_t ws_bytes,
+                        kvsel_stream stream);
+KVSEL_API size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k);
+
+/*
+ * kvsel_gather_attn -- decode attention over the kept rows.
+ * (FastOCR Cross-Layer Propagation: non-focal layers attend only to the
+ *  pruned set; FastKV 2B: decode over the retained KV.)
+ *
+ * q: bf16 [batch][num_q_heads][128], the decode query of position
+ * seq_len[b]-1.  idx: int32 [batch][num_kv_heads][k], segment-relative
+ * indices (row = seg_begin[b] + idx); an index outside the segment is
+ * skipped.  For every q head, attention over R = {kept rows} U [0, seg_begin)
+ * U [seg_end, seq_len): out = sum_R softmax((q . k_i) * scale) v_i.
+ * Duplicate indices are attended once per occurrence: pass distinct indices.
+ *
+ * out: fp32 [batch][num_q_heads][128].  lse: NULL or fp32
+ * [batch][num_q_heads], natural-log softmax normaliser (-inf if R is empty,
+ * with out = 0).  k may be 0 (only the always-kept rows).
+ */
+KVSEL_API kvsel_status kvsel_gather_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
+                               float scale, const int32_t *idx, int32_t k, float *out, float *lse,
+                               void *ws, size_t ws_bytes, kvsel_stream stream);
+/* Workspace bytes for kvsel_gather_attn with budget k (k >= 0), or for
+ * kvsel_dense_attn when k < 0 (with_scores: seg_scores will be passed; norm:
+ * its normalisation).  0 if the descriptor or head count is invalid. */
+KVSEL_API size_t kvsel_attn_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads, int32_t k,
+                            int32_t with_scores, int32_t norm);
+
+/*
+ * kvsel_dense_attn -- decode attention over every present row, optionally
+ * fused with the focal score of the candidate segment.
+ * (FastOCR Focal-Guided Pruning: only focal layers attend over the full KV
+ *  cache, and select from that attention.)
+ *
+ * q, out, lse: as kvsel_gather_attn, with R = [0, seq_len).
+ * seg_scores: NULL, or fp32 [batch][num_kv_heads][ld]: the same scores as
+ * kvsel_score(n_rows = 1, REDUCE_GROUP, norm, pool_width = 1), taken from the
+ * same pass over K.  Requires ld >= max_seg_len when seg_scores is set.
+ * Workspace: kvsel_attn_workspace(kv, num_q_heads, -1, seg_scores != NULL,
+ * norm).
+ */
+KVSEL_API kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
+                              float scale, float *out, float *lse, float *seg_scores, int64_t ld,
+                              int32_t norm, void *ws, size_t ws_bytes, kvsel_stream stream);
+
+/*
+ * kvsel_gather_rows -- dst[j] = src[idx[j]] for j < n_idx, then
+ * dst[n_idx + t] = src[tail_begin + t] for t < n_tail; rows of row_bytes
+ * bytes, copied bit-exactly.
+ * (FastKV 2A: the top-ranked tokens plus the window tokens are propagated.)
+ *
+ * row_bytes must be a positive multiple of 16; src, dst 16-byte aligned.
+ * Indices outside [0, n_src_rows) produce a zero row.
+ */
+KVSEL_API kvsel_status kvsel_gather_rows(const void *src, int64_t row_bytes, int64_t n_src_rows,
+                               const int32_t *idx, int32_t n_idx, int64_t tail_begin,
+                               int32_t n_tail, void *dst, kvsel_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host before any HIP call (so these run without
+a GPU: a call that reached HIP would return KVSEL_EHIP instead of the code
+asserted here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_focal_layer_amd import kvsel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kvsel.h")
+EINVAL, ENOSPC, EUNSUP = -1, -2, -3
+FAKE = 1 << 20        # a 256-byte aligned address that is never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvsel.LIB_PATH):
+        from decode_focal_layer_amd import build
+        build.build()
+    return kvsel.lib()
+
+
+def declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"KVSEL_API\s+[\w\s\*]*?\b(kvsel_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) == 11
+    assert sorted(kvsel.SYMBOLS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.kvsel_version() == 1
+    assert L.kvsel_status_string(-2) == b"workspace too small"
+
+
+def desc(**over):
+    d = kvsel.KvDescC()
+    vals = dict(batch=2, num_kv_heads=8, head_dim=128, block_size=16, max_blocks_per_seq=10, max_seq_len=150,
+                max_seg_len=100, min_seg_len=100, num_blocks=20, k_pool=FAKE, v_pool=FAKE + 4096,
+                block_table=FAKE, seq_len=FAKE, seg_begin=FAKE, seg_end=FAKE)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    return d
+
+
+def gather(L, d, hq=16, q=FAKE, k=5, idx=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, scale=0.088):
+    return L.kvsel_gather_attn(ctypes.byref(d), q, hq, scale, idx, k, out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=64), EUNSUP), (dict(block_size=32), EUNSUP), (dict(batch=0), EINVAL),
+    (dict(num_kv_heads=0), EINVAL), (dict(max_blocks_per_seq=0), EINVAL), (dict(max_seq_len=161), EINVAL),
+    (dict(max_seg_len=151), EINVAL), (dict(min_seg_len=101), EINVAL), (dict(num_blocks=0), EINVAL),
+    (dict(k_pool=0), EINVAL), (dict(v_pool=0), EINVAL), (dict(block_table=0), EINVAL), (dict(seq_len=0), EINVAL),
+    (dict(seg_begin=0), EINVAL), (dict(seg_end=0), EINVAL), (dict(k_pool=FAKE + 8), EINVAL),
+    (dict(batch=4096, num_kv_heads=8), EUNSUP), (dict(num_blocks=1 << 28), EUNSUP),
+])
+def test_gather_attn_rejects_bad_descriptor(L, over, code):
+    assert gather(L, desc(**over)) == code
+    assert L.kvsel_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=12), EINVAL), (dict(hq=24), EUNSUP), (dict(hq=0), EINVAL), (dict(q=0), EINVAL),
+    (dict(q=FAKE + 2), EINVAL), (dict(out=0), EINVAL), (dict(k=-1), EINVAL), (dict(idx=0), EINVAL),
+    (dict(scale=float("inf")), EINVAL), (dict(ws=0), EINVAL), (dict(ws=FAKE + 64), EINVAL),
+    (dict(ws_bytes=64), ENOSPC),
+])
+def test_gather_attn_rejects_bad_args(L, kw, code):
+    assert gather(L, desc(), **kw) == code
+
+
+def test_dense_attn_checks(L):
+    d = desc()
+    r = L.kvsel_dense_attn(ctypes.byref(d), FAKE, 16, 0.088, FAKE, None, FAKE, 99, 0, FAKE, 1 << 30, None)
+    assert r == EINVAL          # ld < max_seg_len
+    r = L.kvsel_dense_attn(ctypes.byref(d), FAKE, 16, 0.088, FAKE, None, FAKE, 100, 7, FAKE, 1 << 30, None)
+    assert r == EINVAL          # bad norm
+    r = L.kvsel_dense_attn(ctypes.byref(d), FAKE, 16, 0.088, FAKE, None, FAKE, 100, 0, FAKE, 16, None)
+    assert r == ENOSPC
+    need = L.kvsel_attn_workspace(ctypes.byref(d), 16, -1, 1, 0)
+    assert need > L.kvsel_attn_workspace(ctypes.byref(d), 16, -1, 0, 0) > 0
+    assert L.kvsel_attn_workspace(ctypes.byref(desc(head_dim=64)), 16, -1, 0, 0) == 0
+
+
+def score(L, d, q=FAKE, n_rows=1, hq=16, reduce=0, norm=0, causal=1, pool=1, scores=FAKE, ld=100,
+          ws=FAKE, ws_bytes=1 << 30):
+    return L.kvsel_score(ctypes.byref(d), q, n_rows, hq, 0.088, reduce, norm, causal, pool, scores, ld, ws,
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_rows=0), EINVAL), (dict(n_rows=65), EINVAL), (dict(reduce=2), EINVAL), (dict(norm=2), EINVAL),
+    (dict(n_rows=8, norm=0), EINVAL), (dict(n_rows=8, norm=1, hq=64), EUNSUP), (dict(pool=2), EINVAL),
+    (dict(pool=0), EINVAL), (dict(ld=99), EINVAL), (dict(scores=0), EINVAL), (dict(q=0), EINVAL),
+    (dict(ws_bytes=8), ENOSPC), (dict(n_rows=8, norm=1, ws_bytes=8), ENOSPC),
+])
+def test_score_rejects(L, kw, code):
+    assert score(L, desc(v_pool=0), **kw) == code
+
+
+def test_score_workspace_sizes(L):
+    d = desc(v_pool=0)
+    assert L.kvsel_score_workspace(ctypes.byref(d), 1, 16, 0, 0) > 0
+    assert L.kvsel_score_workspace(ctypes.byref(d), 8, 32, 1, 1) > 0
+    assert L.kvsel_score_workspace(ctypes.byref(d), 0, 16, 0, 0) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(scores=0), EINVAL), (dict(idx=0), EINVAL), (dict(rows=0), EINVAL), (dict(k=0), EINVAL),
+    (dict(k=11, n=10), EINVAL), (dict(n=20, ld=10), EINVAL),
+])
+def test_topk_rejects(L, args, code):
+    a = dict(scores=FAKE, ld=10, rows=4, n=10, k=3, warm=None, idx=FAKE)
+    a.update(args)
+    assert L.kvsel_topk(a["scores"], a["ld"], a["rows"], a["n"], a["k"], a["warm"], a["idx"], None, 0, None) == code
+    assert L.kvsel_topk_workspace(4, 10, 3) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(src=0), EINVAL), (dict(dst=0), EINVAL), (dict(src=FAKE + 4), EINVAL), (dict(row_bytes=24), EINVAL),
+    (dict(row_bytes=0), EINVAL), (dict(n_idx=-1), EINVAL), (dict(n_tail=-1), EINVAL), (dict(idx=0), EINVAL),
+])
+def test_gather_rows_rejects(L, args, code):
+    a = dict(src=FAKE, row_bytes=8192, n_src=100, idx=FAKE, n_idx=5, tail=90, n_tail=3, dst=FAKE)
+    a.update(args)
+    r = L.kvsel_gather_rows(a["src"], a["row_bytes"], a["n_src"], a["idx"], a["n_idx"], a["tail"], a["n_tail"],
+                            a["dst"], None)
+    assert r == code

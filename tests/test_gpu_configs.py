@@ -1,0 +1,167 @@
+"""Workload-level parity: the whole path (score -> head sum -> top-k ->
+sparse attention, with the focal-layer schedule) against the oracle on the
+seeded synthetic workloads.
+
+Kept sets are accepted when they differ from the oracle's only inside the
+1e-6 relative tie band around the k-th oracle score.  Such a set is then a
+correct selection, and the layers that reuse it are checked against the
+oracle's attention over that same validated set (with the oracle's own set
+whenever the two agree, which is the common case).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle as O
+from synth import gen
+from tests.gpu_util import BAND, assert_attn, log_case, need_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def kvsel():
+    from decode_focal_layer_amd import kvsel as m
+    return m
+
+
+def focal_kvs(w, t=0):
+    kv = kvsel()
+    cfg = w.cfg
+    max_len = int(w.seq_len_np.max())
+    return [kv.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[t], w.seg_begin, w.seg_end,
+                  max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+            for l in range(cfg.layers)]
+
+
+def test_c0_full():
+    """One decode step at the C0 shape: dense attention, focal scores, top-179,
+    gathered sparse attention over the kept visual rows plus the 512 text rows."""
+    kv = kvsel()
+    cfg = synth.C0
+    w = gen.make_focal(cfg, DEV)
+    k = cfg.k
+    assert k == 179
+    kvd = focal_kvs(w)[0]
+    q = w.q[0, 0].contiguous()
+    out = torch.zeros((1, 16, 128), dtype=torch.float32, device=DEV)
+    lse = torch.zeros((1, 16), dtype=torch.float32, device=DEV)
+    sc = torch.zeros((1, 8, cfg.n_visual), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((1, 8, k), dtype=torch.int32, device=DEV)
+    out_s = torch.zeros_like(out)
+    kv.dense_attn(kvd, q, 16, cfg.scale, out, lse, seg_scores=sc)
+    kv.topk(sc, cfg.n_visual, k, idx)
+    kv.gather_attn(kvd, q, 16, cfg.scale, idx, k, out_s)
+    torch.cuda.synchronize()
+    kc, vc, qc = w.k_pool[0].cpu(), w.v_pool[0].cpu(), q.cpu()
+    n = cfg.prefix_len
+    patch = gen.patch_tokens(int(w.patches[0, 0, 0]), int(w.patches[0, 0, 1]), cfg.grid_cols, *cfg.patch)
+    hits = 0
+    for g in range(8):
+        Kl = O.logical_rows(kc, w.table_np[0], g, n)
+        Vl = O.logical_rows(vc, w.table_np[0], g, n)
+        qg = O.widen(qc[0, 2 * g:2 * g + 2])
+        ref, rl = O.dense_attention(qg, Kl, Vl, cfg.scale)
+        assert_attn(out[0, 2 * g:2 * g + 2].cpu().numpy(), ref, f"dense g{g}")
+        s = O.focal_scores(qg, Kl, 0, cfg.n_visual, cfg.scale)
+        gpu_s = sc[0, g].cpu().numpy()
+        assert np.abs(gpu_s - s).max() / s.max() < 2e-6
+        gi = idx[0, g].cpu().numpy()
+        ok, nd = O.tie_band_check(gi, s, k, BAND)
+        assert ok, f"g{g}: kept set differs outside the tie band ({nd})"
+        hits += len(np.intersect1d(gi, patch))
+        refs, _ = O.attention(qg, Kl, Vl, O.kept_rows(gi, 0, cfg.n_visual, n), cfg.scale)
+        assert_attn(out_s[0, 2 * g:2 * g + 2].cpu().numpy(), refs, f"sparse g{g}")
+    print("patch tokens among the kept:", hits, "of", 8 * len(patch))
+
+
+def run_schedule(cfg, w, check_every=1):
+    """Run all steps through FocalDecoder; check every layer of every step."""
+    from decode_focal_layer_amd.decode import FocalDecoder
+    kv = kvsel()
+    kvs = focal_kvs(w)
+    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, warm_start=cfg.warm_start,
+                       device=DEV)
+    kc = [w.k_pool[l].cpu() for l in range(cfg.layers)]
+    vc = [w.v_pool[l].cpu() for l in range(cfg.layers)]
+    G = cfg.group
+    sets = {}          # (t, focal layer) -> validated kept sets [B][hkv][k]
+    worst = 0.0
+    for t in range(cfg.steps):
+        log_case(cfg.name, "step", t)
+        dec.step(t, w.q[t], w.seq_len[t])
+        torch.cuda.synchronize()
+        outs = dec.out.cpu().numpy()
+        qc = w.q[t].cpu()
+        plan = O.focal_layer_plan(cfg.layers, cfg.focal, t)
+        for f in cfg.focal:
+            sets[(t, f)] = dec.selection(f).cpu().numpy()
+        if t % check_every:
+            continue
+        for e in plan:
+            l = e[1]
+            for b in range(cfg.batch):
+                n = int(w.seq_len_np[t, b])
+                for g in range(cfg.hkv):
+                    Kl = O.logical_rows(kc[l], w.table_np[b], g, n)
+                    Vl = O.logical_rows(vc[l], w.table_np[b], g, n)
+                    qg = O.widen(qc[l, b, g * G:(g + 1) * G])
+                    if e[0] in ("dense", "focal"):
+                        ref, _ = O.dense_attention(qg, Kl, Vl, cfg.scale)
+                        if e[0] == "focal":
+                            s = O.focal_scores(qg, Kl, 0, cfg.n_visual, cfg.scale)
+                            ok, nd = O.tie_band_check(sets[(t, l)][b, g], s, cfg.k, BAND)
+                            assert ok, f"t{t} l{l} b{b} g{g}: kept set outside the tie band ({nd})"
+                    else:
+                        _, ts, ls = e[1:]
+                        rows = O.kept_rows(sets[(ts, ls)][b, g], 0, cfg.n_visual, n)
+                        ref, _ = O.attention(qg, Kl, Vl, rows, cfg.scale)
+                    ma, _ = assert_attn(outs[l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
+                    worst = max(worst, ma)
+    print(cfg.name, "worst max-abs error", worst)
+    return dec, sets
+
+
+def test_c1_schedule_small():
+    cfg = synth.small(synth.C1, batch=3, layers=6, steps=4, focal=(2, 4), grid_rows=12, grid_cols=32, n_always=80)
+    w = gen.make_focal(cfg, DEV)
+    run_schedule(cfg, w)
+
+
+def test_c4_branches_small_and_shared_prefix_equals_private_copy():
+    cfg = synth.small(synth.C4, batch=6, layers=5, steps=3, focal=(1, 3), grid_rows=8, grid_cols=32,
+                      n_always=32, suffix_range=(3, 40))
+    w = gen.make_focal(cfg, DEV)
+    dec, sets = run_schedule(cfg, w)
+    out_shared = dec.out.clone()
+    # private copy of the prefix for every branch: same rows, different blocks
+    pref = cfg.prefix_len // 16
+    B = cfg.batch
+    tab = w.table_np.copy()
+    extra = []
+    for b in range(B):
+        new = w.num_blocks + b * pref + np.arange(pref)
+        tab[b, :pref] = new
+        extra.append(new)
+    kp = [torch.cat([w.k_pool[l]] + [w.k_pool[l][:pref]] * B) for l in range(cfg.layers)]
+    vp = [torch.cat([w.v_pool[l]] + [w.v_pool[l][:pref]] * B) for l in range(cfg.layers)]
+    w2 = gen.FocalWorkload(cfg=cfg, k_pool=kp, v_pool=vp, block_table=torch.from_numpy(tab).to(DEV), q=w.q,
+                           seq_len=w.seq_len, seg_begin=w.seg_begin, seg_end=w.seg_end, table_np=tab,
+                           seq_len_np=w.seq_len_np, patches=w.patches, suffix_len=w.suffix_len,
+                           num_blocks=w.num_blocks + B * pref, max_blocks=w.max_blocks)
+    from decode_focal_layer_amd.decode import FocalDecoder
+    dec2 = FocalDecoder(focal_kvs(w2), cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV)
+    for t in range(cfg.steps):
+        dec2.step(t, w.q[t], w.seq_len[t])
+    torch.cuda.synchronize()
+    assert torch.equal(dec2.out, out_shared)
+    for f in cfg.focal:
+        assert torch.equal(dec2.selection(f), dec.selection(f))

@@ -1,0 +1,274 @@
+"""Per-entry-point parity of libkvsel against the oracle on small seeded
+shapes that span several tiles and ragged tails, with edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests.gpu_util import (assert_attn, attn_errors, cpu_pool, log_case, need_gpu, random_paged, rel_err, BAND)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def K():
+    from decode_focal_layer_amd import kvsel
+    return kvsel
+
+
+def make_kv(rng, batch, hkv, lens, segs, max_len=None):
+    kvsel = K()
+    max_len = max_len or max(lens)
+    kp, vp, table = random_paged(rng, batch, hkv, max_len, DEV)
+    seg_b = np.array([s[0] for s in segs], dtype=np.int32)
+    seg_e = np.array([s[1] for s in segs], dtype=np.int32)
+    kv = kvsel.KV(kp, vp, torch.from_numpy(table).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                  torch.from_numpy(seg_b).to(DEV), torch.from_numpy(seg_e).to(DEV),
+                  max_seq_len=max_len, max_seg_len=int((seg_e - seg_b).max()), min_seg_len=int((seg_e - seg_b).min()))
+    return kv, cpu_pool(kp), cpu_pool(vp), table
+
+
+ATTN_CASES = [(1, 1, [1]), (2, 2, [15, 16]), (4, 1, [17]), (8, 2, [300, 33]), (2, 3, [4095, 1000, 2]),
+              (2, 1, [8193]), (4, 2, [1, 1000])]
+
+
+@pytest.mark.parametrize("G,batch,lens", ATTN_CASES)
+def test_dense_and_gather_attention(G, batch, lens):
+    kvsel = K()
+    rng = np.random.default_rng(G * 100 + len(lens))
+    hkv = 2
+    hq = hkv * G
+    segs = [(min(3, n), max(min(3, n), n - min(5, n // 3))) for n in lens]
+    kv, kc, vc, table = make_kv(rng, batch, hkv, lens, segs)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(DEV)
+    out = torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.zeros((batch, hq), dtype=torch.float32, device=DEV)
+    log_case("dense", G, lens)
+    kvsel.dense_attn(kv, q, hq, SCALE, out, lse)
+    seg_lens = [s1 - s0 for s0, s1 in segs]
+    kmax = max(1, min(seg_lens))
+    idx_np = np.zeros((batch, hkv, kmax), dtype=np.int32)
+    for b in range(batch):
+        for g in range(hkv):
+            sl = seg_lens[b]
+            pick = np.sort(rng.choice(sl, size=min(kmax, sl), replace=False)) if sl else np.array([], np.int64)
+            row = np.full(kmax, -1, dtype=np.int32)       # -1: skipped (outside the segment)
+            row[: len(pick)] = pick
+            idx_np[b, g] = row
+    idx = torch.from_numpy(idx_np).to(DEV)
+    out_s = torch.zeros_like(out)
+    lse_s = torch.zeros_like(lse)
+    log_case("gather", G, lens, kmax)
+    kvsel.gather_attn(kv, q, hq, SCALE, idx, kmax, out_s, lse_s)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    for b in range(batch):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            Vl = O.logical_rows(vc, table[b], g, lens[b])
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref, rl = O.dense_attention(qg, Kl, Vl, SCALE)
+            assert_attn(out[b, g * G:(g + 1) * G].cpu().numpy(), ref, f"dense b{b} g{g}")
+            assert np.abs(lse[b, g * G:(g + 1) * G].cpu().numpy() - rl).max() < 1e-4
+            sel = idx_np[b, g][idx_np[b, g] >= 0]
+            rows = O.kept_rows(sel, segs[b][0], segs[b][1], lens[b])
+            ref_s, rl_s = O.attention(qg, Kl, Vl, rows, SCALE)
+            assert_attn(out_s[b, g * G:(g + 1) * G].cpu().numpy(), ref_s, f"gather b{b} g{g}")
+            assert np.abs(lse_s[b, g * G:(g + 1) * G].cpu().numpy() - rl_s).max() < 1e-4
+
+
+def test_gather_full_budget_equals_dense_and_empty_rows():
+    kvsel = K()
+    rng = np.random.default_rng(11)
+    lens = [700, 64]
+    segs = [(0, 700), (0, 64)]
+    kv, kc, vc, table = make_kv(rng, 2, 2, lens, segs)
+    hq = 4
+    q = torch.randn((2, hq, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    d = torch.zeros((2, hq, 128), dtype=torch.float32, device=DEV)
+    kvsel.dense_attn(kv, q, hq, SCALE, d)
+    # k = segment length: every row kept
+    idx = torch.full((2, 2, 700), -1, dtype=torch.int32)
+    idx[0] = torch.arange(700, dtype=torch.int32)
+    idx[1, :, :64] = torch.arange(64, dtype=torch.int32)
+    s = torch.zeros_like(d)
+    kvsel.gather_attn(kv, q, hq, SCALE, idx.to(DEV), 700, s)
+    torch.cuda.synchronize()
+    assert attn_errors(s.cpu().numpy(), d.cpu().numpy())[0] < 1e-5
+    # k = 0 and nothing outside the segment: no rows -> out = 0, lse = -inf
+    z = torch.ones_like(d)
+    lse = torch.zeros((2, hq), dtype=torch.float32, device=DEV)
+    kvsel.gather_attn(kv, q, hq, SCALE, None, 0, z, lse)
+    torch.cuda.synchronize()
+    assert torch.all(z == 0) and torch.all(torch.isinf(lse) & (lse < 0))
+
+
+@pytest.mark.parametrize("n,k,mode", [(1, 1, "rand"), (5, 3, "ties"), (64, 64, "rand"), (3584, 179, "rand"),
+                                      (6400, 320, "ties"), (3072, 154, "equal"), (12288, 600, "rand"),
+                                      (12289, 7, "ties"), (32760, 6554, "rand"), (40000, 2048, "ties")])
+def test_topk_exact(n, k, mode):
+    kvsel = K()
+    rng = np.random.default_rng(n + k)
+    rows = 3
+    if mode == "rand":
+        s = rng.random((rows, n)).astype(np.float32) * 1e-3
+    elif mode == "ties":
+        s = (rng.integers(0, 50, size=(rows, n)) / 50).astype(np.float32)
+    else:
+        s = np.full((rows, n), 1.0 / n, dtype=np.float32)
+    ld = n + 5
+    sp = np.zeros((rows, ld), dtype=np.float32)
+    sp[:, :n] = s
+    sp[:, n:] = 99.0       # past n: never selected
+    st = torch.from_numpy(sp).to(DEV)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    log_case("topk", n, k, mode)
+    kvsel.topk(st, n, k, idx)
+    # warm start from a random valid set, and from an invalid one (ranked cold)
+    warm = np.stack([np.sort(rng.choice(n, size=k, replace=False)) for _ in range(rows)]).astype(np.int32)
+    if k > 1:
+        warm[1, 0], warm[1, 1] = warm[1, 1], warm[1, 0]      # not ascending
+    idx_w = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    kvsel.topk(st, n, k, idx_w, warm=torch.from_numpy(warm).to(DEV))
+    torch.cuda.synchronize()
+    got, got_w = idx.cpu().numpy(), idx_w.cpu().numpy()
+    for r in range(rows):
+        want = O.topk(s[r], k)
+        assert np.array_equal(got[r], want), f"row {r}"
+        assert np.array_equal(got_w[r], want), f"warm row {r}"
+
+
+@pytest.mark.parametrize("norm,reduce,pool", [(0, 0, 1), (1, 0, 1), (0, 1, 1), (1, 0, 7), (0, 1, 7)])
+def test_decode_scores(norm, reduce, pool):
+    kvsel = K()
+    rng = np.random.default_rng(norm * 10 + reduce * 3 + pool)
+    lens = [900, 1500]
+    segs = [(50, 850), (0, 1400)]
+    kv, kc, vc, table = make_kv(rng, 2, 4, lens, segs)
+    G, hq = 2, 8
+    q = torch.randn((2, 1, hq, 128), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    nout = 4 if reduce == 0 else 1
+    ld = 1410
+    sc = torch.full((2, nout, ld), -1.0, dtype=torch.float32, device=DEV)
+    log_case("score", norm, reduce, pool)
+    kvsel.score(kv, q, 1, hq, SCALE, reduce, norm, True, pool, sc)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    qc = q.cpu()
+    nm = "segment" if norm == 0 else "context"
+    worst = 0.0
+    for b in range(2):
+        s0, s1 = segs[b]
+        parts = []
+        for g in range(4):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            parts.append(O.focal_scores(O.widen(qc[b, 0, g * G:(g + 1) * G]), Kl, s0, s1, SCALE, nm))
+        refs = parts if reduce == 0 else [np.sum(parts, axis=0)]
+        for o, ref in enumerate(refs):
+            if pool > 1:
+                ref = O.avg_pool(ref, pool)
+            worst = max(worst, rel_err(got[b, o, : s1 - s0], ref))
+            assert np.all(got[b, o, s1 - s0:] == -1.0)
+    print("max relative score error", worst)
+    assert worst < 2e-6
+
+
+def test_dense_fused_scores_match_score_call():
+    kvsel = K()
+    rng = np.random.default_rng(21)
+    lens = [4096, 3000]
+    segs = [(0, 3584), (0, 2500)]
+    kv, kc, vc, table = make_kv(rng, 2, 8, lens, segs)
+    hq = 16
+    q = torch.randn((2, hq, 128), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
+    out = torch.zeros((2, hq, 128), dtype=torch.float32, device=DEV)
+    s1 = torch.zeros((2, 8, 3584), dtype=torch.float32, device=DEV)
+    s2 = torch.zeros_like(s1)
+    kvsel.dense_attn(kv, q, hq, SCALE, out, seg_scores=s1)
+    kvsel.score(kv, q.view(2, 1, hq, 128), 1, hq, SCALE, 0, 0, True, 1, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1[0], s2[0]) and torch.equal(s1[1, :, :2500], s2[1, :, :2500])
+
+
+@pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True)])
+def test_window_scores(G, W, reduce, causal):
+    kvsel = K()
+    rng = np.random.default_rng(G * 7 + W)
+    hkv = 3
+    hq = hkv * G
+    lens = [2085, 1200]
+    segs = [(0, 2085 - W), (0, 1200 - W)]
+    kv, kc, vc, table = make_kv(rng, 2, hkv, lens, segs)
+    q = torch.randn((2, W, hq, 128), generator=torch.Generator().manual_seed(13)).to(torch.bfloat16).to(DEV)
+    nout = hkv if reduce == 0 else 1
+    ld = 2100
+    sc = torch.full((2, nout, ld), -1.0, dtype=torch.float32, device=DEV)
+    log_case("window", G, W, reduce, causal)
+    kvsel.score(kv, q, W, hq, SCALE, reduce, 1, causal, 7, sc)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    qc = q.cpu()
+    worst = 0.0
+    for b in range(2):
+        s0, s1 = segs[b]
+        parts = []
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            qw = O.widen(qc[b, :, g * G:(g + 1) * G])
+            parts.append(O.window_scores(qw, Kl, s0, s1, SCALE, causal))
+        refs = parts if reduce == 0 else [np.sum(parts, axis=0)]
+        for o, ref in enumerate(refs):
+            ref = O.avg_pool(ref, 7)
+            worst = max(worst, rel_err(got[b, o, : s1 - s0], ref))
+            assert np.all(got[b, o, s1 - s0:] == -1.0)
+            k = max(1, (s1 - s0) // 5)
+            idx = torch.zeros((1, k), dtype=torch.int32, device=DEV)
+            kvsel.topk(sc[b, o:o + 1, :].contiguous(), s1 - s0, k, idx)
+            ok, nd = O.tie_band_check(idx[0].cpu().numpy(), ref, k, BAND)
+            assert ok, f"kept set outside tie band ({nd} differ)"
+    print("max relative window-score error", worst)
+    assert worst < 2e-6
+
+
+def test_gather_rows_exact():
+    kvsel = K()
+    src = torch.randint(-(1 << 15), 1 << 15, (300, 4096), dtype=torch.int16).view(torch.bfloat16).to(DEV)
+    idx = torch.tensor([5, 0, 299, 17, 17, 400, -1], dtype=torch.int32, device=DEV)
+    dst = torch.full((7 + 8, 4096), 3.0, dtype=torch.bfloat16, device=DEV)
+    kvsel.gather_rows(src, idx, 7, 292, 8, dst)
+    torch.cuda.synchronize()
+    s, d = src.cpu().view(torch.int16), dst.cpu().view(torch.int16)
+    want = O.gather_rows(s.numpy(), [5, 0, 299, 17, 17], 292, 8)
+    assert np.array_equal(d[[0, 1, 2, 3, 4]].numpy(), want[:5])
+    assert np.array_equal(d[7:].numpy(), want[5:])
+    assert torch.all(d[5:7] == 0)    # out-of-range indices give zero rows
+
+
+def test_determinism():
+    kvsel = K()
+    rng = np.random.default_rng(5)
+    lens = [3000, 2000, 2500]
+    segs = [(0, 2500), (100, 1900), (0, 2500)]
+    kv, _, _, _ = make_kv(rng, 3, 8, lens, segs)
+    q = torch.randn((3, 16, 128), generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(DEV)
+    res = []
+    for _ in range(2):
+        out = torch.zeros((3, 16, 128), dtype=torch.float32, device=DEV)
+        sc = torch.zeros((3, 8, 2500), dtype=torch.float32, device=DEV)
+        kvsel.dense_attn(kv, q, 16, SCALE, out, seg_scores=sc)
+        idx = torch.zeros((3, 8, 100), dtype=torch.int32, device=DEV)
+        kvsel.topk(sc, 1800, 100, idx)
+        o2 = torch.zeros_like(out)
+        kvsel.gather_attn(kv, q, 16, SCALE, idx, 100, o2)
+        torch.cuda.synchronize()
+        res.append((out.cpu(), sc.cpu(), idx.cpu(), o2.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
