@@ -1,0 +1,241 @@
+"""Benchmark: FastOCR-style decode (28 layers, batch 32, 16 q / 8 kv heads,
+6400 visual + 1024 text tokens, focal layers 3 and 14, top-320 per kv head,
+warm-started top-k, 64-step cycle) through libkvsel on one MI355X.
+
+A step is one decode step of all 28 layers over the batch: 2 focal layers
+(dense attention fused with the focal scores, then top-k) and 26 layers of
+gathered sparse attention (layers 0-2 reuse the previous step's deepest
+focal set; at the first step of the cycle they attend densely).  Inputs (the
+whole paged cache, every step's queries and sequence lengths) are resident
+in HBM before timing starts.
+
+Prints one JSON line.  --gpus N with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_bytes(cfg, t: int, batch: int):
+    """Bytes the method must move at step t of the cycle, per layer kind.
+
+    K/V rows read once each (2 x 256 B per row per kv head), the query, the
+    output, the focal scores (written by the scorer, read by top-k) and the
+    kept indices (written by top-k, read by each sparse layer)."""
+    hkv, hq, d = cfg.hkv, cfg.hq, cfg.head_dim
+    n = cfg.prefix_len + t + 1
+    row = 2 * d * 2                            # K + V bytes per row per kv head
+    q_b = batch * hq * d * 2
+    out_b = batch * hq * d * 4
+    idx_b = batch * hkv * cfg.k * 4
+    sc_b = batch * hkv * cfg.n_visual * 4
+    dense = batch * hkv * n * row + q_b + out_b
+    focal = dense + 2 * sc_b + idx_b           # scores written + read, indices written
+    sparse = batch * hkv * (cfg.k + n - cfg.n_visual) * row + q_b + out_b + idx_b
+    return dense, focal, sparse
+
+
+def step_bytes(cfg, t, batch):
+    dense, focal, sparse = algorithmic_bytes(cfg, t, batch)
+    first = min(cfg.focal)
+    n_focal = len(cfg.focal)
+    n_pre = first
+    n_sparse = cfg.layers - n_focal - (n_pre if t == 0 else 0)
+    return n_focal * focal + (n_pre * dense if t == 0 else 0) + n_sparse * sparse
+
+
+def cpu_baseline(w, cfg, t_sample: int, n_seq: int):
+    """The oracle on the host cores for the same step, on n_seq of the batch's
+    sequences (all 28 layers, every kv head): returns steps/s scaled to the
+    whole batch."""
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    G = cfg.group
+    n = int(w.seq_len_np[t_sample, 0])
+    # inputs for the sample, copied to host memory before timing
+    kc = [w.k_pool[l][w.block_table[:n_seq].flatten().long()].cpu() for l in range(cfg.layers)]
+    vc = [w.v_pool[l][w.block_table[:n_seq].flatten().long()].cpu() for l in range(cfg.layers)]
+    mb = w.max_blocks
+    local_table = np.arange(n_seq * mb).reshape(n_seq, mb)
+    qc = w.q[t_sample].cpu()
+    plan = O.focal_layer_plan(cfg.layers, cfg.focal, t_sample)
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        for b in range(n_seq):
+            for g in range(cfg.hkv):
+                sets = {}
+                # focal layers first: their sets feed the other layers; the layers before the
+                # first focal layer take this step's deepest set in place of the previous
+                # step's (same amount of work)
+                for e in plan:
+                    if e[0] != "focal":
+                        continue
+                    l = e[1]
+                    K = O.logical_rows(kc[l], local_table[b], g, n)
+                    V = O.logical_rows(vc[l], local_table[b], g, n)
+                    qg = O.widen(qc[l, b, g * G:(g + 1) * G])
+                    sets[l] = O.topk(O.focal_scores(qg, K, 0, cfg.n_visual, cfg.scale), cfg.k)
+                    O.dense_attention(qg, K, V, cfg.scale)
+                for e in plan:
+                    if e[0] == "focal":
+                        continue
+                    l = e[1]
+                    K = O.logical_rows(kc[l], local_table[b], g, n)
+                    V = O.logical_rows(vc[l], local_table[b], g, n)
+                    qg = O.widen(qc[l, b, g * G:(g + 1) * G])
+                    if e[0] == "dense":
+                        O.dense_attention(qg, K, V, cfg.scale)
+                    else:
+                        O.attention(qg, K, V, O.kept_rows(sets[e[3]], 0, cfg.n_visual, n), cfg.scale)
+        dt = time.perf_counter() - t0
+    steps_per_s = (n_seq / cfg.batch) / dt
+    return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"decode step t={t_sample} of the cycle, {n_seq} of {cfg.batch} sequences, all "
+                      f"{cfg.layers} layers and {cfg.hkv} kv heads ({dt:.1f} s of host time), scaled to the "
+                      f"full batch; {cores} host cores available"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle sample (0: skip)")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this hot path runs on one GPU; multi-GPU sharding is a design note only "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.decode import FocalDecoder
+
+    kvsel.lib()
+    dev = "cuda"
+    cfg = synth.C1
+    t_gen = time.perf_counter()
+    w = gen.make_focal(cfg, dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] generated C1 inputs in {t_gen:.1f} s "
+          f"({sum(p.numel() for p in w.k_pool) * 4 / 1e9:.1f} GB of K/V)", file=sys.stderr, flush=True)
+    max_len = int(w.seq_len_np.max())
+    kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+           for l in range(cfg.layers)]
+    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, warm_start=True, device=dev)
+    T = cfg.steps
+
+    def run(i0, count, hook=None):
+        for i in range(i0, i0 + count):
+            t = i % T
+            dec.step(t, w.q[t], w.seq_len[t], layer_hook=hook)
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+
+    # per-launch events around every sparse (gathered) attention launch
+    ev = []
+    plan_kind = {}
+
+    def hook(l, kind, phase):
+        if kind != "sparse":
+            return
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        ev.append((phase, e))
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    run(args.warmup, args.steps, None if args.no_kernel_events else hook)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+    ms_per_step = ms / args.steps
+    steps_per_s = 1000.0 / ms_per_step
+
+    total_bytes = sum(step_bytes(cfg, (args.warmup + i) % T, cfg.batch) for i in range(args.steps))
+    gbs = total_bytes / (ms / 1e3) / 1e9
+
+    roof = None
+    if ev:
+        durs = [ev[i][1].elapsed_time(ev[i + 1][1]) for i in range(0, len(ev), 2)]
+        avg_ms = float(np.mean(durs))
+        # algorithmic bytes per sparse launch, averaged over the timed steps
+        per = []
+        for i in range(args.steps):
+            t = (args.warmup + i) % T
+            n_sparse = cfg.layers - len(cfg.focal) - (min(cfg.focal) if t == 0 else 0)
+            per += [algorithmic_bytes(cfg, t, cfg.batch)[2]] * n_sparse
+        bpl = float(np.mean(per))
+        ach = bpl / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "attn_split_kernel<2> (gathered sparse attention)",
+                "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(bpl),
+                "launches_timed": len(durs)}
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        cpu = cpu_baseline(w, cfg, 1, args.cpu_seqs)
+
+    line = {
+        "metric": "decode attn steps/s (score + top-k + sparse attention, 28 layers)",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c1_fastocr_decode: 28 layers, batch 32, 16q/8kv heads, head_dim 128, "
+                               "6400 visual (80x80) + 1024 text tokens, focal layers {3,14}, top-320 per kv head, "
+                               "64-step cycle, bf16 KV with fp32 accumulation",
+                   "global_batch": cfg.batch, "seq_len": cfg.prefix_len, "parallelism": "single GPU"},
+        "tokens_per_s": round(steps_per_s * cfg.batch, 1),
+        "hbm_gbs_algorithmic": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_step_avg": int(total_bytes / args.steps),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,9 +117,9 @@ AttnArgs attn_args(const kvsel_kv_desc *kv, const uint16_t *q, int32_t hq, float
   return a;
 }
 
-NormArgs norm_args(const kvsel_kv_desc *kv, int32_t hq, int heads_per_out, int n_out, int32_t norm, float scale,
-                   const float *logits, int64_t ld_logits) {
-  NormArgs n{};
+SelArgs sel_args(const kvsel_kv_desc *kv, int32_t hq, int heads_per_out, int n_out, int32_t norm, float scale,
+                 const float *logits, int64_t ld_logits) {
+  SelArgs n{};
   n.logits = logits;
   n.ld_logits = ld_logits;
   n.seq_len = kv->seq_len;
@@ -241,10 +241,43 @@ kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_
   hipError_t e = launch_attn(a, kv->batch, G, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "dense_attn launch");
   if (seg_scores == nullptr) return ok();
-  NormArgs n = norm_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, a.logits, p.ld_logits);
+  SelArgs n = sel_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, a.logits, p.ld_logits);
   n.scores = seg_scores;
   n.ld = ld;
   return hip_status(launch_focal_norm(n, kv->batch, (hipStream_t)stream), "focal score launch");
+}
+
+kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale, float *out,
+                              float *lse, int32_t norm, int32_t k, const int32_t *warm_idx, int32_t *idx,
+                              float *seg_scores, int64_t ld, void *ws, size_t ws_bytes, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr || idx == nullptr) return fail(KVSEL_EINVAL, "out and idx are required");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (norm != KVSEL_NORM_SEGMENT && norm != KVSEL_NORM_CONTEXT) return fail(KVSEL_EINVAL, "bad norm %d", norm);
+  if (k < 1) return fail(KVSEL_EINVAL, "k must be >= 1");
+  if (kv->max_seg_len > kSelMaxSeg)
+    return fail(KVSEL_EUNSUPPORTED, "max_seg_len %d > %d: use kvsel_dense_attn + kvsel_topk", kv->max_seg_len,
+                kSelMaxSeg);
+  if (seg_scores != nullptr && (ld < kv->max_seg_len || ld < 1)) return fail(KVSEL_EINVAL, "ld must be >= max_seg_len");
+  const int mode = logit_mode_of(true, norm);
+  const AttnPlan p = attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, kv->max_seq_len > 0 ? kv->max_seq_len : 1,
+                               mode, kv->max_seg_len, kv->max_seq_len);
+  if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
+  AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, p, (char *)ws, out, lse, mode);
+  a.dense = 1;
+  hipError_t e = launch_attn(a, kv->batch, G, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "focal attention launch");
+  SelArgs n = sel_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, a.logits, p.ld_logits);
+  n.scores = seg_scores;
+  n.ld = seg_scores != nullptr ? ld : 0;
+  n.k = k;
+  n.warm = warm_idx;
+  n.idx = idx;
+  return hip_status(launch_focal_select(n, kv->batch, (hipStream_t)stream), "focal select launch");
 }
 
 // ------------------------------------------------------------------------
@@ -326,8 +359,8 @@ kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_r
   const AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, sp.lp, w, nullptr, nullptr, mode);
   hipError_t e = launch_logits(a, kv->batch, G, rows, s);
   if (e != hipSuccess) return hip_status(e, "score logits launch");
-  NormArgs n = norm_args(kv, num_q_heads, reduce == KVSEL_REDUCE_GROUP ? G : num_q_heads, n_out, norm, scale, a.logits,
-                         sp.lp.ld_logits);
+  SelArgs n = sel_args(kv, num_q_heads, reduce == KVSEL_REDUCE_GROUP ? G : num_q_heads, n_out, norm, scale, a.logits,
+                       sp.lp.ld_logits);
   if (pool_width == 1) {
     n.scores = scores;
     n.ld = ld;

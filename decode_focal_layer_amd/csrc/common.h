@@ -44,6 +44,15 @@ __device__ __forceinline__ float rescale(float m, float mnew) {
   return m == -INFINITY ? 0.f : fast_exp2(m - mnew);
 }
 
+// 2^x to about one fp32 ulp of relative error for x in the fp32 exponent
+// range: the fp32 part of x goes through the hardware exp2 and the remainder
+// through the first-order term 2^xl ~ 1 + xl ln 2 (|xl| < 2^-24 |x|).
+__device__ __forceinline__ double exp2_acc(double x) {
+  const float xh = (float)x;
+  const double xl = x - (double)xh;
+  return (double)__builtin_amdgcn_exp2f(xh) * (1.0 + xl * 0.6931471805599453);
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // ---- block reductions (blockDim.x a multiple of 64, <= 1024) ----

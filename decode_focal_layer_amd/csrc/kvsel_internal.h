@@ -22,7 +22,7 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 // ---------------------------------------------------------------------------
 constexpr int kAttnThreads = 256;
 constexpr int kAttnRowsPerIter = 64;   // 16 lane groups x 4 rows
-constexpr int kAttnMaxRps = 1024;
+constexpr int kAttnMaxRps = 8192;   // rows resolved into LDS per work-group (32 KiB)
 constexpr int kRec = 160;              // floats per partial record: acc[128], m, l, pad (640 B)
 
 struct AttnPlan {
@@ -46,7 +46,7 @@ struct AttnArgs {
   int32_t dense;        // 1: every row [0, seq_len); 0: gather
   float scale_log2;     // softmax scale * log2(e)
   int32_t rps, nsplit;
-  uint32_t *counters;   // [batch * hkv], zero on entry, zero on exit
+  uint32_t *counters;   // reserved region at the start of the workspace (unused)
   float *rec;           // [batch][hq][nsplit][kRec]
   float *out, *lse;
   float *logits;        // [batch][hq][ld_logits] raw q.k dots, or null
@@ -60,21 +60,29 @@ hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s);
 hipError_t launch_logits(const AttnArgs &a, int batch, int group, int max_rows, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// focal score normalisation: logits -> group-summed probabilities
+// focal score normalisation (logits -> head-summed probabilities), alone or
+// fused with the top-k of each (sequence, kv head)
 // ---------------------------------------------------------------------------
-struct NormArgs {
-  const float *logits;   // [batch][hq][ld_logits]
+constexpr int kSelMaxSeg = 12288;   // fused selection: candidate segment held in LDS
+
+struct SelArgs {
+  const float *logits;   // [batch][hq][ld_logits] raw q.k dots
   int64_t ld_logits;
   const int32_t *seq_len, *seg_begin, *seg_end;
   int32_t cap_rows;      // max_blocks * block (clamp for seq_len)
   int32_t hq, heads_per_out, n_out;   // output rows per sequence = n_out
   int32_t norm;          // KVSEL_NORM_*
   double scale;
-  float *scores;         // fp32 [batch][n_out][ld] (null: write scores64 instead)
-  double *scores64;      // fp64 [batch][n_out][ld64]
-  int64_t ld, ld64;
+  float *scores;         // fp32 [batch][n_out][ld], or null
+  int64_t ld;
+  double *scores64;      // fp64 [batch][n_out][ld64] (norm kernel, when scores is null)
+  int64_t ld64;
+  int32_t k;             // fused selection: budget, warm start, output
+  const int32_t *warm;
+  int32_t *idx;          // [batch][n_out][k]
 };
-hipError_t launch_focal_norm(const NormArgs &a, int batch, hipStream_t s);
+hipError_t launch_focal_norm(const SelArgs &a, int batch, hipStream_t s);
+hipError_t launch_focal_select(const SelArgs &a, int batch, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // group sum + average pool over fp64 partial scores

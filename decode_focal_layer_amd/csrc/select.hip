@@ -1,0 +1,129 @@
+// Focal score normalisation, alone or fused with the exact top-k, one
+// work-group per (sequence, output row).
+//
+// FastOCR (technical summary, Focal-Guided Pruning): a focal layer ranks the
+// image tokens by the attention its queries give them and keeps the top tau;
+// Cross-Step Fixation Reuse: the previous step's set warm-starts the choice.
+//
+// Input: raw fp32 q.k dot products of bf16 data (exact products, fp32 sums),
+// written by the focal attention pass or the logits kernel and read back from
+// L2.  Per head: the max, then the softmax normaliser in fp64; per token: the
+// probabilities of the heads summed in fp64 and rounded to fp32 once.  Both
+// kernels share this code and reduction order, so their scores agree bit for
+// bit.  The fused kernel keeps the scores in LDS as order-preserving keys and
+// selects with radix_topk.
+#include "common.h"
+#include "kvsel_internal.h"
+#include "radix.h"
+
+namespace kvsel {
+
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kMaxHeadsPerOut = 64;
+
+struct FocalRow {
+  int cnt, off, seg;
+};
+
+__device__ __forceinline__ FocalRow focal_row(const SelArgs &a, int b, int64_t ld_out) {
+  FocalRow r;
+  const int n = clampi(a.seq_len[b], 0, a.cap_rows);
+  const int s0 = clampi(a.seg_begin[b], 0, n);
+  const int s1 = clampi(a.seg_end[b], s0, n);
+  // logit rows: segment mode holds rows [s0, s1) at 0, context mode rows [0, n) at 0
+  r.cnt = (int)min((int64_t)(a.norm == KVSEL_NORM_SEGMENT ? s1 - s0 : n), a.ld_logits);
+  r.off = a.norm == KVSEL_NORM_SEGMENT ? 0 : s0;
+  r.seg = (int)min((int64_t)min(s1 - s0, r.cnt - r.off), ld_out);
+  return r;
+}
+
+// per head of the output row: s_m = max logit, s_iz = 1 / sum 2^((x - max) c)
+__device__ void focal_stats(const SelArgs &a, int b, int o, const FocalRow &r, double c, double *s_m, double *s_iz,
+                            float *redf, double *redd) {
+  for (int hh = 0; hh < a.heads_per_out; ++hh) {
+    const float *row = a.logits + ((size_t)b * a.hq + o * a.heads_per_out + hh) * a.ld_logits;
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < r.cnt; i += kSelThreads) mx = fmaxf(mx, row[i]);
+    mx = block_max(mx, redf);
+    double z = 0.0;
+    for (int i = threadIdx.x; i < r.cnt; i += kSelThreads) z += exp2_acc(((double)row[i] - (double)mx) * c);
+    z = block_sum_d(z, redd);
+    if (threadIdx.x == 0) {
+      s_m[hh] = (double)mx;
+      s_iz[hh] = z > 0.0 ? 1.0 / z : 0.0;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ double focal_score(const SelArgs &a, const float *lg, int i, double c, const double *s_m,
+                                              const double *s_iz) {
+  double sc = 0.0;
+  for (int hh = 0; hh < a.heads_per_out; ++hh)
+    sc += exp2_acc(((double)lg[(size_t)hh * a.ld_logits + i] - s_m[hh]) * c) * s_iz[hh];
+  return sc;
+}
+
+// grid (output rows, sequences): scores only
+__global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
+  __shared__ double s_m[kMaxHeadsPerOut], s_iz[kMaxHeadsPerOut];
+  __shared__ float s_redf[kSelThreads / 64];
+  __shared__ double s_redd[kSelThreads / 64];
+  const int o = blockIdx.x, b = blockIdx.y;
+  const FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : a.ld64);
+  const double c = a.scale * 1.4426950408889634;
+  focal_stats(a, b, o, r, c, s_m, s_iz, s_redf, s_redd);
+  const float *lg = a.logits + ((size_t)b * a.hq + o * a.heads_per_out) * a.ld_logits + r.off;
+  for (int i = threadIdx.x; i < r.seg; i += kSelThreads) {
+    const double sc = focal_score(a, lg, i, c, s_m, s_iz);
+    if (a.scores != nullptr)
+      a.scores[((size_t)b * a.n_out + o) * a.ld + i] = (float)sc;
+    else
+      a.scores64[((size_t)b * a.n_out + o) * a.ld64 + i] = sc;
+  }
+}
+
+// grid (kv heads, sequences): scores + top-k of the group
+__global__ __launch_bounds__(kSelThreads) void focal_select_kernel(SelArgs a) {
+  constexpr int NT = kSelThreads;
+  __shared__ uint32_t s_keys[kSelMaxSeg];
+  __shared__ RadixShared<NT> sh;
+  __shared__ double s_m[8], s_iz[8];
+  __shared__ float s_redf[NT / 64];
+  __shared__ double s_redd[NT / 64];
+  const int g = blockIdx.x, b = blockIdx.y;
+  FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : (int64_t)kSelMaxSeg);
+  r.seg = min(r.seg, kSelMaxSeg);
+  const double c = a.scale * 1.4426950408889634;
+  focal_stats(a, b, g, r, c, s_m, s_iz, s_redf, s_redd);
+  const float *lg = a.logits + ((size_t)b * a.hq + g * a.heads_per_out) * a.ld_logits + r.off;
+  float *so = a.scores != nullptr ? a.scores + ((size_t)b * a.n_out + g) * a.ld : nullptr;
+  for (int i = threadIdx.x; i < r.seg; i += NT) {
+    const float f = (float)focal_score(a, lg, i, c, s_m, s_iz);
+    s_keys[i] = okey(f);
+    if (so != nullptr) so[i] = f;
+  }
+  __syncthreads();
+  auto key = [&](int i) -> uint32_t { return s_keys[i]; };
+  const size_t row = (size_t)b * a.n_out + g;
+  const uint32_t theta = a.warm != nullptr ? warm_theta<NT>(key, a.warm + row * a.k, r.seg, a.k, sh) : 0u;
+  radix_topk<NT>(key, r.seg, a.k, theta, a.idx + row * a.k, sh);
+}
+
+}  // namespace
+
+hipError_t launch_focal_norm(const SelArgs &a, int batch, hipStream_t s) {
+  if (a.heads_per_out > kMaxHeadsPerOut) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(focal_norm_kernel, dim3(a.n_out, batch), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_focal_select(const SelArgs &a, int batch, hipStream_t s) {
+  if (a.heads_per_out > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(focal_select_kernel, dim3(a.n_out, batch), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

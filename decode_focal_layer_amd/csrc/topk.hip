@@ -5,18 +5,12 @@
 // image tokens; Cross-Step Fixation Reuse: the previous step's set is a warm
 // start.  FastKV 2A: keep the top-ranked tokens.
 //
-// One work-group per row.  Scores are mapped to order-preserving uint32 keys
-// (sign-magnitude float -> unsigned order).  A radix select over the key
-// (digits of 11, 11 and 10 bits, LDS histograms) finds the k-th largest key T
-// and how many keys equal to T are kept; a final pass over the row in index
-// order keeps every key > T and the first of those equal to T, using wave
-// ballots for the running position, so the output comes out ascending.
-//
-// Warm start: theta = the lowest key at the warm indices.  At least k keys
-// reach theta, so the k-th largest does too; only keys >= theta enter the
-// histograms.  Rows that fit in LDS are staged there once.
+// One work-group per row.  Rows that fit are staged in LDS as order-preserving
+// keys once; longer rows are read from global memory on every pass.  The
+// selection itself is radix_topk (radix.h).
 #include "common.h"
 #include "kvsel_internal.h"
+#include "radix.h"
 
 namespace kvsel {
 
@@ -24,172 +18,26 @@ namespace {
 
 constexpr int kLdsKeys = 12288;   // rows up to this length are staged in LDS (48 KiB)
 
-__device__ __forceinline__ uint32_t okey(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-template <int NT>
-struct TopkShared {
-  uint32_t hist[2048];
-  uint32_t wsum[NT / 64];
-  uint32_t wsum2[NT / 64];
-  uint32_t misc[4];
-};
-
-// exclusive scan of one value per thread, in thread order; total returned
-template <int NT>
-__device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t *ws, uint32_t &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) ws[w] = x;
-  __syncthreads();
-  uint32_t pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const uint32_t t = ws[i];
-    pre += i < w ? t : 0u;
-    tot += t;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + x - v;
-}
-
 template <int NT, bool IN_LDS>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
-  extern __shared__ uint32_t s_keys[];
-  __shared__ TopkShared<NT> sh;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n = a.n, k = a.k;
+  __shared__ uint32_t s_keys[IN_LDS ? kLdsKeys : 1];
+  __shared__ RadixShared<NT> sh;
+  const int row = blockIdx.x;
   const float *src = a.scores + (size_t)row * a.ld;
-
   if (IN_LDS) {
-    for (int i = tid; i < n; i += NT) s_keys[i] = okey(src[i]);
+    for (int i = threadIdx.x; i < a.n; i += NT) s_keys[i] = okey(src[i]);
     __syncthreads();
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
-
-  // ---- warm threshold ----
-  uint32_t theta = 0;
-  if (a.warm != nullptr) {
-    const int32_t *wi = a.warm + (size_t)row * k;
-    uint32_t bad = 0, mn = 0xffffffffu;
-    for (int j = tid; j < k; j += NT) {
-      const int x = wi[j];
-      if (x < 0 || x >= n) {
-        bad = 1;
-      } else {
-        if (j + 1 < k && wi[j + 1] <= x) bad = 1;
-        mn = min(mn, key(x));
-      }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      bad |= __shfl_xor(bad, o);
-      mn = min(mn, (uint32_t)__shfl_xor(mn, o));
-    }
-    if (lane == 0) {
-      sh.wsum[w] = bad;
-      sh.wsum2[w] = mn;
-    }
-    __syncthreads();
-    uint32_t b2 = 0, m2 = 0xffffffffu;
-    for (int i = 0; i < NT / 64; ++i) {
-      b2 |= sh.wsum[i];
-      m2 = min(m2, sh.wsum2[i]);
-    }
-    __syncthreads();
-    theta = b2 ? 0u : m2;
-  }
-
-  // ---- radix select of the k-th largest key among keys >= theta ----
-  uint32_t prefix = 0, pmask = 0;
-  int krem = k;
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kBits[3] = {11, 11, 10};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = kShift[pass], nb = 1 << kBits[pass];
-    for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t x = key(i);
-      if (x >= theta && (x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    // thread t owns bins [t*per, (t+1)*per); count of bins above its range
-    const int per = nb / NT;
-    uint32_t c = 0;
-    for (int i = 0; i < per; ++i) c += sh.hist[tid * per + i];
-    uint32_t total;
-    const uint32_t below = excl_scan<NT>(c, sh.wsum, total);
-    const uint32_t above = total - below - c;
-    if (above < (uint32_t)krem && (uint32_t)krem <= above + c) {
-      uint32_t run = above;
-      for (int i = per - 1; i >= 0; --i) {
-        const uint32_t hcount = sh.hist[tid * per + i];
-        if (run + hcount >= (uint32_t)krem) {
-          sh.misc[0] = (uint32_t)(tid * per + i);
-          sh.misc[1] = run;
-          break;
-        }
-        run += hcount;
-      }
-    }
-    __syncthreads();
-    prefix |= sh.misc[0] << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    krem -= (int)sh.misc[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t keq = (uint32_t)krem;   // keys equal to T to keep (>= 1)
-
-  // ---- ordered output ----
-  int32_t *dst = a.idx + (size_t)row * k;
-  uint32_t written = 0, eq_seen = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int base = 0; base < n && written < (uint32_t)k; base += NT) {
-    const int i = base + tid;
-    const uint32_t x = i < n ? key(i) : 0u;
-    const bool gt = i < n && x > T;
-    const bool eq = i < n && x == T;
-    const uint64_t meq = __ballot(eq);
-    if (lane == 0) sh.wsum[w] = (uint32_t)__popcll(meq);
-    __syncthreads();
-    uint32_t eq_pre = 0, eq_tot = 0;
-    for (int j = 0; j < NT / 64; ++j) {
-      eq_pre += j < w ? sh.wsum[j] : 0u;
-      eq_tot += sh.wsum[j];
-    }
-    eq_pre += (uint32_t)__popcll(meq & lt);
-    const bool take = gt || (eq && eq_seen + eq_pre < keq);
-    const uint64_t mt = __ballot(take);
-    if (lane == 0) sh.wsum2[w] = (uint32_t)__popcll(mt);
-    __syncthreads();
-    uint32_t t_pre = 0, t_tot = 0;
-    for (int j = 0; j < NT / 64; ++j) {
-      t_pre += j < w ? sh.wsum2[j] : 0u;
-      t_tot += sh.wsum2[j];
-    }
-    t_pre += (uint32_t)__popcll(mt & lt);
-    if (take && written + t_pre < (uint32_t)k) dst[written + t_pre] = i;
-    written += t_tot;
-    eq_seen += eq_tot;
-    __syncthreads();
-  }
+  const uint32_t theta = a.warm != nullptr ? warm_theta<NT>(key, a.warm + (size_t)row * a.k, a.n, a.k, sh) : 0u;
+  radix_topk<NT>(key, a.n, a.k, theta, a.idx + (size_t)row * a.k, sh);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.n <= kLdsKeys) {
-    hipLaunchKernelGGL((topk_kernel<256, true>), dim3(a.rows), dim3(256), (size_t)a.n * 4, s, a);
+    hipLaunchKernelGGL((topk_kernel<1024, true>), dim3(a.rows), dim3(1024), 0, s, a);
   } else {
     hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(a.rows), dim3(1024), 0, s, a);
   }

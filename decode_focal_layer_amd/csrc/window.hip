@@ -35,15 +35,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kWinThreads = 256;
-constexpr double kLn2 = 0.6931471805599453;
-
-// 2^x for x <= 0 to about one fp32 ulp of relative error: the fp32 part of x
-// goes through the hardware exp2, the remainder through its first-order term.
-__device__ __forceinline__ double exp2_acc(double x) {
-  const float xh = (float)x;
-  const double xl = x - (double)xh;
-  return (double)__builtin_amdgcn_exp2f(xh) * (1.0 + xl * kLn2);
-}
 
 __device__ __forceinline__ uint32_t win_phys(const WinArgs &a, int b, int g, int row) {
   const int blk = a.block_table[(size_t)b * a.max_blocks + (row >> 4)];

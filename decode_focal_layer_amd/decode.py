@@ -26,7 +26,7 @@ from . import kvsel
 
 class FocalDecoder:
     def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, k: int, focal: Sequence[int], scale: float,
-                 seg_len: int, warm_start: bool = True, device="cuda", keep_outputs: bool = True):
+                 seg_len: int, warm_start: bool = True, device="cuda", keep_scores: bool = False):
         self.kvs = list(kvs)
         self.L = len(self.kvs)
         self.hq = num_q_heads
@@ -39,7 +39,8 @@ class FocalDecoder:
         B, hkv = kv0.batch, kv0.hkv
         self.B, self.hkv = B, hkv
         self.device = device
-        self.scores = torch.empty((B, hkv, seg_len), dtype=torch.float32, device=device)
+        self.keep_scores = keep_scores
+        self.scores = torch.empty((B, hkv, seg_len), dtype=torch.float32, device=device) if keep_scores else None
         # two selection buffers per focal layer: this step's and the previous step's
         self.idx = {f: [torch.zeros((B, hkv, k), dtype=torch.int32, device=device) for _ in range(2)]
                     for f in self.focal}
@@ -82,13 +83,11 @@ class FocalDecoder:
             if layer_hook is not None:
                 layer_hook(l, kind, "begin")
             if kind == "focal":
-                kvsel._check(L.kvsel_dense_attn(kv.ref(), qp, self.hq, self.scale, op, None,
-                                                ctypes.c_void_p(self.scores.data_ptr()), self.seg_len,
-                                                kvsel.NORM_SEGMENT, self.ws_ptr, self.ws_n, st))
                 warm = self.idx[l][prev].data_ptr() if (self.warm_start and t > 0) else None
-                kvsel._check(L.kvsel_topk(ctypes.c_void_p(self.scores.data_ptr()), self.seg_len, self.B * self.hkv,
-                                          self.seg_len, self.k, warm, ctypes.c_void_p(self.idx[l][cur].data_ptr()),
-                                          None, 0, st))
+                kvsel._check(L.kvsel_focal_attn(kv.ref(), qp, self.hq, self.scale, op, None, kvsel.NORM_SEGMENT,
+                                                self.k, warm, ctypes.c_void_p(self.idx[l][cur].data_ptr()),
+                                                self.scores_ptr(), self.seg_len if self.keep_scores else 0,
+                                                self.ws_ptr, self.ws_n, st))
             elif kind == "dense":
                 kvsel._check(L.kvsel_dense_attn(kv.ref(), qp, self.hq, self.scale, op, None, None, 0,
                                                 kvsel.NORM_SEGMENT, self.ws_ptr, self.ws_n, st))
@@ -101,6 +100,9 @@ class FocalDecoder:
             if layer_hook is not None:
                 layer_hook(l, kind, "end")
         self.cur = prev   # this step's selection becomes "previous"
+
+    def scores_ptr(self):
+        return ctypes.c_void_p(self.scores.data_ptr()) if self.keep_scores else None
 
     def selection(self, layer: int, previous: bool = False) -> torch.Tensor:
         """Kept indices of a focal layer after the last step (or the step before)."""

@@ -29,7 +29,7 @@ SYMBOLS = (
     "kvsel_score", "kvsel_score_workspace",
     "kvsel_topk", "kvsel_topk_workspace",
     "kvsel_gather_attn", "kvsel_attn_workspace",
-    "kvsel_dense_attn", "kvsel_gather_rows",
+    "kvsel_dense_attn", "kvsel_focal_attn", "kvsel_gather_rows",
 )
 
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_attn_workspace.argtypes = [_DP, _I32, _I32, _I32, _I32]
     L.kvsel_dense_attn.restype = _I32
     L.kvsel_dense_attn.argtypes = [_DP, _P, _I32, _F32, _P, _P, _P, _I64, _I32, _P, _SZ, _P]
+    L.kvsel_focal_attn.restype = _I32
+    L.kvsel_focal_attn.argtypes = [_DP, _P, _I32, _F32, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
     L.kvsel_gather_rows.restype = _I32
     L.kvsel_gather_rows.argtypes = [_P, _I64, _I64, _P, _I32, _I64, _I32, _P, _P]
     _lib = L
@@ -289,6 +291,34 @@ def dense_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: tor
     _check(lib().kvsel_dense_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(out), _ptr(lse), _ptr(seg_scores),
                                   ld, norm, p, n, _stream(stream)))
     return out
+
+
+def focal_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: torch.Tensor, k: int,
+               idx: torch.Tensor, warm: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               seg_scores: Optional[torch.Tensor] = None, norm: int = NORM_SEGMENT,
+               ws: Optional[Workspace] = None, stream=None):
+    """kvsel_focal_attn: dense attention + focal scores + top-k per (sequence, kv head).
+    idx (and warm): int32 [batch][hkv][k]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    _need(idx, torch.int32, "idx")
+    if idx.numel() != kv.batch * kv.hkv * k:
+        raise ValueError("idx must be [batch][num_kv_heads][k]")
+    if warm is not None:
+        _need(warm, torch.int32, "warm")
+        if warm.numel() != idx.numel():
+            raise ValueError("warm must be [batch][num_kv_heads][k]")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    ld = 0
+    if seg_scores is not None:
+        _need(seg_scores, torch.float32, "seg_scores")
+        ld = seg_scores.shape[-1]
+    w = _ws(ws, q.device)
+    p, n = w.ptr_and_size(attn_workspace(kv, num_q_heads, -1, True, norm))
+    _check(lib().kvsel_focal_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(out), _ptr(lse), norm, k, _ptr(warm),
+                                  _ptr(idx), _ptr(seg_scores), ld, p, n, _stream(stream)))
+    return idx
 
 
 def gather_rows(src: torch.Tensor, idx: Optional[torch.Tensor], n_idx: int, tail_begin: int, n_tail: int,

@@ -221,6 +221,29 @@ KVSEL_API kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t 
                               int32_t norm, void *ws, size_t ws_bytes, kvsel_stream stream);
 
 /*
+ * kvsel_focal_attn -- the fused focal pass: dense attention over every present
+ * row, the focal score of the candidate segment from the same pass over K,
+ * and the top-k of each (sequence, kv head).
+ * (FastOCR Focal-Guided Pruning: a focal layer attends over the full cache
+ *  and selects the top-attended image tokens; Cross-Step Fixation Reuse: the
+ *  previous step's set warm-starts the selection.)
+ *
+ * Equal to kvsel_dense_attn(..., seg_scores, ld, norm) followed by
+ * kvsel_topk(seg_scores, ld, batch * num_kv_heads, segment length, k,
+ * warm_idx, idx): same out, lse and scores bit for bit, the same idx.  q, out,
+ * lse as kvsel_dense_attn; idx, warm_idx: int32 [batch][num_kv_heads][k]
+ * (warm_idx NULL or a previous selection, see kvsel_topk).  seg_scores: NULL
+ * or fp32 [batch][num_kv_heads][ld].  A sequence whose segment is shorter
+ * than k keeps all of it and pads idx with -1 (skipped by gather attention).
+ * Requires 1 <= k, max_seg_len <= 12288 (KVSEL_EUNSUPPORTED otherwise).
+ * Workspace: kvsel_attn_workspace(kv, num_q_heads, -1, 1, norm).
+ */
+KVSEL_API kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
+                                        float scale, float *out, float *lse, int32_t norm, int32_t k,
+                                        const int32_t *warm_idx, int32_t *idx, float *seg_scores, int64_t ld,
+                                        void *ws, size_t ws_bytes, kvsel_stream stream);
+
+/*
  * kvsel_gather_rows -- dst[j] = src[idx[j]] for j < n_idx, then
  * dst[n_idx + t] = src[tail_begin + t] for t < n_tail; rows of row_bytes
  * bytes, copied bit-exactly.

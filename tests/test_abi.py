@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -88,6 +88,20 @@ def test_dense_attn_checks(L):
     need = L.kvsel_attn_workspace(ctypes.byref(d), 16, -1, 1, 0)
     assert need > L.kvsel_attn_workspace(ctypes.byref(d), 16, -1, 0, 0) > 0
     assert L.kvsel_attn_workspace(ctypes.byref(desc(head_dim=64)), 16, -1, 0, 0) == 0
+
+
+def test_focal_attn_checks(L):
+    d = desc()
+    f = lambda dd, **kw: L.kvsel_focal_attn(ctypes.byref(dd), kw.get("q", FAKE), 16, 0.088, FAKE, None, kw.get("norm", 0),
+                                            kw.get("k", 5), None, kw.get("idx", FAKE), kw.get("sc", None),
+                                            kw.get("ld", 0), FAKE, kw.get("ws_bytes", 1 << 30), None)
+    assert f(d, k=0) == EINVAL
+    assert f(d, idx=0) == EINVAL
+    assert f(d, norm=3) == EINVAL
+    assert f(d, sc=FAKE, ld=50) == EINVAL
+    assert f(d, ws_bytes=100) == ENOSPC
+    big = desc(max_blocks_per_seq=1000, max_seq_len=16000, max_seg_len=12289, min_seg_len=0, num_blocks=4000)
+    assert f(big) == EUNSUP
 
 
 def score(L, d, q=FAKE, n_rows=1, hq=16, reduce=0, norm=0, causal=1, pool=1, scores=FAKE, ld=100,

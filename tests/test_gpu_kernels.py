@@ -198,6 +198,40 @@ def test_dense_fused_scores_match_score_call():
     assert torch.equal(s1[0], s2[0]) and torch.equal(s1[1, :, :2500], s2[1, :, :2500])
 
 
+@pytest.mark.parametrize("G,norm", [(2, 0), (4, 1), (1, 0), (8, 0)])
+def test_focal_attn_equals_dense_then_topk(G, norm):
+    """The fused focal pass gives the same out, lse, scores and kept set as
+    dense attention with scores followed by the standalone top-k."""
+    kvsel = K()
+    rng = np.random.default_rng(31 + G)
+    hkv = 4
+    hq = hkv * G
+    lens = [3000, 2900, 3100]
+    segs = [(0, 2500), (0, 2500), (0, 2500)]
+    kv, kc, vc, table = make_kv(rng, 3, hkv, lens, segs)
+    q = torch.randn((3, hq, 128), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).to(DEV)
+    k = 125
+    o1, o2 = (torch.zeros((3, hq, 128), dtype=torch.float32, device=DEV) for _ in range(2))
+    l1, l2 = (torch.zeros((3, hq), dtype=torch.float32, device=DEV) for _ in range(2))
+    s1, s2 = (torch.zeros((3, hkv, 2500), dtype=torch.float32, device=DEV) for _ in range(2))
+    i1, i2, i3 = (torch.zeros((3, hkv, k), dtype=torch.int32, device=DEV) for _ in range(3))
+    kvsel.dense_attn(kv, q, hq, SCALE, o1, l1, seg_scores=s1, norm=norm)
+    kvsel.topk(s1, 2500, k, i1)
+    kvsel.focal_attn(kv, q, hq, SCALE, o2, k, i2, lse=l2, seg_scores=s2, norm=norm)
+    kvsel.focal_attn(kv, q, hq, SCALE, o2, k, i3, warm=i1, norm=norm)     # warm start: same set
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
+    assert torch.equal(i1, i2) and torch.equal(i1, i3)
+    qc = q.cpu()
+    nm = "segment" if norm == 0 else "context"
+    for b in range(3):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            ref = O.focal_scores(O.widen(qc[b, g * G:(g + 1) * G]), Kl, 0, 2500, SCALE, nm)
+            ok, nd = O.tie_band_check(i2[b, g].cpu().numpy(), ref, k, BAND)
+            assert ok, (b, g, nd)
+
+
 @pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True)])
 def test_window_scores(G, W, reduce, causal):
     kvsel = K()
