@@ -114,6 +114,7 @@ AttnArgs attn_args(const kvsel_kv_desc *kv, const uint16_t *q, int32_t hq, float
   a.logits = logit_mode ? reinterpret_cast<float *>(ws + p.off_logits) : nullptr;
   a.ld_logits = p.ld_logits;
   a.logit_mode = logit_mode;
+  a.scale = (double)scale;
   return a;
 }
 
@@ -269,6 +270,17 @@ kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_
   if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
   AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, p, (char *)ws, out, lse, mode);
   a.dense = 1;
+  if (p.nsplit == 1 && norm == KVSEL_NORM_SEGMENT && fused_focal_fits(G, kv->max_seg_len)) {
+    // one kernel: attention, segment logits kept in LDS, selection per (sequence, kv head)
+    a.logits = nullptr;
+    a.sel_idx = idx;
+    a.sel_warm = warm_idx;
+    a.sel_k = k;
+    a.sel_scores = seg_scores;
+    a.sel_ld = seg_scores != nullptr ? ld : 0;
+    a.seg_cap = (kv->max_seg_len + 3) / 4 * 4;
+    return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "focal attention launch");
+  }
   hipError_t e = launch_attn(a, kv->batch, G, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "focal attention launch");
   SelArgs n = sel_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, a.logits, p.ld_logits);

@@ -25,8 +25,12 @@
 //    group), so the loop has no cross-group synchronisation.
 //  * the lane-group states are merged in registers (the four groups of a
 //    wave) and in LDS (across waves).
+#include <type_traits>
+
 #include "common.h"
+#include "focal.h"
 #include "kvsel_internal.h"
+#include "radix.h"
 
 // Launch shape (defaults chosen by measurement on MI355X; overridable at build
 // time for sweeps): threads per work-group for groups of <= 2 query heads,
@@ -40,6 +44,14 @@
 #endif
 #ifndef KVSEL_ATTN_WAVES_PER_CU
 #define KVSEL_ATTN_WAVES_PER_CU 16
+#endif
+// 1: issue the next iteration's K/V loads before computing the current one
+#ifndef KVSEL_ATTN_PIPE
+#define KVSEL_ATTN_PIPE 0
+#endif
+// minimum resident waves per SIMD the compiler must allow for (0: no bound)
+#ifndef KVSEL_ATTN_WPE
+#define KVSEL_ATTN_WPE 0
 #endif
 
 namespace kvsel {
@@ -81,21 +93,42 @@ __device__ __forceinline__ uint32_t row_to_phys(const AttnArgs &a, int b, int g,
   return ((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row & 15);
 }
 
-template <int G>
-__device__ __forceinline__ void dot_rows(const float (&qf)[G][8], const uint4 &kr, float (&dot)[G]) {
-  float kf[8];
-  unpack8(kr, kf);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float s = qf[h][0] * kf[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) s = fmaf(qf[h][e], kf[e], s);
-    dot[h] = row16_sum(s);
-  }
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// dot product of 8 bf16 pairs packed in two uint4 (v_dot2_f32_bf16: exact
+// bf16 products, fp32 accumulation)
+__device__ __forceinline__ float dot8(const uint4 &x, const uint4 &y) {
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x), __builtin_bit_cast(bf16x2, y.x), 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y), __builtin_bit_cast(bf16x2, y.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z), __builtin_bit_cast(bf16x2, y.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w), __builtin_bit_cast(bf16x2, y.w), s, false);
+  return s;
 }
 
-template <int G, int NT, int U>
-__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
+// full 128-dim dots of one row (this lane's 8 dims + 15 others) for each head
+template <int G>
+__device__ __forceinline__ void dot_rows(const uint4 (&qr)[G], const uint4 &kr, float (&dot)[G]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) dot[h] = row16_sum(dot8(qr[h], kr));
+}
+
+// The running max is a lazy reference: it moves only when a row's logit
+// exceeds it by more than this many log2 units, so most iterations skip the
+// accumulator rescale; probabilities relative to it stay below 2^8.
+constexpr float kLazy = 8.f;
+constexpr float kNegBig = -1e30f;   // finite "empty" max: 2^(kNegBig - x) == 0, no NaN
+
+#if KVSEL_ATTN_WPE > 0
+#define KVSEL_ATTN_OCC __attribute__((amdgpu_waves_per_eu(KVSEL_ATTN_WPE)))
+#else
+#define KVSEL_ATTN_OCC
+#endif
+
+// MODE 0: attention only.  MODE 1: also store the raw logits to the global
+// scratch.  MODE 2 (one split only): keep the segment logits in LDS and end
+// with the focal selection of this (sequence, kv head).
+template <int G, int NT, int U, int MODE>
+__global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   constexpr int NG = NT / 16;    // lane groups
   constexpr int NW = NT / 64;    // waves
   constexpr int ITER = NG * U;   // rows per iteration of the work-group
@@ -108,13 +141,17 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
   __shared__ int32_t s_tab[kTabLds];
   __shared__ float s_acc[NW][G][kD];
   __shared__ float s_m[NW][G], s_l[NW][G];
+  extern __shared__ float s_logit[];   // MODE 2: [G][seg_cap]
 
   const SeqView v = seq_view(a, b, dense);
   const int start = split * a.rps;
   const int cnt = max(0, min(a.rps, v.nR - start));   // rows of this split
 
   int lo = 0, hi = 0;   // logical rows whose logits are stored, at row - lo (dense only)
-  if (a.logits != nullptr) {
+  if (MODE == 2) {
+    lo = v.s0;
+    hi = v.s0 + min(v.s1 - v.s0, a.seg_cap);
+  } else if (MODE == 1) {
     if (a.logit_mode == 1) { lo = v.s0; hi = v.s1; }
     else { lo = 0; hi = v.n; }
   }
@@ -149,16 +186,14 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
     }
   }
 
-  float qf[G][8];
+  const uint16_t *qbase = a.q + ((size_t)b * a.hq + g * G) * kD + sub * 8;
+  uint4 qr[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qv = *reinterpret_cast<const uint4 *>(a.q + ((size_t)b * a.hq + g * G + h) * kD + sub * 8);
-    unpack8(qv, qf[h]);
-  }
+  for (int h = 0; h < G; ++h) qr[h] = *reinterpret_cast<const uint4 *>(qbase + h * kD);
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+    m[h] = kNegBig;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
@@ -167,37 +202,39 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 
   const uint16_t *kbase = a.k_pool + sub * 8;
   const uint16_t *vbase = a.v_pool + sub * 8;
-  for (int base = 0; base < cnt; base += ITER) {
-    uint4 kr[U], vr[U];
-    uint32_t pr[U];
+
+  // K/V rows of one iteration into registers
+  auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + grp + NG * u;
-      pr[u] = t < cnt ? s_prow[t] : kNoRow;
+      const uint32_t pr = t < cnt ? s_prow[t] : kNoRow;
+      ok[u] = pr != kNoRow;
+      // a row that is not attended reads this lane's query (a valid, finite
+      // 16 bytes) and gets probability 0
+      const uint16_t *kp = ok[u] ? kbase + (size_t)pr * kD : qbase;
+      const uint16_t *vp = ok[u] ? vbase + (size_t)pr * kD : qbase;
+      kr[u] = *reinterpret_cast<const uint4 *>(kp);
+      vr[u] = *reinterpret_cast<const uint4 *>(vp);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (pr[u] != kNoRow) {
-        kr[u] = *reinterpret_cast<const uint4 *>(kbase + (size_t)pr[u] * kD);
-        vr[u] = *reinterpret_cast<const uint4 *>(vbase + (size_t)pr[u] * kD);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  };
+  // online softmax over the iteration's rows
+  auto consume = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U], const bool (&ok)[U]) {
     float dot[U][G];
 #pragma unroll
-    for (int u = 0; u < U; ++u) dot_rows<G>(qf, kr[u], dot[u]);
-    if (a.logits != nullptr) {
+    for (int u = 0; u < U; ++u) dot_rows<G>(qr, kr[u], dot[u]);
+    if (MODE != 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = start + base + grp + NG * u;   // dense: logical row = virtual row
-        if (base + grp + NG * u < cnt && sub < G && pr[u] != kNoRow && row >= lo && row < hi &&
-            row - lo < a.ld_logits) {
+        if (ok[u] && sub < G && row >= lo && row < hi) {
           float dv = dot[u][0];
 #pragma unroll
           for (int h = 1; h < G; ++h) dv = sub == h ? dot[u][h] : dv;
-          a.logits[((size_t)b * a.hq + g * G + sub) * a.ld_logits + (row - lo)] = dv;
+          if (MODE == 2)
+            s_logit[sub * a.seg_cap + (row - lo)] = dv;
+          else if (row - lo < a.ld_logits)
+            a.logits[((size_t)b * a.hq + g * G + sub) * a.ld_logits + (row - lo)] = dv;
         }
       }
     }
@@ -207,31 +244,54 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        s[u] = pr[u] != kNoRow ? dot[u][h] * a.scale_log2 : -INFINITY;
+        s[u] = ok[u] ? dot[u][h] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[u]);
       }
-      const float mn = fmaxf(m[h], mx);
-      if (mn != -INFINITY) {
-        const float c = fast_exp2(m[h] - mn);   // m = -inf -> 0
-        float ps = 0.f;
-        float p[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          p[u] = fast_exp2(s[u] - mn);
-          ps += p[u];
-        }
-        l[h] = l[h] * c + ps;
+      if (mx > m[h] + kLazy) {   // move the reference (rare after the first rows)
+        const float c = fast_exp2(m[h] - mx);
+        l[h] *= c;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= c;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float vf[8];
-          unpack8(vr[u], vf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[u], vf[e], acc[h][e]);
-        }
-        m[h] = mn;
+        m[h] = mx;
       }
+      float p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = fast_exp2(s[u] - m[h]);
+        l[h] += p[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint4 w = vr[u];
+        acc[h][0] = fmaf(p[u], bf_lo(w.x), acc[h][0]);
+        acc[h][1] = fmaf(p[u], bf_hi(w.x), acc[h][1]);
+        acc[h][2] = fmaf(p[u], bf_lo(w.y), acc[h][2]);
+        acc[h][3] = fmaf(p[u], bf_hi(w.y), acc[h][3]);
+        acc[h][4] = fmaf(p[u], bf_lo(w.z), acc[h][4]);
+        acc[h][5] = fmaf(p[u], bf_hi(w.z), acc[h][5]);
+        acc[h][6] = fmaf(p[u], bf_lo(w.w), acc[h][6]);
+        acc[h][7] = fmaf(p[u], bf_hi(w.w), acc[h][7]);
+      }
+    }
+  };
+
+  if (KVSEL_ATTN_PIPE) {
+    uint4 ka[U], va[U], kb2[U], vb2[U];
+    bool oa[U], ob[U];
+    if (cnt > 0) load_rows(0, ka, va, oa);
+    for (int base = 0; base < cnt; base += 2 * ITER) {
+      if (base + ITER < cnt) load_rows(base + ITER, kb2, vb2, ob);
+      consume(base, ka, va, oa);
+      if (base + ITER >= cnt) break;
+      if (base + 2 * ITER < cnt) load_rows(base + 2 * ITER, ka, va, oa);
+      consume(base + ITER, kb2, vb2, ob);
+    }
+  } else {
+    for (int base = 0; base < cnt; base += ITER) {
+      uint4 kr[U], vr[U];
+      bool ok[U];
+      load_rows(base, kr, vr, ok);
+      consume(base, kr, vr, ok);
     }
   }
 
@@ -243,7 +303,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
       const float mo = __shfl_xor(m[h], off);
       const float lo_ = __shfl_xor(l[h], off);
       const float mn = fmaxf(m[h], mo);
-      const float ca = rescale(m[h], mn), cb = rescale(mo, mn);
+      const float ca = fast_exp2(m[h] - mn), cb = fast_exp2(mo - mn);
       l[h] = l[h] * ca + lo_ * cb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -274,7 +334,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
     float L = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float c = rescale(s_m[w][h], M);
+      const float c = fast_exp2(s_m[w][h] - M);
       L += s_l[w][h] * c;
       A += s_acc[w][h][dim] * c;
     }
@@ -291,6 +351,33 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
       }
     }
   }
+
+  if constexpr (MODE == 2) {
+    // focal selection from the LDS logits (FastOCR Focal-Guided Pruning)
+    __shared__ RadixShared<NT> sh;
+    __shared__ double s_fm[G], s_fiz[G];
+    __shared__ float s_redf[NW];
+    __shared__ double s_redd[16];
+    __syncthreads();
+    const int seg = hi - lo;
+    const double c = a.scale * 1.4426950408889634;
+    auto logit = [&](int hh, int i) { return s_logit[hh * a.seg_cap + i]; };
+    focal_stats<NT>(logit, G, seg, c, s_fm, s_fiz, s_redf, s_redd);
+    uint32_t *keys = reinterpret_cast<uint32_t *>(s_logit);   // head 0's row, rewritten in place
+    float *so = a.sel_scores != nullptr ? a.sel_scores + ((size_t)b * a.hkv + g) * a.sel_ld : nullptr;
+    const int seg_out = so != nullptr ? (int)min((int64_t)seg, a.sel_ld) : seg;
+    for (int i = tid; i < seg; i += NT) {
+      const float f = (float)focal_score(logit, G, i, c, s_fm, s_fiz);
+      keys[i] = okey(f);
+      if (so != nullptr && i < seg_out) so[i] = f;
+    }
+    __syncthreads();
+    auto key = [&](int i) -> uint32_t { return keys[i]; };
+    const size_t row = (size_t)b * a.hkv + g;
+    const uint32_t theta = a.sel_warm != nullptr ? warm_theta<NT>(key, a.sel_warm + row * a.sel_k, seg, a.sel_k, sh)
+                                                 : 0u;
+    radix_topk<NT>(key, seg, a.sel_k, theta, a.sel_idx + row * a.sel_k, sh);
+  }
 }
 
 // merge of the split records: grid (kv heads, sequences), G*128 threads
@@ -302,11 +389,11 @@ __global__ __launch_bounds__(G * kD) void attn_merge_kernel(AttnArgs a) {
   const int nact = v.nR <= 0 ? 0 : min(a.nsplit, (v.nR + a.rps - 1) / a.rps);
   const size_t hb = (size_t)b * a.hq + g * G + h;
   const float *rec0 = a.rec + hb * a.nsplit * kRec;
-  float M = -INFINITY;
+  float M = kNegBig;
   for (int sp = 0; sp < nact; ++sp) M = fmaxf(M, rec0[sp * kRec + kD]);
   float L = 0.f, A = 0.f;
   for (int sp = 0; sp < nact; ++sp) {
-    const float c = rescale(rec0[sp * kRec + kD], M);
+    const float c = fast_exp2(rec0[sp * kRec + kD] - M);
     L += rec0[sp * kRec + kD + 1] * c;
     A += rec0[sp * kRec + dim] * c;
   }
@@ -327,12 +414,9 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
   const int r0 = lo + chunk * a.rps;
   const int cnt = min(a.rps, hi - r0);
   if (cnt <= 0) return;
-  float qf[G][8];
+  uint4 qr[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qv = *reinterpret_cast<const uint4 *>(a.q + ((size_t)b * a.hq + g * G + h) * kD + sub * 8);
-    unpack8(qv, qf[h]);
-  }
+  for (int h = 0; h < G; ++h) qr[h] = *reinterpret_cast<const uint4 *>(a.q + ((size_t)b * a.hq + g * G + h) * kD + sub * 8);
   const uint16_t *kbase = a.k_pool + sub * 8;
   for (int base = 0; base < cnt; base += NG * U) {
     uint4 kr[U];
@@ -347,7 +431,7 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float dot[G];
-      dot_rows<G>(qf, kr[u], dot);
+      dot_rows<G>(qr, kr[u], dot);
       float dsel = dot[0];
 #pragma unroll
       for (int h = 1; h < G; ++h) dsel = sub == h ? dot[h] : dsel;
@@ -367,7 +451,24 @@ template <int G>
 hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
   constexpr int NT = attn_threads(G);
   dim3 grid(a.nsplit, a.hkv, batch);
-  hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U>), grid, dim3(NT), 0, s, a);
+  if (a.sel_idx != nullptr) {
+    if (a.nsplit != 1) return hipErrorInvalidValue;
+    const size_t dyn = (size_t)G * a.seg_cap * sizeof(float);
+    if (dyn > kFusedLdsBytes) return hipErrorInvalidValue;
+    static bool attr_set = false;   // the LDS above 64 KiB must be allowed once per kernel
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<G, NT, KVSEL_ATTN_U, 2>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedLdsBytes);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 2>), grid, dim3(NT), dyn, s, a);
+    return hipGetLastError();
+  }
+  if (a.logits != nullptr)
+    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 1>), grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 0>), grid, dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel<G>, dim3(a.hkv, batch), dim3(G * kD), 0, s, a);

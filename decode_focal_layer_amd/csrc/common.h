@@ -91,4 +91,47 @@ __device__ __forceinline__ double block_sum_d(double v, double *scratch) {
   return r;
 }
 
+// Sum of val(i) over i in [0, n) with the reduction order of a 1024-thread
+// block: virtual thread v (= tid + r * NT) takes i = v, v + 1024, ... in
+// order, each virtual wave reduces with xor shuffles (32, 16, ..., 1), and the
+// 16 virtual-wave sums are added in order.  The result is bit-identical for
+// any NT dividing 1024.  scratch holds 16 doubles; result in every thread.
+template <int NT, typename F>
+__device__ __forceinline__ double vsum1024(F val, int n, double *scratch) {
+  constexpr int R = 1024 / NT;
+  const int tid = threadIdx.x;
+  double part[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    part[r] = 0.0;
+    for (int i = tid + r * NT; i < n; i += 1024) part[r] += val(i);
+    part[r] = wave_sum_d(part[r]);
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) scratch[(tid >> 6) + r * (NT / 64)] = part[r];
+  }
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < 16; ++w) s += scratch[w];
+  __syncthreads();
+  return s;
+}
+
+// max of val(i) over i in [0, n); scratch holds NT/64 floats
+template <int NT, typename F>
+__device__ __forceinline__ float vmax(F val, int n, float *scratch) {
+  float m = -INFINITY;
+  for (int i = threadIdx.x; i < n; i += NT) m = fmaxf(m, val(i));
+  m = wave_max(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = scratch[0];
+  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
 }  // namespace kvsel

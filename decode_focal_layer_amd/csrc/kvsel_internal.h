@@ -52,7 +52,24 @@ struct AttnArgs {
   float *logits;        // [batch][hq][ld_logits] raw q.k dots, or null
   int64_t ld_logits;
   int32_t logit_mode;
+  // fused focal selection (one work-group per (sequence, kv head)): the
+  // segment logits stay in LDS (seg_cap per head) and the work-group
+  // normalises them and selects sel_k indices itself
+  int32_t *sel_idx;     // [batch][hkv][sel_k], or null (no fused selection)
+  const int32_t *sel_warm;
+  int32_t sel_k;
+  float *sel_scores;    // [batch][hkv][sel_ld] or null
+  int64_t sel_ld;
+  int32_t seg_cap;
+  double scale;
 };
+
+// dynamic LDS the fused focal kernel may take for the segment logits
+constexpr size_t kFusedLdsBytes = 80 * 1024;
+inline bool fused_focal_fits(int group, int max_seg_len) {
+  const size_t cap = (size_t)((max_seg_len + 3) / 4 * 4);
+  return cap > 0 && (size_t)group * cap * sizeof(float) <= kFusedLdsBytes;
+}
 
 hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s);
 

@@ -1,18 +1,15 @@
 // Focal score normalisation, alone or fused with the exact top-k, one
-// work-group per (sequence, output row).
+// work-group per (sequence, output row), reading logits stored by the
+// attention or logits kernel (the path for shapes the fused focal attention
+// kernel does not take: split attention, context normalisation, long
+// segments).
 //
 // FastOCR (technical summary, Focal-Guided Pruning): a focal layer ranks the
 // image tokens by the attention its queries give them and keeps the top tau;
 // Cross-Step Fixation Reuse: the previous step's set warm-starts the choice.
-//
-// Input: raw fp32 q.k dot products of bf16 data (exact products, fp32 sums),
-// written by the focal attention pass or the logits kernel and read back from
-// L2.  Per head: the max, then the softmax normaliser in fp64; per token: the
-// probabilities of the heads summed in fp64 and rounded to fp32 once.  Both
-// kernels share this code and reduction order, so their scores agree bit for
-// bit.  The fused kernel keeps the scores in LDS as order-preserving keys and
-// selects with radix_topk.
+// The arithmetic is focal.h's; selection is radix.h's.
 #include "common.h"
+#include "focal.h"
 #include "kvsel_internal.h"
 #include "radix.h"
 
@@ -39,45 +36,21 @@ __device__ __forceinline__ FocalRow focal_row(const SelArgs &a, int b, int64_t l
   return r;
 }
 
-// per head of the output row: s_m = max logit, s_iz = 1 / sum 2^((x - max) c)
-__device__ void focal_stats(const SelArgs &a, int b, int o, const FocalRow &r, double c, double *s_m, double *s_iz,
-                            float *redf, double *redd) {
-  for (int hh = 0; hh < a.heads_per_out; ++hh) {
-    const float *row = a.logits + ((size_t)b * a.hq + o * a.heads_per_out + hh) * a.ld_logits;
-    float mx = -INFINITY;
-    for (int i = threadIdx.x; i < r.cnt; i += kSelThreads) mx = fmaxf(mx, row[i]);
-    mx = block_max(mx, redf);
-    double z = 0.0;
-    for (int i = threadIdx.x; i < r.cnt; i += kSelThreads) z += exp2_acc(((double)row[i] - (double)mx) * c);
-    z = block_sum_d(z, redd);
-    if (threadIdx.x == 0) {
-      s_m[hh] = (double)mx;
-      s_iz[hh] = z > 0.0 ? 1.0 / z : 0.0;
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ double focal_score(const SelArgs &a, const float *lg, int i, double c, const double *s_m,
-                                              const double *s_iz) {
-  double sc = 0.0;
-  for (int hh = 0; hh < a.heads_per_out; ++hh)
-    sc += exp2_acc(((double)lg[(size_t)hh * a.ld_logits + i] - s_m[hh]) * c) * s_iz[hh];
-  return sc;
-}
-
 // grid (output rows, sequences): scores only
 __global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
   __shared__ double s_m[kMaxHeadsPerOut], s_iz[kMaxHeadsPerOut];
   __shared__ float s_redf[kSelThreads / 64];
-  __shared__ double s_redd[kSelThreads / 64];
+  __shared__ double s_redd[16];
   const int o = blockIdx.x, b = blockIdx.y;
   const FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : a.ld64);
   const double c = a.scale * 1.4426950408889634;
-  focal_stats(a, b, o, r, c, s_m, s_iz, s_redf, s_redd);
-  const float *lg = a.logits + ((size_t)b * a.hq + o * a.heads_per_out) * a.ld_logits + r.off;
+  const float *base = a.logits + ((size_t)b * a.hq + o * a.heads_per_out) * a.ld_logits;
+  auto stat_logit = [&](int hh, int i) { return base[(size_t)hh * a.ld_logits + i]; };
+  focal_stats<kSelThreads>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz, s_redf, s_redd);
+  const float *lg = base + r.off;
+  auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
   for (int i = threadIdx.x; i < r.seg; i += kSelThreads) {
-    const double sc = focal_score(a, lg, i, c, s_m, s_iz);
+    const double sc = focal_score(seg_logit, a.heads_per_out, i, c, s_m, s_iz);
     if (a.scores != nullptr)
       a.scores[((size_t)b * a.n_out + o) * a.ld + i] = (float)sc;
     else
@@ -92,16 +65,19 @@ __global__ __launch_bounds__(kSelThreads) void focal_select_kernel(SelArgs a) {
   __shared__ RadixShared<NT> sh;
   __shared__ double s_m[8], s_iz[8];
   __shared__ float s_redf[NT / 64];
-  __shared__ double s_redd[NT / 64];
+  __shared__ double s_redd[16];
   const int g = blockIdx.x, b = blockIdx.y;
   FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : (int64_t)kSelMaxSeg);
   r.seg = min(r.seg, kSelMaxSeg);
   const double c = a.scale * 1.4426950408889634;
-  focal_stats(a, b, g, r, c, s_m, s_iz, s_redf, s_redd);
-  const float *lg = a.logits + ((size_t)b * a.hq + g * a.heads_per_out) * a.ld_logits + r.off;
+  const float *base = a.logits + ((size_t)b * a.hq + g * a.heads_per_out) * a.ld_logits;
+  auto stat_logit = [&](int hh, int i) { return base[(size_t)hh * a.ld_logits + i]; };
+  focal_stats<NT>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz, s_redf, s_redd);
+  const float *lg = base + r.off;
+  auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
   float *so = a.scores != nullptr ? a.scores + ((size_t)b * a.n_out + g) * a.ld : nullptr;
   for (int i = threadIdx.x; i < r.seg; i += NT) {
-    const float f = (float)focal_score(a, lg, i, c, s_m, s_iz);
+    const float f = (float)focal_score(seg_logit, a.heads_per_out, i, c, s_m, s_iz);
     s_keys[i] = okey(f);
     if (so != nullptr) so[i] = f;
   }

@@ -198,38 +198,50 @@ def test_dense_fused_scores_match_score_call():
     assert torch.equal(s1[0], s2[0]) and torch.equal(s1[1, :, :2500], s2[1, :, :2500])
 
 
-@pytest.mark.parametrize("G,norm", [(2, 0), (4, 1), (1, 0), (8, 0)])
-def test_focal_attn_equals_dense_then_topk(G, norm):
-    """The fused focal pass gives the same out, lse, scores and kept set as
-    dense attention with scores followed by the standalone top-k."""
+# (G, norm, batch, hkv, len, seg): few pairs -> split attention + separate select;
+# >= 256 (G <= 2) or 512 (G = 4) pairs -> the one-kernel fused focal pass
+FOCAL_CASES = [(2, 0, 3, 4, 3000, 2500), (4, 1, 3, 4, 3000, 2500), (1, 0, 3, 4, 3000, 2500), (8, 0, 3, 4, 3000, 2500),
+               (2, 0, 32, 8, 900, 700), (4, 0, 64, 8, 520, 400), (1, 0, 32, 8, 400, 333)]
+
+
+@pytest.mark.parametrize("G,norm,batch,hkv,n,seg", FOCAL_CASES)
+def test_focal_attn_equals_dense_then_topk(G, norm, batch, hkv, n, seg):
+    """The focal pass gives the same out, lse, scores and kept set as dense
+    attention with scores followed by the standalone top-k (bit for bit)."""
     kvsel = K()
-    rng = np.random.default_rng(31 + G)
-    hkv = 4
+    rng = np.random.default_rng(31 + G + batch)
     hq = hkv * G
-    lens = [3000, 2900, 3100]
-    segs = [(0, 2500), (0, 2500), (0, 2500)]
-    kv, kc, vc, table = make_kv(rng, 3, hkv, lens, segs)
-    q = torch.randn((3, hq, 128), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).to(DEV)
-    k = 125
-    o1, o2 = (torch.zeros((3, hq, 128), dtype=torch.float32, device=DEV) for _ in range(2))
-    l1, l2 = (torch.zeros((3, hq), dtype=torch.float32, device=DEV) for _ in range(2))
-    s1, s2 = (torch.zeros((3, hkv, 2500), dtype=torch.float32, device=DEV) for _ in range(2))
-    i1, i2, i3 = (torch.zeros((3, hkv, k), dtype=torch.int32, device=DEV) for _ in range(3))
+    lens = [n - (b % 3) * 7 for b in range(batch)]
+    segs = [(0, seg)] * batch
+    kv, kc, vc, table = make_kv(rng, batch, hkv, lens, segs)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).to(DEV)
+    k = max(1, seg // 20)
+    o1, o2 = (torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV) for _ in range(2))
+    l1, l2 = (torch.zeros((batch, hq), dtype=torch.float32, device=DEV) for _ in range(2))
+    s1, s2 = (torch.zeros((batch, hkv, seg), dtype=torch.float32, device=DEV) for _ in range(2))
+    i1, i2, i3, i4 = (torch.zeros((batch, hkv, k), dtype=torch.int32, device=DEV) for _ in range(4))
+    log_case("focal", G, norm, batch, hkv, n, seg)
     kvsel.dense_attn(kv, q, hq, SCALE, o1, l1, seg_scores=s1, norm=norm)
-    kvsel.topk(s1, 2500, k, i1)
+    kvsel.topk(s1, seg, k, i1)
     kvsel.focal_attn(kv, q, hq, SCALE, o2, k, i2, lse=l2, seg_scores=s2, norm=norm)
     kvsel.focal_attn(kv, q, hq, SCALE, o2, k, i3, warm=i1, norm=norm)     # warm start: same set
+    kvsel.focal_attn(kv, q, hq, SCALE, o2, k, i4, norm=norm)              # without the score output
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2)
-    assert torch.equal(i1, i2) and torch.equal(i1, i3)
+    assert torch.equal(i1, i2) and torch.equal(i1, i3) and torch.equal(i1, i4)
     qc = q.cpu()
     nm = "segment" if norm == 0 else "context"
-    for b in range(3):
+    for b in range(0, batch, max(1, batch // 3)):
         for g in range(hkv):
             Kl = O.logical_rows(kc, table[b], g, lens[b])
-            ref = O.focal_scores(O.widen(qc[b, g * G:(g + 1) * G]), Kl, 0, 2500, SCALE, nm)
+            Vl = O.logical_rows(vc, table[b], g, lens[b])
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref = O.focal_scores(qg, Kl, 0, seg, SCALE, nm)
             ok, nd = O.tie_band_check(i2[b, g].cpu().numpy(), ref, k, BAND)
             assert ok, (b, g, nd)
+            assert rel_err(s2[b, g].cpu().numpy(), ref) < 2e-6
+            refo, _ = O.dense_attention(qg, Kl, Vl, SCALE)
+            assert_attn(o2[b, g * G:(g + 1) * G].cpu().numpy(), refo, f"focal out b{b} g{g}")
 
 
 @pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True)])
