@@ -26,6 +26,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c1_hbm_traffic.md")
+KERNEL_SOURCES = ["decode_focal_layer_amd/csrc/attn.hip", "decode_focal_layer_amd/csrc/common.h",
+                  "decode_focal_layer_amd/csrc/focal.h", "decode_focal_layer_amd/csrc/radix.h",
+                  "decode_focal_layer_amd/csrc/kvsel_internal.h"]
+
+
+def measured_traffic():
+    """HBM bytes per gathered-attention launch from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    import hashlib
+    import re
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, s), "rb").read())
+    m = re.search(r"kernel-sources-sha256-16: ([0-9a-f]{16})", txt)
+    t = re.search(r"Traffic per gathered-attention launch = [0-9.]+ \+ [0-9.]+ = ([0-9.]+) MB", txt)
+    if not m or not t or m.group(1) != h.hexdigest()[:16]:
+        return None
+    return float(t.group(1)) * 1e6
 
 
 def algorithmic_bytes(cfg, t: int, batch: int):
@@ -117,7 +140,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=12, help="sequences in the oracle sample (0: skip)")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
@@ -157,47 +180,64 @@ def main():
     run(0, args.warmup)
     torch.cuda.synchronize()
 
-    # per-launch events around every sparse (gathered) attention launch
-    ev = []
-    plan_kind = {}
-
-    def hook(l, kind, phase):
-        if kind != "sparse":
-            return
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        ev.append((phase, e))
-
+    # timed region: K steps, nothing else on the stream
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    run(args.warmup, args.steps, None if args.no_kernel_events else hook)
+    run(args.warmup, args.steps)
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop)
     ms_per_step = ms / args.steps
     steps_per_s = 1000.0 / ms_per_step
-
     total_bytes = sum(step_bytes(cfg, (args.warmup + i) % T, cfg.batch) for i in range(args.steps))
     gbs = total_bytes / (ms / 1e3) / 1e9
 
+    # roofline of the dominant kernel (gathered sparse attention, 26 of 28 layers):
+    # the same K steps again, with HIP events on the decode stream at the two ends
+    # of every run of consecutive sparse layers (layers 4-13 and 15-27, plus 0-2
+    # after the first step); a run's time / its launches = average launch time.
     roof = None
-    if ev:
-        durs = [ev[i][1].elapsed_time(ev[i + 1][1]) for i in range(0, len(ev), 2)]
-        avg_ms = float(np.mean(durs))
-        # algorithmic bytes per sparse launch, averaged over the timed steps
-        per = []
-        for i in range(args.steps):
-            t = (args.warmup + i) % T
-            n_sparse = cfg.layers - len(cfg.focal) - (min(cfg.focal) if t == 0 else 0)
-            per += [algorithmic_bytes(cfg, t, cfg.batch)[2]] * n_sparse
-        bpl = float(np.mean(per))
-        ach = bpl / (avg_ms / 1e3) / 1e9
+    if not args.no_kernel_events:
+        marks = []          # (event_begin, event_end, launches, bytes)
+        state = {}
+        plans = {t: [e[0] for e in dec.plan(t)] for t in range(T)}
+
+        def hook(l, kind, phase):
+            t = state["t"]
+            if phase == "begin" and kind == "sparse" and (l == 0 or plans[t][l - 1] != "sparse"):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                state["open"] = (e, 0, 0)
+            if phase == "end" and kind == "sparse":
+                e0, nl, nb = state["open"]
+                nl += 1
+                nb += algorithmic_bytes(cfg, t, cfg.batch)[2]
+                state["open"] = (e0, nl, nb)
+                nxt = plans[t][l + 1] if l + 1 < cfg.layers else None
+                if nxt != "sparse":
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record()
+                    marks.append((e0, e1, nl, nb))
+
+        torch.cuda.synchronize()
+        for i in range(args.warmup, args.warmup + args.steps):
+            t = i % T
+            state["t"] = t
+            dec.step(t, w.q[t], w.seq_len[t], layer_hook=hook)
+        torch.cuda.synchronize()
+        tot_ms = sum(a.elapsed_time(b) for a, b, _, _ in marks)
+        launches = sum(n for _, _, n, _ in marks)
+        nbytes = sum(nb for _, _, _, nb in marks)
+        avg_us = tot_ms * 1e3 / launches
+        bpl = nbytes / launches
+        ach = bpl / (avg_us / 1e6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "attn_split_kernel<2> (gathered sparse attention)",
-                "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(bpl),
-                "launches_timed": len(durs)}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, calibrated "
+                                "on a 1 GiB copy)",
+                "kernel": "attn_kernel<2,1024,4,0> (gathered sparse attention)",
+                "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bpl), "launches_timed": launches}
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
