@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"],
+                    help="c1 (default) is the metric's workload; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU sharding is a design note only "
@@ -158,6 +160,8 @@ def main():
 
     kvsel.lib()
     dev = "cuda"
+    if args.workload != "c1":
+        return OTHER[args.workload](args)
     cfg = synth.C1
     t_gen = time.perf_counter()
     w = gen.make_focal(cfg, dev)
@@ -275,6 +279,175 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the other workloads (parity cases of the test suite; timed here on request)
+# ---------------------------------------------------------------------------
+
+def _line(metric, value, unit, args, ms, workload, extra, higher=True):
+    d = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": higher, "scaling": "weak",
+         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+         "config": {"workload": workload, "parallelism": "single GPU"}}
+    d.update(extra)
+    print(json.dumps(d), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(warmup, warmup + steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_c0(args):
+    """One decode step (fused focal pass + gathered attention) at the C0 shape;
+    32 input copies rotate so repeats do not hit the last-level cache."""
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    cfg = synth.C0
+    copies = []
+    for c in range(32):
+        w = gen.make_focal(synth.small(cfg, seed=cfg.seed + 1000 * c), "cuda")
+        kv = kvsel.KV(w.k_pool[0], w.v_pool[0], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                      max_seq_len=cfg.prefix_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+        copies.append((kv, w.q[0, 0].contiguous()))
+    out = torch.empty((1, cfg.hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, cfg.hkv, cfg.k), dtype=torch.int32, device="cuda")
+    ws = kvsel.Workspace("cuda")
+
+    def step(i):
+        kv, q = copies[i % len(copies)]
+        kvsel.focal_attn(kv, q, cfg.hq, cfg.scale, out, cfg.k, idx, ws=ws)
+        kvsel.gather_attn(kv, q, cfg.hq, cfg.scale, idx, cfg.k, out, ws=ws)
+
+    ms = _timed(step, args.steps, args.warmup)
+    dense = cfg.hkv * cfg.prefix_len * 512 + cfg.hq * 256 + cfg.hq * 512
+    sparse = cfg.hkv * (cfg.k + cfg.n_always) * 512 + cfg.hq * 256 + cfg.hq * 512 + cfg.hkv * cfg.k * 4
+    nbytes = dense + cfg.hkv * cfg.k * 4 + sparse
+    _line("decode steps/s (focal pass + sparse attention, 1 layer)", 1000 / ms, "steps/s", args, ms,
+          "c0_single_step: batch 1, 16q/8kv, 3584 visual + 512 text, top-179",
+          {"bytes_per_step": nbytes, "hbm_gbs_algorithmic": round(nbytes / ms / 1e6, 1)})
+
+
+def bench_c2(args):
+    """One FastKV token-selective propagation (window scores on MFMA, pool,
+    top-6554, gather of 6562 hidden rows); 6 input sets rotate."""
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.fastkv import tsp_select
+    cfg = synth.C2
+    s0, s1 = cfg.seg
+    sets = []
+    for c in range(6):
+        w = gen.make_window(synth.small(cfg, seed=cfg.seed + 1000 * c), "cuda")
+        kv = kvsel.KV(w.k_pool, None, w.block_table, w.seq_len, w.seg_begin, w.seg_end,
+                      max_seq_len=cfg.prompt, max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+        sets.append((kv, w.q, w.hidden))
+    scores = torch.empty((1, 1, s1 - s0), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, cfg.k), dtype=torch.int32, device="cuda")
+    dst = torch.empty((cfg.k + cfg.window, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = kvsel.Workspace("cuda")
+
+    def step(i):
+        kv, q, hid = sets[i % len(sets)]
+        tsp_select(kv, q, cfg.hq, cfg.scale, cfg.k, cfg.pool, hidden=hid, window=cfg.window, scores=scores,
+                   idx=idx, dst=dst, ws=ws)
+
+    ms = _timed(step, args.steps, args.warmup)
+    kbytes = cfg.prompt * cfg.hkv * 256
+    nbytes = kbytes + cfg.window * cfg.hq * 256 + 2 * (s1 - s0) * 4 + 2 * cfg.k * 4 + \
+        2 * (cfg.k + cfg.window) * cfg.hidden * 2
+    flops = 2 * cfg.window * cfg.hq * cfg.prompt * 128
+    _line("token selections/s (window score + pool + top-k + hidden gather)", 1000 / ms, "selections/s", args, ms,
+          "c2_fastkv_tsp: prompt 32768, 32q/8kv, window 8, pool 7, top-6554 + 8 window rows, hidden 4096",
+          {"bytes_per_selection": nbytes, "hbm_gbs_algorithmic": round(nbytes / ms / 1e6, 1),
+           "mfma_gflop_per_selection": round(flops / 1e9, 3)})
+
+
+def bench_c3(args):
+    """FastKV decode under a 2048-row budget: decode steps of 32 layers (8
+    aliased caches) after the one-off selection, which is timed separately."""
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.fastkv import BudgetDecoder
+    cfg = synth.C3
+    s0, s1 = cfg.seg
+    w = gen.make_budget(cfg, "cuda")
+    kvs = [kvsel.KV(w.k_pool[p], w.v_pool[p], w.block_table, w.seq_len_sel, w.seg_begin, w.seg_end,
+                    max_seq_len=cfg.src_len + cfg.steps, max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+           for p in range(cfg.phys_layers)]
+    dec = BudgetDecoder(kvs, cfg.hq, cfg.k, cfg.layers, cfg.scale, cfg.window, cfg.pool, device="cuda")
+    torch.cuda.synchronize()
+    sel_ms = _timed(lambda i: dec.select(i % cfg.phys_layers, w.qwin[i % cfg.phys_layers], w.seq_len_sel),
+                    cfg.phys_layers, 2)
+    ms = _timed(lambda i: dec.step(w.q[i % cfg.steps], w.seq_len[i % cfg.steps]), args.steps, args.warmup)
+    per_t = [cfg.layers * (cfg.batch * cfg.hkv * (cfg.k + cfg.recent + t + 1) * 512 + cfg.batch * cfg.hq * 768 +
+                           cfg.batch * cfg.hkv * cfg.k * 4) for t in range(cfg.steps)]
+    nbytes = sum(per_t[(args.warmup + i) % cfg.steps] for i in range(args.steps)) / args.steps
+    sel_bytes = cfg.batch * cfg.hkv * cfg.src_len * 256
+    _line("decode steps/s (gathered attention over a 2048-row budget, 32 layers)", 1000 / ms, "steps/s", args, ms,
+          "c3_fastkv_budget_decode: batch 16, 32q/8kv, 131072-token context, 32 layers over 8 caches, "
+          "2048 kept + 64 recent + generated rows",
+          {"tokens_per_s": round(1000 / ms * cfg.batch, 1), "bytes_per_step_avg": int(nbytes),
+           "hbm_gbs_algorithmic": round(nbytes / ms / 1e6, 1),
+           "selection_ms_per_cache": round(sel_ms, 3), "selection_bytes_per_cache": sel_bytes,
+           "selection_hbm_gbs_algorithmic": round(sel_bytes / sel_ms / 1e6, 1)})
+
+
+def bench_c4(args):
+    """HPD-style branched decode: 512 branches over one shared prefix, 28
+    layers, focal layers {3, 14}, 32-step cycle."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.decode import FocalDecoder
+    cfg = synth.C4
+    w = gen.make_focal(cfg, "cuda")
+    max_len = int(w.seq_len_np.max())
+    kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+           for l in range(cfg.layers)]
+    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device="cuda")
+    T = cfg.steps
+    ms = _timed(lambda i: dec.step(i % T, w.q[i % T], w.seq_len[i % T]), args.steps, args.warmup)
+    suf = w.suffix_len.astype(np.int64)
+    logical, unique = [], []
+    for t in range(T):
+        tail = suf + t + 1
+        n = cfg.prefix_len + tail
+        lg = 2 * n.sum() + (cfg.layers - 2 - (3 if t == 0 else 0)) * (cfg.k + cfg.n_always + tail).sum() + \
+            (3 * n.sum() if t == 0 else 0)
+        un = cfg.layers * (cfg.prefix_len + tail.sum())      # every row once per layer at most
+        logical.append(lg * cfg.hkv * 512)
+        unique.append(un * cfg.hkv * 512)
+    lb = sum(logical[(args.warmup + i) % T] for i in range(args.steps)) / args.steps
+    ub = sum(unique[(args.warmup + i) % T] for i in range(args.steps)) / args.steps
+    _line("branched decode steps/s (28 layers over 512 branches)", 1000 / ms, "steps/s", args, ms,
+          "c4_hpd_branched: 512 branches, shared 3072 visual + 1024 layout prefix, suffix U[32,1024], "
+          "16q/8kv, focal {3,14}, top-154",
+          {"tokens_per_s": round(1000 / ms * cfg.batch, 1), "bytes_per_step_logical": int(lb),
+           "bytes_per_step_unique_upper": int(ub),
+           "hbm_gbs_logical": round(lb / ms / 1e6, 1)})
+
+
+OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4}
 
 
 if __name__ == "__main__":

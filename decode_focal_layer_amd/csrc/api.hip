@@ -347,6 +347,7 @@ kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_r
     a.tile_rows = sp.wp.tile_rows;
     a.ntiles = sp.wp.ntiles;
     a.stat = reinterpret_cast<float *>(w + sp.wp.off_stat);
+    a.rowstat = reinterpret_cast<double *>(w + sp.wp.off_rowstat);
     a.part = reinterpret_cast<double *>(w + sp.wp.off_part);
     a.ld64 = sp.wp.ld64;
     hipError_t e = launch_window(a, sp.wp, kv->batch, s);

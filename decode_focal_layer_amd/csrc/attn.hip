@@ -443,9 +443,10 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 }
 
 // threads per attention work-group for a head group size
-constexpr int attn_threads(int G) {
-  return G <= 2 ? KVSEL_ATTN_NT2 : (G == 4 ? (KVSEL_ATTN_NT2 < 512 ? KVSEL_ATTN_NT2 : 512) : 256);
-}
+#ifndef KVSEL_ATTN_NT4
+#define KVSEL_ATTN_NT4 512
+#endif
+constexpr int attn_threads(int G) { return G <= 2 ? KVSEL_ATTN_NT2 : (G == 4 ? KVSEL_ATTN_NT4 : 256); }
 
 template <int G>
 hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {

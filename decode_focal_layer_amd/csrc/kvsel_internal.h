@@ -129,12 +129,13 @@ struct WinArgs {
   double scale;
   int32_t tile_rows, ntiles;   // keys per work-group tile, tiles per sequence
   float *stat;           // [batch][hkv][ntiles][32] x {max dot (f32), pad, sum (f64)}
+  double *rowstat;       // [batch][hkv][32] x {max dot, 1 / sum}, merged over tiles
   double *part;          // [batch][hkv][ld64] fp64 group scores
   int64_t ld64;
 };
 struct WinPlan {
   int tile_rows = 0, ntiles = 0, rows_q = 0;
-  size_t off_stat = 0, off_part = 0, total = 0;
+  size_t off_stat = 0, off_rowstat = 0, off_part = 0, total = 0;
   int64_t ld64 = 0;
 };
 WinPlan win_plan(int batch, int hkv, int group, int n_rows, int max_seq_len, int max_seg_len);

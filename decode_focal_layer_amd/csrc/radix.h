@@ -1,12 +1,17 @@
 // Exact top-k of one row held as order-preserving uint32 keys, for one
 // work-group: ties to the lower index, output ascending.
 //
-// The k-th largest key T is found by a radix select (digits of 11, 11 and 10
-// bits, LDS histograms); a final pass over the row in index order keeps every
-// key > T and the first (k - #keys > T) keys equal to T, placing them with
-// wave ballots, so the output is ascending without a sort.  Only keys >= theta
-// are ranked; theta must not exceed the k-th largest key (a warm start's
-// minimum does not: at least k keys reach it).
+// The k-th largest key T is found by a radix select over (key - min), where
+// min and max are taken over the candidate keys first: the digits (11 bits,
+// from the top of the candidates' range down) then spread over the range the
+// row actually occupies.  Scores of one softmax share a few float exponents,
+// so digits taken from the raw key would put nearly every key into a handful
+// of histogram bins (serialised LDS atomics).  The output pass gives each
+// thread a contiguous chunk of indices: it counts its keys > T and == T, two
+// block scans place the chunks, and every thread writes its chosen indices in
+// order -- so the output is ascending and ties go to the lower index.  Only
+// keys >= theta are ranked; theta must not exceed the k-th largest key (a warm
+// start's minimum does not: at least k keys reach it).
 #pragma once
 
 #include "common.h"
@@ -86,7 +91,7 @@ __device__ uint32_t warm_theta(KeyFn key, const int32_t *wi, int n, int k, Radix
 }
 
 // keys: key(i) for i in [0, n).  Writes k indices to dst (ascending); when
-// n < k the n indices are followed by -1.
+// n <= k all n indices are kept, followed by -1.
 template <int NT, typename KeyFn>
 __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst, RadixShared<NT> &sh) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -94,33 +99,66 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     for (int i = tid; i < k; i += NT) dst[i] = i < n ? i : -1;
     return;
   }
+  // ---- range of the candidate keys ----
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t x = key(i);
+    if (x >= theta) {
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor(lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    sh.w1[w] = lo;
+    sh.w2[w] = hi;
+  }
+  __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0u;
+  for (int i = 0; i < NT / 64; ++i) {
+    lo = min(lo, sh.w1[i]);
+    hi = max(hi, sh.w2[i]);
+  }
+  __syncthreads();
+  const uint32_t range = hi - lo;
+  const int nbits = range == 0u ? 0 : 32 - __clz(range);
+
+  // ---- radix select of the k-th largest (key - lo) among candidates ----
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kBits[3] = {11, 11, 10};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = kShift[pass], nb = 1 << kBits[pass];
+  for (int top = nbits; top > 0; top -= 11) {
+    const int bits = top < 11 ? top : 11;
+    const int shift = top - bits;
+    const int nb = 1 << bits;
     for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t x = key(i);
-      if (x >= theta && (x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & (nb - 1)], 1u);
+      const uint32_t r = x - lo;
+      if (x >= theta && (r & pmask) == prefix) atomicAdd(&sh.hist[(r >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // thread t owns bins [t*per, (t+1)*per); count of the bins above its range
-    const int per = nb / NT;
+    // thread t owns bins [t*per, (t+1)*per) (empty past nb); bins above its range
+    const int per = (nb + NT - 1) / NT;
     uint32_t c = 0;
-    for (int i = 0; i < per; ++i) c += sh.hist[tid * per + i];
+    for (int i = 0; i < per; ++i) {
+      const int bi = tid * per + i;
+      c += bi < nb ? sh.hist[bi] : 0u;
+    }
     uint32_t total;
     const uint32_t below = excl_scan<NT>(c, sh.w1, total);
     const uint32_t above = total - below - c;
     if (above < (uint32_t)krem && (uint32_t)krem <= above + c) {
       uint32_t run = above;
       for (int i = per - 1; i >= 0; --i) {
-        const uint32_t hcount = sh.hist[tid * per + i];
+        const int bi = tid * per + i;
+        const uint32_t hcount = bi < nb ? sh.hist[bi] : 0u;
         if (run + hcount >= (uint32_t)krem) {
-          sh.misc[0] = (uint32_t)(tid * per + i);
+          sh.misc[0] = (uint32_t)bi;
           sh.misc[1] = run;
           break;
         }
@@ -133,39 +171,36 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     krem -= (int)sh.misc[1];
     __syncthreads();
   }
-  const uint32_t T = prefix;
+  const uint32_t T = lo + prefix;        // the k-th largest key
   const uint32_t keq = (uint32_t)krem;   // keys equal to T to keep (>= 1)
 
-  uint32_t written = 0, eq_seen = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int base = 0; base < n && written < (uint32_t)k; base += NT) {
-    const int i = base + tid;
-    const uint32_t x = i < n ? key(i) : 0u;
-    const bool gt = i < n && x > T;
-    const bool eq = i < n && x == T;
-    const uint64_t meq = __ballot(eq);
-    if (lane == 0) sh.w1[w] = (uint32_t)__popcll(meq);
-    __syncthreads();
-    uint32_t eq_pre = 0, eq_tot = 0;
-    for (int j = 0; j < NT / 64; ++j) {
-      eq_pre += j < w ? sh.w1[j] : 0u;
-      eq_tot += sh.w1[j];
+  // ---- ordered output: contiguous index chunks per thread ----
+  const int C = (n + NT - 1) / NT;
+  const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
+  uint32_t cg = 0, ce = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = key(i);
+    cg += x > T ? 1u : 0u;
+    ce += x == T ? 1u : 0u;
+  }
+  uint32_t tg, te;
+  const uint32_t eq_before = excl_scan<NT>(ce, sh.w1, te);
+  const uint32_t gt_before = excl_scan<NT>(cg, sh.w2, tg);
+  // equal keys kept by earlier chunks, and so this chunk's output position
+  const uint32_t eq_kept_before = eq_before < keq ? eq_before : keq;
+  uint32_t pos = gt_before + eq_kept_before;
+  uint32_t eq_seen = eq_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = key(i);
+    bool take = x > T;
+    if (x == T) {
+      take = eq_seen < keq;
+      ++eq_seen;
     }
-    eq_pre += (uint32_t)__popcll(meq & lt);
-    const bool take = gt || (eq && eq_seen + eq_pre < keq);
-    const uint64_t mt = __ballot(take);
-    if (lane == 0) sh.w2[w] = (uint32_t)__popcll(mt);
-    __syncthreads();
-    uint32_t t_pre = 0, t_tot = 0;
-    for (int j = 0; j < NT / 64; ++j) {
-      t_pre += j < w ? sh.w2[j] : 0u;
-      t_tot += sh.w2[j];
+    if (take) {
+      if (pos < (uint32_t)k) dst[pos] = i;
+      ++pos;
     }
-    t_pre += (uint32_t)__popcll(mt & lt);
-    if (take && written + t_pre < (uint32_t)k) dst[written + t_pre] = i;
-    written += t_tot;
-    eq_seen += eq_tot;
-    __syncthreads();
   }
 }
 

@@ -16,16 +16,33 @@ namespace kvsel {
 
 namespace {
 
-constexpr int kLdsKeys = 12288;   // rows up to this length are staged in LDS (48 KiB)
+// rows up to this length are staged in LDS (144 KiB of dynamic LDS; gfx950
+// gives a work-group up to 160 KiB)
+constexpr int kLdsKeys = 36864;
 
 template <int NT, bool IN_LDS>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t s_keys[IN_LDS ? kLdsKeys : 1];
+  extern __shared__ uint32_t s_keys[];
   __shared__ RadixShared<NT> sh;
   const int row = blockIdx.x;
   const float *src = a.scores + (size_t)row * a.ld;
   if (IN_LDS) {
-    for (int i = threadIdx.x; i < a.n; i += NT) s_keys[i] = okey(src[i]);
+    // eight loads in flight per thread before the LDS stores (one memory
+    // latency per eight keys instead of one per key)
+    constexpr int B = 8;
+    for (int base = 0; base < a.n; base += B * NT) {
+      float v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int i = base + j * NT + threadIdx.x;
+        v[j] = i < a.n ? src[i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int i = base + j * NT + threadIdx.x;
+        if (i < a.n) s_keys[i] = okey(v[j]);
+      }
+    }
     __syncthreads();
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
@@ -37,7 +54,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.n <= kLdsKeys) {
-    hipLaunchKernelGGL((topk_kernel<1024, true>), dim3(a.rows), dim3(1024), 0, s, a);
+    static bool attr_set = false;   // LDS above 64 KiB must be allowed once
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)topk_kernel<1024, true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsKeys * 4);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((topk_kernel<1024, true>), dim3(a.rows), dim3(1024), (size_t)a.n * 4, s, a);
   } else {
     hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(a.rows), dim3(1024), 0, s, a);
   }

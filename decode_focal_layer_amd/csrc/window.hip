@@ -14,8 +14,9 @@
 //     query row and 16 keys of every 32-key block: the per-row running max and
 //     sum of 2^((dot - max) * scale * log2 e) stay lane-local (sum in fp64).
 //     Each tile writes (max, sum) per query row.
-//   pass 2 (scores): the tiles' statistics are merged per query row in fp64;
-//     MFMA with the query rows as A and the keys as B, so each lane holds one
+//   merge: one small kernel combines the tiles' statistics per query row in
+//     fp64 into (max, 1 / sum);
+//   pass 2 (scores): MFMA with the query rows as A and the keys as B, so each lane holds one
 //     key and 16 query rows: the normalised probabilities are summed over the
 //     rows lane-locally in fp64, then across the two half-waves.
 //   The fp64 per-(kv head) scores feed the group-sum / pool post-pass.
@@ -106,9 +107,13 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
   const double c = a.scale * 1.4426950408889634;
   float m = -INFINITY;
   double z = 0.0;
+  bf16x8 knext[8];
+  if (t0 + wave * 32 < t1) load_k(a, b, g, t0 + wave * 32 + qr, t1, lane, knext);
   for (int kb = t0 + wave * 32; kb < t1; kb += 128) {
-    bf16x8 kop[8];
-    load_k(a, b, g, kb + qr, t1, lane, kop);   // A rows: keys kb .. kb+31
+    bf16x8 kop[8];   // A rows: keys kb .. kb+31; the next block's rows are loaded meanwhile
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kop[kk] = knext[kk];
+    if (kb + 128 < t1) load_k(a, b, g, kb + 128 + qr, t1, lane, knext);
     f32x16 d = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], d, 0, 0, 0);
@@ -149,6 +154,41 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
   }
 }
 
+// per query row: merge the key tiles' (max, sum) into (max, 1 / sum);
+// grid (kv heads, sequences), 1024 threads = 32 query rows x 32 tile strides
+__global__ __launch_bounds__(1024) void window_merge_kernel(WinArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int qr = tid & 31, part = tid >> 5;
+  __shared__ float s_m[32][32];
+  __shared__ double s_z[32][32];
+  const WinView v = win_view(a, b);
+  const int nt = min((v.n + a.tile_rows - 1) / a.tile_rows, a.ntiles);
+  const double c = a.scale * 1.4426950408889634;
+  const float *st0 = a.stat + (((size_t)b * a.hkv + g) * a.ntiles * 32 + qr) * 4;
+  float m = -INFINITY;
+  for (int t = part; t < nt; t += 32) m = fmaxf(m, st0[(size_t)t * 32 * 4]);
+  s_m[part][qr] = m;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int p = 0; p < 32; ++p) M = fmaxf(M, s_m[p][qr]);
+  double z = 0.0;
+  if (M != -INFINITY)
+    for (int t = part; t < nt; t += 32) {
+      const float mt = st0[(size_t)t * 32 * 4];
+      if (mt != -INFINITY)
+        z += *reinterpret_cast<const double *>(st0 + (size_t)t * 32 * 4 + 2) * exp2_acc(((double)mt - (double)M) * c);
+    }
+  s_z[part][qr] = z;
+  __syncthreads();
+  if (part == 0) {
+    double Z = 0.0;
+    for (int p = 0; p < 32; ++p) Z += s_z[p][qr];
+    double *rs = a.rowstat + (((size_t)b * a.hkv + g) * 32 + qr) * 2;
+    rs[0] = (double)M;
+    rs[1] = Z > 0.0 ? 1.0 / Z : 0.0;
+  }
+}
+
 __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -159,19 +199,9 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
   __shared__ double s_M[32], s_iZ[32];
   const double c = a.scale * 1.4426950408889634;
   if (tid < 32) {
-    const int nt = min((v.n + a.tile_rows - 1) / a.tile_rows, a.ntiles);
-    const float *st0 = a.stat + (((size_t)b * a.hkv + g) * a.ntiles * 32 + tid) * 4;
-    float M = -INFINITY;
-    for (int t = 0; t < nt; ++t) M = fmaxf(M, st0[(size_t)t * 32 * 4]);
-    double Z = 0.0;
-    if (M != -INFINITY)
-      for (int t = 0; t < nt; ++t) {
-        const float mt = st0[(size_t)t * 32 * 4];
-        if (mt != -INFINITY)
-          Z += *reinterpret_cast<const double *>(st0 + (size_t)t * 32 * 4 + 2) * exp2_acc(((double)mt - (double)M) * c);
-      }
-    s_M[tid] = (double)M;
-    s_iZ[tid] = Z > 0.0 ? 1.0 / Z : 0.0;
+    const double *rs = a.rowstat + (((size_t)b * a.hkv + g) * 32 + tid) * 2;
+    s_M[tid] = rs[0];
+    s_iZ[tid] = rs[1];
   }
   __syncthreads();
 
@@ -180,9 +210,13 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
   const int kl = lane & 31, hf = lane >> 5;
   double *dst = a.part + ((size_t)b * a.hkv + g) * a.ld64;
   // blocks aligned to the tile start so that each wave's keys are contiguous
+  bf16x8 knext[8];
+  if (t0 + wave * 32 < t1) load_k(a, b, g, t0 + wave * 32 + kl, t1, lane, knext);
   for (int kb = t0 + wave * 32; kb < t1; kb += 128) {
-    bf16x8 kop[8];
-    load_k(a, b, g, kb + kl, t1, lane, kop);   // B columns: keys kb .. kb+31
+    bf16x8 kop[8];   // B columns: keys kb .. kb+31; the next block's rows are loaded meanwhile
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kop[kk] = knext[kk];
+    if (kb + 128 < t1) load_k(a, b, g, kb + 128 + kl, t1, lane, knext);
     f32x16 d = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[kk], kop[kk], d, 0, 0, 0);
@@ -204,7 +238,8 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
 WinPlan win_plan(int batch, int hkv, int group, int n_rows, int max_seq_len, int max_seg_len) {
   WinPlan p;
   const int64_t pairs = (int64_t)batch * hkv;
-  int64_t t = ((int64_t)max_seq_len * pairs + 2047) / 2048;
+  // about two work-groups per CU (512), at least 128 keys each
+  int64_t t = ((int64_t)max_seq_len * pairs + 511) / 512;
   t = (t + 127) / 128 * 128;
   if (t < 128) t = 128;
   if (t > 2048) t = 2048;
@@ -216,6 +251,8 @@ WinPlan win_plan(int batch, int hkv, int group, int n_rows, int max_seq_len, int
   size_t off = kCounterBytes;
   p.off_stat = off;
   off = align_up(off + (size_t)pairs * p.ntiles * 32 * 4 * sizeof(float));
+  p.off_rowstat = off;
+  off = align_up(off + (size_t)pairs * 32 * 2 * sizeof(double));
   p.off_part = off;
   off = align_up(off + (size_t)pairs * p.ld64 * sizeof(double));
   p.total = off;
@@ -226,6 +263,9 @@ hipError_t launch_window(const WinArgs &a, const WinPlan &p, int batch, hipStrea
   dim3 grid(p.ntiles, a.hkv, batch), block(kWinThreads);
   hipLaunchKernelGGL(window_stats_kernel, grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(window_merge_kernel, dim3(a.hkv, batch), dim3(1024), 0, s, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(window_scores_kernel, grid, block, 0, s, a);
   return hipGetLastError();
