@@ -49,6 +49,24 @@
 #ifndef KVSEL_ATTN_PIPE
 #define KVSEL_ATTN_PIPE 0
 #endif
+// 1: a work-group barrier after every iteration keeps the waves in step
+#ifndef KVSEL_ATTN_SYNC
+#define KVSEL_ATTN_SYNC 0
+#endif
+// row schedule: 0 = rows interleaved over all lane groups; 1 = each wave a
+// contiguous range, older waves (served first by the issue arbiter, so
+// ahead) given KVSEL_ATTN_LAG4 / 4 iterations' worth more rows than younger
+// ones so that all waves finish together
+#ifndef KVSEL_ATTN_SCHED
+#define KVSEL_ATTN_SCHED 0
+#endif
+#ifndef KVSEL_ATTN_LAG4
+#define KVSEL_ATTN_LAG4 4
+#endif
+// 1: rotate the waves' issue priorities every iteration
+#ifndef KVSEL_ATTN_ROTPRIO
+#define KVSEL_ATTN_ROTPRIO 0
+#endif
 // minimum resident waves per SIMD the compiler must allow for (0: no bound)
 #ifndef KVSEL_ATTN_WPE
 #define KVSEL_ATTN_WPE 0
@@ -64,26 +82,19 @@ struct SeqView {
   int n, s0, s1, nR;
 };
 
-__device__ __forceinline__ SeqView seq_view(const AttnArgs &a, int b, bool dense) {
+// bounds of sequence b from its raw seq_len / segment values, clamped
+__device__ __forceinline__ SeqView seq_view_of(const AttnArgs &a, int n_raw, int s0_raw, int s1_raw, bool dense) {
   SeqView v;
   const int cap = a.max_blocks * kBlk;
-  v.n = clampi(a.seq_len[b], 0, cap);
-  v.s0 = clampi(a.seg_begin[b], 0, v.n);
-  v.s1 = clampi(a.seg_end[b], v.s0, v.n);
+  v.n = clampi(n_raw, 0, cap);
+  v.s0 = clampi(s0_raw, 0, v.n);
+  v.s1 = clampi(s1_raw, v.s0, v.n);
   v.nR = dense ? v.n : (a.k + v.s0 + (v.n - v.s1));
   return v;
 }
 
-// virtual row j -> logical row (or -1)
-__device__ __forceinline__ int virt_to_row(const AttnArgs &a, const SeqView &v, int b, int g, int j,
-                                           bool dense) {
-  if (dense) return j;
-  if (j < a.k) {
-    const int r = a.idx[((size_t)b * a.hkv + g) * a.k + j];
-    return (r >= 0 && r < v.s1 - v.s0) ? v.s0 + r : -1;
-  }
-  if (j < a.k + v.s0) return j - a.k;
-  return v.s1 + (j - a.k - v.s0);
+__device__ __forceinline__ SeqView seq_view(const AttnArgs &a, int b, bool dense) {
+  return seq_view_of(a, a.seq_len[b], a.seg_begin[b], a.seg_end[b], dense);
 }
 
 __device__ __forceinline__ uint32_t row_to_phys(const AttnArgs &a, int b, int g, int row) {
@@ -143,8 +154,35 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   __shared__ float s_m[NW][G], s_l[NW][G];
   extern __shared__ float s_logit[];   // MODE 2: [G][seg_cap]
 
-  const SeqView v = seq_view(a, b, dense);
   const int start = split * a.rps;
+  constexpr int RPT = kAttnMaxRps / NT;
+  constexpr int TPT = kTabLds / NT;
+
+  // Prologue.  Every load it needs is issued before any result is used: the
+  // sequence bounds, the query, the block table (into LDS when it fits) and
+  // the kept indices of this split's rows, read at clamped addresses so that
+  // no load waits for another.  Then each virtual row is resolved to its
+  // physical row in LDS, and the streaming loop issues only K/V loads.
+  const int n_raw = a.seq_len[b], s0_raw = a.seg_begin[b], s1_raw = a.seg_end[b];
+  const uint16_t *qbase = a.q + ((size_t)b * a.hq + g * G) * kD + sub * 8;
+  uint4 qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) qr[h] = *reinterpret_cast<const uint4 *>(qbase + h * kD);
+  const bool tab_lds = a.max_blocks <= kTabLds;
+  const int32_t *tab = a.block_table + (size_t)b * a.max_blocks;
+  int tv[TPT];
+  if (tab_lds) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) tv[i] = tab[min(tid + i * NT, a.max_blocks - 1)];
+  }
+  int iv[RPT];
+  if (!dense && a.k > 0) {   // k = 0: idx may be null and no row is read from it
+    const int32_t *ib = a.idx + ((size_t)b * a.hkv + g) * a.k;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      if (i * NT < a.rps) iv[i] = ib[min(start + tid + i * NT, a.k - 1)];
+  }
+  const SeqView v = seq_view_of(a, n_raw, s0_raw, s1_raw, dense);
   const int cnt = max(0, min(a.rps, v.nR - start));   // rows of this split
 
   int lo = 0, hi = 0;   // logical rows whose logits are stored, at row - lo (dense only)
@@ -156,40 +194,32 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     else { lo = 0; hi = v.n; }
   }
 
-  // Prologue: the kept indices and the block table are loaded together (one
-  // memory latency), then each virtual row is resolved to its physical row.
-  {
-    constexpr int RPT = kAttnMaxRps / NT;
-    const bool tab_lds = a.max_blocks <= kTabLds;
-    int lr[RPT];
+  if (tab_lds) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int t = tid + i * NT;
-      lr[i] = t < cnt ? virt_to_row(a, v, b, g, start + t, dense) : -1;
-    }
-    if (tab_lds)
-      for (int i = tid; i < a.max_blocks; i += NT) s_tab[i] = a.block_table[(size_t)b * a.max_blocks + i];
-    __syncthreads();
+    for (int i = 0; i < TPT; ++i)
+      if (tid + i * NT < a.max_blocks) s_tab[tid + i * NT] = tv[i];
+  }
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int t = tid + i * NT;
-      if (t < cnt) {
-        const int row = lr[i];
-        uint32_t pr = kNoRow;
-        if (row >= 0) {
-          const int blk = tab_lds ? s_tab[row >> 4] : a.block_table[(size_t)b * a.max_blocks + (row >> 4)];
-          if (blk >= 0 && (int64_t)blk < a.num_blocks)
-            pr = ((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row & 15);
-        }
-        s_prow[t] = pr;
+  for (int i = 0; i < RPT; ++i) {
+    const int t = tid + i * NT;
+    if (i * NT < a.rps && t < cnt) {
+      const int j = start + t;   // virtual row
+      int row;
+      if (dense) row = j;
+      else if (j < a.k) row = (iv[i] >= 0 && iv[i] < v.s1 - v.s0) ? v.s0 + iv[i] : -1;
+      else if (j < a.k + v.s0) row = j - a.k;
+      else row = v.s1 + (j - a.k - v.s0);
+      uint32_t pr = kNoRow;
+      if (row >= 0) {
+        const int blk = tab_lds ? s_tab[row >> 4] : tab[row >> 4];
+        if (blk >= 0 && (int64_t)blk < a.num_blocks)
+          pr = ((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row & 15);
       }
+      s_prow[t] = pr;
     }
   }
 
-  const uint16_t *qbase = a.q + ((size_t)b * a.hq + g * G) * kD + sub * 8;
-  uint4 qr[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) qr[h] = *reinterpret_cast<const uint4 *>(qbase + h * kD);
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -203,12 +233,28 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   const uint16_t *kbase = a.k_pool + sub * 8;
   const uint16_t *vbase = a.v_pool + sub * 8;
 
+  // Row schedule.  Interleaved: iteration rows [base, base + ITER), lane
+  // group grp takes base + grp + NG*u.  Wave ranges: wave w walks
+  // [t_beg, t_end) 4*U rows at a time, its lane group takes base + grp%4 + 4*u.
+#if KVSEL_ATTN_SCHED == 1
+  auto wave_off = [&](int w) -> int {
+    const int skew = cnt >= 2 * ITER ? (2 * KVSEL_ATTN_LAG4 * w * (NW - w)) / NW : 0;
+    return min(cnt, (int)(((int64_t)w * cnt) / NW) + skew);
+  };
+  const int t_beg = wave_off(wave), t_end = wave_off(wave + 1);
+  constexpr int STEP = 4 * U;
+#define KVSEL_ROWT(base, u) ((base) + (grp & 3) + 4 * (u))
+#else
+  const int t_beg = 0, t_end = cnt;
+  constexpr int STEP = ITER;
+#define KVSEL_ROWT(base, u) ((base) + grp + NG * (u))
+#endif
   // K/V rows of one iteration into registers
   auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = base + grp + NG * u;
-      const uint32_t pr = t < cnt ? s_prow[t] : kNoRow;
+      const int t = KVSEL_ROWT(base, u);
+      const uint32_t pr = t < t_end ? s_prow[t] : kNoRow;
       ok[u] = pr != kNoRow;
       // a row that is not attended reads this lane's query (a valid, finite
       // 16 bytes) and gets probability 0
@@ -226,7 +272,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     if (MODE != 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int row = start + base + grp + NG * u;   // dense: logical row = virtual row
+        const int row = start + KVSEL_ROWT(base, u);   // dense: logical row = virtual row
         if (ok[u] && sub < G && row >= lo && row < hi) {
           float dv = dot[u][0];
 #pragma unroll
@@ -278,22 +324,36 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   if (KVSEL_ATTN_PIPE) {
     uint4 ka[U], va[U], kb2[U], vb2[U];
     bool oa[U], ob[U];
-    if (cnt > 0) load_rows(0, ka, va, oa);
-    for (int base = 0; base < cnt; base += 2 * ITER) {
-      if (base + ITER < cnt) load_rows(base + ITER, kb2, vb2, ob);
+    if (t_beg < t_end) load_rows(t_beg, ka, va, oa);
+    for (int base = t_beg; base < t_end; base += 2 * STEP) {
+      if (base + STEP < t_end) load_rows(base + STEP, kb2, vb2, ob);
       consume(base, ka, va, oa);
-      if (base + ITER >= cnt) break;
-      if (base + 2 * ITER < cnt) load_rows(base + 2 * ITER, ka, va, oa);
-      consume(base + ITER, kb2, vb2, ob);
+      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
+      if (base + STEP >= t_end) break;
+      if (base + 2 * STEP < t_end) load_rows(base + 2 * STEP, ka, va, oa);
+      consume(base + STEP, kb2, vb2, ob);
+      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
     }
   } else {
-    for (int base = 0; base < cnt; base += ITER) {
+    int it = 0;
+    for (int base = t_beg; base < t_end; base += STEP, ++it) {
+      if (KVSEL_ATTN_ROTPRIO) {
+        switch ((wave + it) & 3) {
+          case 0: __builtin_amdgcn_s_setprio(0); break;
+          case 1: __builtin_amdgcn_s_setprio(1); break;
+          case 2: __builtin_amdgcn_s_setprio(2); break;
+          default: __builtin_amdgcn_s_setprio(3); break;
+        }
+      }
       uint4 kr[U], vr[U];
       bool ok[U];
       load_rows(base, kr, vr, ok);
       consume(base, kr, vr, ok);
+      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
     }
+    if (KVSEL_ATTN_ROTPRIO) __builtin_amdgcn_s_setprio(0);
   }
+#undef KVSEL_ROWT
 
   // merge the four lane groups of each wave (lanes sub, sub+16, sub+32, sub+48)
 #pragma unroll
@@ -356,13 +416,11 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     // focal selection from the LDS logits (FastOCR Focal-Guided Pruning)
     __shared__ RadixShared<NT> sh;
     __shared__ double s_fm[G], s_fiz[G];
-    __shared__ float s_redf[NW];
-    __shared__ double s_redd[16];
     __syncthreads();
     const int seg = hi - lo;
     const double c = a.scale * 1.4426950408889634;
     auto logit = [&](int hh, int i) { return s_logit[hh * a.seg_cap + i]; };
-    focal_stats<NT>(logit, G, seg, c, s_fm, s_fiz, s_redf, s_redd);
+    focal_stats<NT, G>(logit, G, seg, c, s_fm, s_fiz);
     uint32_t *keys = reinterpret_cast<uint32_t *>(s_logit);   // head 0's row, rewritten in place
     float *so = a.sel_scores != nullptr ? a.sel_scores + ((size_t)b * a.hkv + g) * a.sel_ld : nullptr;
     const int seg_out = so != nullptr ? (int)min((int64_t)seg, a.sel_ld) : seg;
@@ -446,11 +504,20 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 #ifndef KVSEL_ATTN_NT4
 #define KVSEL_ATTN_NT4 512
 #endif
+#ifndef KVSEL_ATTN_U4
+#define KVSEL_ATTN_U4 KVSEL_ATTN_U
+#endif
+#ifndef KVSEL_ATTN_WAVES_PER_CU4
+#define KVSEL_ATTN_WAVES_PER_CU4 8
+#endif
 constexpr int attn_threads(int G) { return G <= 2 ? KVSEL_ATTN_NT2 : (G == 4 ? KVSEL_ATTN_NT4 : 256); }
+constexpr int attn_unroll(int G) { return G == 4 ? KVSEL_ATTN_U4 : KVSEL_ATTN_U; }
+constexpr int attn_waves_per_cu(int G) { return G == 4 ? KVSEL_ATTN_WAVES_PER_CU4 : KVSEL_ATTN_WAVES_PER_CU; }
 
 template <int G>
 hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
   constexpr int NT = attn_threads(G);
+  constexpr int U = attn_unroll(G);
   dim3 grid(a.nsplit, a.hkv, batch);
   if (a.sel_idx != nullptr) {
     if (a.nsplit != 1) return hipErrorInvalidValue;
@@ -458,18 +525,18 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
     if (dyn > kFusedLdsBytes) return hipErrorInvalidValue;
     static bool attr_set = false;   // the LDS above 64 KiB must be allowed once per kernel
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<G, NT, KVSEL_ATTN_U, 2>,
+      hipError_t e = hipFuncSetAttribute((const void *)attn_kernel<G, NT, U, 2>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedLdsBytes);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 2>), grid, dim3(NT), dyn, s, a);
+    hipLaunchKernelGGL((attn_kernel<G, NT, U, 2>), grid, dim3(NT), dyn, s, a);
     return hipGetLastError();
   }
   if (a.logits != nullptr)
-    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 1>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<G, NT, U, 1>), grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<G, NT, KVSEL_ATTN_U, 0>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<G, NT, U, 0>), grid, dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel<G>, dim3(a.hkv, batch), dim3(G * kD), 0, s, a);
@@ -484,7 +551,7 @@ AttnPlan attn_plan(int batch, int hkv, int hq, int max_rows, int logit_mode, int
   const int64_t pairs = (int64_t)batch * hkv;
   const int G = hq / hkv;
   // work-group slots: 256 CUs x the waves per CU aimed for / waves per work-group
-  const int64_t slots = 256 * (KVSEL_ATTN_WAVES_PER_CU / (attn_threads(G) / 64));
+  const int64_t slots = 256 * (attn_waves_per_cu(G) / (attn_threads(G) / 64));
   int64_t nsplit = (slots + pairs - 1) / pairs;
   // keep at least 256 rows per split, and at most kAttnMaxRps
   const int64_t by_rows = ((int64_t)max_rows + 255) / 256;

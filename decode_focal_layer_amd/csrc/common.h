@@ -55,83 +55,71 @@ __device__ __forceinline__ double exp2_acc(double x) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// ---- block reductions (blockDim.x a multiple of 64, <= 1024) ----
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// ---- wave64 reductions on DPP row operations and lane reads (no LDS) ----
+// Within a 16-lane row every step combines a value with a mirrored partner,
+// so all lanes of the row end with the same bits; the four row results are
+// then read as scalars and combined in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_u<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_u<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_u<0x140>(v));   // row_mirror
+  return op(op(lane_u(v, 0), lane_u(v, 16)), op(lane_u(v, 32), lane_u(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u<CTRL>((uint32_t)u), hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = lane_u((uint32_t)u, l), hi = lane_u((uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// sum over the wave in a fixed order, the same bits in every lane
 __device__ __forceinline__ double wave_sum_d(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// scratch must hold blockDim.x/64 entries; result valid in every thread
-__device__ __forceinline__ float block_max(float v, float *scratch) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[w] = v;
-  __syncthreads();
-  float r = scratch[0];
-  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
-  return r;
-}
-__device__ __forceinline__ double block_sum_d(double v, double *scratch) {
-  v = wave_sum_d(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[w] = v;
-  __syncthreads();
-  double r = 0.0;
-  for (int i = 0; i < nw; ++i) r += scratch[i];
-  return r;
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
 }
 
-// Sum of val(i) over i in [0, n) with the reduction order of a 1024-thread
-// block: virtual thread v (= tid + r * NT) takes i = v, v + 1024, ... in
-// order, each virtual wave reduces with xor shuffles (32, 16, ..., 1), and the
-// 16 virtual-wave sums are added in order.  The result is bit-identical for
-// any NT dividing 1024.  scratch holds 16 doubles; result in every thread.
-template <int NT, typename F>
-__device__ __forceinline__ double vsum1024(F val, int n, double *scratch) {
-  constexpr int R = 1024 / NT;
-  const int tid = threadIdx.x;
-  double part[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    part[r] = 0.0;
-    for (int i = tid + r * NT; i < n; i += 1024) part[r] += val(i);
-    part[r] = wave_sum_d(part[r]);
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) scratch[(tid >> 6) + r * (NT / 64)] = part[r];
-  }
-  __syncthreads();
-  double s = 0.0;
-  for (int w = 0; w < 16; ++w) s += scratch[w];
-  __syncthreads();
-  return s;
-}
-
-// max of val(i) over i in [0, n); scratch holds NT/64 floats
-template <int NT, typename F>
-__device__ __forceinline__ float vmax(F val, int n, float *scratch) {
-  float m = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += NT) m = fmaxf(m, val(i));
-  m = wave_max(m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = m;
-  __syncthreads();
-  float r = scratch[0];
-  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, scratch[w]);
-  __syncthreads();
-  return r;
+// inclusive prefix sum over the lanes of the wave
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u<0x111>(v);   // row_shr:1 (lanes without a source add 0)
+  v += dpp_u<0x112>(v);   // row_shr:2
+  v += dpp_u<0x114>(v);   // row_shr:4
+  v += dpp_u<0x118>(v);   // row_shr:8
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t t0 = lane_u(v, 15), t1 = lane_u(v, 31), t2 = lane_u(v, 47);
+  return v + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
 }
 
 }  // namespace kvsel

@@ -7,9 +7,10 @@
 // row actually occupies.  Scores of one softmax share a few float exponents,
 // so digits taken from the raw key would put nearly every key into a handful
 // of histogram bins (serialised LDS atomics).  The output pass gives each
-// thread a contiguous chunk of indices: it counts its keys > T and == T, two
-// block scans place the chunks, and every thread writes its chosen indices in
-// order -- so the output is ascending and ties go to the lower index.  Only
+// wave a contiguous range of indices, read 64 consecutive keys at a time (no
+// LDS bank conflicts, coalesced global reads): the waves count their keys > T
+// and == T, and each then places its chosen indices in order with ballot
+// masks -- so the output is ascending and ties go to the lower index.  Only
 // keys >= theta are ranked; theta must not exceed the k-th largest key (a warm
 // start's minimum does not: at least k keys reach it).
 #pragma once
@@ -56,6 +57,45 @@ __device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t *ws, uint32_t
   return pre + x - v;
 }
 
+// f(i, key(i)) for i = tid, tid + NT, ... below n; each thread issues B key
+// reads before using them (one memory latency per B keys)
+template <int NT, int B, typename KeyFn, typename F>
+__device__ __forceinline__ void each_key(KeyFn key, int n, F f) {
+  for (int base = 0; base < n; base += B * NT) {
+    uint32_t x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      x[j] = i < n ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (i < n) f(i, x[j]);
+    }
+  }
+}
+
+// the calling wave walks [i0, i1) 64 consecutive keys at a time:
+// f(i, valid, key) in every lane, the same number of calls in each lane
+template <int B, typename KeyFn, typename F>
+__device__ __forceinline__ void each_key_wave(KeyFn key, int i0, int i1, F f) {
+  const int lane = threadIdx.x & 63;
+  for (int base = i0; base < i1; base += B * 64) {
+    uint32_t x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * 64 + lane;
+      x[j] = i < i1 ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int b2 = base + j * 64;
+      if (b2 < i1) f(b2 + lane, b2 + lane < i1, x[j]);
+    }
+  }
+}
+
 // theta from a warm selection: the smallest key at the warm indices, or 0 (rank
 // everything) if they are not strictly ascending and inside [0, n).
 template <int NT, typename KeyFn>
@@ -100,14 +140,14 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     return;
   }
   // ---- range of the candidate keys ----
+  constexpr int B = 8;
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t x = key(i);
+  each_key<NT, B>(key, n, [&](int, uint32_t x) {
     if (x >= theta) {
       lo = min(lo, x);
       hi = max(hi, x);
     }
-  }
+  });
   for (int o = 32; o > 0; o >>= 1) {
     lo = min(lo, (uint32_t)__shfl_xor(lo, o));
     hi = max(hi, (uint32_t)__shfl_xor(hi, o));
@@ -136,11 +176,10 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     const int nb = 1 << bits;
     for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t x = key(i);
+    each_key<NT, B>(key, n, [&](int, uint32_t x) {
       const uint32_t r = x - lo;
       if (x >= theta && (r & pmask) == prefix) atomicAdd(&sh.hist[(r >> shift) & (nb - 1)], 1u);
-    }
+    });
     __syncthreads();
     // thread t owns bins [t*per, (t+1)*per) (empty past nb); bins above its range
     const int per = (nb + NT - 1) / NT;
@@ -174,34 +213,41 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
   const uint32_t T = lo + prefix;        // the k-th largest key
   const uint32_t keq = (uint32_t)krem;   // keys equal to T to keep (>= 1)
 
-  // ---- ordered output: contiguous index chunks per thread ----
-  const int C = (n + NT - 1) / NT;
-  const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
-  uint32_t cg = 0, ce = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i);
-    cg += x > T ? 1u : 0u;
-    ce += x == T ? 1u : 0u;
+  // ---- ordered output: wave w owns indices [w*cw, (w+1)*cw), walked 64 at a time ----
+  constexpr int NW = NT / 64;
+  const int cw = (n + NW * 64 - 1) / (NW * 64) * 64;
+  const int w0 = min(n, w * cw), w1 = min(n, w0 + cw);
+  uint32_t cg = 0, ce = 0;   // this wave's keys above T and equal to T
+  each_key_wave<B>(key, w0, w1, [&](int, bool valid, uint32_t x) {
+    cg += (uint32_t)__popcll(__ballot(valid && x > T));
+    ce += (uint32_t)__popcll(__ballot(valid && x == T));
+  });
+  if (lane == 0) {
+    sh.w1[w] = cg;
+    sh.w2[w] = ce;
   }
-  uint32_t tg, te;
-  const uint32_t eq_before = excl_scan<NT>(ce, sh.w1, te);
-  const uint32_t gt_before = excl_scan<NT>(cg, sh.w2, tg);
-  // equal keys kept by earlier chunks, and so this chunk's output position
-  const uint32_t eq_kept_before = eq_before < keq ? eq_before : keq;
-  uint32_t pos = gt_before + eq_kept_before;
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int i = 0; i < w; ++i) {
+    gt_before += sh.w1[i];
+    eq_before += sh.w2[i];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;   // lanes below this one
+  // taken keys before this wave: all of its larger keys and the equal keys up to keq
+  uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
   uint32_t eq_seen = eq_before;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i);
-    bool take = x > T;
-    if (x == T) {
-      take = eq_seen < keq;
-      ++eq_seen;
-    }
+  each_key_wave<B>(key, w0, w1, [&](int i, bool valid, uint32_t x) {
+    const bool eq = valid && x == T;
+    const uint64_t me = __ballot(eq);
+    const bool take = valid && (x > T || (eq && eq_seen + (uint32_t)__popcll(me & lt) < keq));
+    const uint64_t mt = __ballot(take);
     if (take) {
-      if (pos < (uint32_t)k) dst[pos] = i;
-      ++pos;
+      const uint32_t p = pos + (uint32_t)__popcll(mt & lt);
+      if (p < (uint32_t)k) dst[p] = i;
     }
-  }
+    pos += (uint32_t)__popcll(mt);
+    eq_seen += (uint32_t)__popcll(me);
+  });
 }
 
 }  // namespace kvsel

@@ -39,14 +39,12 @@ __device__ __forceinline__ FocalRow focal_row(const SelArgs &a, int b, int64_t l
 // grid (output rows, sequences): scores only
 __global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
   __shared__ double s_m[kMaxHeadsPerOut], s_iz[kMaxHeadsPerOut];
-  __shared__ float s_redf[kSelThreads / 64];
-  __shared__ double s_redd[16];
   const int o = blockIdx.x, b = blockIdx.y;
   const FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : a.ld64);
   const double c = a.scale * 1.4426950408889634;
   const float *base = a.logits + ((size_t)b * a.hq + o * a.heads_per_out) * a.ld_logits;
   auto stat_logit = [&](int hh, int i) { return base[(size_t)hh * a.ld_logits + i]; };
-  focal_stats<kSelThreads>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz, s_redf, s_redd);
+  focal_stats<kSelThreads, 4>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz);
   const float *lg = base + r.off;
   auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
   for (int i = threadIdx.x; i < r.seg; i += kSelThreads) {
@@ -64,15 +62,13 @@ __global__ __launch_bounds__(kSelThreads) void focal_select_kernel(SelArgs a) {
   __shared__ uint32_t s_keys[kSelMaxSeg];
   __shared__ RadixShared<NT> sh;
   __shared__ double s_m[8], s_iz[8];
-  __shared__ float s_redf[NT / 64];
-  __shared__ double s_redd[16];
   const int g = blockIdx.x, b = blockIdx.y;
   FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : (int64_t)kSelMaxSeg);
   r.seg = min(r.seg, kSelMaxSeg);
   const double c = a.scale * 1.4426950408889634;
   const float *base = a.logits + ((size_t)b * a.hq + g * a.heads_per_out) * a.ld_logits;
   auto stat_logit = [&](int hh, int i) { return base[(size_t)hh * a.ld_logits + i]; };
-  focal_stats<NT>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz, s_redf, s_redd);
+  focal_stats<NT, 4>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz);
   const float *lg = base + r.off;
   auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
   float *so = a.scores != nullptr ? a.scores + ((size_t)b * a.n_out + g) * a.ld : nullptr;
