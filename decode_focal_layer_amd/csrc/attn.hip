@@ -23,6 +23,12 @@
 //    is reduced with DPP row operations, and each lane group keeps its own
 //    online-softmax state (max, sum, 8 accumulator dims per query head of the
 //    group), so the loop has no cross-group synchronisation.
+//  * rows are handed out in chunks of 4*U consecutive rows per wave from an
+//    LDS counter.  The hardware issues older waves' loads first, so a static
+//    split leaves the younger waves (and with them the CU's memory traffic)
+//    trailing by a quarter of the loop; taking the next chunk on demand ends
+//    every wave within one chunk of the others.  The chunk a wave gets varies
+//    from run to run, so the output's rounding (not its row set) may too.
 //  * the lane-group states are merged in registers (the four groups of a
 //    wave) and in LDS (across waves).
 #include <type_traits>
@@ -44,28 +50,6 @@
 #endif
 #ifndef KVSEL_ATTN_WAVES_PER_CU
 #define KVSEL_ATTN_WAVES_PER_CU 16
-#endif
-// 1: issue the next iteration's K/V loads before computing the current one
-#ifndef KVSEL_ATTN_PIPE
-#define KVSEL_ATTN_PIPE 0
-#endif
-// 1: a work-group barrier after every iteration keeps the waves in step
-#ifndef KVSEL_ATTN_SYNC
-#define KVSEL_ATTN_SYNC 0
-#endif
-// row schedule: 0 = rows interleaved over all lane groups; 1 = each wave a
-// contiguous range, older waves (served first by the issue arbiter, so
-// ahead) given KVSEL_ATTN_LAG4 / 4 iterations' worth more rows than younger
-// ones so that all waves finish together
-#ifndef KVSEL_ATTN_SCHED
-#define KVSEL_ATTN_SCHED 0
-#endif
-#ifndef KVSEL_ATTN_LAG4
-#define KVSEL_ATTN_LAG4 4
-#endif
-// 1: rotate the waves' issue priorities every iteration
-#ifndef KVSEL_ATTN_ROTPRIO
-#define KVSEL_ATTN_ROTPRIO 0
 #endif
 // minimum resident waves per SIMD the compiler must allow for (0: no bound)
 #ifndef KVSEL_ATTN_WPE
@@ -140,9 +124,7 @@ constexpr float kNegBig = -1e30f;   // finite "empty" max: 2^(kNegBig - x) == 0,
 // with the focal selection of this (sequence, kv head).
 template <int G, int NT, int U, int MODE>
 __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
-  constexpr int NG = NT / 16;    // lane groups
   constexpr int NW = NT / 64;    // waves
-  constexpr int ITER = NG * U;   // rows per iteration of the work-group
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = tid >> 4, sub = tid & 15;
@@ -152,6 +134,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   __shared__ int32_t s_tab[kTabLds];
   __shared__ float s_acc[NW][G][kD];
   __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ uint32_t s_next;          // next chunk to hand out
   extern __shared__ float s_logit[];   // MODE 2: [G][seg_cap]
 
   const int start = split * a.rps;
@@ -199,6 +182,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     for (int i = 0; i < TPT; ++i)
       if (tid + i * NT < a.max_blocks) s_tab[tid + i * NT] = tv[i];
   }
+  if (tid == 0) s_next = NW;   // chunks 0 .. NW-1 start the waves
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -233,28 +217,17 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   const uint16_t *kbase = a.k_pool + sub * 8;
   const uint16_t *vbase = a.v_pool + sub * 8;
 
-  // Row schedule.  Interleaved: iteration rows [base, base + ITER), lane
-  // group grp takes base + grp + NG*u.  Wave ranges: wave w walks
-  // [t_beg, t_end) 4*U rows at a time, its lane group takes base + grp%4 + 4*u.
-#if KVSEL_ATTN_SCHED == 1
-  auto wave_off = [&](int w) -> int {
-    const int skew = cnt >= 2 * ITER ? (2 * KVSEL_ATTN_LAG4 * w * (NW - w)) / NW : 0;
-    return min(cnt, (int)(((int64_t)w * cnt) / NW) + skew);
-  };
-  const int t_beg = wave_off(wave), t_end = wave_off(wave + 1);
-  constexpr int STEP = 4 * U;
+  // Chunk c is rows [c*CH, (c+1)*CH) of this split; lane group grp takes
+  // rows c*CH + grp%4 + 4*u, so each load instruction of a wave covers four
+  // consecutive rows.
+  constexpr int CH = 4 * U;
 #define KVSEL_ROWT(base, u) ((base) + (grp & 3) + 4 * (u))
-#else
-  const int t_beg = 0, t_end = cnt;
-  constexpr int STEP = ITER;
-#define KVSEL_ROWT(base, u) ((base) + grp + NG * (u))
-#endif
-  // K/V rows of one iteration into registers
+  // K/V rows of one chunk into registers
   auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = KVSEL_ROWT(base, u);
-      const uint32_t pr = t < t_end ? s_prow[t] : kNoRow;
+      const uint32_t pr = t < cnt ? s_prow[t] : kNoRow;
       ok[u] = pr != kNoRow;
       // a row that is not attended reads this lane's query (a valid, finite
       // 16 bytes) and gets probability 0
@@ -264,7 +237,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       vr[u] = *reinterpret_cast<const uint4 *>(vp);
     }
   };
-  // online softmax over the iteration's rows
+  // online softmax over the chunk's rows
   auto consume = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U], const bool (&ok)[U]) {
     float dot[U][G];
 #pragma unroll
@@ -321,37 +294,16 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     }
   };
 
-  if (KVSEL_ATTN_PIPE) {
-    uint4 ka[U], va[U], kb2[U], vb2[U];
-    bool oa[U], ob[U];
-    if (t_beg < t_end) load_rows(t_beg, ka, va, oa);
-    for (int base = t_beg; base < t_end; base += 2 * STEP) {
-      if (base + STEP < t_end) load_rows(base + STEP, kb2, vb2, ob);
-      consume(base, ka, va, oa);
-      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
-      if (base + STEP >= t_end) break;
-      if (base + 2 * STEP < t_end) load_rows(base + 2 * STEP, ka, va, oa);
-      consume(base + STEP, kb2, vb2, ob);
-      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
-    }
-  } else {
-    int it = 0;
-    for (int base = t_beg; base < t_end; base += STEP, ++it) {
-      if (KVSEL_ATTN_ROTPRIO) {
-        switch ((wave + it) & 3) {
-          case 0: __builtin_amdgcn_s_setprio(0); break;
-          case 1: __builtin_amdgcn_s_setprio(1); break;
-          case 2: __builtin_amdgcn_s_setprio(2); break;
-          default: __builtin_amdgcn_s_setprio(3); break;
-        }
-      }
-      uint4 kr[U], vr[U];
-      bool ok[U];
-      load_rows(base, kr, vr, ok);
-      consume(base, kr, vr, ok);
-      if (KVSEL_ATTN_SYNC) __builtin_amdgcn_s_barrier();
-    }
-    if (KVSEL_ATTN_ROTPRIO) __builtin_amdgcn_s_setprio(0);
+  // Every wave leaves once the counter has passed the last chunk: the counter
+  // only grows, and a wave takes a new chunk only after finishing one.
+  for (int c = wave; c * CH < cnt;) {
+    uint32_t nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&s_next, 1u);   // its latency hides behind the loads
+    uint4 kr[U], vr[U];
+    bool ok[U];
+    load_rows(c * CH, kr, vr, ok);
+    consume(c * CH, kr, vr, ok);
+    c = __builtin_amdgcn_readfirstlane((int)nxt);
   }
 #undef KVSEL_ROWT
 
