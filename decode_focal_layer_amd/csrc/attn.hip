@@ -119,6 +119,27 @@ constexpr float kNegBig = -1e30f;   // finite "empty" max: 2^(kNegBig - x) == 0,
 #define KVSEL_ATTN_OCC
 #endif
 
+// Combine the split records of (sequence b, kv head g) into out / lse:
+// thread x < G*128 of the caller's nt threads takes head x / 128, dim x % 128.
+template <int G>
+__device__ __forceinline__ void merge_records(const AttnArgs &a, int b, int g, int nact, int tid, int nt) {
+  for (int x = tid; x < G * kD; x += nt) {
+    const int h = x / kD, dim = x % kD;
+    const size_t hb = (size_t)b * a.hq + g * G + h;
+    const float *rec0 = a.rec + hb * a.nsplit * kRec;
+    float M = kNegBig;
+    for (int sp = 0; sp < nact; ++sp) M = fmaxf(M, rec0[sp * kRec + kD]);
+    float L = 0.f, A = 0.f;
+    for (int sp = 0; sp < nact; ++sp) {
+      const float c = fast_exp2(rec0[sp * kRec + kD] - M);
+      L += rec0[sp * kRec + kD + 1] * c;
+      A += rec0[sp * kRec + dim] * c;
+    }
+    a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
+    if (dim == 0 && a.lse != nullptr) a.lse[hb] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
 // MODE 0: attention only.  MODE 1: also store the raw logits to the global
 // scratch.  MODE 2 (one split only): keep the segment logits in LDS and end
 // with the focal selection of this (sequence, kv head).
@@ -136,6 +157,11 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ uint32_t s_next;          // next chunk to hand out
   extern __shared__ float s_logit[];   // MODE 2: [G][seg_cap]
+  // MODE 2: chunks after the segment, waves done with the segment, the
+  // selectors' barrier counter, the per-wave segment maxima
+  __shared__ uint32_t s_next2, s_p1done, s_selctr;
+  __shared__ float s_wmax[MODE == 2 ? NW : 1][G];
+  __shared__ uint32_t s_simd_n[4], s_simd_done[4];   // MODE 2: waves per SIMD, and done with phase 1
 
   const int start = split * a.rps;
   constexpr int RPT = kAttnMaxRps / NT;
@@ -167,6 +193,8 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   }
   const SeqView v = seq_view_of(a, n_raw, s0_raw, s1_raw, dense);
   const int cnt = max(0, min(a.rps, v.nR - start));   // rows of this split
+  constexpr int CH = 4 * U;              // rows per chunk
+  const int nch = (cnt + CH - 1) / CH;   // chunks of this split
 
   int lo = 0, hi = 0;   // logical rows whose logits are stored, at row - lo (dense only)
   if (MODE == 2) {
@@ -183,7 +211,21 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       if (tid + i * NT < a.max_blocks) s_tab[tid + i * NT] = tv[i];
   }
   if (tid == 0) s_next = NW;   // chunks 0 .. NW-1 start the waves
+  int c1 = nch;                // MODE 2: chunks up to the segment's end
+  if (MODE == 2) {
+    c1 = min(nch, (hi - start + CH - 1) / CH);
+    if (tid == 0) {
+      s_next2 = c1;
+      s_p1done = 0;
+      s_selctr = 0;
+    }
+    if (tid < 4) s_simd_n[tid] = s_simd_done[tid] = 0u;
+  }
   __syncthreads();
+  // MODE 2: the SIMD this wave runs on (hardware wave id register, SIMD_ID
+  // field); only used to spread the selecting waves over the SIMDs
+  const uint32_t simd = MODE == 2 ? (uint32_t)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3u : 0u;
+  if (MODE == 2 && lane == 0) atomicAdd(&s_simd_n[simd], 1u);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int t = tid + i * NT;
@@ -205,8 +247,10 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   }
 
   float m[G], l[G], acc[G][8];
+  float smax[G];   // MODE 2: largest segment logit per head seen by this lane group
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    smax[h] = -INFINITY;
     m[h] = kNegBig;
     l[h] = 0.f;
 #pragma unroll
@@ -220,7 +264,6 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   // Chunk c is rows [c*CH, (c+1)*CH) of this split; lane group grp takes
   // rows c*CH + grp%4 + 4*u, so each load instruction of a wave covers four
   // consecutive rows.
-  constexpr int CH = 4 * U;
 #define KVSEL_ROWT(base, u) ((base) + (grp & 3) + 4 * (u))
   // K/V rows of one chunk into registers
   auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
@@ -246,6 +289,10 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = start + KVSEL_ROWT(base, u);   // dense: logical row = virtual row
+        if (MODE == 2 && ok[u] && row >= lo && row < hi) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) smax[h] = fmaxf(smax[h], dot[u][h]);
+        }
         if (ok[u] && sub < G && row >= lo && row < hi) {
           float dv = dot[u][0];
 #pragma unroll
@@ -294,16 +341,78 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     }
   };
 
-  // Every wave leaves once the counter has passed the last chunk: the counter
-  // only grows, and a wave takes a new chunk only after finishing one.
-  for (int c = wave; c * CH < cnt;) {
-    uint32_t nxt = 0;
-    if (lane == 0) nxt = atomicAdd(&s_next, 1u);   // its latency hides behind the loads
-    uint4 kr[U], vr[U];
-    bool ok[U];
-    load_rows(c * CH, kr, vr, ok);
-    consume(c * CH, kr, vr, ok);
-    c = __builtin_amdgcn_readfirstlane((int)nxt);
+  // Chunks c .. cend-1, handed out by *ctr.  A wave leaves once the counter
+  // has passed cend: the counter only grows, and a wave takes a new chunk
+  // only after finishing one.
+  auto run = [&](uint32_t *ctr, int c, int cend) {
+    while (c < cend) {
+      uint32_t nxt = 0;
+      if (lane == 0) nxt = atomicAdd(ctr, 1u);   // its latency hides behind the loads
+      uint4 kr[U], vr[U];
+      bool ok[U];
+      load_rows(c * CH, kr, vr, ok);
+      consume(c * CH, kr, vr, ok);
+      c = __builtin_amdgcn_readfirstlane((int)nxt);
+    }
+  };
+  if constexpr (MODE == 2) {
+    // Phase 1: the chunks up to the end of the segment, whose logits the
+    // selection needs.  Phase 2: the rest.  The last four waves to finish
+    // phase 1 wait for the others, then select while the remaining waves
+    // stream phase 2's rows; they join phase 2 when done.  (FastOCR,
+    // Focal-Guided Pruning: the focal layer attends over the full cache and
+    // selects from that attention.)
+    run(&s_next, wave, c1);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mx = wave_max_f(smax[h]);
+      if (lane == 0) s_wmax[wave][h] = mx;
+    }
+    uint32_t ticket = 0, tsimd = 0;
+    if (lane == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // this wave's logits are in LDS
+      ticket = __hip_atomic_fetch_add(&s_p1done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      tsimd = atomicAdd(&s_simd_done[simd], 1u);
+    }
+    ticket = (uint32_t)__builtin_amdgcn_readfirstlane((int)ticket);
+    tsimd = (uint32_t)__builtin_amdgcn_readfirstlane((int)tsimd);
+    // Four selectors: the last wave of each SIMD to finish phase 1 (one per
+    // SIMD, so they do not share issue slots) when every SIMD holds some of
+    // the work-group's waves, else the last four waves to finish.
+    const bool by_simd = s_simd_n[0] != 0u && s_simd_n[1] != 0u && s_simd_n[2] != 0u && s_simd_n[3] != 0u;
+    const bool selector = by_simd ? tsimd + 1u == s_simd_n[simd] : ticket >= (uint32_t)(NW - 4);
+    if (selector) {
+      // every wave increments s_p1done once, after its last phase-1 chunk
+      while ((uint32_t)__builtin_amdgcn_readfirstlane(
+                 (int)__hip_atomic_load(&s_p1done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < (uint32_t)NW)
+        __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      __shared__ FocalSelShared<G> s_fsel;
+      WaveSetSync<kStatThreads> grp{by_simd ? (int)simd : (int)ticket - (NW - 4), &s_selctr, 0u};
+      float mh[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = s_wmax[0][h];
+        for (int w2 = 1; w2 < NW; ++w2) mx = fmaxf(mx, s_wmax[w2][h]);
+        mh[h] = mx;
+      }
+      const int seg = hi - lo;
+      const size_t row = (size_t)b * a.hkv + g;
+      float *so = a.sel_scores != nullptr ? a.sel_scores + row * a.sel_ld : nullptr;
+      const int seg_out = so != nullptr ? (int)min((int64_t)seg, a.sel_ld) : 0;
+      // the selection goes first at the issue arbiter: the streaming waves
+      // mostly wait on memory
+      __builtin_amdgcn_s_setprio(3);
+      focal_select_fused<G>(grp, s_logit, a.seg_cap, seg, a.scale * 1.4426950408889634, mh,
+                            a.sel_warm != nullptr ? a.sel_warm + row * a.sel_k : nullptr, a.sel_k,
+                            a.sel_idx + row * a.sel_k, so, seg_out, s_fsel);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    uint32_t first = 0;
+    if (lane == 0) first = atomicAdd(&s_next2, 1u);
+    run(&s_next2, __builtin_amdgcn_readfirstlane((int)first), nch);
+  } else {
+    run(&s_next, wave, nch);
   }
 #undef KVSEL_ROWT
 
@@ -363,52 +472,14 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       }
     }
   }
-
-  if constexpr (MODE == 2) {
-    // focal selection from the LDS logits (FastOCR Focal-Guided Pruning)
-    __shared__ RadixShared<NT> sh;
-    __shared__ double s_fm[G], s_fiz[G];
-    __syncthreads();
-    const int seg = hi - lo;
-    const double c = a.scale * 1.4426950408889634;
-    auto logit = [&](int hh, int i) { return s_logit[hh * a.seg_cap + i]; };
-    focal_stats<NT, G>(logit, G, seg, c, s_fm, s_fiz);
-    uint32_t *keys = reinterpret_cast<uint32_t *>(s_logit);   // head 0's row, rewritten in place
-    float *so = a.sel_scores != nullptr ? a.sel_scores + ((size_t)b * a.hkv + g) * a.sel_ld : nullptr;
-    const int seg_out = so != nullptr ? (int)min((int64_t)seg, a.sel_ld) : seg;
-    for (int i = tid; i < seg; i += NT) {
-      const float f = (float)focal_score(logit, G, i, c, s_fm, s_fiz);
-      keys[i] = okey(f);
-      if (so != nullptr && i < seg_out) so[i] = f;
-    }
-    __syncthreads();
-    auto key = [&](int i) -> uint32_t { return keys[i]; };
-    const size_t row = (size_t)b * a.hkv + g;
-    const uint32_t theta = a.sel_warm != nullptr ? warm_theta<NT>(key, a.sel_warm + row * a.sel_k, seg, a.sel_k, sh)
-                                                 : 0u;
-    radix_topk<NT>(key, seg, a.sel_k, theta, a.sel_idx + row * a.sel_k, sh);
-  }
 }
 
 // merge of the split records: grid (kv heads, sequences), G*128 threads
 template <int G>
 __global__ __launch_bounds__(G * kD) void attn_merge_kernel(AttnArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
-  const int h = threadIdx.x / kD, dim = threadIdx.x % kD;
   const SeqView v = seq_view(a, b, a.dense != 0);
-  const int nact = v.nR <= 0 ? 0 : min(a.nsplit, (v.nR + a.rps - 1) / a.rps);
-  const size_t hb = (size_t)b * a.hq + g * G + h;
-  const float *rec0 = a.rec + hb * a.nsplit * kRec;
-  float M = kNegBig;
-  for (int sp = 0; sp < nact; ++sp) M = fmaxf(M, rec0[sp * kRec + kD]);
-  float L = 0.f, A = 0.f;
-  for (int sp = 0; sp < nact; ++sp) {
-    const float c = fast_exp2(rec0[sp * kRec + kD] - M);
-    L += rec0[sp * kRec + kD + 1] * c;
-    A += rec0[sp * kRec + dim] * c;
-  }
-  a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
-  if (dim == 0 && a.lse != nullptr) a.lse[hb] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
+  merge_records<G>(a, b, g, v.nR <= 0 ? 0 : min(a.nsplit, (v.nR + a.rps - 1) / a.rps), threadIdx.x, G * kD);
 }
 
 // logits only: grid = (row chunks, kv heads, sequences); rows [lo, hi)

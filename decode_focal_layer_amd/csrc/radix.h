@@ -1,18 +1,24 @@
-// Exact top-k of one row held as order-preserving uint32 keys, for one
-// work-group: ties to the lower index, output ascending.
+// Exact top-k of one row held as order-preserving uint32 keys: ties to the
+// lower index, output ascending.
 //
-// The k-th largest key T is found by a radix select over (key - min), where
-// min and max are taken over the candidate keys first: the digits (11 bits,
-// from the top of the candidates' range down) then spread over the range the
-// row actually occupies.  Scores of one softmax share a few float exponents,
-// so digits taken from the raw key would put nearly every key into a handful
-// of histogram bins (serialised LDS atomics).  The output pass gives each
-// wave a contiguous range of indices, read 64 consecutive keys at a time (no
-// LDS bank conflicts, coalesced global reads): the waves count their keys > T
-// and == T, and each then places its chosen indices in order with ballot
-// masks -- so the output is ascending and ties go to the lower index.  Only
-// keys >= theta are ranked; theta must not exceed the k-th largest key (a warm
-// start's minimum does not: at least k keys reach it).
+// The selection runs on a group of NTS threads (whole waves) with its own
+// barrier: a whole work-group (BlockSync) or a set of waves inside a
+// work-group whose other waves keep streaming (WaveSetSync).
+//
+// The k-th largest key T is found by a radix select over (key - lo), where lo
+// and hi bound the candidate keys: the digits (11 bits, from the top of the
+// candidates' range down) spread over the range the row occupies, because the
+// scores of one softmax share a few float exponents and digits taken from the
+// raw key would pile nearly every key into a handful of histogram bins
+// (serialised LDS atomics).  Once the bin holding T has at most kListCap
+// candidates they are collected into LDS and ranked exactly, which replaces
+// the remaining digit passes.  The output pass gives each wave a contiguous
+// range of indices, read 64 consecutive keys at a time (no LDS bank
+// conflicts, coalesced global reads): the waves count their keys > T and
+// == T, and each then places its chosen indices in order with ballot masks --
+// so the output is ascending and ties go to the lower index.  Only keys >=
+// theta are ranked; theta must not exceed the k-th largest key (a warm start's
+// minimum does not: at least k keys reach it).
 #pragma once
 
 #include "common.h"
@@ -25,52 +31,84 @@ __device__ __forceinline__ uint32_t okey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int NT>
+// candidates of the digit bin holding T collected for an exact rank
+constexpr int kListCap = 256;
+
+template <int NTS>
 struct RadixShared {
   uint32_t hist[2048];
-  uint32_t w1[NT / 64];
-  uint32_t w2[NT / 64];
-  uint32_t misc[4];
+  uint32_t w1[NTS / 64];
+  uint32_t w2[NTS / 64];
+  uint32_t w3[NTS / 64];
+  uint32_t misc[8];
+  uint32_t list_key[kListCap];
+  int32_t list_idx[kListCap];
 };
 
-// exclusive scan of one value per thread in thread order; total returned
-template <int NT>
-__device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t *ws, uint32_t &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+// All threads of the work-group take part.
+template <int NTS>
+struct BlockSync {
+  __device__ int t() const { return (int)threadIdx.x; }
+  __device__ void sync() const { __syncthreads(); }
+};
+
+// NTS / 64 waves of a work-group take part (rank = the wave's place in the
+// set); they meet on an LDS counter that only grows.  Every wave of the set
+// calls sync() equally often, so each wait ends once the last of them has
+// arrived; waves outside the set never wait on it.  The fences order LDS only
+// (the set shares data through LDS), so a wait never includes the wave's
+// outstanding global loads or stores.
+template <int NTS>
+struct WaveSetSync {
+  int rank;
+  uint32_t *ctr;
+  uint32_t target;
+  __device__ int t() const { return rank * 64 + (int)(threadIdx.x & 63); }
+  __device__ void sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    target += NTS / 64;
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while ((uint32_t)__builtin_amdgcn_readfirstlane(
+               (int)__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < target)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
-  if (lane == 63) ws[w] = x;
-  __syncthreads();
+};
+
+// exclusive scan of one value per participant in participant order; total
+// returned.  ws holds NTS / 64 words.
+template <int NTS, typename Grp>
+__device__ __forceinline__ uint32_t excl_scan(Grp &grp, uint32_t v, uint32_t *ws, uint32_t &total) {
+  const int t = grp.t(), w = t >> 6;
+  const uint32_t x = wave_incl_scan_u32(v);
+  if ((t & 63) == 63) ws[w] = x;
+  grp.sync();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const uint32_t t = ws[i];
-    pre += i < w ? t : 0u;
-    tot += t;
+  for (int i = 0; i < NTS / 64; ++i) {
+    const uint32_t s = ws[i];
+    pre += i < w ? s : 0u;
+    tot += s;
   }
-  __syncthreads();
+  grp.sync();
   total = tot;
   return pre + x - v;
 }
 
-// f(i, key(i)) for i = tid, tid + NT, ... below n; each thread issues B key
+// f(i, key(i)) for i = t, t + NTS, ... below n; each thread issues B key
 // reads before using them (one memory latency per B keys)
-template <int NT, int B, typename KeyFn, typename F>
-__device__ __forceinline__ void each_key(KeyFn key, int n, F f) {
-  for (int base = 0; base < n; base += B * NT) {
+template <int NTS, int B, typename KeyFn, typename F>
+__device__ __forceinline__ void each_key(int t, KeyFn key, int n, F f) {
+  for (int base = 0; base < n; base += B * NTS) {
     uint32_t x[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
+      const int i = base + j * NTS + t;
       x[j] = i < n ? key(i) : 0u;
     }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
+      const int i = base + j * NTS + t;
       if (i < n) f(i, x[j]);
     }
   }
@@ -98,11 +136,11 @@ __device__ __forceinline__ void each_key_wave(KeyFn key, int i0, int i1, F f) {
 
 // theta from a warm selection: the smallest key at the warm indices, or 0 (rank
 // everything) if they are not strictly ascending and inside [0, n).
-template <int NT, typename KeyFn>
-__device__ uint32_t warm_theta(KeyFn key, const int32_t *wi, int n, int k, RadixShared<NT> &sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+template <int NTS, typename Grp, typename KeyFn>
+__device__ uint32_t warm_theta(Grp &grp, KeyFn key, const int32_t *wi, int n, int k, RadixShared<NTS> &sh) {
+  const int t = grp.t(), w = t >> 6;
   uint32_t bad = 0, mn = 0xffffffffu;
-  for (int j = threadIdx.x; j < k; j += NT) {
+  for (int j = t; j < k; j += NTS) {
     const int x = wi[j];
     if (x < 0 || x >= n) {
       bad = 1;
@@ -111,110 +149,162 @@ __device__ uint32_t warm_theta(KeyFn key, const int32_t *wi, int n, int k, Radix
       mn = min(mn, key(x));
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    bad |= __shfl_xor(bad, o);
-    mn = min(mn, (uint32_t)__shfl_xor(mn, o));
-  }
-  __syncthreads();
-  if (lane == 0) {
+  bad = wave_max_u32(bad);
+  mn = wave_min_u32(mn);
+  if ((t & 63) == 0) {
     sh.w1[w] = bad;
     sh.w2[w] = mn;
   }
-  __syncthreads();
+  grp.sync();
   uint32_t b2 = 0, m2 = 0xffffffffu;
-  for (int i = 0; i < NT / 64; ++i) {
+  for (int i = 0; i < NTS / 64; ++i) {
     b2 |= sh.w1[i];
     m2 = min(m2, sh.w2[i]);
   }
-  __syncthreads();
+  grp.sync();
   return b2 ? 0u : m2;
 }
 
-// keys: key(i) for i in [0, n).  Writes k indices to dst (ascending); when
-// n <= k all n indices are kept, followed by -1.
-template <int NT, typename KeyFn>
-__device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst, RadixShared<NT> &sh) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (n <= k) {
-    for (int i = tid; i < k; i += NT) dst[i] = i < n ? i : -1;
-    return;
-  }
-  // ---- range of the candidate keys ----
-  constexpr int B = 8;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  each_key<NT, B>(key, n, [&](int, uint32_t x) {
+// lo, hi and the count of the keys >= theta (hi < lo when there are none)
+template <int NTS, typename Grp, typename KeyFn>
+__device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &lo, uint32_t &hi, uint32_t &ncand,
+                          RadixShared<NTS> &sh) {
+  const int t = grp.t(), w = t >> 6;
+  uint32_t l = 0xffffffffu, h = 0u, c = 0u;
+  each_key<NTS, 8>(t, key, n, [&](int, uint32_t x) {
     if (x >= theta) {
-      lo = min(lo, x);
-      hi = max(hi, x);
+      l = min(l, x);
+      h = max(h, x);
+      ++c;
     }
   });
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor(lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor(hi, o));
+  l = wave_min_u32(l);
+  h = wave_max_u32(h);
+  c = wave_reduce_u32(c, [](uint32_t a, uint32_t b) { return a + b; });
+  if ((t & 63) == 0) {
+    sh.w1[w] = l;
+    sh.w2[w] = h;
+    sh.w3[w] = c;
   }
-  if (lane == 0) {
-    sh.w1[w] = lo;
-    sh.w2[w] = hi;
-  }
-  __syncthreads();
+  grp.sync();
   lo = 0xffffffffu;
   hi = 0u;
-  for (int i = 0; i < NT / 64; ++i) {
+  ncand = 0u;
+  for (int i = 0; i < NTS / 64; ++i) {
     lo = min(lo, sh.w1[i]);
     hi = max(hi, sh.w2[i]);
+    ncand += sh.w3[i];
   }
-  __syncthreads();
-  const uint32_t range = hi - lo;
-  const int nbits = range == 0u ? 0 : 32 - __clz(range);
+  grp.sync();
+}
 
-  // ---- radix select of the k-th largest (key - lo) among candidates ----
-  uint32_t prefix = 0, pmask = 0;
-  int krem = k;
-  for (int top = nbits; top > 0; top -= 11) {
+// The k largest of key(i), i in [0, n), among the candidates (keys >= theta),
+// written ascending to dst; n > k >= 1.  lo <= every candidate key <= hi, and
+// nin >= the number of candidates (at least k of them).
+template <int NTS, typename Grp, typename KeyFn>
+__device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
+                             int32_t *dst, RadixShared<NTS> &sh) {
+  constexpr int B = 8;
+  constexpr int NW = NTS / 64;
+  const int t = grp.t(), lane = t & 63, w = t >> 6;
+  const uint32_t range = hi - lo;
+  int top = range == 0u ? 0 : 32 - __clz(range);
+  uint32_t prefix = 0, pmask = 0;   // digits of (key - lo) fixed so far
+  uint32_t krem = (uint32_t)k;      // keys still to take inside the prefix's bin
+  auto in_bin = [&](uint32_t x) { return x >= theta && ((x - lo) & pmask) == prefix; };
+
+  // ---- digit passes until the bin holding T is small ----
+  while (top > 0 && nin > (uint32_t)kListCap) {
     const int bits = top < 11 ? top : 11;
     const int shift = top - bits;
     const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    each_key<NT, B>(key, n, [&](int, uint32_t x) {
-      const uint32_t r = x - lo;
-      if (x >= theta && (r & pmask) == prefix) atomicAdd(&sh.hist[(r >> shift) & (nb - 1)], 1u);
+    for (int i = t; i < nb; i += NTS) sh.hist[i] = 0;
+    grp.sync();
+    each_key<NTS, B>(t, key, n, [&](int, uint32_t x) {
+      if (in_bin(x)) atomicAdd(&sh.hist[((x - lo) >> shift) & (nb - 1)], 1u);
     });
-    __syncthreads();
-    // thread t owns bins [t*per, (t+1)*per) (empty past nb); bins above its range
-    const int per = (nb + NT - 1) / NT;
+    grp.sync();
+    // participant t owns bins [t*per, (t+1)*per) (empty past nb)
+    const int per = (nb + NTS - 1) / NTS;
     uint32_t c = 0;
     for (int i = 0; i < per; ++i) {
-      const int bi = tid * per + i;
+      const int bi = t * per + i;
       c += bi < nb ? sh.hist[bi] : 0u;
     }
     uint32_t total;
-    const uint32_t below = excl_scan<NT>(c, sh.w1, total);
-    const uint32_t above = total - below - c;
-    if (above < (uint32_t)krem && (uint32_t)krem <= above + c) {
+    const uint32_t below = excl_scan<NTS>(grp, c, sh.w1, total);
+    const uint32_t above = total - below - c;   // candidates in bins above this participant's
+    if (above < krem && krem <= above + c) {
       uint32_t run = above;
       for (int i = per - 1; i >= 0; --i) {
-        const int bi = tid * per + i;
+        const int bi = t * per + i;
         const uint32_t hcount = bi < nb ? sh.hist[bi] : 0u;
-        if (run + hcount >= (uint32_t)krem) {
+        if (run + hcount >= krem) {
           sh.misc[0] = (uint32_t)bi;
           sh.misc[1] = run;
+          sh.misc[2] = hcount;
           break;
         }
         run += hcount;
       }
     }
-    __syncthreads();
+    grp.sync();
     prefix |= sh.misc[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
-    krem -= (int)sh.misc[1];
-    __syncthreads();
+    krem -= sh.misc[1];
+    nin = sh.misc[2];
+    top -= bits;
+    grp.sync();
   }
-  const uint32_t T = lo + prefix;        // the k-th largest key
-  const uint32_t keq = (uint32_t)krem;   // keys equal to T to keep (>= 1)
+
+  uint32_t T, keq;   // the k-th largest key; keys equal to it to keep (>= 1)
+  if (top == 0) {
+    T = lo + prefix;   // every digit fixed: the bin is one key value
+    keq = krem;
+  } else {
+    // ---- at most kListCap candidates left in the bin: collect and rank them ----
+    if (t == 0) sh.misc[3] = 0;
+    grp.sync();
+    each_key_wave<B>(key, w * ((n + NW * 64 - 1) / (NW * 64) * 64),
+                     min(n, (w + 1) * ((n + NW * 64 - 1) / (NW * 64) * 64)),
+                     [&](int i, bool valid, uint32_t x) {
+      const bool m = valid && in_bin(x);
+      const uint64_t mask = __ballot(m);
+      if (mask != 0ull) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sh.misc[3], (uint32_t)__popcll(mask));
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        if (m && slot < (uint32_t)kListCap) {
+          sh.list_key[slot] = x;
+          sh.list_idx[slot] = i;
+        }
+      }
+    });
+    grp.sync();
+    const int nl = min((int)sh.misc[3], kListCap);
+    // rank of item j: items with a larger key, or an equal key and a lower index
+    for (int j = t; j < nl; j += NTS) {
+      const uint32_t xj = sh.list_key[j];
+      const int ij = sh.list_idx[j];
+      uint32_t r = 0, gt = 0;
+      for (int i = 0; i < nl; ++i) {
+        const uint32_t xi = sh.list_key[i];
+        const int ii = sh.list_idx[i];
+        gt += xi > xj ? 1u : 0u;
+        r += (xi > xj || (xi == xj && ii < ij)) ? 1u : 0u;
+      }
+      if (r == krem - 1u) {
+        sh.misc[4] = xj;
+        sh.misc[5] = krem - gt;
+      }
+    }
+    grp.sync();
+    T = sh.misc[4];
+    keq = sh.misc[5];
+  }
 
   // ---- ordered output: wave w owns indices [w*cw, (w+1)*cw), walked 64 at a time ----
-  constexpr int NW = NT / 64;
   const int cw = (n + NW * 64 - 1) / (NW * 64) * 64;
   const int w0 = min(n, w * cw), w1 = min(n, w0 + cw);
   uint32_t cg = 0, ce = 0;   // this wave's keys above T and equal to T
@@ -226,7 +316,7 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     sh.w1[w] = cg;
     sh.w2[w] = ce;
   }
-  __syncthreads();
+  grp.sync();
   uint32_t gt_before = 0, eq_before = 0;
   for (int i = 0; i < w; ++i) {
     gt_before += sh.w1[i];
@@ -248,6 +338,23 @@ __device__ void radix_topk(KeyFn key, int n, int k, uint32_t theta, int32_t *dst
     pos += (uint32_t)__popcll(mt);
     eq_seen += (uint32_t)__popcll(me);
   });
+  grp.sync();   // sh is free again
+}
+
+// Top-k of a whole row with a block of NTS threads: warm theta (optional),
+// candidate range, radix select.  When n <= k all n indices are kept,
+// followed by -1.
+template <int NTS, typename Grp, typename KeyFn>
+__device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *warm, int32_t *dst, RadixShared<NTS> &sh) {
+  const int t = grp.t();
+  if (n <= k) {
+    for (int i = t; i < k; i += NTS) dst[i] = i < n ? i : -1;
+    return;
+  }
+  const uint32_t theta = warm != nullptr ? warm_theta<NTS>(grp, key, warm, n, k, sh) : 0u;
+  uint32_t lo, hi, ncand;
+  key_range<NTS>(grp, key, n, theta, lo, hi, ncand, sh);
+  radix_select<NTS>(grp, key, n, k, theta, lo, hi, ncand, dst, sh);
 }
 
 }  // namespace kvsel

@@ -80,8 +80,8 @@ __global__ __launch_bounds__(kSelThreads) void focal_select_kernel(SelArgs a) {
   __syncthreads();
   auto key = [&](int i) -> uint32_t { return s_keys[i]; };
   const size_t row = (size_t)b * a.n_out + g;
-  const uint32_t theta = a.warm != nullptr ? warm_theta<NT>(key, a.warm + row * a.k, r.seg, a.k, sh) : 0u;
-  radix_topk<NT>(key, r.seg, a.k, theta, a.idx + row * a.k, sh);
+  BlockSync<NT> grp;
+  radix_topk<NT>(grp, key, r.seg, a.k, a.warm != nullptr ? a.warm + row * a.k : nullptr, a.idx + row * a.k, sh);
 }
 
 }  // namespace

@@ -46,8 +46,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     __syncthreads();
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
-  const uint32_t theta = a.warm != nullptr ? warm_theta<NT>(key, a.warm + (size_t)row * a.k, a.n, a.k, sh) : 0u;
-  radix_topk<NT>(key, a.n, a.k, theta, a.idx + (size_t)row * a.k, sh);
+  BlockSync<NT> grp;
+  radix_topk<NT>(grp, key, a.n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
+                 a.idx + (size_t)row * a.k, sh);
 }
 
 }  // namespace
