@@ -52,6 +52,7 @@ kvsel_status check_desc(const kvsel_kv_desc *kv, bool need_v) {
   if (kv->num_blocks < 1) return fail(KVSEL_EINVAL, "num_blocks must be >= 1");
   if ((uint64_t)kv->num_blocks * (uint64_t)kv->num_kv_heads * kBlk >= 0xffffffffull)
     return fail(KVSEL_EUNSUPPORTED, "pool has 2^32 or more rows");
+  if (kv->shared_rows < 0) return fail(KVSEL_EINVAL, "shared_rows must be >= 0");
   if (!kv->k_pool || !kv->block_table || !kv->seq_len || !kv->seg_begin || !kv->seg_end)
     return fail(KVSEL_EINVAL, "k_pool, block_table, seq_len, seg_begin and seg_end are required");
   if (need_v && !kv->v_pool) return fail(KVSEL_EINVAL, "v_pool is required");
@@ -99,6 +100,7 @@ AttnArgs attn_args(const kvsel_kv_desc *kv, const uint16_t *q, int32_t hq, float
   a.seg_end = kv->seg_end;
   a.num_blocks = kv->num_blocks;
   a.max_blocks = kv->max_blocks_per_seq;
+  a.shared_rows = kv->shared_rows;
   a.hkv = kv->num_kv_heads;
   a.hq = hq;
   a.k = k;

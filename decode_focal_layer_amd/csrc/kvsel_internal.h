@@ -41,6 +41,7 @@ struct AttnArgs {
   const int32_t *block_table, *seq_len, *seg_begin, *seg_end;
   int64_t num_blocks;
   int32_t max_blocks, hkv, hq, k;
+  int32_t shared_rows;  // > 0: rows are shared across sequences, load them through the caches
   const uint16_t *q;
   const int32_t *idx;   // [batch][hkv][k] kept indices (gather)
   int32_t dense;        // 1: every row [0, seq_len); 0: gather

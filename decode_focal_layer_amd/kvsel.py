@@ -49,6 +49,7 @@ class KvDescC(ctypes.Structure):
         ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
         ("seg_begin", ctypes.c_void_p), ("seg_end", ctypes.c_void_p),
+        ("shared_rows", ctypes.c_int32),
     ]
 
 
@@ -132,6 +133,7 @@ class KV:
     max_seq_len: int
     max_seg_len: int
     min_seg_len: int = 0
+    shared_rows: int = 0   # cache hint: leading rows shared across sequences
 
     def __post_init__(self):
         _need(self.k_pool, torch.bfloat16, "k_pool")
@@ -158,6 +160,7 @@ class KV:
         c.seq_len = self.seq_len.data_ptr()
         c.seg_begin = self.seg_begin.data_ptr()
         c.seg_end = self.seg_end.data_ptr()
+        c.shared_rows = int(self.shared_rows)
         self.c = c
 
     @property
@@ -173,7 +176,8 @@ class KV:
 
     def with_seq_len(self, seq_len: torch.Tensor, max_seq_len: Optional[int] = None) -> "KV":
         return KV(self.k_pool, self.v_pool, self.block_table, seq_len, self.seg_begin, self.seg_end,
-                  self.max_seq_len if max_seq_len is None else max_seq_len, self.max_seg_len, self.min_seg_len)
+                  self.max_seq_len if max_seq_len is None else max_seq_len, self.max_seg_len, self.min_seg_len,
+                  self.shared_rows)
 
 
 class Workspace:

@@ -71,7 +71,7 @@ typedef int32_t kvsel_status;
 #define KVSEL_EUNSUPPORTED (-3)  /* head_dim != 128, block_size != 16, group > 8  */
 #define KVSEL_EHIP         (-4)  /* a HIP launch failed                           */
 
-#define KVSEL_VERSION 1
+#define KVSEL_VERSION 2
 
 #define KVSEL_REDUCE_GROUP 0     /* one score per (sequence, kv head)            */
 #define KVSEL_REDUCE_ALL   1     /* one score per (sequence): summed over heads  */
@@ -94,6 +94,14 @@ typedef void *kvsel_stream;      /* hipStream_t */
  *
  * Candidate segment: rows [seg_begin[b], seg_end[b]) are scored and
  * selectable; every row outside it is always attended by gather attention.
+ *
+ * shared_rows is a cache hint for a shared prefix: rows [0, shared_rows) of
+ * every sequence are read by many sequences (their blocks appear in many
+ * tables).  With shared_rows == 0 every K/V row is read by one sequence, and
+ * the attention kernels stream rows with non-temporal loads so that they do
+ * not evict what is reused from call to call (block tables, indices,
+ * queries); with shared_rows > 0 they load every row through the caches so
+ * that the prefix stays there.  Results do not depend on it.
  */
 typedef struct {
   int32_t batch;               /* sequences (or branches)                        */
@@ -113,6 +121,7 @@ typedef struct {
   const int32_t *seq_len;      /* [batch], device                                */
   const int32_t *seg_begin;    /* [batch], device                                */
   const int32_t *seg_end;      /* [batch], device                                */
+  int32_t shared_rows;         /* >= 0: leading rows shared across sequences      */
 } kvsel_kv_desc;
 
 /* Version of this header's ABI (KVSEL_VERSION). */

@@ -33,12 +33,17 @@ def kvsel():
     return m
 
 
-def focal_kvs(w, t=0):
+def focal_kvs(w, t=0, shared_rows=None):
+    """Per-layer views; a shared prefix is declared cacheable unless
+    shared_rows says otherwise (the hint does not change results)."""
     kv = kvsel()
     cfg = w.cfg
     max_len = int(w.seq_len_np.max())
+    if shared_rows is None:
+        shared_rows = cfg.prefix_len if cfg.shared_prefix else 0
     return [kv.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[t], w.seg_begin, w.seg_end,
-                  max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+                  max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                  shared_rows=shared_rows)
             for l in range(cfg.layers)]
 
 
@@ -158,7 +163,8 @@ def test_c4_branches_small_and_shared_prefix_equals_private_copy():
                            seq_len_np=w.seq_len_np, patches=w.patches, suffix_len=w.suffix_len,
                            num_blocks=w.num_blocks + B * pref, max_blocks=w.max_blocks)
     from decode_focal_layer_amd.decode import FocalDecoder
-    dec2 = FocalDecoder(focal_kvs(w2), cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV)
+    # the private copy streams every row (no shared-prefix hint)
+    dec2 = FocalDecoder(focal_kvs(w2, shared_rows=0), cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV)
     for t in range(cfg.steps):
         dec2.step(t, w.q[t], w.seq_len[t])
     torch.cuda.synchronize()

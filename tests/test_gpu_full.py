@@ -182,7 +182,8 @@ def test_c4_full_sampled():
     w = gen.make_focal(cfg, DEV)
     max_len = int(w.seq_len_np.max())
     kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
-                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                    shared_rows=cfg.prefix_len)
            for l in range(cfg.layers)]
     dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV)
     check_steps = {0, 1, cfg.steps - 1}
