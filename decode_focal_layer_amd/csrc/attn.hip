@@ -387,11 +387,14 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     }
     ticket = (uint32_t)__builtin_amdgcn_readfirstlane((int)ticket);
     tsimd = (uint32_t)__builtin_amdgcn_readfirstlane((int)tsimd);
-    // Four selectors: the last wave of each SIMD to finish phase 1 (one per
-    // SIMD, so they do not share issue slots) when every SIMD holds some of
-    // the work-group's waves, else the last four waves to finish.
-    const bool by_simd = s_simd_n[0] != 0u && s_simd_n[1] != 0u && s_simd_n[2] != 0u && s_simd_n[3] != 0u;
-    const bool selector = by_simd ? tsimd + 1u == s_simd_n[simd] : ticket >= (uint32_t)(NW - 4);
+    // Eight selectors: the last two waves of each SIMD to finish phase 1 (two
+    // per SIMD, so the selection spreads over all of them) when every SIMD
+    // holds at least two of the work-group's waves, else the last eight waves
+    // to finish.
+    constexpr int NSEL = kStatThreads / 64;
+    static_assert(MODE != 2 || NW >= NSEL, "the fused selection needs kStatThreads / 64 waves");
+    const bool by_simd = s_simd_n[0] >= 2u && s_simd_n[1] >= 2u && s_simd_n[2] >= 2u && s_simd_n[3] >= 2u;
+    const bool selector = by_simd ? tsimd + 2u >= s_simd_n[simd] : ticket >= (uint32_t)(NW - NSEL);
     if (selector) {
       // every wave increments s_p1done once, after its last phase-1 chunk
       while ((uint32_t)__builtin_amdgcn_readfirstlane(
@@ -399,7 +402,8 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
         __builtin_amdgcn_s_sleep(1);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       __shared__ FocalSelShared<G> s_fsel;
-      WaveSetSync<kStatThreads> grp{by_simd ? (int)simd : (int)ticket - (NW - 4), &s_selctr, 0u};
+      WaveSetSync<kStatThreads> grp{by_simd ? (int)(simd * 2u + (tsimd + 2u - s_simd_n[simd])) : (int)ticket - (NW - NSEL),
+                                    &s_selctr, 0u};
       float mh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -555,6 +559,9 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
   const bool stream = a.shared_rows == 0;   // rows shared across sequences stay cached
   dim3 grid(a.nsplit, a.hkv, batch);
   if (a.sel_idx != nullptr) {
+    if constexpr (NT < kStatThreads) {
+      return hipErrorInvalidValue;   // the fused selection needs kStatThreads / 64 waves
+    } else {
     if (a.nsplit != 1) return hipErrorInvalidValue;
     const size_t dyn = (size_t)G * a.seg_cap * sizeof(float);
     if (dyn > kFusedLdsBytes) return hipErrorInvalidValue;
@@ -571,6 +578,7 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
     else
       hipLaunchKernelGGL((attn_kernel<G, NT, U, 2, false>), grid, dim3(NT), dyn, s, a);
     return hipGetLastError();
+    }
   }
   if (a.logits != nullptr) {
     if (stream)

@@ -17,11 +17,11 @@
 
 namespace kvsel {
 
-// The normaliser's summation order: virtual thread v in [0, 256) adds its
-// tokens i = v, v + 256, ... in order; each virtual wave's 64 partial sums are
-// reduced by wave_sum_d; the four wave sums are added in order.  Any group of
+// The normaliser's summation order: virtual thread v in [0, 512) adds its
+// tokens i = v, v + 512, ... in order; each virtual wave's 64 partial sums are
+// reduced by wave_sum_d; the eight wave sums are added in order.  Any group of
 // threads that runs virtual thread v as its thread v gets the same bits.
-constexpr int kStatThreads = 256;
+constexpr int kStatThreads = 512;
 
 // The term 2^((x - m) c) for fp32 x and m (m is a float held in a double),
 // c = ch + cl split into two floats.  The exponent is formed with fp32
@@ -46,7 +46,7 @@ __device__ __forceinline__ float focal_term(float x, double m, double c) {
 template <int NT, int NH, typename LF>
 __device__ void focal_stats(LF logit, int nh, int cnt, double c, double *s_m, double *s_iz) {
   constexpr int NW = NT / 64, SW = kStatThreads / 64;
-  static_assert(NT % 64 == 0 && NT >= kStatThreads, "block of at least 256 threads");
+  static_assert(NT % 64 == 0 && NT >= kStatThreads, "block of at least kStatThreads threads");
   __shared__ float s_wm[NH][NW];
   __shared__ double s_wz[NH][SW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -116,11 +116,11 @@ struct FocalSelShared {
   uint32_t lo[kStatThreads / 64], hi[kStatThreads / 64], wmin[kStatThreads / 64], wbad[kStatThreads / 64];
 };
 
-// warm indices read per selection thread (k up to this many times 256)
-constexpr int kWarmPerThread = 4;
+// warm indices read per selection thread (k up to this many times kStatThreads)
+constexpr int kWarmPerThread = 2;
 
 // Focal selection of one (sequence, kv head) inside the attention kernel, run
-// by a set of four waves (grp, kStatThreads participants) while the other
+// by a set of eight waves (grp, kStatThreads participants) while the other
 // waves of the work-group stream.  s_logit holds the G heads' segment logits
 // at h * cap + i (i < seg); they are overwritten (terms, then keys in head 0's
 // row).  mh[h] is the logits' max per head.  warm (null: none) is the

@@ -69,7 +69,8 @@ struct AttnArgs {
 constexpr size_t kFusedLdsBytes = 80 * 1024;
 inline bool fused_focal_fits(int group, int max_seg_len) {
   const size_t cap = (size_t)((max_seg_len + 3) / 4 * 4);
-  return cap > 0 && (size_t)group * cap * sizeof(float) <= kFusedLdsBytes;
+  // the selection runs on eight waves: work-groups of 512 or more threads (G <= 4)
+  return group <= 4 && cap > 0 && (size_t)group * cap * sizeof(float) <= kFusedLdsBytes;
 }
 
 hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s);

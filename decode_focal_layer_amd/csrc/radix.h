@@ -12,11 +12,10 @@
 // raw key would pile nearly every key into a handful of histogram bins
 // (serialised LDS atomics).  Once the bin holding T has at most kListCap
 // candidates they are collected into LDS and ranked exactly, which replaces
-// the remaining digit passes.  The output pass gives each wave a contiguous
-// range of indices, read 64 consecutive keys at a time (no LDS bank
-// conflicts, coalesced global reads): the waves count their keys > T and
-// == T, and each then places its chosen indices in order with ballot masks --
-// so the output is ascending and ties go to the lower index.  Only keys >=
+// the remaining digit passes.  The output pass gives each thread a contiguous
+// range of indices: the threads count their keys > T and == T, exclusive
+// scans place them, and each writes its chosen indices in order -- so the
+// output is ascending and ties go to the lower index.  Only keys >=
 // theta are ranked; theta must not exceed the k-th largest key (a warm start's
 // minimum does not: at least k keys reach it).
 #pragma once
@@ -93,6 +92,28 @@ __device__ __forceinline__ uint32_t excl_scan(Grp &grp, uint32_t v, uint32_t *ws
   grp.sync();
   total = tot;
   return pre + x - v;
+}
+
+// exclusive scans of two values per participant (one pair of barriers)
+template <int NTS, typename Grp>
+__device__ __forceinline__ void excl_scan2(Grp &grp, uint32_t a, uint32_t b, uint32_t *wa, uint32_t *wb,
+                                           uint32_t &pa, uint32_t &pb) {
+  const int t = grp.t(), w = t >> 6;
+  const uint32_t xa = wave_incl_scan_u32(a), xb = wave_incl_scan_u32(b);
+  if ((t & 63) == 63) {
+    wa[w] = xa;
+    wb[w] = xb;
+  }
+  grp.sync();
+  uint32_t sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < NTS / 64; ++i) {
+    sa += i < w ? wa[i] : 0u;
+    sb += i < w ? wb[i] : 0u;
+  }
+  grp.sync();
+  pa = sa + xa - a;
+  pb = sb + xb - b;
 }
 
 // f(i, key(i)) for i = t, t + NTS, ... below n; each thread issues B key
@@ -304,40 +325,46 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     keq = sh.misc[5];
   }
 
-  // ---- ordered output: wave w owns indices [w*cw, (w+1)*cw), walked 64 at a time ----
-  const int cw = (n + NW * 64 - 1) / (NW * 64) * 64;
-  const int w0 = min(n, w * cw), w1 = min(n, w0 + cw);
-  uint32_t cg = 0, ce = 0;   // this wave's keys above T and equal to T
-  each_key_wave<B>(key, w0, w1, [&](int, bool valid, uint32_t x) {
-    cg += (uint32_t)__popcll(__ballot(valid && x > T));
-    ce += (uint32_t)__popcll(__ballot(valid && x == T));
-  });
-  if (lane == 0) {
-    sh.w1[w] = cg;
-    sh.w2[w] = ce;
+  // ---- ordered output: participant t owns the indices [t*C, (t+1)*C) ----
+  // It counts its keys above T and equal to T, the exclusive scans of those
+  // counts place it, and it writes its chosen indices in order: ascending
+  // output, and the equal keys taken are the lowest-indexed keq.
+  const int C = (n + NTS - 1) / NTS;
+  const int i0 = min(n, t * C), i1 = min(n, i0 + C);
+  uint32_t cg = 0, ce = 0;
+  for (int b0 = i0; b0 < i1; b0 += B) {
+    uint32_t x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      cg += (b0 + j < i1 && x[j] > T) ? 1u : 0u;
+      ce += (b0 + j < i1 && x[j] == T) ? 1u : 0u;
+    }
   }
-  grp.sync();
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int i = 0; i < w; ++i) {
-    gt_before += sh.w1[i];
-    eq_before += sh.w2[i];
-  }
-  const uint64_t lt = (1ull << lane) - 1ull;   // lanes below this one
-  // taken keys before this wave: all of its larger keys and the equal keys up to keq
+  uint32_t gt_before, eq_before;
+  excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
   uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
   uint32_t eq_seen = eq_before;
-  each_key_wave<B>(key, w0, w1, [&](int i, bool valid, uint32_t x) {
-    const bool eq = valid && x == T;
-    const uint64_t me = __ballot(eq);
-    const bool take = valid && (x > T || (eq && eq_seen + (uint32_t)__popcll(me & lt) < keq));
-    const uint64_t mt = __ballot(take);
-    if (take) {
-      const uint32_t p = pos + (uint32_t)__popcll(mt & lt);
-      if (p < (uint32_t)k) dst[p] = i;
+  for (int b0 = i0; b0 < i1; b0 += B) {
+    uint32_t x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (b0 + j < i1) {
+        bool take = x[j] > T;
+        if (x[j] == T) {
+          take = eq_seen < keq;
+          ++eq_seen;
+        }
+        if (take) {
+          if (pos < (uint32_t)k) dst[pos] = b0 + j;
+          ++pos;
+        }
+      }
     }
-    pos += (uint32_t)__popcll(mt);
-    eq_seen += (uint32_t)__popcll(me);
-  });
+  }
   grp.sync();   // sh is free again
 }
 
