@@ -221,8 +221,11 @@ __device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &
 
 // The k largest of key(i), i in [0, n), among the candidates (keys >= theta),
 // written ascending to dst; n > k >= 1.  lo <= every candidate key <= hi, and
-// nin >= the number of candidates (at least k of them).
-template <int NTS, typename Grp, typename KeyFn>
+// nin >= the number of candidates (at least k of them).  LDS_KEYS: key(i)
+// reads LDS (the output pass then walks per-thread index ranges); otherwise
+// global memory (the output pass walks per-wave ranges 64 consecutive keys at
+// a time, so that the reads coalesce).
+template <int NTS, bool LDS_KEYS = true, typename Grp, typename KeyFn>
 __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
                              int32_t *dst, RadixShared<NTS> &sh) {
   constexpr int B = 8;
@@ -325,53 +328,93 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     keq = sh.misc[5];
   }
 
-  // ---- ordered output: participant t owns the indices [t*C, (t+1)*C) ----
-  // It counts its keys above T and equal to T, the exclusive scans of those
-  // counts place it, and it writes its chosen indices in order: ascending
-  // output, and the equal keys taken are the lowest-indexed keq.
-  const int C = (n + NTS - 1) / NTS;
-  const int i0 = min(n, t * C), i1 = min(n, i0 + C);
-  uint32_t cg = 0, ce = 0;
-  for (int b0 = i0; b0 < i1; b0 += B) {
-    uint32_t x[B];
+  if constexpr (LDS_KEYS) {
+    // ---- ordered output: participant t owns the indices [t*C, (t+1)*C) ----
+    // It counts its keys above T and equal to T, the exclusive scans of those
+    // counts place it, and it writes its chosen indices in order: ascending
+    // output, and the equal keys taken are the lowest-indexed keq.
+    // C odd: a wave's 64 lanes read 64 different LDS banks
+    const int C = ((n + NTS - 1) / NTS) | 1;
+    const int i0 = min(n, t * C), i1 = min(n, i0 + C);
+    uint32_t cg = 0, ce = 0;
+    for (int b0 = i0; b0 < i1; b0 += B) {
+      uint32_t x[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+      for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      cg += (b0 + j < i1 && x[j] > T) ? 1u : 0u;
-      ce += (b0 + j < i1 && x[j] == T) ? 1u : 0u;
+      for (int j = 0; j < B; ++j) {
+        cg += (b0 + j < i1 && x[j] > T) ? 1u : 0u;
+        ce += (b0 + j < i1 && x[j] == T) ? 1u : 0u;
+      }
     }
-  }
-  uint32_t gt_before, eq_before;
-  excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
-  uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
-  uint32_t eq_seen = eq_before;
-  for (int b0 = i0; b0 < i1; b0 += B) {
-    uint32_t x[B];
+    uint32_t gt_before, eq_before;
+    excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
+    uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
+    uint32_t eq_seen = eq_before;
+    for (int b0 = i0; b0 < i1; b0 += B) {
+      uint32_t x[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+      for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      if (b0 + j < i1) {
-        bool take = x[j] > T;
-        if (x[j] == T) {
-          take = eq_seen < keq;
-          ++eq_seen;
-        }
-        if (take) {
-          if (pos < (uint32_t)k) dst[pos] = b0 + j;
-          ++pos;
+      for (int j = 0; j < B; ++j) {
+        if (b0 + j < i1) {
+          bool take = x[j] > T;
+          if (x[j] == T) {
+            take = eq_seen < keq;
+            ++eq_seen;
+          }
+          if (take) {
+            if (pos < (uint32_t)k) dst[pos] = b0 + j;
+            ++pos;
+          }
         }
       }
     }
+  } else {
+    // ---- ordered output: wave w owns indices [w*cw, (w+1)*cw), walked 64 at a time ----
+    // The waves count their keys above T and equal to T, and each then places
+    // its chosen indices in order with ballot masks.
+    const int cw = (n + NW * 64 - 1) / (NW * 64) * 64;
+    const int w0 = min(n, w * cw), w1 = min(n, w0 + cw);
+    uint32_t cg = 0, ce = 0;   // this wave's keys above T and equal to T
+    each_key_wave<B>(key, w0, w1, [&](int, bool valid, uint32_t x) {
+      cg += (uint32_t)__popcll(__ballot(valid && x > T));
+      ce += (uint32_t)__popcll(__ballot(valid && x == T));
+    });
+    if (lane == 0) {
+      sh.w1[w] = cg;
+      sh.w2[w] = ce;
+    }
+    grp.sync();
+    uint32_t gt_before = 0, eq_before = 0;
+    for (int i = 0; i < w; ++i) {
+      gt_before += sh.w1[i];
+      eq_before += sh.w2[i];
+    }
+    const uint64_t lt = (1ull << lane) - 1ull;   // lanes below this one
+    // taken keys before this wave: all of its larger keys and the equal keys up to keq
+    uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
+    uint32_t eq_seen = eq_before;
+    each_key_wave<B>(key, w0, w1, [&](int i, bool valid, uint32_t x) {
+      const bool eq = valid && x == T;
+      const uint64_t me = __ballot(eq);
+      const bool take = valid && (x > T || (eq && eq_seen + (uint32_t)__popcll(me & lt) < keq));
+      const uint64_t mt = __ballot(take);
+      if (take) {
+        const uint32_t p = pos + (uint32_t)__popcll(mt & lt);
+        if (p < (uint32_t)k) dst[p] = i;
+      }
+      pos += (uint32_t)__popcll(mt);
+      eq_seen += (uint32_t)__popcll(me);
+    });
   }
   grp.sync();   // sh is free again
 }
 
 // Top-k of a whole row with a block of NTS threads: warm theta (optional),
 // candidate range, radix select.  When n <= k all n indices are kept,
-// followed by -1.
-template <int NTS, typename Grp, typename KeyFn>
+// followed by -1.  LDS_KEYS as for radix_select.
+template <int NTS, bool LDS_KEYS = true, typename Grp, typename KeyFn>
 __device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *warm, int32_t *dst, RadixShared<NTS> &sh) {
   const int t = grp.t();
   if (n <= k) {
@@ -381,7 +424,7 @@ __device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *war
   const uint32_t theta = warm != nullptr ? warm_theta<NTS>(grp, key, warm, n, k, sh) : 0u;
   uint32_t lo, hi, ncand;
   key_range<NTS>(grp, key, n, theta, lo, hi, ncand, sh);
-  radix_select<NTS>(grp, key, n, k, theta, lo, hi, ncand, dst, sh);
+  radix_select<NTS, LDS_KEYS>(grp, key, n, k, theta, lo, hi, ncand, dst, sh);
 }
 
 }  // namespace kvsel

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
   BlockSync<NT> grp;
-  radix_topk<NT>(grp, key, a.n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
+  radix_topk<NT, IN_LDS>(grp, key, a.n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
                  a.idx + (size_t)row * a.k, sh);
 }
 
