@@ -240,6 +240,37 @@ def gather_rows(src, idx, tail_begin: int = 0, n_tail: int = 0):
 
 
 # ---------------------------------------------------------------------------
+# focal-layer profiling
+# ---------------------------------------------------------------------------
+
+def visual_mass(qg, K, s0: int, s1: int, scale) -> np.ndarray:
+    """Image-attention ratio of each head of one GQA group: the share of the
+    head's attention -- a softmax over all N rows -- that falls on the
+    candidate (image) segment [s0, s1).  FastOCR, Focal-Guided Pruning,
+    "Focal Layer Selection": the warm-up profiles every layer's
+    image-attention ratio.  qg [G, d], K [N, d]; result [G]."""
+    p = softmax(logits(qg, K, scale))
+    return p[:, s0:s1].sum(axis=1)
+
+
+def pick_focal_layers(ratios, n_pick: int) -> np.ndarray:
+    """The focal layers: the n_pick layers whose image-attention ratio is
+    highest on average (same page and section: a small fixed set of layers
+    with high concentration on image tokens).
+
+    ratios: [n_layers, n], each layer's ratios over the warm-up steps,
+    sequences and heads.  Mean per layer in float64; layers ranked by mean
+    descending, equal means to the lower layer; the first n_pick are
+    returned ascending."""
+    r = np.asarray(ratios, F64)
+    if not 1 <= n_pick <= r.shape[0]:
+        raise ValueError("need 1 <= n_pick <= n_layers")
+    mean = r.sum(axis=1) / r.shape[1]
+    order = np.lexsort((np.arange(r.shape[0]), -mean))
+    return np.sort(order[:n_pick]).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
 # layer / step schedule
 # ---------------------------------------------------------------------------
 

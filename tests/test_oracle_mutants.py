@@ -81,6 +81,25 @@ def _warm_uses_max(scores, k, warm):
     return cand[O.topk(s32[cand], k)]
 
 
+def _mass_segment_softmax(qg, K, s0, s1, scale):
+    if s1 <= s0:
+        return np.zeros(np.asarray(qg).shape[0])
+    return O.softmax(O.logits(qg, np.asarray(K, F64)[s0:s1], scale)).sum(axis=1)
+
+
+def _pick_high_layer_wins(ratios, n_pick):
+    r = np.asarray(ratios, F64)
+    mean = r.mean(axis=1)
+    order = np.lexsort((-np.arange(r.shape[0]), -mean))
+    return np.sort(order[:n_pick])
+
+
+def _pick_by_peak(ratios, n_pick):
+    r = np.asarray(ratios, F64)
+    order = np.lexsort((np.arange(r.shape[0]), -r.max(axis=1)))
+    return np.sort(order[:n_pick])
+
+
 MUTANTS = [
     ("logits", _no_scale, [P.test_attention_matches_sdpa, P.test_window_scores_scale_sensitive]),
     ("softmax", _softmax_axis0, [lambda: P.test_score_sums(2), lambda: P.test_golden_focal_scores("softmax_three_keys")]),
@@ -91,10 +110,13 @@ MUTANTS = [
     ("kept_rows", _kept_rows_unshifted, [P.test_full_budget_is_dense]),
     ("focal_scores", _focal_sum_over_keys, [lambda: P.test_golden_focal_scores("group_sum_two_heads")]),
     ("topk_warm", _warm_uses_max, [lambda: P.test_topk_warm_equals_cold(0)]),
+    ("visual_mass", _mass_segment_softmax, [P.test_visual_mass_closed_forms, lambda: P.test_visual_mass_matches_sdpa_indicator(0)]),
+    ("pick_focal_layers", _pick_high_layer_wins, [P.test_pick_focal_layers_cases, lambda: P.test_pick_focal_layers_brute_force(0)]),
+    ("pick_focal_layers", _pick_by_peak, [P.test_pick_focal_layers_cases]),
 ]
 
 
-@pytest.mark.parametrize("name,bad,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+@pytest.mark.parametrize("name,bad,pins", MUTANTS, ids=[f"{m[0]}-{m[1].__name__}" for m in MUTANTS])
 def test_pins_catch_mutant(monkeypatch, name, bad, pins):
     monkeypatch.setattr(O, name, bad)
     for pin in pins:

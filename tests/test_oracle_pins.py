@@ -317,3 +317,71 @@ def test_gather_rows_exact():
     src = np.arange(40 * 6).reshape(40, 6)
     got = O.gather_rows(src, [3, 7, 20], 36, 4)
     np.testing.assert_array_equal(got, src[[3, 7, 20, 36, 37, 38, 39]])
+
+
+# --------------------------------------------------------------------------
+# focal-layer profiling (FastOCR, Focal-Guided Pruning, "Focal Layer
+# Selection"): the image-attention ratio and the choice of the focal layers
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_visual_mass_matches_sdpa_indicator(seed):
+    """The ratio is attention whose value rows are the segment's indicator:
+    torch's scaled_dot_product_attention (fp64, CPU) with V[i] = [i in seg]."""
+    rng = np.random.default_rng(100 + seed)
+    G, N = int(rng.integers(1, 9)), int(rng.integers(2, 400))
+    s0 = int(rng.integers(0, N))
+    s1 = int(rng.integers(s0, N + 1))
+    q, K = _rand(rng, G, D) * 3.0, _rand(rng, N, D)
+    ind = np.zeros((N, 1))
+    ind[s0:s1] = 1.0
+    tq = torch.from_numpy(q)[None, :, None, :]
+    tk = torch.from_numpy(K)[None, None].expand(1, G, -1, -1)
+    tv = torch.from_numpy(ind)[None, None].expand(1, G, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=SCALE)[0, :, 0, 0].numpy()
+    np.testing.assert_allclose(O.visual_mass(q, K, s0, s1, SCALE), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_visual_mass_closed_forms():
+    rng = np.random.default_rng(7)
+    N, G = 300, 4
+    K = _rand(rng, N, D)
+    # a zero query attends uniformly: the ratio is the segment's share of rows
+    np.testing.assert_allclose(O.visual_mass(np.zeros((G, D)), K, 40, 250, SCALE), np.full(G, 210 / 300), rtol=1e-14)
+    q = _rand(rng, G, D)
+    np.testing.assert_allclose(O.visual_mass(q, K, 0, N, SCALE), np.ones(G), rtol=1e-14)   # everything
+    np.testing.assert_allclose(O.visual_mass(q, K, 77, 77, SCALE), np.zeros(G), atol=0)   # empty segment
+    # a query aligned with one segment key puts (almost) all its mass there
+    q1 = np.tile(K[120] * 60.0, (G, 1))
+    assert np.all(O.visual_mass(q1, K, 100, 130, SCALE) > 0.999)
+    assert np.all(O.visual_mass(q1, K, 0, 100, SCALE) < 1e-3)
+
+
+def test_pick_focal_layers_cases():
+    r = np.array([[0.1, 0.3], [0.5, 0.5], [0.2, 0.2], [0.9, 0.1], [0.5, 0.5]])   # means .2 .5 .2 .5 .5
+    # three layers tie at 0.5: the lower indices win
+    assert list(O.pick_focal_layers(r, 2)) == [1, 3]
+    assert list(O.pick_focal_layers(r, 3)) == [1, 3, 4]
+    assert list(O.pick_focal_layers(r, 4)) == [0, 1, 3, 4]
+    assert list(O.pick_focal_layers(r, 5)) == [0, 1, 2, 3, 4]
+    # the mean, not the peak, decides
+    r2 = np.array([[0.0, 0.0, 1.0], [0.4, 0.4, 0.4]])
+    assert list(O.pick_focal_layers(r2, 1)) == [1]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pick_focal_layers_brute_force(seed):
+    """Every n_pick-subset of layers: the chosen one has the largest sum of
+    means, and among equal sums the lexicographically smallest layers."""
+    rng = np.random.default_rng(seed)
+    L = 6
+    r = rng.integers(0, 4, size=(L, 3)) / 4.0   # many ties
+    mean = r.mean(axis=1)
+    for n_pick in range(1, L + 1):
+        best = None
+        for sub in itertools.combinations(range(L), n_pick):
+            # rank order: a subset is better if its sorted means are larger
+            key = sorted(((-mean[l], l) for l in sub))
+            if best is None or key < best[0]:
+                best = (key, sub)
+        assert list(O.pick_focal_layers(r, n_pick)) == list(best[1])
