@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"],
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile"],
                     help="c1 (default) is the metric's workload; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -340,6 +340,44 @@ def bench_c0(args):
           {"bytes_per_step": nbytes, "hbm_gbs_algorithmic": round(nbytes / ms / 1e6, 1)})
 
 
+def bench_profile(args):
+    """Focal-layer profiling at the C1 shape: a warm-up step is the
+    image-attention ratio of all 28 layers (batch 32, 16 heads, K only); the
+    layer choice follows the last warm-up step."""
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.decode import FocalProfiler
+    cfg = synth.C1
+    w = gen.make_focal(cfg, "cuda")
+    max_len = int(w.seq_len_np.max())
+    kvs = [kvsel.KV(w.k_pool[l], None, w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+           for l in range(cfg.layers)]
+    W = 4
+    prof = FocalProfiler(kvs, cfg.hq, cfg.scale, W, device="cuda")
+    T = cfg.steps
+    ms = _timed(lambda i: prof.step(i % W, w.q[i % T], w.seq_len[i % T]), args.steps, args.warmup)
+    prof.pick(len(cfg.focal))   # first call loads the kernel
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        prof.pick(len(cfg.focal))
+    b.record()
+    torch.cuda.synchronize()
+    pick_us = a.elapsed_time(b) * 1e3 / 10
+    per_t = [cfg.layers * (cfg.batch * cfg.hkv * int(w.seq_len_np[t, 0]) * 256 + cfg.batch * cfg.hq * (256 + 4))
+             for t in range(T)]
+    nbytes = sum(per_t[(args.warmup + i) % T] for i in range(args.steps)) / args.steps
+    _line("focal-layer profiling steps/s (image-attention ratio of 28 layers)", 1000 / ms, "steps/s", args, ms,
+          "c1_profile: C1 cache (28 layers, batch 32, 16q/8kv, 6400 visual + 1024 text), ratio per layer "
+          "from K only, top-2 layers after 4 warm-up steps",
+          {"bytes_per_step_avg": int(nbytes), "hbm_gbs_algorithmic": round(nbytes / ms / 1e6, 1),
+           "hbm_frac_of_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4), "pick_us": round(pick_us, 2)})
+
+
 def bench_c2(args):
     """One FastKV token-selective propagation (window scores on MFMA, pool,
     top-6554, gather of 6562 hidden rows); 6 input sets rotate."""
@@ -449,7 +487,7 @@ def bench_c4(args):
            "hbm_gbs_logical": round(lb / ms / 1e6, 1)})
 
 
-OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4}
+OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "profile": bench_profile}
 
 
 if __name__ == "__main__":

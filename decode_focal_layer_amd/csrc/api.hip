@@ -250,6 +250,43 @@ kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_
   return hip_status(launch_focal_norm(n, kv->batch, (hipStream_t)stream), "focal score launch");
 }
 
+size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads) {
+  int G;
+  if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;
+  return attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, kv->max_seq_len > 0 ? kv->max_seq_len : 1, 0,
+                   kv->max_seg_len, kv->max_seq_len)
+      .total;
+}
+
+kvsel_status kvsel_visual_mass(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
+                               float *mass, void *ws, size_t ws_bytes, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, false)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (mass == nullptr) return fail(KVSEL_EINVAL, "mass is NULL");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  const AttnPlan p = attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, kv->max_seq_len > 0 ? kv->max_seq_len : 1, 0,
+                               kv->max_seg_len, kv->max_seq_len);
+  if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
+  AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, p, (char *)ws, nullptr, nullptr, 0);
+  a.dense = 1;
+  a.mass = mass;
+  return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "visual_mass launch");
+}
+
+kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_t n_layers, int32_t n, int32_t n_pick,
+                               int32_t *layers, kvsel_stream stream) {
+  if (ratios == nullptr || layers == nullptr) return fail(KVSEL_EINVAL, "ratios and layers are required");
+  if (n_layers < 1 || n_layers > kMaxLayers) return fail(KVSEL_EINVAL, "n_layers must be in [1, %d]", kMaxLayers);
+  if (n < 1) return fail(KVSEL_EINVAL, "n must be >= 1");
+  if (ld < n) return fail(KVSEL_EINVAL, "ld must be >= n");
+  if (n_pick < 1 || n_pick > n_layers) return fail(KVSEL_EINVAL, "n_pick must be in [1, n_layers]");
+  return hip_status(launch_pick_layers(ratios, ld, n_layers, n, n_pick, layers, (hipStream_t)stream),
+                    "pick_layers launch");
+}
+
 kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale, float *out,
                               float *lse, int32_t norm, int32_t k, const int32_t *warm_idx, int32_t *idx,
                               float *seg_scores, int64_t ld, void *ws, size_t ws_bytes, kvsel_stream stream) {

@@ -135,14 +135,21 @@ __device__ __forceinline__ void merge_records(const AttnArgs &a, int b, int g, i
       L += rec0[sp * kRec + kD + 1] * c;
       A += rec0[sp * kRec + dim] * c;
     }
-    a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
+    if (a.mass != nullptr) {
+      if (dim == 0) a.mass[hb] = L > 0.f ? A / L : 0.f;
+    } else {
+      a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
+    }
     if (dim == 0 && a.lse != nullptr) a.lse[hb] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
 // MODE 0: attention only.  MODE 1: also store the raw logits to the global
 // scratch.  MODE 2 (one split only): keep the segment logits in LDS and end
-// with the focal selection of this (sequence, kv head).  STREAM: K/V rows are
+// with the focal selection of this (sequence, kv head).  MODE 3 (dense): the
+// share of each head's attention on the candidate segment -- attention whose
+// value rows are the segment's indicator, so V is never read; the share is
+// dim 0 of that output.  STREAM: K/V rows are
 // loaded non-temporally (each is read once), so they do not evict the data
 // that is reused from launch to launch (block tables, kept indices, queries);
 // off when the rows themselves are shared by many sequences (a shared
@@ -208,6 +215,9 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   } else if (MODE == 1) {
     if (a.logit_mode == 1) { lo = v.s0; hi = v.s1; }
     else { lo = 0; hi = v.n; }
+  } else if (MODE == 3) {   // the segment, whose attention share is measured
+    lo = v.s0;
+    hi = v.s1;
   }
 
   if (tab_lds) {
@@ -281,14 +291,17 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       // 16 bytes) and gets probability 0
       const uint16_t *kp = ok[u] ? kbase + (size_t)pr * kD : qbase;
       const uint16_t *vp = ok[u] ? vbase + (size_t)pr * kD : qbase;
-      if (STREAM) {   // each row is read once: do not displace reused lines
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      if (STREAM)   // each row is read once: do not displace reused lines
         kr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp)));
-        vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp)));
-      } else {
+      else
         kr[u] = *reinterpret_cast<const uint4 *>(kp);
+      if (MODE == 3)
+        vr[u] = make_uint4(0u, 0u, 0u, 0u);   // not read
+      else if (STREAM)
+        vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp)));
+      else
         vr[u] = *reinterpret_cast<const uint4 *>(vp);
-      }
     }
   };
   // online softmax over the chunk's rows
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     float dot[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) dot_rows<G>(qr, kr[u], dot[u]);
-    if (MODE != 0) {
+    if (MODE == 1 || MODE == 2) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = start + KVSEL_ROWT(base, u);   // dense: logical row = virtual row
@@ -336,6 +349,15 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       for (int u = 0; u < U; ++u) {
         p[u] = fast_exp2(s[u] - m[h]);
         l[h] += p[u];
+      }
+      if constexpr (MODE == 3) {
+        // the indicator row: 1 in dim 0 (lane sub 0) for segment rows
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int row = start + KVSEL_ROWT(base, u);
+          acc[h][0] = fmaf(p[u], (sub == 0 && row >= lo && row < hi) ? 1.f : 0.f, acc[h][0]);
+        }
+        continue;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -476,7 +498,11 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     }
     const size_t hb = (size_t)b * a.hq + g * G + h;
     if (a.nsplit == 1) {
-      a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
+      if (MODE == 3) {
+        if (dim == 0) a.mass[hb] = L > 0.f ? A / L : 0.f;
+      } else {
+        a.out[hb * kD + dim] = L > 0.f ? A / L : 0.f;
+      }
       if (dim == 0 && a.lse != nullptr) a.lse[hb] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
     } else {
       float *rec = a.rec + (hb * a.nsplit + split) * kRec;
@@ -580,7 +606,13 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
     return hipGetLastError();
     }
   }
-  if (a.logits != nullptr) {
+  if (a.mass != nullptr) {
+    if (a.dense == 0 || a.logits != nullptr) return hipErrorInvalidValue;
+    if (stream)
+      hipLaunchKernelGGL((attn_kernel<G, NT, U, 3, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<G, NT, U, 3, false>), grid, dim3(NT), 0, s, a);
+  } else if (a.logits != nullptr) {
     if (stream)
       hipLaunchKernelGGL((attn_kernel<G, NT, U, 1, true>), grid, dim3(NT), 0, s, a);
     else

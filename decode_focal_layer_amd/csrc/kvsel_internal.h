@@ -50,6 +50,7 @@ struct AttnArgs {
   uint32_t *counters;   // reserved region at the start of the workspace (unused)
   float *rec;           // [batch][hq][nsplit][kRec]
   float *out, *lse;
+  float *mass;          // non-null: the segment's attention share per head instead of out
   float *logits;        // [batch][hq][ld_logits] raw q.k dots, or null
   int64_t ld_logits;
   int32_t logit_mode;
@@ -74,6 +75,11 @@ inline bool fused_focal_fits(int group, int max_seg_len) {
 }
 
 hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s);
+
+// focal-layer choice: one work-group
+constexpr int kMaxLayers = 1024;
+hipError_t launch_pick_layers(const float *ratios, int64_t ld, int n_layers, int n, int n_pick, int32_t *layers,
+                              hipStream_t s);
 
 // logits only (no V): rows [lo, hi) per mode into the logit scratch
 hipError_t launch_logits(const AttnArgs &a, int batch, int group, int max_rows, hipStream_t s);

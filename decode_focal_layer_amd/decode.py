@@ -107,3 +107,42 @@ class FocalDecoder:
     def selection(self, layer: int, previous: bool = False) -> torch.Tensor:
         """Kept indices of a focal layer after the last step (or the step before)."""
         return self.idx[layer][self.cur if previous else 1 - self.cur]
+
+
+class FocalProfiler:
+    """Warm-up profiling and the choice of the focal layers.
+
+    FastOCR (technical summary, Focal-Guided Pruning, "Focal Layer
+    Selection"): during w warm-up steps every layer's image-attention ratio
+    is profiled, and the small fixed set of layers that concentrate most on
+    the image tokens becomes the focal set.  Each step writes each layer's
+    per-(sequence, head) ratios (kvsel_visual_mass) into that layer's row of
+    one buffer; pick() ranks the layers by mean ratio (kvsel_pick_layers).
+    """
+
+    def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, scale: float, warmup_steps: int, device="cuda"):
+        self.kvs = list(kvs)
+        self.L = len(self.kvs)
+        self.hq = num_q_heads
+        self.scale = float(scale)
+        self.w = int(warmup_steps)
+        self.B = self.kvs[0].batch
+        self.per_step = self.B * num_q_heads
+        self.ratios = torch.zeros((self.L, self.w * self.per_step), dtype=torch.float32, device=device)
+        self.ws = kvsel.Workspace(device)
+        need = max(kvsel.lib().kvsel_mass_workspace(kv.ref(), num_q_heads) for kv in self.kvs)
+        self.ws.ptr_and_size(need)
+        self.layers = torch.zeros((self.L,), dtype=torch.int32, device=device)
+
+    def step(self, t: int, q: torch.Tensor, seq_len: torch.Tensor, stream=None):
+        """Warm-up step t < w; q: bf16 [layers][batch][hq][128]."""
+        if not 0 <= t < self.w:
+            raise ValueError("warm-up step out of range")
+        for l, kv in enumerate(self.kvs):
+            kv.c.seq_len = seq_len.data_ptr()
+            kvsel.visual_mass(kv, q[l], self.hq, self.scale,
+                              self.ratios[l, t * self.per_step:(t + 1) * self.per_step], ws=self.ws, stream=stream)
+
+    def pick(self, n_focal: int, stream=None) -> torch.Tensor:
+        """The n_focal layers with the highest mean ratio, ascending (int32, device)."""
+        return kvsel.pick_layers(self.ratios, n_focal, self.layers[:n_focal], stream=stream)

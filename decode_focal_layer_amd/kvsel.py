@@ -30,6 +30,7 @@ SYMBOLS = (
     "kvsel_topk", "kvsel_topk_workspace",
     "kvsel_gather_attn", "kvsel_attn_workspace",
     "kvsel_dense_attn", "kvsel_focal_attn", "kvsel_gather_rows",
+    "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
 )
 
 
@@ -90,6 +91,12 @@ def lib() -> ctypes.CDLL:
     L.kvsel_focal_attn.argtypes = [_DP, _P, _I32, _F32, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
     L.kvsel_gather_rows.restype = _I32
     L.kvsel_gather_rows.argtypes = [_P, _I64, _I64, _P, _I32, _I64, _I32, _P, _P]
+    L.kvsel_visual_mass.restype = _I32
+    L.kvsel_visual_mass.argtypes = [_DP, _P, _I32, _F32, _P, _P, _SZ, _P]
+    L.kvsel_mass_workspace.restype = _SZ
+    L.kvsel_mass_workspace.argtypes = [_DP, _I32]
+    L.kvsel_pick_layers.restype = _I32
+    L.kvsel_pick_layers.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P]
     _lib = L
     return L
 
@@ -295,6 +302,32 @@ def dense_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: tor
     _check(lib().kvsel_dense_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(out), _ptr(lse), _ptr(seg_scores),
                                   ld, norm, p, n, _stream(stream)))
     return out
+
+
+def visual_mass(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, mass: torch.Tensor,
+                ws: Optional[Workspace] = None, stream=None):
+    """kvsel_visual_mass.  q: bf16 [batch][hq][128]; mass: fp32, batch * hq
+    contiguous values (e.g. a slice of a per-layer ratio buffer)."""
+    _need(q, torch.bfloat16, "q")
+    _need(mass, torch.float32, "mass")
+    if mass.numel() < kv.batch * num_q_heads:
+        raise ValueError("mass needs batch * num_q_heads values")
+    w = _ws(ws, q.device)
+    p, n = w.ptr_and_size(lib().kvsel_mass_workspace(kv.ref(), num_q_heads))
+    _check(lib().kvsel_visual_mass(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(mass), p, n, _stream(stream)))
+    return mass
+
+
+def pick_layers(ratios: torch.Tensor, n_pick: int, layers: torch.Tensor, stream=None):
+    """kvsel_pick_layers.  ratios: fp32 [n_layers][n] (row stride = its
+    second dimension); layers: int32 [n_pick]."""
+    _need(ratios, torch.float32, "ratios")
+    _need(layers, torch.int32, "layers")
+    if ratios.dim() != 2 or layers.numel() < n_pick:
+        raise ValueError("ratios must be [n_layers][n] and layers hold n_pick values")
+    _check(lib().kvsel_pick_layers(_ptr(ratios), ratios.shape[1], ratios.shape[0], ratios.shape[1], n_pick,
+                                   _ptr(layers), _stream(stream)))
+    return layers
 
 
 def focal_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: torch.Tensor, k: int,

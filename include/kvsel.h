@@ -239,7 +239,8 @@ KVSEL_API kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t 
  *
  * Equal to kvsel_dense_attn(..., seg_scores, ld, norm) followed by
  * kvsel_topk(seg_scores, ld, batch * num_kv_heads, segment length, k,
- * warm_idx, idx): same out, lse and scores bit for bit, the same idx.  q, out,
+ * warm_idx, idx): the same scores bit for bit and the same idx; out and lse
+ * equal up to summation order (rows are handed to waves on demand).  q, out,
  * lse as kvsel_dense_attn; idx, warm_idx: int32 [batch][num_kv_heads][k]
  * (warm_idx NULL or a previous selection, see kvsel_topk).  seg_scores: NULL
  * or fp32 [batch][num_kv_heads][ld].  A sequence whose segment is shorter
@@ -264,6 +265,37 @@ KVSEL_API kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t 
 KVSEL_API kvsel_status kvsel_gather_rows(const void *src, int64_t row_bytes, int64_t n_src_rows,
                                const int32_t *idx, int32_t n_idx, int64_t tail_begin,
                                int32_t n_tail, void *dst, kvsel_stream stream);
+
+/*
+ * kvsel_visual_mass -- the image-attention ratio of each query head: the
+ * share of its attention on the candidate segment.
+ * (FastOCR Focal-Guided Pruning, Focal Layer Selection: a short warm-up
+ *  profiles this ratio for every layer.)
+ *
+ * mass[b][h] = sum over i in [seg_begin[b], seg_end[b]) of softmax_i(scale *
+ * q[b][h] . K[b][g(h)][i]), the softmax over every present row [0,
+ * seq_len[b]); 0 for an empty segment.  q: bf16 [batch][num_q_heads][128];
+ * mass: fp32 [batch][num_q_heads].  K is read once and V is not read
+ * (v_pool may be NULL).  Workspace: kvsel_mass_workspace(kv, num_q_heads).
+ */
+KVSEL_API kvsel_status kvsel_visual_mass(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
+                                         float scale, float *mass, void *ws, size_t ws_bytes, kvsel_stream stream);
+KVSEL_API size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads);
+
+/*
+ * kvsel_pick_layers -- the focal layers: the n_pick layers with the highest
+ * mean image-attention ratio.
+ * (FastOCR Focal-Guided Pruning, Focal Layer Selection: a small fixed set of
+ *  layers with high concentration on image tokens.)
+ *
+ * ratios: fp32, device, layer l's n values at ratios[l * ld + j], j < n (for
+ * instance the kvsel_visual_mass outputs of every warm-up step).  Means in
+ * fp64; layers ranked by mean descending, equal means to the lower layer;
+ * layers: int32 [n_pick], the chosen layers ascending.  Requires 1 <= n_pick
+ * <= n_layers <= 1024, n >= 1, ld >= n.
+ */
+KVSEL_API kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_t n_layers, int32_t n,
+                                         int32_t n_pick, int32_t *layers, kvsel_stream stream);
 
 #ifdef __cplusplus
 }

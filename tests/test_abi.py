@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 15
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -149,3 +149,31 @@ def test_gather_rows_rejects(L, args, code):
     r = L.kvsel_gather_rows(a["src"], a["row_bytes"], a["n_src"], a["idx"], a["n_idx"], a["tail"], a["n_tail"],
                             a["dst"], None)
     assert r == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=12), EINVAL), (dict(q=0), EINVAL), (dict(q=FAKE + 2), EINVAL), (dict(mass=0), EINVAL),
+    (dict(scale=float("nan")), EINVAL), (dict(ws_bytes=16), ENOSPC), (dict(ws=0), EINVAL),
+    (dict(d=dict(head_dim=64)), EUNSUP), (dict(d=dict(k_pool=0)), EINVAL),
+])
+def test_visual_mass_rejects(L, kw, code):
+    d = desc(v_pool=0, **kw.get("d", {}))    # V is never read: v_pool may be NULL
+    r = L.kvsel_visual_mass(ctypes.byref(d), kw.get("q", FAKE), kw.get("hq", 16), kw.get("scale", 0.088),
+                            kw.get("mass", FAKE), kw.get("ws", FAKE), kw.get("ws_bytes", 1 << 30), None)
+    assert r == code
+    assert L.kvsel_last_error()
+
+
+def test_mass_workspace(L):
+    assert L.kvsel_mass_workspace(ctypes.byref(desc(v_pool=0)), 16) > 0
+    assert L.kvsel_mass_workspace(ctypes.byref(desc(head_dim=64)), 16) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(ratios=0), EINVAL), (dict(layers=0), EINVAL), (dict(n_layers=0), EINVAL), (dict(n_layers=1025), EINVAL),
+    (dict(n=0), EINVAL), (dict(ld=3), EINVAL), (dict(n_pick=0), EINVAL), (dict(n_pick=29), EINVAL),
+])
+def test_pick_layers_rejects(L, args, code):
+    a = dict(ratios=FAKE, ld=64, n_layers=28, n=64, n_pick=2, layers=FAKE)
+    a.update(args)
+    assert L.kvsel_pick_layers(a["ratios"], a["ld"], a["n_layers"], a["n"], a["n_pick"], a["layers"], None) == code

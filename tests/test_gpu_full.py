@@ -75,6 +75,39 @@ def test_c1_full_sampled():
                 assert_attn(outs[t][l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
 
 
+def test_c1_focal_layer_profiling():
+    """Focal-layer choice on the C1 cache: 4 warm-up steps x 28 layers of
+    image-attention ratios (batch 32, 16 heads), then the top-2 layers.
+    Checked: 64 sampled (step, layer, sequence, kv head) ratios against the
+    oracle, and the choice against the oracle's choice on the same ratios."""
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.decode import FocalProfiler
+    cfg = synth.C1
+    w = gen.make_focal(cfg, DEV)
+    max_len = int(w.seq_len_np.max())
+    kvs = [kvsel.KV(w.k_pool[l], None, w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+           for l in range(cfg.layers)]
+    W = 4
+    prof = FocalProfiler(kvs, cfg.hq, cfg.scale, W, device=DEV)
+    for t in range(W):
+        prof.step(t, w.q[t], w.seq_len[t])
+    layers = prof.pick(len(cfg.focal)).cpu().numpy()
+    torch.cuda.synchronize()
+    ratios = prof.ratios.cpu().numpy()
+    assert np.array_equal(layers, O.pick_focal_layers(ratios.astype(np.float64), len(cfg.focal)))
+    rng = np.random.default_rng(9)
+    G, per = cfg.group, cfg.batch * cfg.hq
+    for _ in range(64):
+        t, l, b, g = (int(rng.integers(W)), int(rng.integers(cfg.layers)), int(rng.integers(cfg.batch)),
+                      int(rng.integers(cfg.hkv)))
+        n = int(w.seq_len_np[t, b])
+        Kl = O.logical_rows(w.k_pool[l], w.table_np[b], g, n)
+        ref = O.visual_mass(O.widen(w.q[t][l, b, g * G:(g + 1) * G].cpu()), Kl, 0, cfg.n_visual, cfg.scale)
+        got = ratios[l, t * per + b * cfg.hq + g * G: t * per + b * cfg.hq + (g + 1) * G]
+        assert np.abs(got - ref).max() <= 1e-5, (t, l, b, g)
+
+
 def _rows(pool, table_row, g, rows):
     """K or V rows `rows` (logical positions) of one sequence's kv head g, as
     float64 on the host: the oracle's own paged-read applied to a subset."""

@@ -85,6 +85,60 @@ def test_dense_and_gather_attention(G, batch, lens):
             assert np.abs(lse_s[b, g * G:(g + 1) * G].cpu().numpy() - rl_s).max() < 1e-4
 
 
+# (G, batch, lens, segments): split (few pairs) and one work-group per pair,
+# ragged lengths, empty and whole segments
+MASS_CASES = [(1, 1, [1], [(0, 1)]), (2, 2, [17, 300], [(3, 15), (0, 300)]),
+              (4, 3, [4095, 1000, 2], [(100, 4000), (7, 7), (1, 2)]), (8, 1, [8193], [(0, 8000)]),
+              (2, 32, None, None)]
+
+
+@pytest.mark.parametrize("G,batch,lens,segs", MASS_CASES)
+def test_visual_mass(G, batch, lens, segs):
+    """The image-attention ratio per head against the oracle (fp32 sums:
+    absolute error <= 1e-5 on a value in [0, 1]); V is not needed."""
+    kvsel = K()
+    rng = np.random.default_rng(700 + G * batch)
+    hkv = 8 if batch == 32 else 2
+    if lens is None:
+        lens = [int(x) for x in rng.integers(200, 900, size=batch)]
+        segs = [(int(rng.integers(0, 50)), n - int(rng.integers(0, 100))) for n in lens]
+    hq = hkv * G
+    kv, kc, _, table = make_kv(rng, batch, hkv, lens, segs)
+    kv = kvsel.KV(kv.k_pool, None, kv.block_table, kv.seq_len, kv.seg_begin, kv.seg_end,
+                  max_seq_len=kv.max_seq_len, max_seg_len=kv.max_seg_len, min_seg_len=kv.min_seg_len)
+    q = (torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(3)) * 2).to(torch.bfloat16).to(DEV)
+    mass = torch.full((batch, hq), -1.0, dtype=torch.float32, device=DEV)
+    log_case("visual_mass", G, batch, lens[:4])
+    kvsel.visual_mass(kv, q, hq, SCALE, mass)
+    torch.cuda.synchronize()
+    got = mass.cpu().numpy()
+    qc = q.cpu()
+    for b in range(batch):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            ref = O.visual_mass(O.widen(qc[b, g * G:(g + 1) * G]), Kl, segs[b][0], segs[b][1], SCALE)
+            assert np.abs(got[b, g * G:(g + 1) * G] - ref).max() <= 1e-5, f"b{b} g{g}"
+    # the whole segment is the whole attention
+    assert all(abs(got[b] - 1.0).max() <= 1e-6 for b in range(batch) if segs[b] == (0, lens[b]))
+
+
+@pytest.mark.parametrize("L,n,quant", [(1, 1, 4), (5, 7, 4), (28, 2048, 64), (100, 33, 0), (1024, 3, 2)])
+def test_pick_layers(L, n, quant):
+    """Exact against the oracle on the same fp32 ratios (quantised ratios
+    make many equal means: ties go to the lower layer)."""
+    kvsel = K()
+    rng = np.random.default_rng(L * 7 + n)
+    r = rng.random((L, n)).astype(np.float32)
+    if quant:
+        r = (np.floor(r * quant) / quant).astype(np.float32)
+    rt = torch.from_numpy(r).to(DEV)
+    for n_pick in sorted({1, min(2, L), max(1, L // 3), L}):
+        out = torch.full((n_pick,), -1, dtype=torch.int32, device=DEV)
+        kvsel.pick_layers(rt, n_pick, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), O.pick_focal_layers(r.astype(np.float64), n_pick)), n_pick
+
+
 def test_gather_full_budget_equals_dense_and_empty_rows():
     kvsel = K()
     rng = np.random.default_rng(11)
