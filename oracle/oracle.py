@@ -78,6 +78,31 @@ def logical_rows(pool, table_row, g: int, n: int, block: int = 16) -> np.ndarray
     return widen(np.asarray(pool)[blk, g, off, :])
 
 
+def fork_child_table(parent_table, parent_len: int, new_block: int, block: int = 16) -> np.ndarray:
+    """A branch's block table at a fork.  HPD-Parsing wiki, inference
+    scheduling: a content branch is spawned at a fork token and shares the
+    parent's KV through a fork pointer, zero copy, released by reference
+    count.  The blocks holding only rows before the fork point are shared as
+    they are; a block the parent has only partly filled is replaced by
+    new_block, a private copy, because both branches append after the fork
+    point (copy on write).  Entries past the fork point are -1."""
+    parent_table = np.asarray(parent_table, dtype=np.int64)
+    t = np.full(parent_table.shape, -1, dtype=np.int64)
+    nfull = parent_len // block
+    t[:nfull] = parent_table[:nfull]
+    if parent_len % block:
+        t[nfull] = new_block
+    return t
+
+
+def copy_block(pool, src: int, dst: int) -> np.ndarray:
+    """Pool with block dst replaced by a copy of block src (every kv head and
+    row): the copy-on-write of a fork."""
+    out = np.array(pool, copy=True)
+    out[dst] = out[src]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # scoring
 # ---------------------------------------------------------------------------

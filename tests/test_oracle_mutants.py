@@ -125,3 +125,16 @@ def test_pins_catch_mutant(monkeypatch, name, bad, pins):
             fn = lambda p=pin: p(0)    # noqa: E731  seeded pins take a seed
         with pytest.raises((AssertionError, ValueError, IndexError)):
             fn()
+
+
+def _fork_shares_partial(parent_table, parent_len, new_block, block=16):
+    t = np.full(np.asarray(parent_table).shape, -1, dtype=np.int64)
+    n = -(-parent_len // block)
+    t[:n] = np.asarray(parent_table)[:n]
+    return t
+
+
+def test_fork_pin_catches_shared_partial_block(monkeypatch):
+    monkeypatch.setattr(O, "fork_child_table", _fork_shares_partial)
+    with pytest.raises(AssertionError):
+        P.test_fork_child_sees_parent_rows_and_stays_isolated(37)

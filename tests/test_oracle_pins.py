@@ -385,3 +385,45 @@ def test_pick_focal_layers_brute_force(seed):
             if best is None or key < best[0]:
                 best = (key, sub)
         assert list(O.pick_focal_layers(r, n_pick)) == list(best[1])
+
+
+# --------------------------------------------------------------------------
+# fork lifecycle (HPD-Parsing wiki, inference scheduling: fork pointer, zero
+# copy, reference-counted release)
+# --------------------------------------------------------------------------
+
+def _scatter(rng, pool, table, rows, start=0):
+    for j in range(rows.shape[1]):
+        pos = start + j
+        pool[table[pos // 16], :, pos % 16, :] = rows[:, j, :]
+
+
+@pytest.mark.parametrize("L", [0, 5, 16, 37, 64, 79])
+def test_fork_child_sees_parent_rows_and_stays_isolated(L):
+    rng = np.random.default_rng(L)
+    hkv, d, nb = 2, 8, 20
+    pool = np.zeros((nb, hkv, 16, d))
+    parent = np.full(8, -1)
+    parent[:6] = [3, 11, 4, 17, 8, 0]
+    _scatter(rng, pool, parent, rng.standard_normal((hkv, L, d)))
+    child = O.fork_child_table(parent, L, new_block=19)
+    pool2 = O.copy_block(pool, parent[L // 16], 19) if L % 16 else pool
+    for g in range(hkv):   # the child reads the parent's rows before the fork, bit for bit
+        np.testing.assert_array_equal(O.logical_rows(pool2, child, g, L), O.logical_rows(pool, parent, g, L))
+    # blocks wholly before the fork are shared; a partly filled one is a fresh copy
+    assert list(child[:L // 16]) == list(parent[:L // 16])
+    assert (L % 16 == 0) == (19 not in child)
+    # both append 9 rows after the fork point: neither sees the other's
+    if L + 9 <= 6 * 16 and L % 16:
+        before_c = O.logical_rows(pool2, child, 0, L)
+        before_p = O.logical_rows(pool2, parent, 0, L)
+        pnew, cnew = rng.standard_normal((hkv, 9, d)), rng.standard_normal((hkv, 9, d))
+        child_ext = child.copy()   # fresh blocks for the child's rows past its copied block
+        for i, blk in zip(range(L // 16 + 1, (L + 8) // 16 + 1), [1, 2, 5, 6, 7]):
+            child_ext[i] = blk
+        _scatter(rng, pool2, parent, pnew, start=L)
+        _scatter(rng, pool2, child_ext, cnew, start=L)
+        np.testing.assert_array_equal(O.logical_rows(pool2, child_ext, 0, L), before_c)
+        np.testing.assert_array_equal(O.logical_rows(pool2, parent, 0, L), before_p)
+        np.testing.assert_array_equal(O.logical_rows(pool2, parent, 0, L + 9)[L:], pnew[0])
+        np.testing.assert_array_equal(O.logical_rows(pool2, child_ext, 0, L + 9)[L:], cnew[0])
