@@ -10,8 +10,22 @@
 using namespace kvsel;
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
+
+namespace kvsel {
+// sets the calling thread's error text (also used by the block pool)
+kvsel_status pool_fail(kvsel_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+void clear_error() { g_err[0] = 0; }
+}  // namespace kvsel
+
+namespace {
 
 kvsel_status fail(kvsel_status st, const char *fmt, ...) {
   va_list ap;

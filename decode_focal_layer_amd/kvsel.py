@@ -31,6 +31,8 @@ SYMBOLS = (
     "kvsel_gather_attn", "kvsel_attn_workspace",
     "kvsel_dense_attn", "kvsel_focal_attn", "kvsel_gather_rows",
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
+    "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
+    "kvsel_pool_alloc", "kvsel_pool_retain", "kvsel_pool_release", "kvsel_fork",
 )
 
 
@@ -97,6 +99,19 @@ def lib() -> ctypes.CDLL:
     L.kvsel_mass_workspace.argtypes = [_DP, _I32]
     L.kvsel_pick_layers.restype = _I32
     L.kvsel_pick_layers.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P]
+    L.kvsel_pool_create.restype = _P
+    L.kvsel_pool_create.argtypes = [_I64]
+    L.kvsel_pool_destroy.restype = None
+    L.kvsel_pool_destroy.argtypes = [_P]
+    L.kvsel_pool_free_count.restype = _I64
+    L.kvsel_pool_free_count.argtypes = [_P]
+    L.kvsel_pool_refcount.restype = _I32
+    L.kvsel_pool_refcount.argtypes = [_P, _I32]
+    for fn in (L.kvsel_pool_alloc, L.kvsel_pool_retain, L.kvsel_pool_release):
+        fn.restype = _I32
+        fn.argtypes = [_P, _P, _I32] if fn is not L.kvsel_pool_alloc else [_P, _I32, _P]
+    L.kvsel_fork.restype = _I32
+    L.kvsel_fork.argtypes = [_P, _P, _I32, _I32, _P, _P, _P, _I64, _I32, _P]
     _lib = L
     return L
 
@@ -369,3 +384,62 @@ def gather_rows(src: torch.Tensor, idx: Optional[torch.Tensor], n_idx: int, tail
     _check(lib().kvsel_gather_rows(_ptr(src), row_bytes, src.shape[0], _ptr(idx), n_idx, tail_begin, n_tail,
                                    _ptr(dst), _stream(stream)))
     return dst
+
+
+# ---------------------------------------------------------------------------
+# branch lifecycle
+
+class BlockPool:
+    """kvsel_block_pool: reference-counted physical block ids of one paged
+    cache (host side), and the fork of a branch (kvsel_fork)."""
+
+    def __init__(self, num_blocks: int):
+        self._p = lib().kvsel_pool_create(int(num_blocks))
+        if not self._p:
+            raise ValueError("num_blocks must be in [1, 2^31)")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        if getattr(self, "_p", None):
+            lib().kvsel_pool_destroy(self._p)
+            self._p = None
+
+    @staticmethod
+    def _ids(ids):
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        return a, a.ctypes.data_as(ctypes.c_void_p)
+
+    def free_count(self) -> int:
+        return lib().kvsel_pool_free_count(self._p)
+
+    def refcount(self, block: int) -> int:
+        return lib().kvsel_pool_refcount(self._p, int(block))
+
+    def alloc(self, n: int):
+        import numpy as np
+        a = np.zeros(max(n, 1), dtype=np.int32)
+        _check(lib().kvsel_pool_alloc(self._p, int(n), a.ctypes.data_as(ctypes.c_void_p)))
+        return a[:n]
+
+    def retain(self, ids):
+        a, p = self._ids(ids)
+        _check(lib().kvsel_pool_retain(self._p, p, a.shape[0]))
+
+    def release(self, ids):
+        a, p = self._ids(ids)
+        _check(lib().kvsel_pool_release(self._p, p, a.shape[0]))
+
+    def fork(self, parent_table, parent_len: int, k_pool: Optional[torch.Tensor] = None,
+             v_pool: Optional[torch.Tensor] = None, stream=None):
+        """The child's block table (numpy int32, like parent_table).  A
+        partly filled last block is copied on the device (k_pool, v_pool:
+        the cache's bf16 pools)."""
+        import numpy as np
+        pt = np.ascontiguousarray(np.asarray(parent_table, dtype=np.int32))
+        ct = np.full_like(pt, -1)
+        nb, hkv = (k_pool.shape[0], k_pool.shape[1]) if k_pool is not None else (self.num_blocks, 0)
+        st = _stream(stream) if k_pool is not None else None
+        _check(lib().kvsel_fork(self._p, pt.ctypes.data_as(ctypes.c_void_p), int(parent_len), pt.shape[0],
+                                ct.ctypes.data_as(ctypes.c_void_p), _ptr(k_pool), _ptr(v_pool), nb, hkv, st))
+        return ct

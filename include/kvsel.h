@@ -297,6 +297,50 @@ KVSEL_API size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_hea
 KVSEL_API kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_t n_layers, int32_t n,
                                          int32_t n_pick, int32_t *layers, kvsel_stream stream);
 
+/*
+ * Branch lifecycle: a reference-counted block pool (host side) and the fork
+ * of a branch.
+ * (HPD-Parsing wiki, inference scheduling: a content branch spawned at a
+ *  fork token shares the parent's KV through a fork pointer, zero copy; the
+ *  shared blocks are released by reference count once every branch holding
+ *  them is done.)
+ *
+ * The pool hands out the physical block ids of one paged cache (as used in
+ * block tables); each id has a reference count, and an id is free when its
+ * count is 0.  A pool is not thread-safe.  kvsel_pool_create returns NULL
+ * for num_blocks outside [1, 2^31).  kvsel_pool_refcount returns -1 for an
+ * id out of range; kvsel_pool_free_count -1 for a NULL pool.
+ */
+typedef struct kvsel_block_pool kvsel_block_pool;
+KVSEL_API kvsel_block_pool *kvsel_pool_create(int64_t num_blocks);
+KVSEL_API void kvsel_pool_destroy(kvsel_block_pool *pool);
+KVSEL_API int64_t kvsel_pool_free_count(const kvsel_block_pool *pool);
+KVSEL_API int32_t kvsel_pool_refcount(const kvsel_block_pool *pool, int32_t block);
+/* n free ids into ids, each with count 1 (KVSEL_ENOSPC if fewer are free). */
+KVSEL_API kvsel_status kvsel_pool_alloc(kvsel_block_pool *pool, int32_t n, int32_t *ids);
+/* Count + 1 for each allocated id (KVSEL_EINVAL for a free or bad id). */
+KVSEL_API kvsel_status kvsel_pool_retain(kvsel_block_pool *pool, const int32_t *ids, int32_t n);
+/* Count - 1 for each id; an id reaching 0 is free again.  Rejects (EINVAL,
+ * nothing changed) a list holding an id more often than its count. */
+KVSEL_API kvsel_status kvsel_pool_release(kvsel_block_pool *pool, const int32_t *ids, int32_t n);
+
+/*
+ * kvsel_fork -- the child's block table at a fork.  parent_table and
+ * child_table are HOST int32 [max_blocks]; the parent holds parent_len rows.
+ * Every block holding only rows below parent_len is shared (count + 1).  If
+ * parent_len ends inside a block, a newly allocated block receives a copy of
+ * it (every kv head's 16 rows of K and V, bit for bit; copy on write, since
+ * both branches append after the fork point): one kernel enqueued on stream
+ * (k_pool, v_pool: the cache's device pools [num_blocks][num_kv_heads][16][128]
+ * bf16, and the pool's ids must all be below num_blocks; not needed when
+ * parent_len is a multiple of 16).  child_table entries past the fork point
+ * are -1.  KVSEL_ENOSPC if no block is free for the copy; nothing changes on
+ * an error.
+ */
+KVSEL_API kvsel_status kvsel_fork(kvsel_block_pool *pool, const int32_t *parent_table, int32_t parent_len,
+                                  int32_t max_blocks, int32_t *child_table, uint16_t *k_pool, uint16_t *v_pool,
+                                  int64_t num_blocks, int32_t num_kv_heads, kvsel_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 23
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n

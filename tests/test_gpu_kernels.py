@@ -380,3 +380,61 @@ def test_determinism():
     assert torch.equal(sc_a, sc_b) and torch.equal(i_a, i_b)
     assert (o_a - o_b).abs().max().item() < 1e-5
     assert (s_a - s_b).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("L", [5, 37, 100])
+def test_fork_copy_on_write(L):
+    """kvsel_fork on a partly filled last block: the child reads the parent's
+    rows bit for bit through its own table; rows appended afterwards by
+    either branch stay invisible to the other; attention through the child's
+    table matches the oracle on the child's rows; reference counts."""
+    kvsel = K()
+    hkv, nb, maxb = 4, 24, 10
+    pool = kvsel.BlockPool(nb)
+    kp = torch.randn((nb, hkv, 16, 128), generator=torch.Generator().manual_seed(L)).to(torch.bfloat16).to(DEV)
+    vp = torch.randn((nb, hkv, 16, 128), generator=torch.Generator().manual_seed(L + 1)).to(torch.bfloat16).to(DEV)
+    parent = np.full(maxb, -1, dtype=np.int32)
+    nblk = -(-(L + 7) // 16)
+    parent[:nblk] = pool.alloc(nblk)[::-1]          # any order of physical blocks
+    log_case("fork", L)
+    child = pool.fork(parent, L, kp, vp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(child[:L // 16], parent[:L // 16])
+    fresh = child[L // 16]
+    assert fresh not in parent and pool.refcount(fresh) == 1
+    assert all(pool.refcount(b) == 2 for b in parent[:L // 16]) and pool.refcount(parent[L // 16]) == 1
+    kc, vc = kp.cpu(), vp.cpu()
+    for g in range(hkv):
+        for pc in (kc, vc):
+            np.testing.assert_array_equal(O.logical_rows(pc, child, g, L), O.logical_rows(pc, parent, g, L))
+    # both branches append 7 rows after the fork point
+    newp = torch.randn((hkv, 7, 128), generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    newc = torch.randn((hkv, 7, 128), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    child_t = child.copy()
+    if (L + 6) // 16 > L // 16:
+        child_t[(L + 6) // 16] = pool.alloc(1)[0]
+    for j in range(7):
+        pos = L + j
+        kp[int(parent[pos // 16]), :, pos % 16, :] = newp[:, j].to(DEV)
+        kp[int(child_t[pos // 16]), :, pos % 16, :] = newc[:, j].to(DEV)
+        vp[int(child_t[pos // 16]), :, pos % 16, :] = newc[:, j].to(DEV)
+    kc, vc = kp.cpu(), vp.cpu()
+    for g in range(hkv):
+        cl = O.logical_rows(kc, child_t, g, L + 7)
+        pl = O.logical_rows(kc, parent, g, L + 7)
+        np.testing.assert_array_equal(cl[:L], pl[:L])
+        np.testing.assert_array_equal(cl[L:], O.widen(newc[g]))
+        np.testing.assert_array_equal(pl[L:], O.widen(newp[g]))
+    # attention through the child's table
+    G, n = 2, L + 7
+    kv = kvsel.KV(kp, vp, torch.from_numpy(child_t[None]).to(DEV), torch.tensor([n], dtype=torch.int32, device=DEV),
+                  torch.zeros(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.int32, device=DEV),
+                  max_seq_len=n, max_seg_len=0, min_seg_len=0)
+    q = torch.randn((1, hkv * G, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    out = torch.zeros((1, hkv * G, 128), dtype=torch.float32, device=DEV)
+    kvsel.dense_attn(kv, q, hkv * G, SCALE, out)
+    torch.cuda.synchronize()
+    for g in range(hkv):
+        ref, _ = O.dense_attention(O.widen(q.cpu()[0, g * G:(g + 1) * G]), O.logical_rows(kc, child_t, g, n),
+                                   O.logical_rows(vc, child_t, g, n), SCALE)
+        assert_attn(out[0, g * G:(g + 1) * G].cpu().numpy(), ref, f"child g{g}")
