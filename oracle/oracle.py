@@ -251,6 +251,27 @@ def attention(qg, K, V, rows, scale):
     return out, (m + np.log(z))[:, 0]
 
 
+def verify_attention(qd, K, V, rows, n: int, scale):
+    """Verification attention of m drafted tokens (HPD-Parsing wiki, P-MTP:
+    each branch drafts several tokens and verifies them in parallel).
+
+    qd: [m, G, d], the queries of the drafts at positions n-m .. n-1 (the
+    drafts' own K/V rows are the last m rows).  Draft r attends over the
+    rows of `rows` (the branch's attended set) at positions <= n-m+r:
+    everything before the drafts, and the drafts up to its own (causal).
+    Returns (out [m, G, d], lse [m, G])."""
+    qd = np.asarray(qd, F64)
+    m = qd.shape[0]
+    r_all = np.unique(np.asarray(rows, dtype=np.int64))
+    outs, lses = [], []
+    for r in range(m):
+        vis = r_all[r_all <= n - m + r]
+        o, l = attention(qd[r], K, V, vis, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
 def dense_attention(qg, K, V, scale):
     return attention(qg, K, V, np.arange(np.asarray(K).shape[0]), scale)
 

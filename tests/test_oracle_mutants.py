@@ -138,3 +138,24 @@ def test_fork_pin_catches_shared_partial_block(monkeypatch):
     monkeypatch.setattr(O, "fork_child_table", _fork_shares_partial)
     with pytest.raises(AssertionError):
         P.test_fork_child_sees_parent_rows_and_stays_isolated(37)
+
+
+def _verify_not_causal(qd, K, V, rows, n, scale):
+    qd = np.asarray(qd, F64)
+    outs, lses = zip(*[O.attention(qd[r], K, V, np.unique(rows), scale) for r in range(qd.shape[0])])
+    return np.stack(outs), np.stack(lses)
+
+
+def _verify_off_by_one(qd, K, V, rows, n, scale):
+    qd = np.asarray(qd, F64)
+    r_all = np.unique(np.asarray(rows))
+    outs, lses = zip(*[O.attention(qd[r], K, V, r_all[r_all < max(n - qd.shape[0] + r, 1)], scale)
+                       for r in range(qd.shape[0])])
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("bad", [_verify_not_causal, _verify_off_by_one])
+def test_verify_pin_catches(monkeypatch, bad):
+    monkeypatch.setattr(O, "verify_attention", bad)
+    with pytest.raises(AssertionError):
+        P.test_verify_attention_matches_causal_sdpa()

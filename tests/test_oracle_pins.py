@@ -427,3 +427,40 @@ def test_fork_child_sees_parent_rows_and_stays_isolated(L):
         np.testing.assert_array_equal(O.logical_rows(pool2, parent, 0, L), before_p)
         np.testing.assert_array_equal(O.logical_rows(pool2, parent, 0, L + 9)[L:], pnew[0])
         np.testing.assert_array_equal(O.logical_rows(pool2, child_ext, 0, L + 9)[L:], cnew[0])
+
+
+# --------------------------------------------------------------------------
+# draft verification (HPD-Parsing wiki, P-MTP: drafts verified in parallel)
+# --------------------------------------------------------------------------
+
+def test_verify_attention_matches_causal_sdpa():
+    """Over every row, m drafts at the end of the sequence: torch's causal
+    scaled_dot_product_attention on the last m query positions (fp64)."""
+    rng = np.random.default_rng(21)
+    n, m, G = 90, 6, 2
+    K, V = _rand(rng, n, D), _rand(rng, n, D)
+    qd = _rand(rng, m, G, D)
+    out, _ = O.verify_attention(qd, K, V, np.arange(n), n, SCALE)
+    # causal SDPA over the full sequence, with the drafts' queries in the last m positions
+    Q = np.zeros((G, n, D))
+    Q[:, n - m:, :] = qd.transpose(1, 0, 2)
+    tq = torch.from_numpy(Q)[None]
+    tk = torch.from_numpy(K)[None, None].expand(1, G, -1, -1)
+    tv = torch.from_numpy(V)[None, None].expand(1, G, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=SCALE)[0].numpy()
+    np.testing.assert_allclose(out, ref[:, n - m:, :].transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+def test_verify_attention_single_draft_is_attention():
+    rng = np.random.default_rng(22)
+    n = 50
+    K, V = _rand(rng, n, D), _rand(rng, n, D)
+    rows = np.sort(rng.choice(n - 1, size=20, replace=False).tolist() + [n - 1])
+    qd = _rand(rng, 1, 4, D)
+    out, lse = O.verify_attention(qd, K, V, rows, n, SCALE)
+    ref, rl = O.attention(qd[0], K, V, rows, SCALE)
+    np.testing.assert_array_equal(out[0], ref)
+    # the first of two drafts does not see the second
+    out2, _ = O.verify_attention(_rand(rng, 2, 4, D) * 0 + qd, K, V, rows, n, SCALE)
+    ref1, _ = O.attention(qd[0], K, V, [x for x in rows if x <= n - 2], SCALE)
+    np.testing.assert_allclose(out2[0], ref1, rtol=1e-14)
