@@ -264,6 +264,44 @@ kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_
   return hip_status(launch_focal_norm(n, kv->batch, (hipStream_t)stream), "focal score launch");
 }
 
+kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t m, int32_t num_q_heads,
+                               float scale, const int32_t *idx, int32_t k, float *out, float *lse,
+                               kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (m < 1) return fail(KVSEL_EINVAL, "m must be >= 1");
+  if (m * G > 32) return fail(KVSEL_EUNSUPPORTED, "m * group = %d query rows per kv head (1 .. 32)", m * G);
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr) return fail(KVSEL_EINVAL, "out is NULL");
+  if (k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
+  if (k > 0 && idx == nullptr) return fail(KVSEL_EINVAL, "idx is NULL with k > 0");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (gather_rows_bound(kv, k) > kVerifyMaxRows)
+    return fail(KVSEL_EUNSUPPORTED, "more than %d attended rows per (sequence, kv head)", kVerifyMaxRows);
+  VerifyArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = kv->block_table;
+  a.seq_len = kv->seq_len;
+  a.seg_begin = kv->seg_begin;
+  a.seg_end = kv->seg_end;
+  a.num_blocks = kv->num_blocks;
+  a.max_blocks = kv->max_blocks_per_seq;
+  a.hkv = kv->num_kv_heads;
+  a.hq = num_q_heads;
+  a.group = G;
+  a.m = m;
+  a.k = k;
+  a.q = q;
+  a.idx = idx;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(launch_verify(a, kv->batch, (hipStream_t)stream), "verify_attn launch");
+}
+
 size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads) {
   int G;
   if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;

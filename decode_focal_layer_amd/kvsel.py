@@ -33,6 +33,7 @@ SYMBOLS = (
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
     "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
     "kvsel_pool_alloc", "kvsel_pool_retain", "kvsel_pool_release", "kvsel_fork",
+    "kvsel_verify_attn",
 )
 
 
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
     for fn in (L.kvsel_pool_alloc, L.kvsel_pool_retain, L.kvsel_pool_release):
         fn.restype = _I32
         fn.argtypes = [_P, _P, _I32] if fn is not L.kvsel_pool_alloc else [_P, _I32, _P]
+    L.kvsel_verify_attn.restype = _I32
+    L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_fork.restype = _I32
     L.kvsel_fork.argtypes = [_P, _P, _I32, _I32, _P, _P, _P, _I64, _I32, _P]
     _lib = L
@@ -316,6 +319,20 @@ def dense_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, out: tor
     p, n = w.ptr_and_size(attn_workspace(kv, num_q_heads, -1, seg_scores is not None, norm))
     _check(lib().kvsel_dense_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(out), _ptr(lse), _ptr(seg_scores),
                                   ld, norm, p, n, _stream(stream)))
+    return out
+
+
+def verify_attn(kv: KV, q: torch.Tensor, m: int, num_q_heads: int, scale: float, idx: Optional[torch.Tensor], k: int,
+                out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_verify_attn.  q: bf16 [batch][m][hq][128]; out: fp32 [batch][m][hq][128]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().kvsel_verify_attn(kv.ref(), _ptr(q), m, num_q_heads, scale, _ptr(idx), k, _ptr(out), _ptr(lse),
+                                   _stream(stream)))
     return out
 
 

@@ -298,6 +298,27 @@ KVSEL_API kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_
                                          int32_t n_pick, int32_t *layers, kvsel_stream stream);
 
 /*
+ * kvsel_verify_attn -- attention of m drafted tokens, verified in parallel.
+ * (HPD-Parsing wiki, P-MTP: each branch drafts several tokens and verifies
+ *  them in one step.)
+ *
+ * The drafts' own K/V rows are the last m rows of each sequence (positions
+ * seq_len[b]-m .. seq_len[b]-1); a segment reaching into them is taken as
+ * ending at seq_len[b]-m, so the drafts are always attended.  Draft r's
+ * query, q[b][r][h], attends over the rows kvsel_gather_attn would attend
+ * (kept rows seg_begin + idx, every row outside the segment) whose position
+ * is <= seq_len[b]-m+r: everything before the drafts, and the drafts up to
+ * its own.  q: bf16 [batch][m][num_q_heads][128]; idx: as kvsel_gather_attn
+ * (NULL when k = 0); out: fp32 [batch][m][num_q_heads][128]; lse: NULL or
+ * fp32 [batch][m][num_q_heads].  Requires m * (num_q_heads / num_kv_heads)
+ * <= 32 and at most 8192 attended rows per (sequence, kv head)
+ * (KVSEL_EUNSUPPORTED otherwise).  No workspace.
+ */
+KVSEL_API kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t m,
+                                         int32_t num_q_heads, float scale, const int32_t *idx, int32_t k,
+                                         float *out, float *lse, kvsel_stream stream);
+
+/*
  * Branch lifecycle: a reference-counted block pool (host side) and the fork
  * of a branch.
  * (HPD-Parsing wiki, inference scheduling: a content branch spawned at a

@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 23
+    assert len(names) == 24
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -177,3 +177,18 @@ def test_pick_layers_rejects(L, args, code):
     a = dict(ratios=FAKE, ld=64, n_layers=28, n=64, n_pick=2, layers=FAKE)
     a.update(args)
     assert L.kvsel_pick_layers(a["ratios"], a["ld"], a["n_layers"], a["n"], a["n_pick"], a["layers"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=0), EINVAL), (dict(m=17), EUNSUP), (dict(m=33, hq=8), EUNSUP), (dict(q=0), EINVAL),
+    (dict(q=FAKE + 2), EINVAL), (dict(out=0), EINVAL), (dict(k=-1), EINVAL), (dict(idx=0), EINVAL),
+    (dict(scale=float("inf")), EINVAL), (dict(hq=12), EINVAL), (dict(k=8200), EUNSUP),
+    (dict(d=dict(v_pool=0)), EINVAL),
+])
+def test_verify_attn_rejects(L, kw, code):
+    d = desc(**kw.get("d", {}))
+    r = L.kvsel_verify_attn(ctypes.byref(d), kw.get("q", FAKE), kw.get("m", 4), kw.get("hq", 16),
+                            kw.get("scale", 0.088), kw.get("idx", FAKE), kw.get("k", 5), kw.get("out", FAKE), None,
+                            None)
+    assert r == code
+    assert L.kvsel_last_error()

@@ -438,3 +438,51 @@ def test_fork_copy_on_write(L):
         ref, _ = O.dense_attention(O.widen(q.cpu()[0, g * G:(g + 1) * G]), O.logical_rows(kc, child_t, g, n),
                                    O.logical_rows(vc, child_t, g, n), SCALE)
         assert_attn(out[0, g * G:(g + 1) * G].cpu().numpy(), ref, f"child g{g}")
+
+
+# (G, m, batch, lens, segments, k): the drafts are each sequence's last m rows;
+# ragged tiles, k = 0, a segment reaching into the drafts (cut at n - m), and
+# m * G at its limit of 32 query rows
+VERIFY_CASES = [(1, 1, 1, [1], [(0, 1)], 0), (2, 4, 2, [17, 300], [(3, 10), (0, 290)], 5),
+                (4, 8, 1, [4000], [(10, 3900)], 200), (8, 4, 2, [700, 129], [(64, 600), (0, 100)], 33),
+                (1, 32, 1, [96], [(0, 40)], 40), (2, 4, 1, [50], [(5, 50)], 30),
+                (2, 4, 1, [8300], [(100, 8200)], 7900), (4, 2, 3, [33, 34, 35], [(1, 30), (2, 2), (0, 33)], 0)]
+
+
+@pytest.mark.parametrize("G,m,batch,lens,segs,k", VERIFY_CASES)
+def test_verify_attention(G, m, batch, lens, segs, k):
+    kvsel = K()
+    rng = np.random.default_rng(1000 + G * 37 + m)
+    hkv = 2
+    hq = hkv * G
+    kv, kc, vc, table = make_kv(rng, batch, hkv, lens, segs)
+    # the segment each sequence is cut to: it ends no later than n - m
+    cut = [(min(s0, max(n - m, 0)), min(max(s1, min(s0, max(n - m, 0))), max(n - m, 0)))
+           for (s0, s1), n in zip(segs, lens)]
+    idx_np = np.full((batch, hkv, max(k, 1)), -1, dtype=np.int32)
+    for b in range(batch):
+        sl = segs[b][1] - segs[b][0]          # picks over the declared segment; those past the cut are dropped
+        for g in range(hkv):
+            pick = rng.choice(sl, size=min(k, sl), replace=False) if sl and k else np.array([], np.int64)
+            idx_np[b, g, : len(pick)] = pick
+    idx = torch.from_numpy(idx_np).to(DEV) if k else None
+    q = torch.randn((batch, m, hq, 128), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    out = torch.full((batch, m, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((batch, m, hq), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("verify", G, m, lens, k)
+    kvsel.verify_attn(kv, q, m, hq, SCALE, idx, k, out, lse)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    for b in range(batch):
+        s0, s1 = cut[b]
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            Vl = O.logical_rows(vc, table[b], g, lens[b])
+            sel = idx_np[b, g][(idx_np[b, g] >= 0) & (idx_np[b, g] < s1 - s0)] if k else np.array([], np.int64)
+            rows = O.kept_rows(sel, s0, s1, lens[b])
+            qd = O.widen(qc[b, :, g * G:(g + 1) * G])
+            ref, rl = O.verify_attention(qd, Kl, Vl, rows, lens[b], SCALE)
+            for r in range(m):
+                got = out[b, r, g * G:(g + 1) * G].cpu().numpy()
+                assert_attn(got, ref[r], f"verify b{b} g{g} draft{r}")
+                assert np.abs(lse[b, r, g * G:(g + 1) * G].cpu().numpy() - rl[r]).max() < 1e-4
