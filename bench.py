@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile"],
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile", "verify"],
                     help="c1 (default) is the metric's workload; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -487,7 +487,53 @@ def bench_c4(args):
            "hbm_gbs_logical": round(lb / ms / 1e6, 1)})
 
 
-OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "profile": bench_profile}
+def bench_verify(args):
+    """Draft verification at the C4 shape: every branch's m = 8 drafted
+    tokens attend, in each of the 28 layers, over the kept visual rows (a
+    fixed set of 154 per kv head), the 1024 layout rows, its suffix and,
+    causally, the drafts (the last 8 rows of each branch)."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import gen
+    from decode_focal_layer_amd import kvsel
+    cfg = synth.C4
+    m = 8
+    w = gen.make_focal(cfg, "cuda")
+    seq = w.seq_len[cfg.steps - 1]
+    n_np = w.seq_len_np[cfg.steps - 1].astype(np.int64)
+    max_len = int(n_np.max())
+    kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, seq, w.seg_begin, w.seg_end,
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                    shared_rows=cfg.prefix_len)
+           for l in range(cfg.layers)]
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 77)
+    keys = torch.rand((cfg.batch * cfg.hkv, cfg.n_visual), generator=g, device="cuda")
+    idx = keys.argsort(dim=1)[:, :cfg.k].sort(dim=1).values.to(torch.int32).view(cfg.batch, cfg.hkv, cfg.k)
+    qs = [torch.randn((cfg.batch, m, cfg.hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+          for _ in range(4)]
+    out = torch.empty((cfg.batch, m, cfg.hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        q = qs[i % len(qs)]
+        for l in range(cfg.layers):
+            kvsel.verify_attn(kvs[l], q, m, cfg.hq, cfg.scale, idx, cfg.k, out, lse)
+
+    ms = _timed(step, args.steps, args.warmup)
+    rows = int((cfg.k + n_np - cfg.n_visual).sum())             # kept + layout + suffix (drafts included)
+    per_layer = cfg.hkv * rows * 512 + cfg.batch * m * cfg.hq * (256 + 512 + 4) + cfg.batch * cfg.hkv * cfg.k * 4
+    nbytes = cfg.layers * per_layer
+    flops = cfg.layers * 4 * cfg.hkv * rows * (m * cfg.group) * 128
+    _line("verification steps/s (8 drafts per branch, 28 layers over 512 branches)", 1000 / ms, "steps/s", args, ms,
+          "c4_hpd_verify: 512 branches, shared 3072 visual + 1024 layout prefix, suffix U[32,1024] + 32, "
+          "16q/8kv, 8 drafts, 154 kept visual rows per kv head",
+          {"draft_tokens_per_s": round(1000 / ms * cfg.batch * m, 1), "bytes_per_step_logical": int(nbytes),
+           "hbm_gbs_logical": round(nbytes / ms / 1e6, 1), "tflops": round(flops / ms / 1e9, 2)})
+
+
+OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "profile": bench_profile,
+         "verify": bench_verify}
 
 
 if __name__ == "__main__":

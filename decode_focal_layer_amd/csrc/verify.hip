@@ -60,16 +60,24 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
 // transposed V row of dim d (dims d and d + 64 in adjacent rows: different banks)
 __device__ __forceinline__ int vt_row(int d) { return (d & 63) * 2 + (d >> 6); }
 
-__global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
+// LDS: the rows and the V^T tiles while the tiles run, then the same bytes
+// hold the waves' partial outputs for the merge (two work-groups per CU)
+constexpr size_t kRowBytes = sizeof(uint32_t) * kVerifyMaxRows;
+constexpr size_t kVtBytes = sizeof(uint16_t) * kVWaves * 128 * kVtStride;
+constexpr size_t kOBytes = sizeof(float) * kVWaves * 32 * 129;
+constexpr size_t kVLds = kRowBytes + kVtBytes > kOBytes ? kRowBytes + kVtBytes : kOBytes;
+
+__global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(VerifyArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int G = a.group, R = a.m * G;
 
-  __shared__ uint32_t s_prow[kVerifyMaxRows];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kVWaves][128 * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kVLds];
   __shared__ float s_m[kVWaves][32], s_l[kVWaves][32];
-  __shared__ float s_o[kVWaves][32][129];
+  uint32_t *s_prow = reinterpret_cast<uint32_t *>(s_raw);
+  uint16_t(*s_vt)[128 * kVtStride] = reinterpret_cast<uint16_t(*)[128 * kVtStride]>(s_raw + kRowBytes);
+  float(*s_o)[32][129] = reinterpret_cast<float(*)[32][129]>(s_raw);
 
   // ---- rows: kept (segment-relative idx), before the segment, after it ----
   const int cap = a.max_blocks * kBlk;
@@ -117,21 +125,30 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
   uint16_t *vt = s_vt[wave];
-  const int first_draft = cnt - a.m;    // virtual index of draft 0
+  const int last_vis = cnt - a.m + qr;  // virtual index of this column's draft: the last it sees
 
-  for (int t0 = wave * 32; t0 < cnt; t0 += kVWaves * 32) {
-    // K and V of key t0 + col, this lane's half of the dims (invalid: the query row, masked)
+  // K and V of key t0 + col, this lane's half of the dims (invalid: the query row, masked).
+  // Software pipelined: the next tile's loads are issued once this tile's
+  // K has gone into S and its V into LDS, and land during softmax and P V.
+  bf16x8 kop[8];
+  uint4 vv[8];
+  uint32_t tile_mask = 0;   // bit i: key t0 + i of the loaded tile is attended
+  auto load_tile = [&](int t0) {
     const int key = t0 + col;
     const uint32_t pr = key < cnt ? s_prow[key] : kNoRow;
+    tile_mask = (uint32_t)__ballot(pr != kNoRow);   // lanes 0..31 (hf = 0) cover the 32 keys
     const uint16_t *krow = pr != kNoRow ? a.k_pool + (size_t)pr * kD : a.q;
     const uint16_t *vrow = pr != kNoRow ? a.v_pool + (size_t)pr * kD : a.q;
-    bf16x8 kop[8];
-    uint4 vv[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       kop[kk] = __builtin_bit_cast(bf16x8, reinterpret_cast<const uint4 *>(krow + hf * 64)[kk]);
       vv[kk] = reinterpret_cast<const uint4 *>(vrow + hf * 64)[kk];
     }
+  };
+  if (wave * 32 < cnt) load_tile(wave * 32);
+
+  for (int t0 = wave * 32; t0 < cnt; t0 += kVWaves * 32) {
+    const uint32_t vmask = tile_mask;
     // V transposed into this wave's LDS: vt[vt_row(d)][key]
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -147,14 +164,15 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
     f32x16 s = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], s, 0, 0, 0);
+    if (t0 + kVWaves * 32 < cnt) load_tile(t0 + kVWaves * 32);
     float x[16];
     float tm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int kj = t0 + 8 * (j >> 2) + 4 * hf + (j & 3);
-      const uint32_t pj = kj < cnt ? s_prow[kj] : kNoRow;
-      bool vis = pj != kNoRow && col < R;
-      if (kj >= first_draft) vis = vis && (kj - first_draft) <= qr;   // drafts: causal
+      // attended, a real column, and not a draft after this column's own
+      // (a row before the drafts always passes the last test)
+      const int kr = 8 * (j >> 2) + 4 * hf + (j & 3);
+      const bool vis = (((vmask >> kr) & 1u) != 0) & (col < R) & (t0 + kr <= last_vis);
       x[j] = vis ? s[j] * a.scale_log2 : -INFINITY;
       tm = fmaxf(tm, x[j]);
     }
@@ -209,6 +227,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 
   // ---- merge: the column's two half-sums, then the waves ----
   const float lcol = lsum + __shfl_xor(lsum, 32);
+  __syncthreads();   // every wave is done with the rows and V^T before s_o overwrites them
   if (hf == 0) {
     s_m[wave][col] = mrun;
     s_l[wave][col] = lcol;
