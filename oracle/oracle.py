@@ -28,6 +28,8 @@ printed there, the readings below are the plainest ones the text supports):
   tokens plus the window tokens are propagated.
 * FastKV section 2B (Decoupled KV Retention): a KV budget per layer chosen
   independently of the propagation rate.
+* FastKV section 2A, two-stage prefill: the layers after the TSP layer
+  process only the propagated tokens (causal prefill over that sequence).
 * HPD-Parsing wiki, method item 2 (shared-prefix KV reuse): branches read
   the shared visual context zero-copy and attend to it, their own layout
   prefix and their own history.
@@ -270,6 +272,28 @@ def verify_attention(qd, K, V, rows, n: int, scale):
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def causal_prefill(Q, K, V, scale, rows=None):
+    """Causal self-attention over the propagated tokens (FastKV, section 2A,
+    Token-Selective Propagation: the layers after the TSP layer process only
+    the top-ranked tokens and the window tokens).  The propagated tokens keep
+    their order of position, so token i sees tokens 0..i.
+
+    Q [n, hq, d]; K, V [n, hkv, d]; query head h reads kv head h // (hq/hkv).
+    rows: (position, head) pairs to compute (default: every one, position
+    major).  Returns (out [len(rows), d], lse [len(rows)])."""
+    Q, K, V = np.asarray(Q, F64), np.asarray(K, F64), np.asarray(V, F64)
+    n, hq = Q.shape[0], Q.shape[1]
+    G = hq // K.shape[1]
+    if rows is None:
+        rows = [(i, h) for i in range(n) for h in range(hq)]
+    outs, lses = [], []
+    for i, h in rows:
+        o, l = attention(Q[i, h][None], K[:, h // G], V[:, h // G], np.arange(i + 1), scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.array(lses)
 
 
 def dense_attention(qg, K, V, scale):

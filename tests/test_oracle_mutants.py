@@ -159,3 +159,35 @@ def test_verify_pin_catches(monkeypatch, bad):
     monkeypatch.setattr(O, "verify_attention", bad)
     with pytest.raises(AssertionError):
         P.test_verify_attention_matches_causal_sdpa()
+
+
+def _prefill_sees_one_less(Q, K, V, scale, rows=None):
+    Q, K, V = np.asarray(Q, F64), np.asarray(K, F64), np.asarray(V, F64)
+    G = Q.shape[1] // K.shape[1]
+    rows = rows or [(i, h) for i in range(Q.shape[0]) for h in range(Q.shape[1])]
+    res = [O.attention(Q[i, h][None], K[:, h // G], V[:, h // G], np.arange(max(i, 1)), scale) for i, h in rows]
+    return np.stack([o[0] for o, _ in res]), np.array([l[0] for _, l in res])
+
+
+def _prefill_head_modulo(Q, K, V, scale, rows=None):
+    Q, K, V = np.asarray(Q, F64), np.asarray(K, F64), np.asarray(V, F64)
+    hkv = K.shape[1]
+    rows = rows or [(i, h) for i in range(Q.shape[0]) for h in range(Q.shape[1])]
+    res = [O.attention(Q[i, h][None], K[:, h % hkv], V[:, h % hkv], np.arange(i + 1), scale) for i, h in rows]
+    return np.stack([o[0] for o, _ in res]), np.array([l[0] for _, l in res])
+
+
+def _prefill_not_causal(Q, K, V, scale, rows=None):
+    Q, K, V = np.asarray(Q, F64), np.asarray(K, F64), np.asarray(V, F64)
+    n, G = Q.shape[0], Q.shape[1] // K.shape[1]
+    rows = rows or [(i, h) for i in range(n) for h in range(Q.shape[1])]
+    res = [O.attention(Q[i, h][None], K[:, h // G], V[:, h // G], np.arange(n), scale) for i, h in rows]
+    return np.stack([o[0] for o, _ in res]), np.array([l[0] for _, l in res])
+
+
+@pytest.mark.parametrize("bad", [_prefill_sees_one_less, _prefill_head_modulo, _prefill_not_causal])
+@pytest.mark.parametrize("pin", ["test_causal_prefill_matches_causal_sdpa", "test_causal_prefill_ends"])
+def test_prefill_pins_catch(monkeypatch, bad, pin):
+    monkeypatch.setattr(O, "causal_prefill", bad)
+    with pytest.raises(AssertionError):
+        getattr(P, pin)()

@@ -464,3 +464,46 @@ def test_verify_attention_single_draft_is_attention():
     out2, _ = O.verify_attention(_rand(rng, 2, 4, D) * 0 + qd, K, V, rows, n, SCALE)
     ref1, _ = O.attention(qd[0], K, V, [x for x in rows if x <= n - 2], SCALE)
     np.testing.assert_allclose(out2[0], ref1, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# TSP stage 2 (FastKV 2A: later layers run over the propagated tokens only)
+# --------------------------------------------------------------------------
+
+def test_causal_prefill_matches_causal_sdpa():
+    """Every (position, head): torch's causal scaled_dot_product_attention in
+    fp64 with each kv head repeated over its G query heads."""
+    rng = np.random.default_rng(31)
+    n, hkv, G = 37, 3, 2
+    Q = _rand(rng, n, hkv * G, D)
+    K, V = _rand(rng, n, hkv, D), _rand(rng, n, hkv, D)
+    out, lse = O.causal_prefill(Q, K, V, SCALE)
+    tq = torch.from_numpy(Q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=SCALE)[0]
+    ref = ref.permute(1, 0, 2).reshape(n * hkv * G, D).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # lse: the log of the causal normaliser, written out for a few rows
+    S = np.einsum("ihd,jhd->hij", Q, np.repeat(K, G, axis=1)) * SCALE
+    for i, h in [(0, 0), (5, 3), (n - 1, hkv * G - 1)]:
+        assert abs(lse[i * hkv * G + h] - np.log(np.exp(S[h, i, : i + 1]).sum())) < 1e-12
+
+
+def test_causal_prefill_ends():
+    """The first token sees only itself (out = its V row); the last sees the
+    whole sequence (dense attention); a sampled row equals the full run."""
+    rng = np.random.default_rng(32)
+    n, hkv, G = 20, 2, 4
+    Q = _rand(rng, n, hkv * G, D)
+    K, V = _rand(rng, n, hkv, D), _rand(rng, n, hkv, D)
+    out, lse = O.causal_prefill(Q, K, V, SCALE, rows=[(0, h) for h in range(hkv * G)])
+    for h in range(hkv * G):
+        np.testing.assert_array_equal(out[h], V[0, h // G])
+        assert abs(lse[h] - SCALE * float(Q[0, h] @ K[0, h // G])) < 1e-12
+    last, _ = O.causal_prefill(Q, K, V, SCALE, rows=[(n - 1, 5)])
+    np.testing.assert_allclose(last[0], O.dense_attention(Q[n - 1, 5][None], K[:, 1], V[:, 1], SCALE)[0][0],
+                               rtol=1e-14)
+    full, _ = O.causal_prefill(Q, K, V, SCALE)
+    one, _ = O.causal_prefill(Q, K, V, SCALE, rows=[(13, 6)])
+    np.testing.assert_array_equal(one[0], full[13 * hkv * G + 6])
