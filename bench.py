@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile", "verify"],
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile", "verify", "prefill"],
                     help="c1 (default) is the metric's workload; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -532,8 +532,36 @@ def bench_verify(args):
            "hbm_gbs_logical": round(nbytes / ms / 1e6, 1), "tflops": round(flops / ms / 1e9, 2)})
 
 
+def bench_prefill(args):
+    """TSP stage 2 at the C2 shape: one later layer's causal prefill over the
+    6562 propagated tokens (6554 top-ranked + 8 window), 32q/8kv; 4 input
+    sets rotate."""
+    import torch
+    import synth
+    from decode_focal_layer_amd import kvsel
+    cfg = synth.C2
+    n, hq, hkv = cfg.k + cfg.window, cfg.hq, cfg.hkv
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 5)
+    sets = [tuple(torch.randn((n, h, 128), generator=g, device="cuda").to(torch.bfloat16) for h in (hq, hkv, hkv))
+            for _ in range(4)]
+    cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    out = torch.empty((n, hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n, hq), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        q, k, v = sets[i % len(sets)]
+        kvsel.prefill_attn(q, k, v, cu, n, cfg.scale, out, lse)
+
+    ms = _timed(step, args.steps, args.warmup)
+    flops = 4 * 128 * hq * n * (n + 1) // 2          # S and P V over the causal triangle
+    tfs = flops / ms / 1e9
+    _line("TSP stage-2 prefill layers/s (causal attention over the propagated tokens)", 1000 / ms, "layers/s", args,
+          ms, "c2_tsp_stage2: 6562 propagated tokens (6554 top-ranked + 8 window), 32q/8kv, head_dim 128",
+          {"tflops": round(tfs, 1), "mfma_frac_of_bf16_peak": round(tfs / 2500.0, 4), "flop_per_layer": flops})
+
+
 OTHER = {"c0": bench_c0, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "profile": bench_profile,
-         "verify": bench_verify}
+         "verify": bench_verify, "prefill": bench_prefill}
 
 
 if __name__ == "__main__":

@@ -302,6 +302,39 @@ kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   return hip_status(launch_verify(a, kv->batch, (hipStream_t)stream), "verify_attn launch");
 }
 
+kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
+                                int32_t batch, int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                                float scale, float *out, float *lse, kvsel_stream stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens == nullptr || out == nullptr)
+    return fail(KVSEL_EINVAL, "q, k, v, cu_seqlens and out are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(KVSEL_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (batch < 1 || batch > 65535) return fail(KVSEL_EINVAL, "batch must be in [1, 65535]");
+  if (num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(KVSEL_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads (1 .. 65535)");
+  if (max_seqlen < 0) return fail(KVSEL_EINVAL, "max_seqlen must be >= 0");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  const int G = num_q_heads / num_kv_heads;
+  if ((int64_t)max_seqlen * G > 0x7fffff00ll) return fail(KVSEL_EUNSUPPORTED, "max_seqlen * group >= 2^31");
+  if (max_seqlen == 0) {
+    clear_error();
+    return KVSEL_OK;
+  }
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.max_seqlen = max_seqlen;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = G;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(launch_prefill(a, batch, (hipStream_t)stream), "prefill_attn launch");
+}
+
 size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads) {
   int G;
   if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;

@@ -90,6 +90,17 @@ struct VerifyArgs {
 };
 hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s);
 
+// causal prefill over a compacted sequence (MFMA): one work-group per
+// (128 query rows, kv head, sequence)
+struct PrefillArgs {
+  const uint16_t *q, *k, *v;     // [total][hq][128], [total][hkv][128] x2
+  const int32_t *cu_seqlens;     // [batch + 1]
+  float *out, *lse;              // [total][hq][128], [total][hq]
+  int32_t max_seqlen, hq, hkv, group;
+  float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
+
 // focal-layer choice: one work-group
 constexpr int kMaxLayers = 1024;
 hipError_t launch_pick_layers(const float *ratios, int64_t ld, int n_layers, int n, int n_pick, int32_t *layers,

@@ -1,0 +1,234 @@
+// Causal prefill attention over the propagated tokens, on MFMA.
+//
+// FastKV (section 2A, Token-Selective Propagation, two-stage prefill): after
+// the TSP layer only the top-ranked tokens and the window tokens go on to
+// the later layers, which run ordinary causal prefill attention over that
+// shorter sequence.  The propagated tokens keep their order of position, so
+// token i of the compacted sequence sees tokens 0..i.
+//
+// One work-group per (128 query rows, kv head, sequence), four waves of 32
+// query rows.  A query row is a (position, head) pair of the kv head's
+// group, numbered position-major, so a work-group covers 128/G positions
+// for any group size G.  Keys go through LDS in tiles of 64:
+//  * K row-major, bf16, the 16-byte chunks of a row XOR-swizzled by the key
+//    (conflict-free writes of whole rows and reads of one chunk per key);
+//  * V transposed, converted to fp16 (exact for bf16 values inside the fp16
+//    range), its key order permuted so that P leaves the S product already
+//    in the operand order of the P V product (no lane exchange).
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as A rows, query rows as
+// B columns: each lane owns one query row and 16 keys of a 32-key block);
+// online softmax per row in fp32; O^T += V^T P with
+// v_mfma_f32_32x32x16_f16, P rounded to fp16 (11 significant bits).  The
+// next tile's K/V are fetched into registers while the current one runs.
+// Work-groups are launched latest rows first (the causal triangle's
+// heaviest blocks start first).
+#include "common.h"
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kPThreads = 256;
+constexpr int kPWaves = kPThreads / 64;
+constexpr int kPRows = 32 * kPWaves;   // query rows per work-group
+constexpr int kBN = 64;                // keys per tile
+
+// byte offset of K chunk c (dims 8c .. 8c+7) of tile key r
+__device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+// byte offset of V^T element (dim d, tile position p); the 16-byte blocks of
+// a row are XOR-swizzled by the dim
+__device__ __forceinline__ int vt_off(int d, int p) {
+  const int sw = ((d >> 1) ^ (d >> 3)) & 7;
+  return d * 128 + ((((p >> 3) ^ sw) & 7) << 4) + (p & 7) * 2;
+}
+
+// tile position of keys 4q .. 4q+3 (q = 0..15).  Key 32*blk + 8*a + 4*hf + r
+// comes out of S in lane half hf, register 4a + r of block blk; the P V
+// product's k-step s takes register 8*(s&1) + i of block s>>1 from lane half
+// hf as k-index hf*8 + i, so that key goes to position
+// 32*blk + 16*(a>>1) + 8*hf + 4*(a&1) + r.
+__device__ __forceinline__ int quad_pos(int q) {
+  const int blk = q >> 3, a = (q & 7) >> 1, hf = q & 1;
+  return blk * 32 + (a >> 1) * 16 + hf * 8 + (a & 1) * 4;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// two bf16 values -> two fp16 (exact inside the fp16 range; toward zero
+// outside it, so no infinity appears)
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t lo_bits, uint32_t hi_bits) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_bits << 16), __uint_as_float(hi_bits << 16));
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// staging of one tile: K chunk i = tid + 256u is (key i/16, chunk i%16); V
+// holds keys 4*(tid/16) .. +3 of chunk tid%16.  Keys past the sequence read
+// its last row (masked later).
+struct Stage {
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ Stage fetch(const PrefillArgs &a, int64_t base, int g, int n, int t0, int tid) {
+  auto krow = [&](int u) {
+    const int i = tid + kPThreads * u;
+    const int key = min(t0 + (i >> 4), n - 1);
+    return *reinterpret_cast<const uint4 *>(a.k + ((base + key) * a.hkv + g) * kD + (i & 15) * 8);
+  };
+  auto vrow = [&](int u) {
+    const int key = min(t0 + (tid >> 4) * 4 + u, n - 1);
+    return *reinterpret_cast<const uint4 *>(a.v + ((base + key) * a.hkv + g) * kD + (tid & 15) * 8);
+  };
+  return Stage{krow(0), krow(1), krow(2), krow(3), vrow(0), vrow(1), vrow(2), vrow(3)};
+}
+
+__device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_vt, int tid) {
+  const uint4 ks[4] = {st.k0, st.k1, st.k2, st.k3};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + kPThreads * u;
+    *reinterpret_cast<uint4 *>(s_k + k_off(i >> 4, i & 15)) = ks[u];
+  }
+  const int p = quad_pos(tid >> 4), vc = tid & 15;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w0 = word_of(st.v0, e >> 1), w1 = word_of(st.v1, e >> 1);
+    const uint32_t w2 = word_of(st.v2, e >> 1), w3 = word_of(st.v3, e >> 1);
+    const int sh = (e & 1) * 16;
+    *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + e, p)) =
+        make_uint2(bf16_pair_to_f16((w0 >> sh) & 0xffffu, (w1 >> sh) & 0xffffu),
+                   bf16_pair_to_f16((w2 >> sh) & 0xffffu, (w3 >> sh) & 0xffffu));
+  }
+}
+
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
+
+  const int blk = gridDim.x - 1 - blockIdx.x;   // latest rows first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int G = a.group;
+  const int64_t base = a.cu_seqlens[b];
+  const int n = (int)min((int64_t)a.max_seqlen, max((int64_t)0, (int64_t)a.cu_seqlens[b + 1] - base));
+  const int nrows = n * G;
+  const int row0 = blk * kPRows;
+  if (row0 >= nrows) return;   // the whole work-group
+  const int kend = (min(row0 + kPRows, nrows) - 1) / G + 1;   // keys any row here sees
+
+  // this lane's query row (B operand: dims hf*64 + kk*8 .. +8)
+  const int rr = row0 + wave * 32 + col;
+  const bool live = rr < nrows;
+  const int pos = live ? rr / G : -1;   // -1 sees no key
+  const int h = rr % G;
+  const int wave_last = min(row0 + wave * 32 + 31, nrows - 1);
+  const int wave_kend = wave_last >= row0 + wave * 32 ? wave_last / G + 1 : 0;   // keys this wave's rows see
+  bf16x8 qop[8];
+  if (live) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.q + ((base + pos) * a.hq + g * G + h) * kD + hf * 64);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, p[kk]);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+
+
+  float mrun = -INFINITY, lsum = 0.f;   // this row's running max; this lane's share of the sum
+  f32x16 acc[4];                        // O^T: dims dt*32 + 8*(j/4) + 4*hf + j%4 of this row
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
+
+  Stage st = fetch(a, base, g, n, 0, tid);
+  for (int t0 = 0; t0 < kend; t0 += kBN) {
+    __syncthreads();   // the previous tile's reads are done
+    stash(st, s_k, s_vt, tid);
+    __syncthreads();
+    if (t0 + kBN < kend) st = fetch(a, base, g, n, t0 + kBN, tid);
+    if (t0 >= wave_kend) continue;   // every row of this wave is before the tile
+
+    // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
+    f32x16 s[2];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      s[bk] = {};
+      const int r = bk * 32 + col;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(s_k + k_off(r, hf * 8 + kk));
+        s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[bk], 0, 0, 0);
+      }
+    }
+    float tm = -INFINITY;
+    float x[2][16];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3);
+        x[bk][j] = key <= pos ? s[bk][j] * a.scale_log2 : -INFINITY;
+        tm = fmaxf(tm, x[bk][j]);
+      }
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mnew = fmaxf(mrun, tm);
+    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
+    mrun = mnew;
+    float ps = 0.f;
+    f16x8 pop[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xv = x[ks >> 1][(ks & 1) * 8 + i];
+        const float p = xv == -INFINITY ? 0.f : fast_exp2(xv - mnew);
+        ps += p;
+        pop[ks][i] = (_Float16)p;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[dt][j] *= alpha;
+      const int d = dt * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 vop = *reinterpret_cast<const f16x8 *>(s_vt + vt_off(d, ks * 16 + hf * 8));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[ks], acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  const float lrow = lsum + __shfl_xor(lsum, 32);
+  if (!live) return;
+  const int64_t orow = (base + pos) * a.hq + g * G + h;
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  float *o = a.out + orow * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq)
+      *reinterpret_cast<float4 *>(o + dt * 32 + 8 * jq + 4 * hf) =
+          make_float4(acc[dt][4 * jq] * inv, acc[dt][4 * jq + 1] * inv, acc[dt][4 * jq + 2] * inv,
+                      acc[dt][4 * jq + 3] * inv);
+  if (hf == 0 && a.lse != nullptr)
+    a.lse[orow] = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s) {
+  if (a.group < 1 || a.max_seqlen < 1 || batch < 1) return hipErrorInvalidValue;
+  const int64_t blocks = ((int64_t)a.max_seqlen * a.group + kPRows - 1) / kPRows;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks, a.hkv, batch), dim3(kPThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -33,7 +33,7 @@ SYMBOLS = (
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
     "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
     "kvsel_pool_alloc", "kvsel_pool_retain", "kvsel_pool_release", "kvsel_fork",
-    "kvsel_verify_attn",
+    "kvsel_verify_attn", "kvsel_prefill_attn",
 )
 
 
@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = [_P, _P, _I32] if fn is not L.kvsel_pool_alloc else [_P, _I32, _P]
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
+    L.kvsel_prefill_attn.restype = _I32
+    L.kvsel_prefill_attn.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P]
     L.kvsel_fork.restype = _I32
     L.kvsel_fork.argtypes = [_P, _P, _I32, _I32, _P, _P, _P, _I64, _I32, _P]
     _lib = L
@@ -333,6 +335,23 @@ def verify_attn(kv: KV, q: torch.Tensor, m: int, num_q_heads: int, scale: float,
         _need(lse, torch.float32, "lse")
     _check(lib().kvsel_verify_attn(kv.ref(), _ptr(q), m, num_q_heads, scale, _ptr(idx), k, _ptr(out), _ptr(lse),
                                    _stream(stream)))
+    return out
+
+
+def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                 scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_prefill_attn.  q: bf16 [total][hq][128]; k, v: bf16 [total][hkv][128];
+    cu_seqlens: int32 [batch + 1]; out: fp32 [total][hq][128]."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, name)
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(out, torch.float32, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[0] != k.shape[0]:
+        raise ValueError("q [total, hq, 128], k and v [total, hkv, 128]")
+    _check(lib().kvsel_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, max_seqlen,
+                                    q.shape[1], k.shape[1], scale, _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

@@ -319,6 +319,27 @@ KVSEL_API kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t
                                          float *out, float *lse, kvsel_stream stream);
 
 /*
+ * kvsel_prefill_attn -- causal prefill attention over the propagated tokens.
+ * (FastKV, section 2A, Token-Selective Propagation: the layers after the
+ *  TSP layer process only the top-ranked tokens and the window tokens.)
+ *
+ * Sequences are packed: sequence b holds rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1 (device array of batch + 1 non-decreasing int32; every
+ * length <= max_seqlen, rows past max_seqlen are not computed).  The rows
+ * keep their order of position, so row i of a sequence sees rows 0..i of
+ * it.  q: bf16 [total][num_q_heads][128]; k, v: bf16
+ * [total][num_kv_heads][128]; query head h reads kv head
+ * h / (num_q_heads / num_kv_heads); out: fp32 [total][num_q_heads][128];
+ * lse: NULL or fp32 [total][num_q_heads] (natural log).  q, k, v and out
+ * 16-byte aligned.  P V runs in fp16: V values of magnitude above 65504
+ * are clamped to it.  No workspace.
+ */
+KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                          const int32_t *cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                          int32_t num_q_heads, int32_t num_kv_heads, float scale, float *out,
+                                          float *lse, kvsel_stream stream);
+
+/*
  * Branch lifecycle: a reference-counted block pool (host side) and the fork
  * of a branch.
  * (HPD-Parsing wiki, inference scheduling: a content branch spawned at a

@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 24
+    assert len(names) == 25
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -192,3 +192,21 @@ def test_verify_attn_rejects(L, kw, code):
                             None)
     assert r == code
     assert L.kvsel_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), EINVAL), (dict(k=0), EINVAL), (dict(v=0), EINVAL), (dict(cu=0), EINVAL), (dict(out=0), EINVAL),
+    (dict(q=FAKE + 2), EINVAL), (dict(out=FAKE + 4), EINVAL), (dict(batch=0), EINVAL), (dict(hq=12), EINVAL),
+    (dict(hkv=0), EINVAL), (dict(max_len=-1), EINVAL), (dict(scale=float("nan")), EINVAL),
+    (dict(max_len=1 << 28, hq=64, hkv=8), EUNSUP),
+])
+def test_prefill_attn_rejects(L, kw, code):
+    r = L.kvsel_prefill_attn(kw.get("q", FAKE), kw.get("k", FAKE), kw.get("v", FAKE), kw.get("cu", FAKE),
+                             kw.get("batch", 1), kw.get("max_len", 100), kw.get("hq", 16), kw.get("hkv", 8),
+                             kw.get("scale", 0.088), kw.get("out", FAKE), None, None)
+    assert r == code
+    assert L.kvsel_last_error()
+
+
+def test_prefill_attn_empty_is_a_no_op(L):
+    assert L.kvsel_prefill_attn(FAKE, FAKE, FAKE, FAKE, 1, 0, 16, 8, 0.088, FAKE, None, None) == 0

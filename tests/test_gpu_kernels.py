@@ -486,3 +486,62 @@ def test_verify_attention(G, m, batch, lens, segs, k):
                 got = out[b, r, g * G:(g + 1) * G].cpu().numpy()
                 assert_attn(got, ref[r], f"verify b{b} g{g} draft{r}")
                 assert np.abs(lse[b, r, g * G:(g + 1) * G].cpu().numpy() - rl[r]).max() < 1e-4
+
+
+# (G, hkv, lengths): packed ragged sequences, one row, an empty sequence,
+# several 128-row blocks with a ragged tail, every group size
+PREFILL_CASES = [(1, 2, [1]), (2, 2, [31, 100]), (4, 2, [257]), (8, 1, [130, 0, 3, 64]), (4, 8, [700]),
+                 (1, 1, [129, 64])]
+
+
+def _prefill_inputs(seed, lens, hq, hkv):
+    g = torch.Generator().manual_seed(seed)
+    total = sum(lens)
+    q = torch.randn((total, hq, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((total, hkv, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((total, hkv, 128), generator=g).to(torch.bfloat16)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    return q, k, v, cu
+
+
+@pytest.mark.parametrize("G,hkv,lens", PREFILL_CASES)
+def test_prefill_attention(G, hkv, lens):
+    kvsel = K()
+    hq = hkv * G
+    q, k, v, cu = _prefill_inputs(40 + G * 7 + len(lens), lens, hq, hkv)
+    total = sum(lens)
+    out = torch.full((total, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((total, hq), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("prefill", G, hkv, lens)
+    kvsel.prefill_attn(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lens), SCALE, out, lse)
+    torch.cuda.synchronize()
+    got, gl = out.cpu().numpy(), lse.cpu().numpy()
+    for b, n in enumerate(lens):
+        s0 = int(cu[b])
+        if n == 0:
+            continue
+        ref, rl = O.causal_prefill(O.widen(q[s0:s0 + n]), O.widen(k[s0:s0 + n]), O.widen(v[s0:s0 + n]), SCALE)
+        assert_attn(got[s0:s0 + n].reshape(n * hq, 128), ref, f"prefill b{b}")
+        assert np.abs(gl[s0:s0 + n].reshape(-1) - rl).max() < 1e-4
+
+
+def test_prefill_attention_propagated_tokens():
+    """The later layers' attention after a TSP layer at 32768 tokens: 6554
+    top-ranked tokens plus 8 window tokens, 32q/8kv; sampled rows (the first
+    and last positions of every head, random ones) against the oracle."""
+    kvsel = K()
+    n, hq, hkv = 6562, 32, 8
+    q, k, v, cu = _prefill_inputs(77, [n], hq, hkv)
+    out = torch.empty((n, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((n, hq), dtype=torch.float32, device=DEV)
+    log_case("prefill-full", n, hq, hkv)
+    kvsel.prefill_attn(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), n, SCALE, out, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    rows = [(0, h) for h in range(0, hq, 5)] + [(n - 1, h) for h in range(hq)] + \
+        [(int(i), int(h)) for i, h in zip(rng.integers(0, n, 24), rng.integers(0, hq, 24))] + [(127, 3), (128, 4)]
+    ref, rl = O.causal_prefill(O.widen(q), O.widen(k), O.widen(v), SCALE, rows=rows)
+    got = out.cpu().numpy()
+    gl = lse.cpu().numpy()
+    assert_attn(np.stack([got[i, h] for i, h in rows]), ref, "prefill full")
+    assert np.abs(np.array([gl[i, h] for i, h in rows]) - rl).max() < 1e-4
