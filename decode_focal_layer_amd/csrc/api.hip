@@ -313,9 +313,12 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
   if (num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
     return fail(KVSEL_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads (1 .. 65535)");
   if (max_seqlen < 0) return fail(KVSEL_EINVAL, "max_seqlen must be >= 0");
-  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(KVSEL_EINVAL, "scale must be finite and positive");
   const int G = num_q_heads / num_kv_heads;
+  if ((int64_t)num_kv_heads * kD * 2 * 64 >= 0xffffffffll) return fail(KVSEL_EUNSUPPORTED, "num_kv_heads too large");
   if ((int64_t)max_seqlen * G > 0x7fffff00ll) return fail(KVSEL_EUNSUPPORTED, "max_seqlen * group >= 2^31");
+  if (((int64_t)max_seqlen * G + 127) / 128 * num_kv_heads * batch >= 0x7ffffff0ll)
+    return fail(KVSEL_EUNSUPPORTED, "too many 128-row blocks");
   if (max_seqlen == 0) {
     clear_error();
     return KVSEL_OK;

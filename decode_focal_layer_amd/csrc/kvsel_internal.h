@@ -98,6 +98,7 @@ struct PrefillArgs {
   float *out, *lse;              // [total][hq][128], [total][hq]
   int32_t max_seqlen, hq, hkv, group;
   float scale_log2;
+  int32_t nblk, items;           // set by launch_prefill
 };
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
 

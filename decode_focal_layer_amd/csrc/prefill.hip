@@ -17,11 +17,15 @@
 //    in the operand order of the P V product (no lane exchange).
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as A rows, query rows as
 // B columns: each lane owns one query row and 16 keys of a 32-key block);
-// online softmax per row in fp32; O^T += V^T P with
-// v_mfma_f32_32x32x16_f16, P rounded to fp16 (11 significant bits).  The
+// online softmax per row in fp32 whose running max is moved only when a
+// row's max grows by more than 8 (log2 units), so the O rescale is rare;
+// O^T += V^T P with v_mfma_f32_32x32x16_f16, P rounded to nearest fp16
+// (11 significant bits, P <= 256).  The
 // next tile's K/V are fetched into registers while the current one runs.
-// Work-groups are launched latest rows first (the causal triangle's
-// heaviest blocks start first).
+// Work items (sequence, kv head, row block) are ordered head-major with each
+// head's latest (heaviest) row blocks first, and cut into eight contiguous
+// runs, one per XCD (work-groups are dealt to the XCDs in turn): each XCD
+// then works through about one head at a time, whose K/V stays in its L2.
 #include "common.h"
 #include "kvsel_internal.h"
 
@@ -32,11 +36,14 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
 
 constexpr int kPThreads = 256;
 constexpr int kPWaves = kPThreads / 64;
 constexpr int kPRows = 32 * kPWaves;   // query rows per work-group
 constexpr int kBN = 64;                // keys per tile
+constexpr float kSlack = 8.f;          // log2 headroom of the running max (p <= 256 in fp16)
 
 // byte offset of K chunk c (dims 8c .. 8c+7) of tile key r
 __device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -76,17 +83,28 @@ struct Stage {
   uint4 k0, k1, k2, k3, v0, v1, v2, v3;
 };
 
-__device__ __forceinline__ Stage fetch(const PrefillArgs &a, int64_t base, int g, int n, int t0, int tid) {
-  auto krow = [&](int u) {
+// byte offsets of this thread's rows from the tile's first row (K: u = 0..3,
+// V: u = 4..7); keys past the sequence are clamped to its last row
+struct StageOff {
+  uint32_t o[8];
+};
+
+__device__ __forceinline__ StageOff stage_off(int t0, int n, int tid, uint32_t row_bytes) {
+  StageOff s;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
     const int i = tid + kPThreads * u;
-    const int key = min(t0 + (i >> 4), n - 1);
-    return *reinterpret_cast<const uint4 *>(a.k + ((base + key) * a.hkv + g) * kD + (i & 15) * 8);
-  };
-  auto vrow = [&](int u) {
-    const int key = min(t0 + (tid >> 4) * 4 + u, n - 1);
-    return *reinterpret_cast<const uint4 *>(a.v + ((base + key) * a.hkv + g) * kD + (tid & 15) * 8);
-  };
-  return Stage{krow(0), krow(1), krow(2), krow(3), vrow(0), vrow(1), vrow(2), vrow(3)};
+    s.o[u] = (uint32_t)(min(t0 + (i >> 4), n - 1) - t0) * row_bytes + (uint32_t)(i & 15) * 16u;
+    s.o[4 + u] = (uint32_t)(min(t0 + (tid >> 4) * 4 + u, n - 1) - t0) * row_bytes + (uint32_t)(tid & 15) * 16u;
+  }
+  return s;
+}
+
+// tile base (uniform) + 32-bit per-thread offsets: scalar-base global loads
+__device__ __forceinline__ Stage fetch(const uint8_t *kt, const uint8_t *vt, const StageOff &s) {
+  auto ld = [](const uint8_t *p, uint32_t o) { return *reinterpret_cast<const uint4 *>(p + o); };
+  return Stage{ld(kt, s.o[0]), ld(kt, s.o[1]), ld(kt, s.o[2]), ld(kt, s.o[3]),
+               ld(vt, s.o[4]), ld(vt, s.o[5]), ld(vt, s.o[6]), ld(vt, s.o[7])};
 }
 
 __device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_vt, int tid) {
@@ -112,8 +130,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
 
-  const int blk = gridDim.x - 1 - blockIdx.x;   // latest rows first
-  const int g = blockIdx.y, b = blockIdx.z;
+  const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
+  const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run, in order
+  if (w >= (uint32_t)a.items) return;
+  const int blk = a.nblk - 1 - (int)(w % (uint32_t)a.nblk);
+  const int g = (int)((w / (uint32_t)a.nblk) % (uint32_t)a.hkv), b = (int)(w / ((uint32_t)a.nblk * a.hkv));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int G = a.group;
@@ -147,12 +168,26 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
 
-  Stage st = fetch(a, base, g, n, 0, tid);
+  // K/V rows of this (sequence, kv head): row r at byte (r * hkv) * 256
+  const uint32_t row_bytes = (uint32_t)a.hkv * kD * 2;
+  const uint8_t *kseq = reinterpret_cast<const uint8_t *>(a.k + (base * a.hkv + g) * kD);
+  const uint8_t *vseq = reinterpret_cast<const uint8_t *>(a.v + (base * a.hkv + g) * kD);
+  const StageOff full = stage_off(0, kBN, tid, row_bytes);   // a tile wholly inside the sequence
+  auto fetch_tile = [&](int t0) {
+    const size_t o = (size_t)t0 * row_bytes;
+    return fetch(kseq + o, vseq + o, t0 + kBN <= n ? full : stage_off(t0, n, tid, row_bytes));
+  };
+
+  const int wave_row0 = row0 + wave * 32;
+  const bool wave_full = wave_row0 + 31 < nrows;
+  const int wave_pos0 = wave_row0 / G;   // the wave's earliest position
+
+  Stage st = fetch_tile(0);
   for (int t0 = 0; t0 < kend; t0 += kBN) {
     __syncthreads();   // the previous tile's reads are done
     stash(st, s_k, s_vt, tid);
     __syncthreads();
-    if (t0 + kBN < kend) st = fetch(a, base, g, n, t0 + kBN, tid);
+    if (t0 + kBN < kend) st = fetch_tile(t0 + kBN);
     if (t0 >= wave_kend) continue;   // every row of this wave is before the tile
 
     // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
@@ -167,36 +202,51 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[bk], 0, 0, 0);
       }
     }
-    float tm = -INFINITY;
-    float x[2][16];
+    // the causal mask, only on tiles that reach past a row of this wave
+    if (!wave_full || t0 + kBN - 1 > wave_pos0) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos) s[bk][j] = -INFINITY;
+    }
+    float tm = s[0][0];
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3);
-        x[bk][j] = key <= pos ? s[bk][j] * a.scale_log2 : -INFINITY;
-        tm = fmaxf(tm, x[bk][j]);
-      }
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float mnew = fmaxf(mrun, tm);
-    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
-    mrun = mnew;
+      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, s[bk][j]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32)) * a.scale_log2;   // the row's max in this tile, log2 units (scale > 0)
+    // the running max moves only when a row's max grows by more than kSlack:
+    // p then stays below 2^kSlack and the rescale is skipped on most tiles
+    if (__ballot(tm > mrun + kSlack) != 0) {
+      const float mnew = fmaxf(mrun, tm);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[dt][j] *= alpha;
+    }
+    const float neg = mrun == -INFINITY ? 0.f : -mrun;   // a row that has seen nothing yet keeps p = 0
     float ps = 0.f;
     f16x8 pop[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float xv = x[ks >> 1][(ks & 1) * 8 + i];
-        const float p = xv == -INFINITY ? 0.f : fast_exp2(xv - mnew);
-        ps += p;
-        pop[ks][i] = (_Float16)p;
+        p[i] = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + i], a.scale_log2, neg));
+        ps += p[i];
       }
-    lsum = lsum * alpha + ps;
+      const h2 p01 = __builtin_convertvector((f2){p[0], p[1]}, h2), p23 = __builtin_convertvector((f2){p[2], p[3]}, h2);
+      const h2 p45 = __builtin_convertvector((f2){p[4], p[5]}, h2), p67 = __builtin_convertvector((f2){p[6], p[7]}, h2);
+      pop[ks] = __builtin_shufflevector(__builtin_shufflevector(p01, p23, 0, 1, 2, 3),
+                                        __builtin_shufflevector(p45, p67, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    lsum += ps;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[dt][j] *= alpha;
       const int d = dt * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -226,8 +276,13 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s) {
   if (a.group < 1 || a.max_seqlen < 1 || batch < 1) return hipErrorInvalidValue;
-  const int64_t blocks = ((int64_t)a.max_seqlen * a.group + kPRows - 1) / kPRows;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks, a.hkv, batch), dim3(kPThreads), 0, s, a);
+  PrefillArgs c = a;
+  c.nblk = (int32_t)(((int64_t)a.max_seqlen * a.group + kPRows - 1) / kPRows);
+  const int64_t items = (int64_t)c.nblk * a.hkv * batch;
+  if (items >= 0x7ffffff0ll) return hipErrorInvalidValue;
+  c.items = (int32_t)items;
+  const int64_t grid = (items + 7) / 8 * 8;   // a multiple of the XCD count
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, s, c);
   return hipGetLastError();
 }
 

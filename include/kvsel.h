@@ -329,7 +329,7 @@ KVSEL_API kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t
  * keep their order of position, so row i of a sequence sees rows 0..i of
  * it.  q: bf16 [total][num_q_heads][128]; k, v: bf16
  * [total][num_kv_heads][128]; query head h reads kv head
- * h / (num_q_heads / num_kv_heads); out: fp32 [total][num_q_heads][128];
+ * h / (num_q_heads / num_kv_heads); scale > 0; out: fp32 [total][num_q_heads][128];
  * lse: NULL or fp32 [total][num_q_heads] (natural log).  q, k, v and out
  * 16-byte aligned.  P V runs in fp16: V values of magnitude above 65504
  * are clamped to it.  No workspace.

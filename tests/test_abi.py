@@ -197,7 +197,7 @@ def test_verify_attn_rejects(L, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), EINVAL), (dict(k=0), EINVAL), (dict(v=0), EINVAL), (dict(cu=0), EINVAL), (dict(out=0), EINVAL),
     (dict(q=FAKE + 2), EINVAL), (dict(out=FAKE + 4), EINVAL), (dict(batch=0), EINVAL), (dict(hq=12), EINVAL),
-    (dict(hkv=0), EINVAL), (dict(max_len=-1), EINVAL), (dict(scale=float("nan")), EINVAL),
+    (dict(hkv=0), EINVAL), (dict(max_len=-1), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(scale=-0.1), EINVAL),
     (dict(max_len=1 << 28, hq=64, hkv=8), EUNSUP),
 ])
 def test_prefill_attn_rejects(L, kw, code):
