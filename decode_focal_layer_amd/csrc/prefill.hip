@@ -49,9 +49,10 @@ constexpr float kSlack = 8.f;          // log2 headroom of the running max (p <=
 __device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 // byte offset of V^T element (dim d, tile position p); the 16-byte blocks of
-// a row are XOR-swizzled by the dim
+// a row are XOR-swizzled by the dim, so that the 16-byte reads of 8 (or 16)
+// consecutive dims fall in distinct banks
 __device__ __forceinline__ int vt_off(int d, int p) {
-  const int sw = ((d >> 1) ^ (d >> 3)) & 7;
+  const int sw = (d ^ (d >> 3)) & 7;
   return d * 128 + ((((p >> 3) ^ sw) & 7) << 4) + (p & 7) * 2;
 }
 
@@ -65,15 +66,25 @@ __device__ __forceinline__ int quad_pos(int q) {
   return blk * 32 + (a >> 1) * 16 + hf * 8 + (a & 1) * 4;
 }
 
+// lane l and lane l ^ 32 hold the two halves of one row: combine them
+// (v_permlane32_swap leaves both values in every lane; no LDS)
+__device__ __forceinline__ float half_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// two bf16 values -> two fp16 (exact inside the fp16 range; toward zero
-// outside it, so no infinity appears)
-__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t lo_bits, uint32_t hi_bits) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo_bits << 16), __uint_as_float(hi_bits << 16));
-  return __builtin_bit_cast(uint32_t, h);
+// two floats (bf16 values) -> two fp16 (exact inside the fp16 range; toward
+// zero outside it, so no infinity appears)
+__device__ __forceinline__ uint32_t f16_pair(uint32_t a_bits, uint32_t b_bits) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(a_bits), __uint_as_float(b_bits)));
 }
 
 // staging of one tile: K chunk i = tid + 256u is (key i/16, chunk i%16); V
@@ -116,13 +127,13 @@ __device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_
   }
   const int p = quad_pos(tid >> 4), vc = tid & 15;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t w0 = word_of(st.v0, e >> 1), w1 = word_of(st.v1, e >> 1);
-    const uint32_t w2 = word_of(st.v2, e >> 1), w3 = word_of(st.v3, e >> 1);
-    const int sh = (e & 1) * 16;
-    *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + e, p)) =
-        make_uint2(bf16_pair_to_f16((w0 >> sh) & 0xffffu, (w1 >> sh) & 0xffffu),
-                   bf16_pair_to_f16((w2 >> sh) & 0xffffu, (w3 >> sh) & 0xffffu));
+  for (int e2 = 0; e2 < 4; ++e2) {   // dims vc*8 + 2*e2 (low halves) and + 1 (high halves)
+    const uint32_t w0 = word_of(st.v0, e2), w1 = word_of(st.v1, e2);
+    const uint32_t w2 = word_of(st.v2, e2), w3 = word_of(st.v3, e2);
+    *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + 2 * e2, p)) =
+        make_uint2(f16_pair(w0 << 16, w1 << 16), f16_pair(w2 << 16, w3 << 16));
+    *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + 2 * e2 + 1, p)) =
+        make_uint2(f16_pair(w0 & 0xffff0000u, w1 & 0xffff0000u), f16_pair(w2 & 0xffff0000u, w3 & 0xffff0000u));
   }
 }
 
@@ -191,16 +202,35 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (t0 >= wave_kend) continue;   // every row of this wave is before the tile
 
     // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
-    f32x16 s[2];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      s[bk] = {};
-      const int r = bk * 32 + col;
+    // (operands read one k-step ahead of the products that use them)
+    f32x16 s[2] = {{}, {}};
+    {
+      auto kread = [&](int bk, int kk) {
+        return *reinterpret_cast<const bf16x8 *>(s_k + k_off(bk * 32 + col, hf * 8 + kk));
+      };
+      bf16x8 c0 = kread(0, 0), c1 = kread(1, 0);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(s_k + k_off(r, hf * 8 + kk));
-        s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[bk], 0, 0, 0);
+        bf16x8 n0, n1;
+        if (kk < 7) {
+          n0 = kread(0, kk + 1);
+          n1 = kread(1, kk + 1);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, qop[kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, qop[kk], s[1], 0, 0, 0);
+        if (kk < 7) {
+          c0 = n0;
+          c1 = n1;
+        }
       }
+      // keep the order: reads of k-steps 0 and 1, then (2 products, 2 reads of the next step) ...
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kk = 0; kk < 6; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     // the causal mask, only on tiles that reach past a row of this wave
     if (!wave_full || t0 + kBN - 1 > wave_pos0) {
@@ -215,7 +245,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, s[bk][j]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32)) * a.scale_log2;   // the row's max in this tile, log2 units (scale > 0)
+    tm = half_pair_max(tm) * a.scale_log2;   // the row's max in this tile, log2 units (scale > 0)
     // the running max moves only when a row's max grows by more than kSlack:
     // p then stays below 2^kSlack and the rescale is skipped on most tiles
     if (__ballot(tm > mrun + kSlack) != 0) {
@@ -245,18 +275,27 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                                         __builtin_shufflevector(p45, p67, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     }
     lsum += ps;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + col;
+    {
+      auto vread = [&](int dt, int ks) {
+        return *reinterpret_cast<const f16x8 *>(s_vt + vt_off(dt * 32 + col, ks * 16 + hf * 8));
+      };
+      f16x8 c[4] = {vread(0, 0), vread(1, 0), vread(2, 0), vread(3, 0)};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f16x8 vop = *reinterpret_cast<const f16x8 *>(s_vt + vt_off(d, ks * 16 + hf * 8));
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[ks], acc[dt], 0, 0, 0);
+        f16x8 nx[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          if (ks < 3) nx[dt] = vread(dt, ks + 1);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[dt], pop[ks], acc[dt], 0, 0, 0);
+        }
+        if (ks < 3)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) c[dt] = nx[dt];
       }
     }
   }
 
-  const float lrow = lsum + __shfl_xor(lsum, 32);
+  const float lrow = half_pair_sum(lsum);
   if (!live) return;
   const int64_t orow = (base + pos) * a.hq + g * G + h;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
