@@ -6,6 +6,7 @@
 
 #include "common.h"
 #include "kvsel_internal.h"
+#include "mfma_kernels.h"
 
 using namespace kvsel;
 

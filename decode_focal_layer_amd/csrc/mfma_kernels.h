@@ -1,0 +1,35 @@
+// Launchers of the MFMA attention kernels (draft verification, causal
+// prefill over a compacted sequence); host side.
+#pragma once
+
+#include "kvsel_internal.h"
+
+namespace kvsel {
+
+// draft verification attention (MFMA): one work-group per (sequence, kv head)
+constexpr int kVerifyMaxRows = 8192;   // attended rows per (sequence, kv head), resolved into LDS
+struct VerifyArgs {
+  const uint16_t *k_pool, *v_pool;
+  const int32_t *block_table, *seq_len, *seg_begin, *seg_end;
+  int64_t num_blocks;
+  int32_t max_blocks, hkv, hq, group, m, k;
+  const uint16_t *q;     // [batch][m][hq][128]
+  const int32_t *idx;    // [batch][hkv][k]
+  float scale_log2;
+  float *out, *lse;      // [batch][m][hq][128], [batch][m][hq]
+};
+hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s);
+
+// causal prefill over a compacted sequence (MFMA): one work-group per
+// (128 query rows, kv head, sequence)
+struct PrefillArgs {
+  const uint16_t *q, *k, *v;     // [total][hq][128], [total][hkv][128] x2
+  const int32_t *cu_seqlens;     // [batch + 1]
+  float *out, *lse;              // [total][hq][128], [total][hq]
+  int32_t max_seqlen, hq, hkv, group;
+  float scale_log2;
+  int32_t nblk, items;           // set by launch_prefill
+};
+hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
+
+}  // namespace kvsel

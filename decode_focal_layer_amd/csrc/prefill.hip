@@ -28,6 +28,7 @@
 // then works through about one head at a time, whose K/V stays in its L2.
 #include "common.h"
 #include "kvsel_internal.h"
+#include "mfma_kernels.h"
 
 namespace kvsel {
 

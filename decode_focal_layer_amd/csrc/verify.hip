@@ -24,6 +24,7 @@
 // when that is <= r.
 #include "common.h"
 #include "kvsel_internal.h"
+#include "mfma_kernels.h"
 
 namespace kvsel {
 
