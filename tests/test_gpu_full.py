@@ -256,3 +256,43 @@ def test_c4_full_sampled():
                     ref, _ = O.attention(qg, Kl, Vl, O.kept_rows(sets[(e[2], e[3])][b, g], 0, cfg.n_visual, n),
                                          cfg.scale)
                 assert_attn(outs[t][l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
+
+
+def test_c4_verify_full_sampled():
+    """Draft verification at the benchmark's size: 512 branches over the C4
+    cache (shared 3072 + 1024 prefix, suffix U[32,1024] + 32 appended rows),
+    8 drafts, 154 kept visual rows per kv head, the launch the benchmark times
+    (one layer here).  Checked: 24 sampled (branch, kv head) pairs, every
+    draft and head, against the oracle."""
+    from decode_focal_layer_amd import kvsel
+    cfg = synth.small(synth.C4, layers=1)
+    m = 8
+    w = gen.make_focal(cfg, DEV)
+    T = cfg.steps
+    seq = w.seq_len[T - 1]
+    n_np = w.seq_len_np[T - 1].astype(np.int64)
+    kv = kvsel.KV(w.k_pool[0], w.v_pool[0], w.block_table, seq, w.seg_begin, w.seg_end,
+                  max_seq_len=int(n_np.max()), max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                  shared_rows=cfg.prefix_len)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 77)
+    keys = torch.rand((cfg.batch * cfg.hkv, cfg.n_visual), generator=g, device=DEV)
+    idx = keys.argsort(dim=1)[:, :cfg.k].sort(dim=1).values.to(torch.int32).view(cfg.batch, cfg.hkv, cfg.k)
+    q = torch.randn((cfg.batch, m, cfg.hq, 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.empty((cfg.batch, m, cfg.hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device=DEV)
+    log_case("c4-verify-full", cfg.batch, m)
+    kvsel.verify_attn(kv, q, m, cfg.hq, cfg.scale, idx, cfg.k, out, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    G = cfg.group
+    idx_c, q_c = idx.cpu().numpy(), q.cpu()
+    for _ in range(24):
+        b, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.hkv))
+        n = int(n_np[b])
+        Kl = O.logical_rows(w.k_pool[0], w.table_np[b], h, n)
+        Vl = O.logical_rows(w.v_pool[0], w.table_np[b], h, n)
+        rows = O.kept_rows(idx_c[b, h], 0, cfg.n_visual, n)
+        ref, rl = O.verify_attention(O.widen(q_c[b, :, h * G:(h + 1) * G]), Kl, Vl, rows, n, cfg.scale)
+        got = out[b, :, h * G:(h + 1) * G].cpu().numpy()
+        assert_attn(got.reshape(-1, 128), ref.reshape(-1, 128), f"c4 verify b{b} g{h}")
+        assert np.abs(lse[b, :, h * G:(h + 1) * G].cpu().numpy() - rl).max() < 1e-4
