@@ -58,8 +58,9 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
   lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
-// transposed V row of dim d (dims d and d + 64 in adjacent rows: different banks)
-__device__ __forceinline__ int vt_row(int d) { return (d & 63) * 2 + (d >> 6); }
+// transposed V row of dim d: dims d and d + 8 (the two lane halves' dims of
+// one load) in adjacent rows, so their writes fall in different banks
+__device__ __forceinline__ int vt_row(int d) { return (d & ~15) + (d & 7) * 2 + ((d >> 3) & 1); }
 
 // LDS: the rows and the V^T tiles while the tiles run, then the same bytes
 // hold the waves' partial outputs for the merge (two work-groups per CU)
@@ -108,13 +109,14 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     s_prow[j] = pr;
   }
 
-  // ---- this lane's query column (B operand: dims hf*64 + kk*8 .. +8) ----
+  // ---- this lane's query column (B operand of k-step kk: dims kk*16 + hf*8 .. +8,
+  // so the two lane halves of a key read adjacent 16-byte pieces) ----
   bf16x8 qop[8];
   const int qr = col / max(G, 1), qh = col % max(G, 1);
   if (col < R) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(a.q + (((size_t)b * a.m + qr) * a.hq + g * G + qh) * kD + hf * 64);
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.q + (((size_t)b * a.m + qr) * a.hq + g * G + qh) * kD + hf * 8);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, p[kk]);
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, p[2 * kk]);
   } else {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
@@ -142,8 +144,8 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const uint16_t *vrow = pr != kNoRow ? a.v_pool + (size_t)pr * kD : a.q;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      kop[kk] = __builtin_bit_cast(bf16x8, reinterpret_cast<const uint4 *>(krow + hf * 64)[kk]);
-      vv[kk] = reinterpret_cast<const uint4 *>(vrow + hf * 64)[kk];
+      kop[kk] = __builtin_bit_cast(bf16x8, reinterpret_cast<const uint4 *>(krow + hf * 8)[2 * kk]);
+      vv[kk] = reinterpret_cast<const uint4 *>(vrow + hf * 8)[2 * kk];
     }
   };
   if (wave * 32 < cnt) load_tile(wave * 32);
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       const uint32_t w4[4] = {vv[kk].x, vv[kk].y, vv[kk].z, vv[kk].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = hf * 64 + kk * 8 + e;
+        const int d = kk * 16 + hf * 8 + e;
         const uint32_t word = w4[e >> 1];
         vt[vt_row(d) * kVtStride + col] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
       }
