@@ -279,7 +279,9 @@ kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   if (k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
   if (k > 0 && idx == nullptr) return fail(KVSEL_EINVAL, "idx is NULL with k > 0");
   if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
-  if (gather_rows_bound(kv, k) > kVerifyMaxRows)
+  // a segment reaching into the drafts is cut before them: up to m more rows
+  const int64_t rows_cap = (int64_t)gather_rows_bound(kv, k) + m;
+  if (rows_cap > kVerifyMaxRows)
     return fail(KVSEL_EUNSUPPORTED, "more than %d attended rows per (sequence, kv head)", kVerifyMaxRows);
   VerifyArgs a{};
   a.k_pool = kv->k_pool;
@@ -300,6 +302,7 @@ kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
+  a.rows_cap = (int32_t)rows_cap;
   return hip_status(launch_verify(a, kv->batch, (hipStream_t)stream), "verify_attn launch");
 }
 

@@ -17,6 +17,7 @@ struct VerifyArgs {
   const int32_t *idx;    // [batch][hkv][k]
   float scale_log2;
   float *out, *lse;      // [batch][m][hq][128], [batch][m][hq]
+  int32_t rows_cap;      // attended rows per (sequence, kv head), at most kVerifyMaxRows
 };
 hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s);
 
