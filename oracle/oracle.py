@@ -274,6 +274,26 @@ def verify_attention(qd, K, V, rows, n: int, scale):
     return np.stack(outs), np.stack(lses)
 
 
+def merge_attention(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint row sets from the attention
+    over each (out normalised per set, lse its log normaliser): the softmax
+    normaliser of the union is the sum of the two, so each part is weighted
+    by exp(lse_i - lse).  HPD-Parsing wiki, method item 2: a branch attends
+    to the shared context and to its own rows, here computed apart and
+    combined.  A part with no rows has lse = -inf and weight 0.
+    o1, o2 [..., d]; lse1, lse2 [...].  Returns (out, lse)."""
+    o1, o2 = np.asarray(o1, F64), np.asarray(o2, F64)
+    l1, l2 = np.asarray(lse1, F64), np.asarray(lse2, F64)
+    m = np.maximum(l1, l2)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    w1, w2 = np.exp(l1 - safe), np.exp(l2 - safe)
+    z = w1 + w2
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where((z > 0)[..., None], (o1 * w1[..., None] + o2 * w2[..., None]) / np.where(z > 0, z, 1.0)[..., None], 0.0)
+        lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    return out, lse
+
+
 def causal_prefill(Q, K, V, scale, rows=None):
     """Causal self-attention over the propagated tokens (FastKV, section 2A,
     Token-Selective Propagation: the layers after the TSP layer process only

@@ -191,3 +191,34 @@ def test_prefill_pins_catch(monkeypatch, bad, pin):
     monkeypatch.setattr(O, "causal_prefill", bad)
     with pytest.raises(AssertionError):
         getattr(P, pin)()
+
+
+def _merge_unweighted(o1, lse1, o2, lse2):
+    out = (np.asarray(o1, F64) + np.asarray(o2, F64)) / 2
+    return out, np.logaddexp(lse1, lse2)
+
+
+def _merge_swapped_weights(o1, lse1, o2, lse2):
+    l1, l2 = np.asarray(lse1, F64), np.asarray(lse2, F64)
+    m = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - m), np.exp(l2 - m)
+    return (np.asarray(o1, F64) * w2[..., None] + np.asarray(o2, F64) * w1[..., None]) / (w1 + w2)[..., None], \
+        m + np.log(w1 + w2)
+
+
+@pytest.mark.parametrize("bad", [_merge_unweighted, _merge_swapped_weights])
+def test_merge_pin_catches(monkeypatch, bad):
+    monkeypatch.setattr(O, "merge_attention", bad)
+    with pytest.raises(AssertionError):
+        P.test_merge_attention_equals_union(41)
+
+
+def test_merge_pin_catches_wrong_lse(monkeypatch):
+    real = O.merge_attention
+
+    def bad(o1, lse1, o2, lse2):
+        out, _ = real(o1, lse1, o2, lse2)
+        return out, np.maximum(np.asarray(lse1, F64), np.asarray(lse2, F64))
+    monkeypatch.setattr(O, "merge_attention", bad)
+    with pytest.raises(AssertionError):
+        P.test_merge_attention_equals_union(41)

@@ -507,3 +507,33 @@ def test_causal_prefill_ends():
     full, _ = O.causal_prefill(Q, K, V, SCALE)
     one, _ = O.causal_prefill(Q, K, V, SCALE, rows=[(13, 6)])
     np.testing.assert_array_equal(one[0], full[13 * hkv * G + 6])
+
+
+# --------------------------------------------------------------------------
+# merging two partial attentions (shared rows apart from a branch's own rows)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [41, 42])
+def test_merge_attention_equals_union(seed):
+    """Attention over A and over B, merged, equals attention over A u B
+    (A, B disjoint); either part empty leaves the other unchanged."""
+    rng = np.random.default_rng(seed)
+    n, G = 80, 3
+    K, V = _rand(rng, n, D), _rand(rng, n, D)
+    qg = _rand(rng, G, D)
+    perm = rng.permutation(n)
+    A, B = np.sort(perm[:30]), np.sort(perm[30:])
+    oa, la = O.attention(qg, K, V, A, SCALE)
+    ob, lb = O.attention(qg, K, V, B, SCALE)
+    ou, lu = O.attention(qg, K, V, np.arange(n), SCALE)
+    om, lm = O.merge_attention(oa, la, ob, lb)
+    np.testing.assert_allclose(om, ou, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lm, lu, rtol=1e-13)
+    om2, _ = O.merge_attention(ob, lb, oa, la)
+    np.testing.assert_allclose(om2, ou, rtol=1e-12, atol=1e-13)
+    empty_o, empty_l = np.zeros_like(oa), np.full(G, -np.inf)
+    oe, le = O.merge_attention(oa, la, empty_o, empty_l)
+    np.testing.assert_array_equal(oe, oa)
+    np.testing.assert_array_equal(le, la)
+    oz, lz = O.merge_attention(empty_o, empty_l, empty_o, empty_l)
+    assert np.all(oz == 0) and np.all(np.isneginf(lz))
