@@ -342,6 +342,49 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
   return hip_status(launch_prefill(a, batch, (hipStream_t)stream), "prefill_attn launch");
 }
 
+kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
+                               int32_t row_begin, int32_t row_end, float *out, float *lse, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr || !aligned(out, 16)) return fail(KVSEL_EINVAL, "out must be a 16-byte aligned pointer");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(KVSEL_EINVAL, "scale must be finite and positive");
+  if (row_begin < 0 || row_end < row_begin || row_end > kv->shared_rows ||
+      (int64_t)row_end > (int64_t)kv->max_blocks_per_seq * kBlk)
+    return fail(KVSEL_EINVAL, "rows [%d, %d) must lie inside the shared rows [0, %d)", row_begin, row_end,
+                kv->shared_rows);
+  if (row_end > row_begin && ((row_end - 1) >> 4) - (row_begin >> 4) + 1 > kSharedMaxBlocks)
+    return fail(KVSEL_EUNSUPPORTED, "the range touches more than %d cache blocks", kSharedMaxBlocks);
+  SharedArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.table = kv->block_table;   // sequence 0's row: the shared rows are the same blocks in every table
+  a.num_blocks = kv->num_blocks;
+  a.hkv = kv->num_kv_heads;
+  a.hq = num_q_heads;
+  a.group = G;
+  a.batch = kv->batch;
+  a.row_begin = row_begin;
+  a.row_end = row_end;
+  a.q = q;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(launch_shared(a, (hipStream_t)stream), "shared_attn launch");
+}
+
+kvsel_status kvsel_merge_attn(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
+                              float *out, float *lse, kvsel_stream stream) {
+  if (o1 == nullptr || lse1 == nullptr || o2 == nullptr || lse2 == nullptr || out == nullptr || lse == nullptr)
+    return fail(KVSEL_EINVAL, "o1, lse1, o2, lse2, out and lse are required");
+  if (!aligned(o1, 16) || !aligned(o2, 16) || !aligned(out, 16))
+    return fail(KVSEL_EINVAL, "o1, o2 and out must be 16-byte aligned");
+  if (rows < 0) return fail(KVSEL_EINVAL, "rows must be >= 0");
+  return hip_status(launch_merge(o1, lse1, o2, lse2, rows, out, lse, (hipStream_t)stream), "merge_attn launch");
+}
+
 size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads) {
   int G;
   if (check_desc(kv, false) != KVSEL_OK || check_heads(kv, num_q_heads, &G) != KVSEL_OK) return 0;

@@ -33,4 +33,25 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s);
 
+// every sequence's queries over one row range that all sequences share,
+// read through one block table (MFMA): one work-group per (128 query rows,
+// kv head)
+constexpr int kSharedMaxBlocks = 1024;   // cache blocks the range may touch (their ids go to LDS)
+struct SharedArgs {
+  const uint16_t *k_pool, *v_pool;
+  const int32_t *table;          // the block table the rows are read through
+  int64_t num_blocks;
+  int32_t hkv, hq, group, batch;
+  int32_t row_begin, row_end;
+  const uint16_t *q;             // [batch][hq][128]
+  float scale_log2;
+  float *out, *lse;              // [batch][hq][128], [batch][hq]
+  int32_t nblk, items;           // set by launch_shared
+};
+hipError_t launch_shared(const SharedArgs &a, hipStream_t s);
+
+// out = attention over the union of two disjoint row sets from the two parts
+hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
+                        float *out, float *lse, hipStream_t s);
+
 }  // namespace kvsel

@@ -138,6 +138,107 @@ __device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_
   }
 }
 
+// One 64-key tile for this lane's query row: S^T = K Q^T from the LDS K
+// tile, the online softmax, O^T += V^T P from the LDS V^T tile.  masked(bk, j)
+// drops key 32*bk + 8*(j/4) + 4*hf + j%4 of the tile; it is evaluated only
+// when need_mask.
+template <typename MaskFn>
+__device__ __forceinline__ void attend_tile(const uint8_t *s_k, const uint8_t *s_vt, const bf16x8 (&qop)[8], int col,
+                                            int hf, float scale_log2, bool need_mask, MaskFn masked,
+                                            f32x16 (&acc)[4], float &mrun, float &lsum) {
+    // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
+    // (operands read one k-step ahead of the products that use them)
+    f32x16 s[2] = {{}, {}};
+    {
+      auto kread = [&](int bk, int kk) {
+        return *reinterpret_cast<const bf16x8 *>(s_k + k_off(bk * 32 + col, hf * 8 + kk));
+      };
+      bf16x8 c0 = kread(0, 0), c1 = kread(1, 0);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        bf16x8 n0, n1;
+        if (kk < 7) {
+          n0 = kread(0, kk + 1);
+          n1 = kread(1, kk + 1);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, qop[kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, qop[kk], s[1], 0, 0, 0);
+        if (kk < 7) {
+          c0 = n0;
+          c1 = n1;
+        }
+      }
+      // keep the order: reads of k-steps 0 and 1, then (2 products, 2 reads of the next step) ...
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kk = 0; kk < 6; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (masked(bk, j)) s[bk][j] = -INFINITY;
+    }
+    float tm = s[0][0];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, s[bk][j]);
+    tm = half_pair_max(tm) * scale_log2;   // the row's max in this tile, log2 units (scale > 0)
+    // the running max moves only when a row's max grows by more than kSlack:
+    // p then stays below 2^kSlack and the rescale is skipped on most tiles
+    if (__ballot(tm > mrun + kSlack) != 0) {
+      const float mnew = fmaxf(mrun, tm);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[dt][j] *= alpha;
+    }
+    const float neg = mrun == -INFINITY ? 0.f : -mrun;   // a row that has seen nothing yet keeps p = 0
+    float ps = 0.f;
+    f16x8 pop[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + i], scale_log2, neg));
+        ps += p[i];
+      }
+      const h2 p01 = __builtin_convertvector((f2){p[0], p[1]}, h2), p23 = __builtin_convertvector((f2){p[2], p[3]}, h2);
+      const h2 p45 = __builtin_convertvector((f2){p[4], p[5]}, h2), p67 = __builtin_convertvector((f2){p[6], p[7]}, h2);
+      pop[ks] = __builtin_shufflevector(__builtin_shufflevector(p01, p23, 0, 1, 2, 3),
+                                        __builtin_shufflevector(p45, p67, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    lsum += ps;
+    {
+      auto vread = [&](int dt, int ks) {
+        return *reinterpret_cast<const f16x8 *>(s_vt + vt_off(dt * 32 + col, ks * 16 + hf * 8));
+      };
+      f16x8 c[4] = {vread(0, 0), vread(1, 0), vread(2, 0), vread(3, 0)};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        f16x8 nx[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          if (ks < 3) nx[dt] = vread(dt, ks + 1);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[dt], pop[ks], acc[dt], 0, 0, 0);
+        }
+        if (ks < 3)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) c[dt] = nx[dt];
+      }
+    }
+}
+
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
@@ -202,98 +303,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (t0 + kBN < kend) st = fetch_tile(t0 + kBN);
     if (t0 >= wave_kend) continue;   // every row of this wave is before the tile
 
-    // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
-    // (operands read one k-step ahead of the products that use them)
-    f32x16 s[2] = {{}, {}};
-    {
-      auto kread = [&](int bk, int kk) {
-        return *reinterpret_cast<const bf16x8 *>(s_k + k_off(bk * 32 + col, hf * 8 + kk));
-      };
-      bf16x8 c0 = kread(0, 0), c1 = kread(1, 0);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        bf16x8 n0, n1;
-        if (kk < 7) {
-          n0 = kread(0, kk + 1);
-          n1 = kread(1, kk + 1);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, qop[kk], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, qop[kk], s[1], 0, 0, 0);
-        if (kk < 7) {
-          c0 = n0;
-          c1 = n1;
-        }
-      }
-      // keep the order: reads of k-steps 0 and 1, then (2 products, 2 reads of the next step) ...
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int kk = 0; kk < 6; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
     // the causal mask, only on tiles that reach past a row of this wave
-    if (!wave_full || t0 + kBN - 1 > wave_pos0) {
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos) s[bk][j] = -INFINITY;
-    }
-    float tm = s[0][0];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, s[bk][j]);
-    tm = half_pair_max(tm) * a.scale_log2;   // the row's max in this tile, log2 units (scale > 0)
-    // the running max moves only when a row's max grows by more than kSlack:
-    // p then stays below 2^kSlack and the rescale is skipped on most tiles
-    if (__ballot(tm > mrun + kSlack) != 0) {
-      const float mnew = fmaxf(mrun, tm);
-      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mrun - mnew);
-      mrun = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[dt][j] *= alpha;
-    }
-    const float neg = mrun == -INFINITY ? 0.f : -mrun;   // a row that has seen nothing yet keeps p = 0
-    float ps = 0.f;
-    f16x8 pop[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + i], a.scale_log2, neg));
-        ps += p[i];
-      }
-      const h2 p01 = __builtin_convertvector((f2){p[0], p[1]}, h2), p23 = __builtin_convertvector((f2){p[2], p[3]}, h2);
-      const h2 p45 = __builtin_convertvector((f2){p[4], p[5]}, h2), p67 = __builtin_convertvector((f2){p[6], p[7]}, h2);
-      pop[ks] = __builtin_shufflevector(__builtin_shufflevector(p01, p23, 0, 1, 2, 3),
-                                        __builtin_shufflevector(p45, p67, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    lsum += ps;
-    {
-      auto vread = [&](int dt, int ks) {
-        return *reinterpret_cast<const f16x8 *>(s_vt + vt_off(dt * 32 + col, ks * 16 + hf * 8));
-      };
-      f16x8 c[4] = {vread(0, 0), vread(1, 0), vread(2, 0), vread(3, 0)};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        f16x8 nx[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          if (ks < 3) nx[dt] = vread(dt, ks + 1);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[dt], pop[ks], acc[dt], 0, 0, 0);
-        }
-        if (ks < 3)
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) c[dt] = nx[dt];
-      }
-    }
+    attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_full || t0 + kBN - 1 > wave_pos0,
+                [&](int bk, int j) { return t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos; }, acc, mrun, lsum);
   }
 
   const float lrow = half_pair_sum(lsum);
@@ -312,6 +324,140 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     a.lse[orow] = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Every sequence's queries over one shared row range (a shared prefix read
+// zero-copy through one block table): the part of each branch's attention
+// that all branches have in common, computed once per kv head for all of
+// them.  HPD-Parsing wiki, method item 2: the branches reuse the shared
+// context's KV.  Query row rr = sequence * G + head of the group; no mask but
+// the range's end and invalid blocks.  Same tiles and tile step as the
+// prefill kernel; the output is normalised over the range, with its lse.
+// ---------------------------------------------------------------------------
+// (one wave per SIMD: each K/V load has its own paged address, and the
+// launches are small -- one work-group per 128 query rows and kv head)
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void shared_kernel(SharedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
+  __shared__ int32_t s_tab[kSharedMaxBlocks];
+
+  const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
+  const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run: one kv head's row blocks together
+  if (w >= (uint32_t)a.items) return;
+  const int blk = (int)(w % (uint32_t)a.nblk), g = (int)(w / (uint32_t)a.nblk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int G = a.group;
+  const int nrows = a.batch * G;
+  const int row0 = blk * kPRows;
+  if (row0 >= nrows) return;   // the whole work-group
+
+  const int first = a.row_begin >> 4;
+  const int nb = a.row_end > a.row_begin ? ((a.row_end - 1) >> 4) - first + 1 : 0;
+  for (int i = tid; i < nb; i += kPThreads) s_tab[i] = a.table[first + i];
+
+  const int rr = row0 + wave * 32 + col;
+  const bool live = rr < nrows;
+  const int b = rr / G, h = rr % G;
+  const bool wave_live = row0 + wave * 32 + 31 < nrows;   // every row of this wave is a real query
+  bf16x8 qop[8];
+  if (live) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.q + ((size_t)b * a.hq + g * G + h) * kD + hf * 64);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, p[kk]);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+  __syncthreads();   // the block ids
+
+  // a row's bytes, or the queries (valid memory) for a row outside the range
+  // or in an invalid block; those keys are masked
+  auto row_ok = [&](int key, int32_t &blk_id) {
+    if (key >= a.row_end) return false;
+    blk_id = s_tab[(key >> 4) - first];
+    return blk_id >= 0 && (int64_t)blk_id < a.num_blocks;
+  };
+  auto row_ptr = [&](const uint16_t *pool, int key) {
+    int32_t bi = 0;
+    if (!row_ok(key, bi)) return reinterpret_cast<const uint8_t *>(a.q);
+    return reinterpret_cast<const uint8_t *>(pool + ((size_t)((uint32_t)bi * (uint32_t)a.hkv + (uint32_t)g) * kBlk +
+                                                     (uint32_t)(key & 15)) * kD);
+  };
+  auto fetch_tile = [&](int t0) {
+    auto kld = [&](int u) {
+      const int i = tid + kPThreads * u;
+      return *reinterpret_cast<const uint4 *>(row_ptr(a.k_pool, t0 + (i >> 4)) + (i & 15) * 16);
+    };
+    auto vld = [&](int u) {
+      return *reinterpret_cast<const uint4 *>(row_ptr(a.v_pool, t0 + (tid >> 4) * 4 + u) + (tid & 15) * 16);
+    };
+    return Stage{kld(0), kld(1), kld(2), kld(3), vld(0), vld(1), vld(2), vld(3)};
+  };
+
+  float mrun = -INFINITY, lsum = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
+
+  Stage st = fetch_tile(a.row_begin);
+  for (int t0 = a.row_begin; t0 < a.row_end; t0 += kBN) {
+    __syncthreads();   // the previous tile's reads are done
+    stash(st, s_k, s_vt, tid);
+    __syncthreads();
+    if (t0 + kBN < a.row_end) st = fetch_tile(t0 + kBN);
+    int32_t bi = 0;
+    const uint64_t vmask = __ballot(row_ok(t0 + lane, bi));   // bit i: key t0 + i is attended
+    attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_live || vmask != ~0ull,
+                [&](int bk, int j) {
+                  return !live || ((vmask >> (32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3))) & 1ull) == 0ull;
+                },
+                acc, mrun, lsum);
+  }
+
+  const float lrow = half_pair_sum(lsum);
+  if (!live) return;
+  const size_t orow = (size_t)b * a.hq + g * G + h;
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  float *o = a.out + orow * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq)
+      *reinterpret_cast<float4 *>(o + dt * 32 + 8 * jq + 4 * hf) =
+          make_float4(acc[dt][4 * jq] * inv, acc[dt][4 * jq + 1] * inv, acc[dt][4 * jq + 2] * inv,
+                      acc[dt][4 * jq + 3] * inv);
+  if (hf == 0 && a.lse != nullptr)
+    a.lse[orow] = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;
+}
+
+// eight (sequence, head) rows per work-group, 32 threads of 4 floats per row;
+// every thread reads before any writes, so out and lse may be o1/o2 and lse1/lse2
+__global__ __launch_bounds__(256) void merge_kernel(const float4 *o1, const float *lse1, const float4 *o2,
+                                                    const float *lse2, int64_t rows, float4 *out, float *lse) {
+  const int64_t r = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int d4 = threadIdx.x & 31;
+  float l1 = -INFINITY, l2 = -INFINITY;
+  float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f), x2 = x1;
+  if (r < rows) {
+    l1 = lse1[r];
+    l2 = lse2[r];
+    x1 = o1[r * 32 + d4];
+    x2 = o2[r * 32 + d4];
+  }
+  __syncthreads();
+  if (r >= rows) return;
+  const float m = fmaxf(l1, l2);
+  if (m == -INFINITY) {
+    out[r * 32 + d4] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (d4 == 0) lse[r] = -INFINITY;
+    return;
+  }
+  const float w1 = expf(l1 - m), w2 = expf(l2 - m), z = w1 + w2, iz = 1.f / z;
+  out[r * 32 + d4] = make_float4((x1.x * w1 + x2.x * w2) * iz, (x1.y * w1 + x2.y * w2) * iz,
+                                 (x1.z * w1 + x2.z * w2) * iz, (x1.w * w1 + x2.w * w2) * iz);
+  if (d4 == 0) lse[r] = m + logf(z);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s) {
@@ -323,6 +469,34 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s) {
   c.items = (int32_t)items;
   const int64_t grid = (items + 7) / 8 * 8;   // a multiple of the XCD count
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel
+
+namespace kvsel {
+
+hipError_t launch_shared(const SharedArgs &a, hipStream_t s) {
+  if (a.group < 1 || a.batch < 1 || a.hkv < 1 || a.row_begin < 0 || a.row_end < a.row_begin) return hipErrorInvalidValue;
+  if (a.row_end > a.row_begin && ((a.row_end - 1) >> 4) - (a.row_begin >> 4) + 1 > kSharedMaxBlocks)
+    return hipErrorInvalidValue;
+  SharedArgs c = a;
+  c.nblk = (int32_t)(((int64_t)a.batch * a.group + kPRows - 1) / kPRows);
+  const int64_t items = (int64_t)c.nblk * a.hkv;
+  if (items >= 0x7ffffff0ll) return hipErrorInvalidValue;
+  c.items = (int32_t)items;
+  const int64_t grid = (items + 7) / 8 * 8;   // a multiple of the XCD count
+  hipLaunchKernelGGL(shared_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, s, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
+                        float *out, float *lse, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + 7) / 8;
+  if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4 *>(o1), lse1,
+                     reinterpret_cast<const float4 *>(o2), lse2, rows, reinterpret_cast<float4 *>(out), lse);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ SYMBOLS = (
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
     "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
     "kvsel_pool_alloc", "kvsel_pool_retain", "kvsel_pool_release", "kvsel_fork",
-    "kvsel_verify_attn", "kvsel_prefill_attn",
+    "kvsel_verify_attn", "kvsel_prefill_attn", "kvsel_shared_attn", "kvsel_merge_attn",
 )
 
 
@@ -113,6 +113,10 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = [_P, _P, _I32] if fn is not L.kvsel_pool_alloc else [_P, _I32, _P]
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
+    L.kvsel_shared_attn.restype = _I32
+    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _F32, _I32, _I32, _P, _P, _P]
+    L.kvsel_merge_attn.restype = _I32
+    L.kvsel_merge_attn.argtypes = [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P]
     L.kvsel_prefill_attn.restype = _I32
     L.kvsel_prefill_attn.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P]
     L.kvsel_fork.restype = _I32
@@ -352,6 +356,32 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
         raise ValueError("q [total, hq, 128], k and v [total, hkv, 128]")
     _check(lib().kvsel_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, max_seqlen,
                                     q.shape[1], k.shape[1], scale, _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_begin: int, row_end: int,
+                out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_shared_attn.  q: bf16 [batch][hq][128]; out: fp32 [batch][hq][128]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), num_q_heads, scale, row_begin, row_end, _ptr(out), _ptr(lse),
+                                   _stream(stream)))
+    return out
+
+
+def merge_attn(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor, out: torch.Tensor,
+               lse: torch.Tensor, stream=None):
+    """kvsel_merge_attn over rows = lse1.numel() (out may be o1 or o2)."""
+    for t, name in ((o1, "o1"), (lse1, "lse1"), (o2, "o2"), (lse2, "lse2"), (out, "out"), (lse, "lse")):
+        _need(t, torch.float32, name)
+    rows = lse1.numel()
+    if o1.numel() != rows * 128 or o2.numel() != rows * 128 or out.numel() != rows * 128 or \
+            lse2.numel() != rows or lse.numel() != rows:
+        raise ValueError("o1, o2, out: [rows][128]; lse1, lse2, lse: [rows]")
+    _check(lib().kvsel_merge_attn(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, _ptr(out), _ptr(lse),
+                                  _stream(stream)))
     return out
 
 

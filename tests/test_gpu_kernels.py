@@ -545,3 +545,82 @@ def test_prefill_attention_propagated_tokens():
     gl = lse.cpu().numpy()
     assert_attn(np.stack([got[i, h] for i, h in rows]), ref, "prefill full")
     assert np.abs(np.array([gl[i, h] for i, h in rows]) - rl).max() < 1e-4
+
+
+def _shared_prefix_kv(rng, batch, hkv, prefix_len, suffix_max):
+    """A paged cache whose sequences share their first prefix_len rows (the
+    same blocks, placed at random), each with a private suffix."""
+    from synth.gen import shared_prefix_table
+    kvsel = K()
+    pb = -(-prefix_len // 16)
+    suffix = rng.integers(1, suffix_max + 1, size=batch)
+    table, nb = shared_prefix_table(pb, -(-suffix // 16))
+    perm = rng.permutation(nb + 2).astype(np.int32)    # scatter the blocks over a slightly larger pool
+    table = perm[table]
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    kp = torch.randn((nb + 2, hkv, 16, 128), generator=g).to(torch.bfloat16).to(DEV)
+    vp = torch.randn((nb + 2, hkv, 16, 128), generator=g).to(torch.bfloat16).to(DEV)
+    lens = (pb * 16 + suffix).astype(np.int32)
+    zeros = torch.zeros(batch, dtype=torch.int32, device=DEV)
+    kv = kvsel.KV(kp, vp, torch.from_numpy(table).to(DEV), torch.from_numpy(lens).to(DEV), zeros, zeros,
+                  max_seq_len=int(lens.max()), max_seg_len=0, min_seg_len=0, shared_rows=prefix_len)
+    return kv, cpu_pool(kp), cpu_pool(vp), table, lens
+
+
+# (G, batch, prefix rows, [row_begin, row_end)): ranges not on block edges,
+# several 128-row query blocks with a ragged last one, an empty range
+SHARED_CASES = [(2, 5, 160, (37, 160)), (1, 3, 64, (0, 64)), (4, 70, 1024, (300, 1024)), (8, 20, 96, (5, 90)),
+                (2, 9, 48, (10, 10)), (2, 600, 256, (64, 250))]
+
+
+@pytest.mark.parametrize("G,batch,prefix,rng_rows", SHARED_CASES)
+def test_shared_attention(G, batch, prefix, rng_rows):
+    kvsel = K()
+    rng = np.random.default_rng(3000 + G * 11 + batch)
+    hkv = 2
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 40)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
+    out = torch.full((batch, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((batch, hq), float("nan"), dtype=torch.float32, device=DEV)
+    rb, re = rng_rows
+    log_case("shared", G, batch, prefix, rb, re)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, out, lse)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    check = range(batch) if batch <= 20 else rng.choice(batch, size=20, replace=False)
+    for b in check:
+        for g in range(hkv):
+            got = out[b, g * G:(g + 1) * G].cpu().numpy()
+            gl = lse[b, g * G:(g + 1) * G].cpu().numpy()
+            if re == rb:
+                assert np.all(got == 0) and np.all(np.isneginf(gl))
+                continue
+            Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+            Vl = O.logical_rows(vc, table[b], g, int(lens[b]))
+            ref, rl = O.attention(O.widen(qc[b, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
+            assert_attn(got, ref, f"shared b{b} g{g}")
+            assert np.abs(gl - rl).max() < 1e-4
+
+
+@pytest.mark.parametrize("rows,inplace", [(1, False), (37, False), (1000, True)])
+def test_merge_attention(rows, inplace):
+    kvsel = K()
+    g = torch.Generator().manual_seed(rows)
+    o1 = torch.randn((rows, 128), generator=g)
+    o2 = torch.randn((rows, 128), generator=g)
+    l1 = torch.randn(rows, generator=g) * 3
+    l2 = torch.randn(rows, generator=g) * 3
+    l1[::7] = float("-inf")           # some rows with one empty part
+    l2[::11] = float("-inf")          # and some with both (row 0)
+    ref, rl = O.merge_attention(o1.numpy(), l1.numpy(), o2.numpy(), l2.numpy())
+    d1, d2, e1, e2 = o1.to(DEV), o2.to(DEV), l1.to(DEV), l2.to(DEV)
+    out, lse = (d2, e2) if inplace else (torch.empty_like(d1), torch.empty_like(e1))
+    log_case("merge", rows, inplace)
+    kvsel.merge_attn(d1, e1, d2, e2, out, lse)
+    torch.cuda.synchronize()
+    got, gl = out.cpu().numpy(), lse.cpu().numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(gl[fin], rl[fin], rtol=1e-6, atol=1e-5)
+    assert np.all(np.isneginf(gl[~fin])) and np.all(got[~fin] == 0)
