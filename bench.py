@@ -464,7 +464,9 @@ def bench_c4(args):
                     max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
                     shared_rows=cfg.prefix_len)
            for l in range(cfg.layers)]
-    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device="cuda")
+    # sparse layers: the shared layout rows once per kv head for all branches, merged with each branch's own rows
+    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device="cuda",
+                       shared_tail=(cfg.n_visual, cfg.prefix_len))
     T = cfg.steps
     ms = _timed(lambda i: dec.step(i % T, w.q[i % T], w.seq_len[i % T]), args.steps, args.warmup)
     suf = w.suffix_len.astype(np.int64)

@@ -343,7 +343,8 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
 }
 
 kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
-                               int32_t row_begin, int32_t row_end, float *out, float *lse, kvsel_stream stream) {
+                               int32_t row_begin, int32_t row_end, int32_t splits, float *out, float *lse,
+                               kvsel_stream stream) {
   kvsel_status st;
   int G;
   if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
@@ -357,6 +358,8 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
                 kv->shared_rows);
   if (row_end > row_begin && ((row_end - 1) >> 4) - (row_begin >> 4) + 1 > kSharedMaxBlocks)
     return fail(KVSEL_EUNSUPPORTED, "the range touches more than %d cache blocks", kSharedMaxBlocks);
+  if (splits < 1 || splits > kMaxMergeParts) return fail(KVSEL_EINVAL, "splits must be in [1, %d]", kMaxMergeParts);
+  if (splits > 1 && lse == nullptr) return fail(KVSEL_EINVAL, "lse is required with splits > 1");
   SharedArgs a{};
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
@@ -368,6 +371,7 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   a.batch = kv->batch;
   a.row_begin = row_begin;
   a.row_end = row_end;
+  a.splits = splits;
   a.q = q;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
@@ -375,14 +379,14 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   return hip_status(launch_shared(a, (hipStream_t)stream), "shared_attn launch");
 }
 
-kvsel_status kvsel_merge_attn(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
-                              float *out, float *lse, kvsel_stream stream) {
-  if (o1 == nullptr || lse1 == nullptr || o2 == nullptr || lse2 == nullptr || out == nullptr || lse == nullptr)
-    return fail(KVSEL_EINVAL, "o1, lse1, o2, lse2, out and lse are required");
-  if (!aligned(o1, 16) || !aligned(o2, 16) || !aligned(out, 16))
-    return fail(KVSEL_EINVAL, "o1, o2 and out must be 16-byte aligned");
+kvsel_status kvsel_merge_attn(const float *o, const float *lse, int32_t parts, int64_t rows, float *out,
+                              float *lse_out, kvsel_stream stream) {
+  if (o == nullptr || lse == nullptr || out == nullptr || lse_out == nullptr)
+    return fail(KVSEL_EINVAL, "o, lse, out and lse_out are required");
+  if (!aligned(o, 16) || !aligned(out, 16)) return fail(KVSEL_EINVAL, "o and out must be 16-byte aligned");
+  if (parts < 1 || parts > kMaxMergeParts) return fail(KVSEL_EINVAL, "parts must be in [1, %d]", kMaxMergeParts);
   if (rows < 0) return fail(KVSEL_EINVAL, "rows must be >= 0");
-  return hip_status(launch_merge(o1, lse1, o2, lse2, rows, out, lse, (hipStream_t)stream), "merge_attn launch");
+  return hip_status(launch_merge(o, lse, parts, rows, out, lse_out, (hipStream_t)stream), "merge_attn launch");
 }
 
 size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_heads) {

@@ -43,15 +43,17 @@ struct SharedArgs {
   int64_t num_blocks;
   int32_t hkv, hq, group, batch;
   int32_t row_begin, row_end;
+  int32_t splits, chunk;         // the range in `splits` parts of `chunk` rows (a multiple of 64)
   const uint16_t *q;             // [batch][hq][128]
   float scale_log2;
-  float *out, *lse;              // [batch][hq][128], [batch][hq]
+  float *out, *lse;              // [splits][batch][hq][128], [splits][batch][hq]
   int32_t nblk, items;           // set by launch_shared
 };
 hipError_t launch_shared(const SharedArgs &a, hipStream_t s);
 
-// out = attention over the union of two disjoint row sets from the two parts
-hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
-                        float *out, float *lse, hipStream_t s);
+// out = attention over the union of `parts` disjoint row sets from the parts
+constexpr int kMaxMergeParts = 64;
+hipError_t launch_merge(const float *o, const float *lse, int parts, int64_t rows, float *out, float *lse_out,
+                        hipStream_t s);
 
 }  // namespace kvsel

@@ -341,9 +341,13 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   __shared__ int32_t s_tab[kSharedMaxBlocks];
 
   const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
-  const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run: one kv head's row blocks together
+  const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run: one kv head's work together
   if (w >= (uint32_t)a.items) return;
-  const int blk = (int)(w % (uint32_t)a.nblk), g = (int)(w / (uint32_t)a.nblk);
+  const int blk = (int)(w % (uint32_t)a.nblk);
+  const int part = (int)((w / (uint32_t)a.nblk) % (uint32_t)a.splits);
+  const int g = (int)(w / ((uint32_t)a.nblk * (uint32_t)a.splits));
+  const int r0 = min(a.row_end, a.row_begin + part * a.chunk);   // this part's rows [r0, r1)
+  const int r1 = min(a.row_end, r0 + a.chunk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int G = a.group;
@@ -351,8 +355,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   const int row0 = blk * kPRows;
   if (row0 >= nrows) return;   // the whole work-group
 
-  const int first = a.row_begin >> 4;
-  const int nb = a.row_end > a.row_begin ? ((a.row_end - 1) >> 4) - first + 1 : 0;
+  const int first = r0 >> 4;
+  const int nb = r1 > r0 ? ((r1 - 1) >> 4) - first + 1 : 0;
   for (int i = tid; i < nb; i += kPThreads) s_tab[i] = a.table[first + i];
 
   const int rr = row0 + wave * 32 + col;
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   // a row's bytes, or the queries (valid memory) for a row outside the range
   // or in an invalid block; those keys are masked
   auto row_ok = [&](int key, int32_t &blk_id) {
-    if (key >= a.row_end) return false;
+    if (key >= r1) return false;
     blk_id = s_tab[(key >> 4) - first];
     return blk_id >= 0 && (int64_t)blk_id < a.num_blocks;
   };
@@ -399,12 +403,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
 
-  Stage st = fetch_tile(a.row_begin);
-  for (int t0 = a.row_begin; t0 < a.row_end; t0 += kBN) {
+  Stage st = fetch_tile(r0);
+  for (int t0 = r0; t0 < r1; t0 += kBN) {
     __syncthreads();   // the previous tile's reads are done
     stash(st, s_k, s_vt, tid);
     __syncthreads();
-    if (t0 + kBN < a.row_end) st = fetch_tile(t0 + kBN);
+    if (t0 + kBN < r1) st = fetch_tile(t0 + kBN);
     int32_t bi = 0;
     const uint64_t vmask = __ballot(row_ok(t0 + lane, bi));   // bit i: key t0 + i is attended
     attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_live || vmask != ~0ull,
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 
   const float lrow = half_pair_sum(lsum);
   if (!live) return;
-  const size_t orow = (size_t)b * a.hq + g * G + h;
+  const size_t orow = ((size_t)part * a.batch + b) * a.hq + g * G + h;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
   float *o = a.out + orow * kD;
 #pragma unroll
@@ -431,31 +435,37 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 }
 
 // eight (sequence, head) rows per work-group, 32 threads of 4 floats per row;
-// every thread reads before any writes, so out and lse may be o1/o2 and lse1/lse2
-__global__ __launch_bounds__(256) void merge_kernel(const float4 *o1, const float *lse1, const float4 *o2,
-                                                    const float *lse2, int64_t rows, float4 *out, float *lse) {
+// every thread reads all its parts before any thread writes, so out and
+// lse_out may be one of the parts (in place)
+__global__ __launch_bounds__(256) void merge_kernel(const float4 *o, const float *lse, int parts, int64_t rows,
+                                                    float4 *out, float *lse_out) {
   const int64_t r = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int d4 = threadIdx.x & 31;
-  float l1 = -INFINITY, l2 = -INFINITY;
-  float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f), x2 = x1;
-  if (r < rows) {
-    l1 = lse1[r];
-    l2 = lse2[r];
-    x1 = o1[r * 32 + d4];
-    x2 = o2[r * 32 + d4];
-  }
+  float m = -INFINITY;
+  if (r < rows)
+    for (int p = 0; p < parts; ++p) m = fmaxf(m, lse[(size_t)p * rows + r]);
+  float z = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (r < rows && m != -INFINITY)
+    for (int p = 0; p < parts; ++p) {
+      const float wp = expf(lse[(size_t)p * rows + r] - m);   // 0 for an empty part
+      const float4 x = o[((size_t)p * rows + r) * 32 + d4];
+      z += wp;
+      acc.x += x.x * wp;
+      acc.y += x.y * wp;
+      acc.z += x.z * wp;
+      acc.w += x.w * wp;
+    }
   __syncthreads();
   if (r >= rows) return;
-  const float m = fmaxf(l1, l2);
   if (m == -INFINITY) {
     out[r * 32 + d4] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (d4 == 0) lse[r] = -INFINITY;
+    if (d4 == 0) lse_out[r] = -INFINITY;
     return;
   }
-  const float w1 = expf(l1 - m), w2 = expf(l2 - m), z = w1 + w2, iz = 1.f / z;
-  out[r * 32 + d4] = make_float4((x1.x * w1 + x2.x * w2) * iz, (x1.y * w1 + x2.y * w2) * iz,
-                                 (x1.z * w1 + x2.z * w2) * iz, (x1.w * w1 + x2.w * w2) * iz);
-  if (d4 == 0) lse[r] = m + logf(z);
+  const float iz = 1.f / z;
+  out[r * 32 + d4] = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+  if (d4 == 0) lse_out[r] = m + logf(z);
 }
 
 }  // namespace
@@ -477,12 +487,16 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, hipStream_t s) {
 namespace kvsel {
 
 hipError_t launch_shared(const SharedArgs &a, hipStream_t s) {
-  if (a.group < 1 || a.batch < 1 || a.hkv < 1 || a.row_begin < 0 || a.row_end < a.row_begin) return hipErrorInvalidValue;
+  if (a.group < 1 || a.batch < 1 || a.hkv < 1 || a.row_begin < 0 || a.row_end < a.row_begin || a.splits < 1)
+    return hipErrorInvalidValue;
   if (a.row_end > a.row_begin && ((a.row_end - 1) >> 4) - (a.row_begin >> 4) + 1 > kSharedMaxBlocks)
     return hipErrorInvalidValue;
   SharedArgs c = a;
+  // parts of whole 64-row tiles
+  c.chunk = (int32_t)(((int64_t)(a.row_end - a.row_begin) + a.splits * kBN - 1) / (a.splits * kBN) * kBN);
+  if (c.chunk < kBN) c.chunk = kBN;
   c.nblk = (int32_t)(((int64_t)a.batch * a.group + kPRows - 1) / kPRows);
-  const int64_t items = (int64_t)c.nblk * a.hkv;
+  const int64_t items = (int64_t)c.nblk * a.hkv * a.splits;
   if (items >= 0x7ffffff0ll) return hipErrorInvalidValue;
   c.items = (int32_t)items;
   const int64_t grid = (items + 7) / 8 * 8;   // a multiple of the XCD count
@@ -490,13 +504,14 @@ hipError_t launch_shared(const SharedArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const float *o1, const float *lse1, const float *o2, const float *lse2, int64_t rows,
-                        float *out, float *lse, hipStream_t s) {
+hipError_t launch_merge(const float *o, const float *lse, int parts, int64_t rows, float *out, float *lse_out,
+                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (parts < 1 || parts > kMaxMergeParts) return hipErrorInvalidValue;
   const int64_t blocks = (rows + 7) / 8;
   if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4 *>(o1), lse1,
-                     reinterpret_cast<const float4 *>(o2), lse2, rows, reinterpret_cast<float4 *>(out), lse);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const float4 *>(o), lse,
+                     parts, rows, reinterpret_cast<float4 *>(out), lse_out);
   return hipGetLastError();
 }
 

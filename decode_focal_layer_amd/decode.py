@@ -17,7 +17,8 @@ block table.
 from __future__ import annotations
 
 import ctypes
-from typing import List, Optional, Sequence
+import dataclasses
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -26,7 +27,16 @@ from . import kvsel
 
 class FocalDecoder:
     def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, k: int, focal: Sequence[int], scale: float,
-                 seg_len: int, warm_start: bool = True, device="cuda", keep_scores: bool = False):
+                 seg_len: int, warm_start: bool = True, device="cuda", keep_scores: bool = False,
+                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: int = 4):
+        """shared_tail = (row_begin, row_end): every sequence's segment ends
+        at row_begin, and rows [row_begin, row_end) are shared by all of them
+        (the same cache blocks; HPD's layout rows after the shared visual
+        prefix).  Sparse layers then attend in two parts merged exactly: the
+        shared rows once per kv head for all sequences (kvsel_shared_attn),
+        and each sequence's kept rows and rows from row_end on
+        (kvsel_gather_attn with the segment extended to row_end); the shared
+        rows in shared_splits parts, all parts merged by one kvsel_merge_attn."""
         self.kvs = list(kvs)
         self.L = len(self.kvs)
         self.hq = num_q_heads
@@ -54,6 +64,21 @@ class FocalDecoder:
         self.ws_ptr, self.ws_n = self.ws.ptr_and_size(need)
         self.t = 0
         self._lib = kvsel.lib()
+        self.tail = None
+        if shared_tail is not None:
+            rb, re = int(shared_tail[0]), int(shared_tail[1])
+            if not 0 <= rb <= re or any(re > kv.shared_rows for kv in self.kvs):
+                raise ValueError("shared_tail must lie inside the shared rows")
+            ext = torch.full((B,), re, dtype=torch.int32, device=device)
+            # the private part: the segment reaches to row_end, so the shared rows are left out
+            self.priv = [dataclasses.replace(kv, seg_end=ext, max_seg_len=kv.max_seg_len + (re - rb),
+                                             min_seg_len=kv.min_seg_len + (re - rb)) for kv in self.kvs]
+            self.tail = (rb, re)
+            self.splits = int(shared_splits)
+            # part 0: each sequence's own rows; parts 1 .. splits: the shared rows
+            self.parts_o = torch.empty((1 + self.splits, B, num_q_heads, 128), dtype=torch.float32, device=device)
+            self.parts_lse = torch.empty((1 + self.splits, B, num_q_heads), dtype=torch.float32, device=device)
+            self.lse_out = torch.empty((B, num_q_heads), dtype=torch.float32, device=device)
 
     def plan(self, t: int):
         """(kind, src_step_is_previous, src_layer) per layer."""
@@ -94,9 +119,24 @@ class FocalDecoder:
             else:
                 which, ls = src
                 buf = self.idx[ls][cur if which == "cur" else prev]
-                kvsel._check(L.kvsel_gather_attn(kv.ref(), qp, self.hq, self.scale,
-                                                 ctypes.c_void_p(buf.data_ptr()), self.k, op, None,
-                                                 self.ws_ptr, self.ws_n, st))
+                if self.tail is None:
+                    kvsel._check(L.kvsel_gather_attn(kv.ref(), qp, self.hq, self.scale,
+                                                     ctypes.c_void_p(buf.data_ptr()), self.k, op, None,
+                                                     self.ws_ptr, self.ws_n, st))
+                else:
+                    pk = self.priv[l]
+                    pk.c.seq_len = sl
+                    po, pl = self.parts_o, self.parts_lse
+                    kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale,
+                                                     ctypes.c_void_p(buf.data_ptr()), self.k,
+                                                     ctypes.c_void_p(po[0].data_ptr()),
+                                                     ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
+                    kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, self.hq, self.scale, self.tail[0], self.tail[1],
+                                                     self.splits, ctypes.c_void_p(po[1].data_ptr()),
+                                                     ctypes.c_void_p(pl[1].data_ptr()), st))
+                    kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
+                                                    1 + self.splits, self.B * self.hq, op,
+                                                    ctypes.c_void_p(self.lse_out.data_ptr()), st))
             if layer_hook is not None:
                 layer_hook(l, kind, "end")
         self.cur = prev   # this step's selection becomes "previous"

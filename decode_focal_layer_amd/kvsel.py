@@ -114,9 +114,9 @@ def lib() -> ctypes.CDLL:
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_shared_attn.restype = _I32
-    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _F32, _I32, _I32, _P, _P, _P]
+    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _F32, _I32, _I32, _I32, _P, _P, _P]
     L.kvsel_merge_attn.restype = _I32
-    L.kvsel_merge_attn.argtypes = [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P]
+    L.kvsel_merge_attn.argtypes = [_P, _P, _I32, ctypes.c_int64, _P, _P, _P]
     L.kvsel_prefill_attn.restype = _I32
     L.kvsel_prefill_attn.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P]
     L.kvsel_fork.restype = _I32
@@ -360,28 +360,28 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
 
 
 def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_begin: int, row_end: int,
-                out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
-    """kvsel_shared_attn.  q: bf16 [batch][hq][128]; out: fp32 [batch][hq][128]."""
+                out: torch.Tensor, lse: Optional[torch.Tensor] = None, splits: int = 1, stream=None):
+    """kvsel_shared_attn.  q: bf16 [batch][hq][128]; out: fp32 [splits][batch][hq][128]
+    (or [batch][hq][128] when splits = 1); lse: fp32 [splits][batch][hq]."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.float32, "out")
     if lse is not None:
         _need(lse, torch.float32, "lse")
-    _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), num_q_heads, scale, row_begin, row_end, _ptr(out), _ptr(lse),
-                                   _stream(stream)))
+    _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), num_q_heads, scale, row_begin, row_end, splits, _ptr(out),
+                                   _ptr(lse), _stream(stream)))
     return out
 
 
-def merge_attn(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor, out: torch.Tensor,
-               lse: torch.Tensor, stream=None):
-    """kvsel_merge_attn over rows = lse1.numel() (out may be o1 or o2)."""
-    for t, name in ((o1, "o1"), (lse1, "lse1"), (o2, "o2"), (lse2, "lse2"), (out, "out"), (lse, "lse")):
+def merge_attn(o: torch.Tensor, lse: torch.Tensor, out: torch.Tensor, lse_out: torch.Tensor, stream=None):
+    """kvsel_merge_attn.  o: fp32 [parts][rows..][128]; lse: fp32 [parts][rows..];
+    out: fp32 [rows..][128]; lse_out: fp32 [rows..] (out may be a part of o)."""
+    for t, name in ((o, "o"), (lse, "lse"), (out, "out"), (lse_out, "lse_out")):
         _need(t, torch.float32, name)
-    rows = lse1.numel()
-    if o1.numel() != rows * 128 or o2.numel() != rows * 128 or out.numel() != rows * 128 or \
-            lse2.numel() != rows or lse.numel() != rows:
-        raise ValueError("o1, o2, out: [rows][128]; lse1, lse2, lse: [rows]")
-    _check(lib().kvsel_merge_attn(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, _ptr(out), _ptr(lse),
-                                  _stream(stream)))
+    parts = lse.shape[0]
+    rows = lse[0].numel()
+    if o.numel() != parts * rows * 128 or out.numel() != rows * 128 or lse_out.numel() != rows:
+        raise ValueError("o: [parts][rows][128]; lse: [parts][rows]; out: [rows][128]; lse_out: [rows]")
+    _check(lib().kvsel_merge_attn(_ptr(o), _ptr(lse), parts, rows, _ptr(out), _ptr(lse_out), _stream(stream)))
     return out
 
 

@@ -348,27 +348,32 @@ KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, 
  *
  * Rows [row_begin, row_end) must lie inside the shared rows
  * (kv->shared_rows) and be the same cache blocks in every sequence's block
- * table; they are read through sequence 0's.  q: bf16
- * [batch][num_q_heads][128]; out: fp32 [batch][num_q_heads][128],
- * normalised over the range; lse: NULL or fp32 [batch][num_q_heads] (natural
- * log; -inf and out = 0 for an empty range).  q and out 16-byte aligned;
- * scale > 0; the range may touch at most 1024 cache blocks
- * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to +-65504).
- * No workspace.
+ * table; they are read through sequence 0's.  The range is cut into
+ * `splits` parts of whole 64-row tiles (1 .. 64; more parts, more
+ * work-groups), each attended apart: part s writes out[s] and lse[s], to be
+ * combined by kvsel_merge_attn.  q: bf16 [batch][num_q_heads][128]; out:
+ * fp32 [splits][batch][num_q_heads][128], each part normalised over its
+ * rows; lse: fp32 [splits][batch][num_q_heads] (natural log; -inf and out =
+ * 0 for an empty part), NULL allowed when splits = 1.  q and out 16-byte
+ * aligned; scale > 0; the range may touch at most 1024 cache blocks
+ * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to
+ * +-65504).  No workspace.
  */
 KVSEL_API kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
-                                         float scale, int32_t row_begin, int32_t row_end, float *out, float *lse,
-                                         kvsel_stream stream);
+                                         float scale, int32_t row_begin, int32_t row_end, int32_t splits,
+                                         float *out, float *lse, kvsel_stream stream);
 
 /*
- * kvsel_merge_attn -- attention over the union of two disjoint row sets from
- * the attention over each: out = (o1 e^lse1 + o2 e^lse2) / (e^lse1 + e^lse2),
- * lse = log(e^lse1 + e^lse2) (a part with lse = -inf counts for nothing).
- * o1, o2, out: fp32 [rows][128], 16-byte aligned; lse1, lse2, lse: fp32
- * [rows].  out may be o1 or o2 and lse may be lse1 or lse2 (in place).
+ * kvsel_merge_attn -- attention over the union of `parts` disjoint row sets
+ * from the attention over each: out = sum_p o[p] e^lse[p] / sum_p e^lse[p],
+ * lse_out = log sum_p e^lse[p] (a part with lse = -inf counts for nothing;
+ * all empty gives out = 0, lse_out = -inf).  o: fp32 [parts][rows][128] and
+ * out: fp32 [rows][128], 16-byte aligned; lse: fp32 [parts][rows]; lse_out:
+ * fp32 [rows]; 1 <= parts <= 64.  out may be one of the parts of o and
+ * lse_out one of the parts of lse (in place).
  */
-KVSEL_API kvsel_status kvsel_merge_attn(const float *o1, const float *lse1, const float *o2, const float *lse2,
-                                        int64_t rows, float *out, float *lse, kvsel_stream stream);
+KVSEL_API kvsel_status kvsel_merge_attn(const float *o, const float *lse, int32_t parts, int64_t rows, float *out,
+                                        float *lse_out, kvsel_stream stream);
 
 /*
  * Branch lifecycle: a reference-counted block pool (host side) and the fork

@@ -88,13 +88,13 @@ def test_c0_full():
     print("patch tokens among the kept:", hits, "of", 8 * len(patch))
 
 
-def run_schedule(cfg, w, check_every=1):
+def run_schedule(cfg, w, check_every=1, **dec_kw):
     """Run all steps through FocalDecoder; check every layer of every step."""
     from decode_focal_layer_amd.decode import FocalDecoder
     kv = kvsel()
     kvs = focal_kvs(w)
     dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, warm_start=cfg.warm_start,
-                       device=DEV)
+                       device=DEV, **dec_kw)
     kc = [w.k_pool[l].cpu() for l in range(cfg.layers)]
     vc = [w.v_pool[l].cpu() for l in range(cfg.layers)]
     G = cfg.group
@@ -139,6 +139,17 @@ def test_c1_schedule_small():
     cfg = synth.small(synth.C1, batch=3, layers=6, steps=4, focal=(2, 4), grid_rows=12, grid_cols=32, n_always=80)
     w = gen.make_focal(cfg, DEV)
     run_schedule(cfg, w)
+
+
+def test_c4_branches_small_cascade():
+    """The branched decode with sparse layers split into the shared layout
+    rows (once per kv head for all branches) and each branch's own rows,
+    merged: every layer of every step against the oracle's attention over
+    the union."""
+    cfg = synth.small(synth.C4, batch=150, layers=4, steps=2, focal=(1, 2), grid_rows=8, grid_cols=32,
+                      n_always=48, suffix_range=(3, 40))
+    w = gen.make_focal(cfg, DEV)
+    run_schedule(cfg, w, check_every=1, shared_tail=(cfg.n_visual, cfg.prefix_len))
 
 
 def test_c4_branches_small_and_shared_prefix_equals_private_copy():

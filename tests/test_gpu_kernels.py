@@ -567,26 +567,31 @@ def _shared_prefix_kv(rng, batch, hkv, prefix_len, suffix_max):
     return kv, cpu_pool(kp), cpu_pool(vp), table, lens
 
 
-# (G, batch, prefix rows, [row_begin, row_end)): ranges not on block edges,
-# several 128-row query blocks with a ragged last one, an empty range
-SHARED_CASES = [(2, 5, 160, (37, 160)), (1, 3, 64, (0, 64)), (4, 70, 1024, (300, 1024)), (8, 20, 96, (5, 90)),
-                (2, 9, 48, (10, 10)), (2, 600, 256, (64, 250))]
+# (G, batch, prefix rows, [row_begin, row_end), parts): ranges not on block
+# edges, several 128-row query blocks with a ragged last one, an empty range,
+# parts of the range (some empty)
+SHARED_CASES = [(2, 5, 160, (37, 160), 1), (1, 3, 64, (0, 64), 1), (4, 70, 1024, (300, 1024), 4),
+                (8, 20, 96, (5, 90), 3), (2, 9, 48, (10, 10), 1), (2, 600, 256, (64, 250), 2), (1, 4, 128, (0, 100), 5)]
 
 
-@pytest.mark.parametrize("G,batch,prefix,rng_rows", SHARED_CASES)
-def test_shared_attention(G, batch, prefix, rng_rows):
+@pytest.mark.parametrize("G,batch,prefix,rng_rows,splits", SHARED_CASES)
+def test_shared_attention(G, batch, prefix, rng_rows, splits):
     kvsel = K()
     rng = np.random.default_rng(3000 + G * 11 + batch)
     hkv = 2
     hq = hkv * G
     kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 40)
     q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
-    out = torch.full((batch, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
-    lse = torch.full((batch, hq), float("nan"), dtype=torch.float32, device=DEV)
+    parts = torch.full((splits, batch, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    plse = torch.full((splits, batch, hq), float("nan"), dtype=torch.float32, device=DEV)
     rb, re = rng_rows
-    log_case("shared", G, batch, prefix, rb, re)
-    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, out, lse)
+    log_case("shared", G, batch, prefix, rb, re, splits)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, parts, plse, splits=splits)
+    out = torch.empty((batch, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=DEV)
+    kvsel.merge_attn(parts, plse, out, lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(parts).any() and not torch.isnan(plse).any()   # every part written
     qc = q.cpu()
     check = range(batch) if batch <= 20 else rng.choice(batch, size=20, replace=False)
     for b in check:
@@ -603,21 +608,24 @@ def test_shared_attention(G, batch, prefix, rng_rows):
             assert np.abs(gl - rl).max() < 1e-4
 
 
-@pytest.mark.parametrize("rows,inplace", [(1, False), (37, False), (1000, True)])
-def test_merge_attention(rows, inplace):
+@pytest.mark.parametrize("rows,parts,inplace", [(1, 2, False), (37, 2, False), (1000, 2, True), (300, 5, True),
+                                                (9, 1, False)])
+def test_merge_attention(rows, parts, inplace):
+    """N parts against the oracle's pairwise merges folded left."""
     kvsel = K()
-    g = torch.Generator().manual_seed(rows)
-    o1 = torch.randn((rows, 128), generator=g)
-    o2 = torch.randn((rows, 128), generator=g)
-    l1 = torch.randn(rows, generator=g) * 3
-    l2 = torch.randn(rows, generator=g) * 3
-    l1[::7] = float("-inf")           # some rows with one empty part
-    l2[::11] = float("-inf")          # and some with both (row 0)
-    ref, rl = O.merge_attention(o1.numpy(), l1.numpy(), o2.numpy(), l2.numpy())
-    d1, d2, e1, e2 = o1.to(DEV), o2.to(DEV), l1.to(DEV), l2.to(DEV)
-    out, lse = (d2, e2) if inplace else (torch.empty_like(d1), torch.empty_like(e1))
-    log_case("merge", rows, inplace)
-    kvsel.merge_attn(d1, e1, d2, e2, out, lse)
+    g = torch.Generator().manual_seed(rows + parts)
+    o = torch.randn((parts, rows, 128), generator=g)
+    ls = torch.randn((parts, rows), generator=g) * 3
+    for p in range(parts):
+        ls[p, p::7] = float("-inf")    # some rows with empty parts
+    ls[:, 0] = float("-inf")           # a row with every part empty
+    ref, rl = np.zeros((rows, 128)), np.full(rows, -np.inf)   # the empty set, then every part merged in
+    for p in range(parts):
+        ref, rl = O.merge_attention(ref, rl, o[p].numpy(), ls[p].numpy())
+    do, dl = o.to(DEV), ls.to(DEV)
+    out, lse = (do[parts - 1], dl[parts - 1]) if inplace else (torch.empty_like(do[0]), torch.empty_like(dl[0]))
+    log_case("merge", rows, parts, inplace)
+    kvsel.merge_attn(do, dl, out, lse)
     torch.cuda.synchronize()
     got, gl = out.cpu().numpy(), lse.cpu().numpy()
     np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
