@@ -517,10 +517,14 @@ def bench_verify(args):
     out = torch.empty((cfg.batch, m, cfg.hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device="cuda")
 
+    from decode_focal_layer_amd.decode import DraftVerifier
+    # the shared layout rows once per kv head for every draft of every branch, merged with each branch's own rows
+    vers = [DraftVerifier(kv, m, cfg.hq, cfg.scale, shared_tail=(cfg.n_visual, cfg.prefix_len)) for kv in kvs]
+
     def step(i):
         q = qs[i % len(qs)]
         for l in range(cfg.layers):
-            kvsel.verify_attn(kvs[l], q, m, cfg.hq, cfg.scale, idx, cfg.k, out, lse)
+            vers[l].verify(q, idx, cfg.k, out, lse)
 
     ms = _timed(step, args.steps, args.warmup)
     rows = int((cfg.k + n_np - cfg.n_visual).sum())             # kept + layout + suffix (drafts included)

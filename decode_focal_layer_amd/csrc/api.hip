@@ -342,9 +342,9 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
   return hip_status(launch_prefill(a, batch, (hipStream_t)stream), "prefill_attn launch");
 }
 
-kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
-                               int32_t row_begin, int32_t row_end, int32_t splits, float *out, float *lse,
-                               kvsel_stream stream) {
+kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq, int32_t num_q_heads,
+                               float scale, int32_t row_begin, int32_t row_end, int32_t splits, float *out,
+                               float *lse, kvsel_stream stream) {
   kvsel_status st;
   int G;
   if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
@@ -360,6 +360,8 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
     return fail(KVSEL_EUNSUPPORTED, "the range touches more than %d cache blocks", kSharedMaxBlocks);
   if (splits < 1 || splits > kMaxMergeParts) return fail(KVSEL_EINVAL, "splits must be in [1, %d]", kMaxMergeParts);
   if (splits > 1 && lse == nullptr) return fail(KVSEL_EINVAL, "lse is required with splits > 1");
+  if (q_per_seq < 1 || (int64_t)kv->batch * q_per_seq * G > 0x7fffff00ll)
+    return fail(KVSEL_EINVAL, "q_per_seq must be >= 1 (and batch * q_per_seq * group < 2^31)");
   SharedArgs a{};
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
@@ -368,7 +370,7 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   a.hkv = kv->num_kv_heads;
   a.hq = num_q_heads;
   a.group = G;
-  a.batch = kv->batch;
+  a.batch = kv->batch * q_per_seq;   // every query of every sequence sees the same shared rows
   a.row_begin = row_begin;
   a.row_end = row_end;
   a.splits = splits;

@@ -131,8 +131,8 @@ class FocalDecoder:
                                                      ctypes.c_void_p(buf.data_ptr()), self.k,
                                                      ctypes.c_void_p(po[0].data_ptr()),
                                                      ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
-                    kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, self.hq, self.scale, self.tail[0], self.tail[1],
-                                                     self.splits, ctypes.c_void_p(po[1].data_ptr()),
+                    kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, 1, self.hq, self.scale, self.tail[0],
+                                                     self.tail[1], self.splits, ctypes.c_void_p(po[1].data_ptr()),
                                                      ctypes.c_void_p(pl[1].data_ptr()), st))
                     kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
                                                     1 + self.splits, self.B * self.hq, op,
@@ -186,3 +186,56 @@ class FocalProfiler:
     def pick(self, n_focal: int, stream=None) -> torch.Tensor:
         """The n_focal layers with the highest mean ratio, ascending (int32, device)."""
         return kvsel.pick_layers(self.ratios, n_focal, self.layers[:n_focal], stream=stream)
+
+
+class DraftVerifier:
+    """Verification attention of m drafts per sequence (HPD-Parsing wiki,
+    P-MTP) over one layer's cache.  With shared_tail = (row_begin, row_end)
+    -- every sequence's segment ends at row_begin and rows [row_begin,
+    row_end) are the same cache blocks in every table -- it runs as a
+    cascade: each sequence's own rows (kvsel_verify_attn with the segment
+    extended to row_end), the shared rows once per kv head for every draft of
+    every sequence (kvsel_shared_attn), and one exact merge
+    (kvsel_merge_attn)."""
+
+    def __init__(self, kv: kvsel.KV, m: int, num_q_heads: int, scale: float,
+                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: int = 4, device="cuda"):
+        self.kv, self.m, self.hq, self.scale = kv, int(m), num_q_heads, float(scale)
+        B = kv.batch
+        self.tail = None
+        if shared_tail is not None:
+            rb, re = int(shared_tail[0]), int(shared_tail[1])
+            if not 0 <= rb <= re or re > kv.shared_rows:
+                raise ValueError("shared_tail must lie inside the shared rows")
+            ext = torch.full((B,), re, dtype=torch.int32, device=device)
+            self.priv = dataclasses.replace(kv, seg_end=ext, max_seg_len=kv.max_seg_len + (re - rb),
+                                            min_seg_len=kv.min_seg_len + (re - rb))
+            self.tail = (rb, re)
+            self.splits = int(shared_splits)
+            self.parts_o = torch.empty((1 + self.splits, B, self.m, num_q_heads, 128), dtype=torch.float32,
+                                       device=device)
+            self.parts_lse = torch.empty((1 + self.splits, B, self.m, num_q_heads), dtype=torch.float32,
+                                         device=device)
+            self.lse_out = torch.empty((B, self.m, num_q_heads), dtype=torch.float32, device=device)
+
+    def verify(self, q: torch.Tensor, idx: Optional[torch.Tensor], k: int, out: torch.Tensor,
+               lse: Optional[torch.Tensor] = None, stream=None):
+        """q: bf16 [B][m][hq][128]; out: fp32 [B][m][hq][128]."""
+        if self.tail is None:
+            return kvsel.verify_attn(self.kv, q, self.m, self.hq, self.scale, idx, k, out, lse, stream=stream)
+        L = kvsel.lib()
+        st = kvsel._stream(stream)
+        self.priv.c.seq_len = self.kv.c.seq_len
+        po, pl = self.parts_o, self.parts_lse
+        qp = ctypes.c_void_p(q.data_ptr())
+        kvsel._check(L.kvsel_verify_attn(self.priv.ref(), qp, self.m, self.hq, self.scale,
+                                         ctypes.c_void_p(idx.data_ptr()) if idx is not None else None, k,
+                                         ctypes.c_void_p(po[0].data_ptr()), ctypes.c_void_p(pl[0].data_ptr()), st))
+        kvsel._check(L.kvsel_shared_attn(self.kv.ref(), qp, self.m, self.hq, self.scale, self.tail[0], self.tail[1],
+                                         self.splits, ctypes.c_void_p(po[1].data_ptr()),
+                                         ctypes.c_void_p(pl[1].data_ptr()), st))
+        lo = lse if lse is not None else self.lse_out
+        kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
+                                        1 + self.splits, self.kv.batch * self.m * self.hq,
+                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lo.data_ptr()), st))
+        return out

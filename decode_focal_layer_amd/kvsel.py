@@ -114,7 +114,7 @@ def lib() -> ctypes.CDLL:
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_shared_attn.restype = _I32
-    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _F32, _I32, _I32, _I32, _P, _P, _P]
+    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _P]
     L.kvsel_merge_attn.restype = _I32
     L.kvsel_merge_attn.argtypes = [_P, _P, _I32, ctypes.c_int64, _P, _P, _P]
     L.kvsel_prefill_attn.restype = _I32
@@ -360,15 +360,16 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
 
 
 def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_begin: int, row_end: int,
-                out: torch.Tensor, lse: Optional[torch.Tensor] = None, splits: int = 1, stream=None):
-    """kvsel_shared_attn.  q: bf16 [batch][hq][128]; out: fp32 [splits][batch][hq][128]
-    (or [batch][hq][128] when splits = 1); lse: fp32 [splits][batch][hq]."""
+                out: torch.Tensor, lse: Optional[torch.Tensor] = None, splits: int = 1, q_per_seq: int = 1,
+                stream=None):
+    """kvsel_shared_attn.  q: bf16 [batch][q_per_seq][hq][128]; out: fp32
+    [splits][batch][q_per_seq][hq][128]; lse: fp32 [splits][batch][q_per_seq][hq]."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.float32, "out")
     if lse is not None:
         _need(lse, torch.float32, "lse")
-    _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), num_q_heads, scale, row_begin, row_end, splits, _ptr(out),
-                                   _ptr(lse), _stream(stream)))
+    _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), q_per_seq, num_q_heads, scale, row_begin, row_end, splits,
+                                   _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

@@ -351,17 +351,19 @@ KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, 
  * table; they are read through sequence 0's.  The range is cut into
  * `splits` parts of whole 64-row tiles (1 .. 64; more parts, more
  * work-groups), each attended apart: part s writes out[s] and lse[s], to be
- * combined by kvsel_merge_attn.  q: bf16 [batch][num_q_heads][128]; out:
- * fp32 [splits][batch][num_q_heads][128], each part normalised over its
- * rows; lse: fp32 [splits][batch][num_q_heads] (natural log; -inf and out =
+ * combined by kvsel_merge_attn.  q: bf16 [batch][q_per_seq][num_q_heads][128]
+ * (q_per_seq queries per sequence: 1 for a decode step, m for m drafts);
+ * out: fp32 [splits][batch][q_per_seq][num_q_heads][128], each part
+ * normalised over its rows; lse: fp32 [splits][batch][q_per_seq][num_q_heads]
+ * (natural log; -inf and out =
  * 0 for an empty part), NULL allowed when splits = 1.  q and out 16-byte
  * aligned; scale > 0; the range may touch at most 1024 cache blocks
  * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to
  * +-65504).  No workspace.
  */
-KVSEL_API kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
-                                         float scale, int32_t row_begin, int32_t row_end, int32_t splits,
-                                         float *out, float *lse, kvsel_stream stream);
+KVSEL_API kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq,
+                                         int32_t num_q_heads, float scale, int32_t row_begin, int32_t row_end,
+                                         int32_t splits, float *out, float *lse, kvsel_stream stream);
 
 /*
  * kvsel_merge_attn -- attention over the union of `parts` disjoint row sets

@@ -258,12 +258,14 @@ def test_c4_full_sampled():
                 assert_attn(outs[t][l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
 
 
-def test_c4_verify_full_sampled():
+@pytest.mark.parametrize("cascade", [False, True])
+def test_c4_verify_full_sampled(cascade):
     """Draft verification at the benchmark's size: 512 branches over the C4
     cache (shared 3072 + 1024 prefix, suffix U[32,1024] + 32 appended rows),
     8 drafts, 154 kept visual rows per kv head, the launch the benchmark times
-    (one layer here).  Checked: 24 sampled (branch, kv head) pairs, every
-    draft and head, against the oracle."""
+    (one layer here), directly and as the cascade (the shared layout rows
+    once for all drafts).  Checked: 24 sampled (branch, kv head) pairs,
+    every draft and head, against the oracle."""
     from decode_focal_layer_amd import kvsel
     cfg = synth.small(synth.C4, layers=1)
     m = 8
@@ -280,8 +282,11 @@ def test_c4_verify_full_sampled():
     q = torch.randn((cfg.batch, m, cfg.hq, 128), generator=g, device=DEV).to(torch.bfloat16)
     out = torch.empty((cfg.batch, m, cfg.hq, 128), dtype=torch.float32, device=DEV)
     lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device=DEV)
-    log_case("c4-verify-full", cfg.batch, m)
-    kvsel.verify_attn(kv, q, m, cfg.hq, cfg.scale, idx, cfg.k, out, lse)
+    log_case("c4-verify-full", cfg.batch, m, cascade)
+    from decode_focal_layer_amd.decode import DraftVerifier
+    ver = DraftVerifier(kv, m, cfg.hq, cfg.scale, shared_tail=(cfg.n_visual, cfg.prefix_len) if cascade else None,
+                        device=DEV)
+    ver.verify(q, idx, cfg.k, out, lse)
     torch.cuda.synchronize()
     rng = np.random.default_rng(12)
     G = cfg.group

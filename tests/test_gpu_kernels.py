@@ -570,41 +570,44 @@ def _shared_prefix_kv(rng, batch, hkv, prefix_len, suffix_max):
 # (G, batch, prefix rows, [row_begin, row_end), parts): ranges not on block
 # edges, several 128-row query blocks with a ragged last one, an empty range,
 # parts of the range (some empty)
-SHARED_CASES = [(2, 5, 160, (37, 160), 1), (1, 3, 64, (0, 64), 1), (4, 70, 1024, (300, 1024), 4),
-                (8, 20, 96, (5, 90), 3), (2, 9, 48, (10, 10), 1), (2, 600, 256, (64, 250), 2), (1, 4, 128, (0, 100), 5)]
+SHARED_CASES = [(2, 5, 160, (37, 160), 1, 1), (1, 3, 64, (0, 64), 1, 1), (4, 70, 1024, (300, 1024), 4, 1),
+                (8, 20, 96, (5, 90), 3, 1), (2, 9, 48, (10, 10), 1, 1), (2, 600, 256, (64, 250), 2, 1),
+                (1, 4, 128, (0, 100), 5, 1), (2, 30, 200, (16, 180), 2, 3)]
 
 
-@pytest.mark.parametrize("G,batch,prefix,rng_rows,splits", SHARED_CASES)
-def test_shared_attention(G, batch, prefix, rng_rows, splits):
+@pytest.mark.parametrize("G,batch,prefix,rng_rows,splits,qps", SHARED_CASES)
+def test_shared_attention(G, batch, prefix, rng_rows, splits, qps):
     kvsel = K()
     rng = np.random.default_rng(3000 + G * 11 + batch)
     hkv = 2
     hq = hkv * G
     kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 40)
-    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
-    parts = torch.full((splits, batch, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
-    plse = torch.full((splits, batch, hq), float("nan"), dtype=torch.float32, device=DEV)
+    q = torch.randn((batch, qps, hq, 128), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
+    parts = torch.full((splits, batch, qps, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    plse = torch.full((splits, batch, qps, hq), float("nan"), dtype=torch.float32, device=DEV)
     rb, re = rng_rows
-    log_case("shared", G, batch, prefix, rb, re, splits)
-    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, parts, plse, splits=splits)
-    out = torch.empty((batch, hq, 128), dtype=torch.float32, device=DEV)
-    lse = torch.empty((batch, hq), dtype=torch.float32, device=DEV)
+    log_case("shared", G, batch, prefix, rb, re, splits, qps)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, parts, plse, splits=splits, q_per_seq=qps)
+    out = torch.empty((batch, qps, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((batch, qps, hq), dtype=torch.float32, device=DEV)
     kvsel.merge_attn(parts, plse, out, lse)
     torch.cuda.synchronize()
     assert not torch.isnan(parts).any() and not torch.isnan(plse).any()   # every part written
     qc = q.cpu()
-    check = range(batch) if batch <= 20 else rng.choice(batch, size=20, replace=False)
-    for b in check:
+    check = [(b, r) for b in range(batch) for r in range(qps)]
+    if len(check) > 20:
+        check = [check[i] for i in rng.choice(len(check), size=20, replace=False)]
+    for b, r in check:
         for g in range(hkv):
-            got = out[b, g * G:(g + 1) * G].cpu().numpy()
-            gl = lse[b, g * G:(g + 1) * G].cpu().numpy()
+            got = out[b, r, g * G:(g + 1) * G].cpu().numpy()
+            gl = lse[b, r, g * G:(g + 1) * G].cpu().numpy()
             if re == rb:
                 assert np.all(got == 0) and np.all(np.isneginf(gl))
                 continue
             Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
             Vl = O.logical_rows(vc, table[b], g, int(lens[b]))
-            ref, rl = O.attention(O.widen(qc[b, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
-            assert_attn(got, ref, f"shared b{b} g{g}")
+            ref, rl = O.attention(O.widen(qc[b, r, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
+            assert_attn(got, ref, f"shared b{b} q{r} g{g}")
             assert np.abs(gl - rl).max() < 1e-4
 
 
