@@ -28,17 +28,12 @@
 // then works through about one head at a time, whose K/V stays in its L2.
 #include "common.h"
 #include "kvsel_internal.h"
+#include "mfma_common.h"
 #include "mfma_kernels.h"
 
 namespace kvsel {
 
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
 
 constexpr int kPThreads = 256;
 constexpr int kPWaves = kPThreads / 64;
@@ -65,27 +60,6 @@ __device__ __forceinline__ int vt_off(int d, int p) {
 __device__ __forceinline__ int quad_pos(int q) {
   const int blk = q >> 3, a = (q & 7) >> 1, hf = q & 1;
   return blk * 32 + (a >> 1) * 16 + hf * 8 + (a & 1) * 4;
-}
-
-// lane l and lane l ^ 32 hold the two halves of one row: combine them
-// (v_permlane32_swap leaves both values in every lane; no LDS)
-__device__ __forceinline__ float half_pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// two floats (bf16 values) -> two fp16 (exact inside the fp16 range; toward
-// zero outside it, so no infinity appears)
-__device__ __forceinline__ uint32_t f16_pair(uint32_t a_bits, uint32_t b_bits) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(a_bits), __uint_as_float(b_bits)));
 }
 
 // staging of one tile: K chunk i = tid + 256u is (key i/16, chunk i%16); V

@@ -31,14 +31,12 @@
 // visible to draft r when that is <= r.
 #include "common.h"
 #include "kvsel_internal.h"
+#include "mfma_common.h"
 #include "mfma_kernels.h"
 
 namespace kvsel {
 
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kVThreads = 256;
 constexpr int kVWaves = kVThreads / 64;
@@ -73,13 +71,6 @@ __device__ __forceinline__ int key_pos(int r) {
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + i;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
-
 // 8 floats -> high bf16 parts and bf16 remainders, packed as MFMA operands
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
   uint32_t h[4], l[4];
@@ -92,20 +83,6 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
   }
   hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
   lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
-}
-
-// lane l and lane l ^ 32 hold the two halves of one column: combine them
-__device__ __forceinline__ float half_pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_kernel(VerifyArgs a) {
@@ -343,9 +320,6 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // tile.  Half the accumulators of the 32-column kernel: 16 waves per CU.
 // ---------------------------------------------------------------------------
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
 constexpr int kW16Threads = 512;
 constexpr int kW16Waves = kW16Threads / 64;
 constexpr int kVt16Bytes = kD * 16 * 2;   // V^T [128 dims][16 keys] bf16 per wave
@@ -356,16 +330,6 @@ constexpr int kLds16 = kW16Waves * kVt16Bytes > kO16Bytes ? kW16Waves * kVt16Byt
 // groups of 4 keys, the groups XOR-swizzled by (d >> 3) & 3
 __device__ __forceinline__ int vt16_off(int d, int r) {
   return d * 32 + ((((r >> 2) ^ (d >> 3)) & 3) << 3) + (r & 3) * 2;
-}
-
-// lanes l and l ^ 16 (v_permlane16_swap leaves both values in every lane)
-__device__ __forceinline__ float row_pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float row_pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 4 floats -> high bf16 parts and bf16 remainders
