@@ -591,13 +591,10 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
     if (a.nsplit != 1) return hipErrorInvalidValue;
     const size_t dyn = (size_t)G * a.seg_cap * sizeof(float);
     if (dyn > kFusedLdsBytes) return hipErrorInvalidValue;
-    static bool attr_set = false;   // the LDS above 64 KiB must be allowed once per kernel
-    if (!attr_set) {
-      for (const void *f : {(const void *)attn_kernel<G, NT, U, 2, true>, (const void *)attn_kernel<G, NT, U, 2, false>}) {
-        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedLdsBytes);
-        if (e != hipSuccess) return e;
-      }
-      attr_set = true;
+    // the LDS above 64 KiB must be allowed (once per device)
+    for (const void *f : {(const void *)attn_kernel<G, NT, U, 2, true>, (const void *)attn_kernel<G, NT, U, 2, false>}) {
+      const hipError_t e = allow_dynamic_lds(f, (int)kFusedLdsBytes);
+      if (e != hipSuccess) return e;
     }
     if (stream)
       hipLaunchKernelGGL((attn_kernel<G, NT, U, 2, true>), grid, dim3(NT), dyn, s, a);

@@ -76,6 +76,10 @@ inline bool fused_focal_fits(int group, int max_seg_len) {
 
 hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s);
 
+// Allows kernel `fn` up to `bytes` of dynamic LDS on the current device: set
+// once per (device, kernel, size), thread-safe (launch_util.hip).
+hipError_t allow_dynamic_lds(const void *fn, int bytes);
+
 // focal-layer choice: one work-group
 constexpr int kMaxLayers = 1024;
 hipError_t launch_pick_layers(const float *ratios, int64_t ld, int n_layers, int n, int n_pick, int32_t *layers,

@@ -55,13 +55,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.n <= kLdsKeys) {
-    static bool attr_set = false;   // LDS above 64 KiB must be allowed once
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)topk_kernel<1024, true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsKeys * 4);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    // LDS above 64 KiB must be allowed (once per device)
+    const hipError_t e = allow_dynamic_lds((const void *)topk_kernel<1024, true>, kLdsKeys * 4);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((topk_kernel<1024, true>), dim3(a.rows), dim3(1024), (size_t)a.n * 4, s, a);
   } else {
     hipLaunchKernelGGL((topk_kernel<1024, false>), dim3(a.rows), dim3(1024), 0, s, a);

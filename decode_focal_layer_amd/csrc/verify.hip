@@ -540,14 +540,10 @@ __global__ __launch_bounds__(kW16Threads) __attribute__((amdgpu_waves_per_eu(4, 
 hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s) {
   if (a.m < 1 || a.group < 1 || a.m * a.group > 32 || a.rows_cap < 1 || a.rows_cap > kVerifyMaxRows)
     return hipErrorInvalidValue;
-  static bool attr_set = false;   // the row table is dynamic LDS beside 65 KiB of static LDS
-  if (!attr_set) {
-    for (const void *f : {(const void *)verify_kernel, (const void *)verify16_kernel}) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               kVerifyMaxRows * (int)sizeof(uint32_t));
-      if (e != hipSuccess) return e;
-    }
-    attr_set = true;
+  // the row table is dynamic LDS beside up to 70 KiB of static LDS (allowed once per device)
+  for (const void *f : {(const void *)verify_kernel, (const void *)verify16_kernel}) {
+    const hipError_t e = allow_dynamic_lds(f, kVerifyMaxRows * (int)sizeof(uint32_t));
+    if (e != hipSuccess) return e;
   }
   const size_t dyn = (size_t)a.rows_cap * sizeof(uint32_t);
   if (a.m * a.group <= 16)
