@@ -344,7 +344,7 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
 
 kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq, int32_t num_q_heads,
                                float scale, int32_t row_begin, int32_t row_end, int32_t splits, float *out,
-                               float *lse, kvsel_stream stream) {
+                               float *lse, float *logits, int64_t ld_logits, kvsel_stream stream) {
   kvsel_status st;
   int G;
   if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
@@ -362,6 +362,8 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   if (splits > 1 && lse == nullptr) return fail(KVSEL_EINVAL, "lse is required with splits > 1");
   if (q_per_seq < 1 || (int64_t)kv->batch * q_per_seq * G > 0x7fffff00ll)
     return fail(KVSEL_EINVAL, "q_per_seq must be >= 1 (and batch * q_per_seq * group < 2^31)");
+  if (logits != nullptr && (q_per_seq != 1 || ld_logits < kv->max_seg_len || ld_logits < 1))
+    return fail(KVSEL_EINVAL, "logits need q_per_seq = 1 and ld_logits >= max_seg_len");
   SharedArgs a{};
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
@@ -378,7 +380,35 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
+  a.logits = logits;
+  a.ld_logits = ld_logits;
+  a.seg_begin = kv->seg_begin;
+  a.seg_end = kv->seg_end;
   return hip_status(launch_shared(a, (hipStream_t)stream), "shared_attn launch");
+}
+
+kvsel_status kvsel_select_logits(const kvsel_kv_desc *kv, const float *logits, int64_t ld_logits,
+                                 int32_t num_q_heads, float scale, int32_t norm, int32_t k, const int32_t *warm_idx,
+                                 int32_t *idx, float *seg_scores, int64_t ld, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, false)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (logits == nullptr || idx == nullptr) return fail(KVSEL_EINVAL, "logits and idx are required");
+  if (ld_logits < kv->max_seg_len || ld_logits < 1) return fail(KVSEL_EINVAL, "ld_logits must be >= max_seg_len");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (norm != KVSEL_NORM_SEGMENT) return fail(KVSEL_EINVAL, "only the segment normalisation is selected from logits");
+  if (k < 1) return fail(KVSEL_EINVAL, "k must be >= 1");
+  if (kv->max_seg_len > kSelMaxSeg)
+    return fail(KVSEL_EUNSUPPORTED, "max_seg_len %d > %d", kv->max_seg_len, kSelMaxSeg);
+  if (seg_scores != nullptr && (ld < kv->max_seg_len || ld < 1)) return fail(KVSEL_EINVAL, "ld must be >= max_seg_len");
+  SelArgs n = sel_args(kv, num_q_heads, G, kv->num_kv_heads, norm, scale, logits, ld_logits);
+  n.scores = seg_scores;
+  n.ld = seg_scores != nullptr ? ld : 0;
+  n.k = k;
+  n.warm = warm_idx;
+  n.idx = idx;
+  return hip_status(launch_focal_select(n, kv->batch, (hipStream_t)stream), "select from logits launch");
 }
 
 kvsel_status kvsel_merge_attn(const float *o, const float *lse, int32_t parts, int64_t rows, float *out,

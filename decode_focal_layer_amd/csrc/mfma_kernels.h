@@ -47,6 +47,9 @@ struct SharedArgs {
   const uint16_t *q;             // [batch][hq][128]
   float scale_log2;
   float *out, *lse;              // [splits][batch][hq][128], [splits][batch][hq]
+  float *logits;                 // or null: raw dots [batch][hq][ld_logits] of each sequence's segment rows
+  int64_t ld_logits;
+  const int32_t *seg_begin, *seg_end;
   int32_t nblk, items;           // set by launch_shared
 };
 hipError_t launch_shared(const SharedArgs &a, hipStream_t s);

@@ -115,10 +115,10 @@ __device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_
 // One 64-key tile for this lane's query row: S^T = K Q^T from the LDS K
 // tile, the online softmax, O^T += V^T P from the LDS V^T tile.  masked(bk, j)
 // drops key 32*bk + 8*(j/4) + 4*hf + j%4 of the tile; it is evaluated only
-// when need_mask.
-template <typename MaskFn>
+// when need_mask.  on_dots(s) sees the raw dots before the mask.
+template <typename MaskFn, typename DotsFn>
 __device__ __forceinline__ void attend_tile(const uint8_t *s_k, const uint8_t *s_vt, const bf16x8 (&qop)[8], int col,
-                                            int hf, float scale_log2, bool need_mask, MaskFn masked,
+                                            int hf, float scale_log2, bool need_mask, MaskFn masked, DotsFn on_dots,
                                             f32x16 (&acc)[4], float &mrun, float &lsum) {
     // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
     // (operands read one k-step ahead of the products that use them)
@@ -151,6 +151,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t *s_k, const uint8_t *s
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    on_dots(s);
     if (need_mask) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     // the causal mask, only on tiles that reach past a row of this wave
     attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_full || t0 + kBN - 1 > wave_pos0,
-                [&](int bk, int j) { return t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos; }, acc, mrun, lsum);
+                [&](int bk, int j) { return t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos; },
+                [](const f32x16 (&)[2]) {}, acc, mrun, lsum);
   }
 
   const float lrow = half_pair_sum(lsum);
@@ -377,6 +379,15 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
 
+  // raw dots of this row's segment keys inside [r0, r1), when asked for
+  int lg0 = 0, lg1 = 0;
+  float *lgrow = nullptr;
+  if (a.logits != nullptr && live) {
+    lg0 = clampi(a.seg_begin[b], 0, a.row_end);
+    lg1 = clampi(a.seg_end[b], lg0, a.row_end);
+    lgrow = a.logits + ((size_t)b * a.hq + g * G + h) * a.ld_logits;   // entry i: segment row lg0 + i
+  }
+
   Stage st = fetch_tile(r0);
   for (int t0 = r0; t0 < r1; t0 += kBN) {
     __syncthreads();   // the previous tile's reads are done
@@ -388,6 +399,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_live || vmask != ~0ull,
                 [&](int bk, int j) {
                   return !live || ((vmask >> (32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3))) & 1ull) == 0ull;
+                },
+                [&](const f32x16 (&s)[2]) {
+                  if (lgrow == nullptr || t0 + kBN <= lg0 || t0 >= lg1) return;
+#pragma unroll
+                  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                      const int key = t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3);
+                      if (key >= lg0 && key < lg1 && key < r1) lgrow[key - lg0] = s[bk][j];
+                    }
                 },
                 acc, mrun, lsum);
   }

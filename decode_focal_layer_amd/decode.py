@@ -29,14 +29,15 @@ class FocalDecoder:
     def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, k: int, focal: Sequence[int], scale: float,
                  seg_len: int, warm_start: bool = True, device="cuda", keep_scores: bool = False,
                  shared_tail: Optional[Tuple[int, int]] = None, shared_splits: int = 4):
-        """shared_tail = (row_begin, row_end): every sequence's segment ends
-        at row_begin, and rows [row_begin, row_end) are shared by all of them
-        (the same cache blocks; HPD's layout rows after the shared visual
-        prefix).  Sparse layers then attend in two parts merged exactly: the
-        shared rows once per kv head for all sequences (kvsel_shared_attn),
-        and each sequence's kept rows and rows from row_end on
-        (kvsel_gather_attn with the segment extended to row_end); the shared
-        rows in shared_splits parts, all parts merged by one kvsel_merge_attn."""
+        """shared_tail = (row_begin, row_end): every sequence's segment is
+        [0, row_begin), and rows [0, row_end) are shared by all of them (the
+        same cache blocks: HPD's visual and layout prefix).  Layers then attend
+        in parts merged exactly (kvsel_merge_attn): each sequence's own rows
+        by kvsel_gather_attn over a view whose segment reaches to row_end, and
+        the shared rows once per kv head for all sequences by
+        kvsel_shared_attn -- rows [row_begin, row_end) for sparse layers (in
+        shared_splits parts); the whole prefix for focal layers, whose segment
+        logits then feed kvsel_select_logits."""
         self.kvs = list(kvs)
         self.L = len(self.kvs)
         self.hq = num_q_heads
@@ -75,10 +76,14 @@ class FocalDecoder:
                                              min_seg_len=kv.min_seg_len + (re - rb)) for kv in self.kvs]
             self.tail = (rb, re)
             self.splits = int(shared_splits)
-            # part 0: each sequence's own rows; parts 1 .. splits: the shared rows
-            self.parts_o = torch.empty((1 + self.splits, B, num_q_heads, 128), dtype=torch.float32, device=device)
-            self.parts_lse = torch.empty((1 + self.splits, B, num_q_heads), dtype=torch.float32, device=device)
+            # the whole prefix in about as many rows per part as the tail
+            self.focal_splits = min(64, self.splits * max(1, -(-re // max(re - rb, 1))))
+            # part 0: each sequence's own rows; parts 1 ..: the shared rows
+            np_ = 1 + max(self.splits, self.focal_splits)
+            self.parts_o = torch.empty((np_, B, num_q_heads, 128), dtype=torch.float32, device=device)
+            self.parts_lse = torch.empty((np_, B, num_q_heads), dtype=torch.float32, device=device)
             self.lse_out = torch.empty((B, num_q_heads), dtype=torch.float32, device=device)
+            self.logits = torch.empty((B, num_q_heads, seg_len), dtype=torch.float32, device=device)
 
     def plan(self, t: int):
         """(kind, src_step_is_previous, src_layer) per layer."""
@@ -107,7 +112,27 @@ class FocalDecoder:
             op = ctypes.c_void_p(self.out[l].data_ptr())
             if layer_hook is not None:
                 layer_hook(l, kind, "begin")
-            if kind == "focal":
+            if kind == "focal" and self.tail is not None:
+                warm = self.idx[l][prev].data_ptr() if (self.warm_start and t > 0) else None
+                pk = self.priv[l]
+                pk.c.seq_len = sl
+                po, pl = self.parts_o, self.parts_lse
+                S = self.focal_splits
+                # own rows (after the prefix): no kept rows, the segment view covers the prefix
+                kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale, None, 0,
+                                                 ctypes.c_void_p(po[0].data_ptr()),
+                                                 ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
+                lg = ctypes.c_void_p(self.logits.data_ptr())
+                kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, 1, self.hq, self.scale, 0, self.tail[1], S,
+                                                 ctypes.c_void_p(po[1].data_ptr()), ctypes.c_void_p(pl[1].data_ptr()),
+                                                 lg, self.seg_len, st))
+                kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()), 1 + S,
+                                                self.B * self.hq, op, ctypes.c_void_p(self.lse_out.data_ptr()), st))
+                kvsel._check(L.kvsel_select_logits(kv.ref(), lg, self.seg_len, self.hq, self.scale,
+                                                   kvsel.NORM_SEGMENT, self.k, warm,
+                                                   ctypes.c_void_p(self.idx[l][cur].data_ptr()), self.scores_ptr(),
+                                                   self.seg_len if self.keep_scores else 0, st))
+            elif kind == "focal":
                 warm = self.idx[l][prev].data_ptr() if (self.warm_start and t > 0) else None
                 kvsel._check(L.kvsel_focal_attn(kv.ref(), qp, self.hq, self.scale, op, None, kvsel.NORM_SEGMENT,
                                                 self.k, warm, ctypes.c_void_p(self.idx[l][cur].data_ptr()),
@@ -133,7 +158,7 @@ class FocalDecoder:
                                                      ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
                     kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, 1, self.hq, self.scale, self.tail[0],
                                                      self.tail[1], self.splits, ctypes.c_void_p(po[1].data_ptr()),
-                                                     ctypes.c_void_p(pl[1].data_ptr()), st))
+                                                     ctypes.c_void_p(pl[1].data_ptr()), None, 0, st))
                     kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
                                                     1 + self.splits, self.B * self.hq, op,
                                                     ctypes.c_void_p(self.lse_out.data_ptr()), st))
@@ -233,7 +258,7 @@ class DraftVerifier:
                                          ctypes.c_void_p(po[0].data_ptr()), ctypes.c_void_p(pl[0].data_ptr()), st))
         kvsel._check(L.kvsel_shared_attn(self.kv.ref(), qp, self.m, self.hq, self.scale, self.tail[0], self.tail[1],
                                          self.splits, ctypes.c_void_p(po[1].data_ptr()),
-                                         ctypes.c_void_p(pl[1].data_ptr()), st))
+                                         ctypes.c_void_p(pl[1].data_ptr()), None, 0, st))
         lo = lse if lse is not None else self.lse_out
         kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
                                         1 + self.splits, self.kv.batch * self.m * self.hq,

@@ -33,7 +33,7 @@ SYMBOLS = (
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
     "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
     "kvsel_pool_alloc", "kvsel_pool_retain", "kvsel_pool_release", "kvsel_fork",
-    "kvsel_verify_attn", "kvsel_prefill_attn", "kvsel_shared_attn", "kvsel_merge_attn",
+    "kvsel_verify_attn", "kvsel_prefill_attn", "kvsel_shared_attn", "kvsel_merge_attn", "kvsel_select_logits",
 )
 
 
@@ -114,7 +114,9 @@ def lib() -> ctypes.CDLL:
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_shared_attn.restype = _I32
-    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _P]
+    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P]
+    L.kvsel_select_logits.restype = _I32
+    L.kvsel_select_logits.argtypes = [_DP, _P, ctypes.c_int64, _I32, _F32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P]
     L.kvsel_merge_attn.restype = _I32
     L.kvsel_merge_attn.argtypes = [_P, _P, _I32, ctypes.c_int64, _P, _P, _P]
     L.kvsel_prefill_attn.restype = _I32
@@ -361,16 +363,31 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
 
 def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_begin: int, row_end: int,
                 out: torch.Tensor, lse: Optional[torch.Tensor] = None, splits: int = 1, q_per_seq: int = 1,
-                stream=None):
+                logits: Optional[torch.Tensor] = None, stream=None):
     """kvsel_shared_attn.  q: bf16 [batch][q_per_seq][hq][128]; out: fp32
-    [splits][batch][q_per_seq][hq][128]; lse: fp32 [splits][batch][q_per_seq][hq]."""
+    [splits][batch][q_per_seq][hq][128]; lse: fp32 [splits][batch][q_per_seq][hq];
+    logits: fp32 [batch][hq][ld] (segment rows' raw dots) or None."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.float32, "out")
     if lse is not None:
         _need(lse, torch.float32, "lse")
+    if logits is not None:
+        _need(logits, torch.float32, "logits")
     _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), q_per_seq, num_q_heads, scale, row_begin, row_end, splits,
-                                   _ptr(out), _ptr(lse), _stream(stream)))
+                                   _ptr(out), _ptr(lse), _ptr(logits), logits.shape[-1] if logits is not None else 0,
+                                   _stream(stream)))
     return out
+
+
+def select_logits(kv: KV, logits: torch.Tensor, num_q_heads: int, scale: float, k: int, idx: torch.Tensor,
+                  warm: Optional[torch.Tensor] = None, seg_scores: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_select_logits.  logits: fp32 [batch][hq][ld]; idx: int32 [batch][hkv][k]."""
+    _need(logits, torch.float32, "logits")
+    _need(idx, torch.int32, "idx")
+    _check(lib().kvsel_select_logits(kv.ref(), _ptr(logits), logits.shape[-1], num_q_heads, scale, NORM_SEGMENT, k,
+                                     _ptr(warm), _ptr(idx), _ptr(seg_scores),
+                                     seg_scores.shape[-1] if seg_scores is not None else 0, _stream(stream)))
+    return idx
 
 
 def merge_attn(o: torch.Tensor, lse: torch.Tensor, out: torch.Tensor, lse_out: torch.Tensor, stream=None):

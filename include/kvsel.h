@@ -359,11 +359,32 @@ KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, 
  * 0 for an empty part), NULL allowed when splits = 1.  q and out 16-byte
  * aligned; scale > 0; the range may touch at most 1024 cache blocks
  * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to
- * +-65504).  No workspace.
+ * +-65504).  logits: NULL, or fp32 [batch][num_q_heads][ld_logits]
+ * (q_per_seq = 1, ld_logits >= max_seg_len): the raw dots q.k of each
+ * sequence's segment rows that lie inside the range, entry i for segment
+ * row seg_begin + i (the input of kvsel_select_logits; rows outside the
+ * range are not written).  No workspace.
  */
 KVSEL_API kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq,
                                          int32_t num_q_heads, float scale, int32_t row_begin, int32_t row_end,
-                                         int32_t splits, float *out, float *lse, kvsel_stream stream);
+                                         int32_t splits, float *out, float *lse, float *logits, int64_t ld_logits,
+                                         kvsel_stream stream);
+
+/*
+ * kvsel_select_logits -- the focal selection from segment logits: per
+ * (sequence, kv head) the softmax over the candidate segment of each query
+ * head of the group, summed over the group, and the exact top-k (ties to the
+ * lower index, ascending, warm start as kvsel_focal_attn).  (FastOCR,
+ * Focal-Guided Pruning: the focal layers select the top-attended image
+ * tokens.)  logits: fp32 [batch][num_q_heads][ld_logits], the raw dots q.k
+ * of segment row seg_begin + i at entry i (as kvsel_shared_attn writes them);
+ * norm: KVSEL_NORM_SEGMENT; idx: [batch][num_kv_heads][k]; seg_scores: NULL
+ * or fp32 [batch][num_kv_heads][ld].  max_seg_len <= 12288.
+ */
+KVSEL_API kvsel_status kvsel_select_logits(const kvsel_kv_desc *kv, const float *logits, int64_t ld_logits,
+                                           int32_t num_q_heads, float scale, int32_t norm, int32_t k,
+                                           const int32_t *warm_idx, int32_t *idx, float *seg_scores, int64_t ld,
+                                           kvsel_stream stream);
 
 /*
  * kvsel_merge_attn -- attention over the union of `parts` disjoint row sets

@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 27
+    assert len(names) == 28
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -216,20 +216,34 @@ def test_prefill_attn_empty_is_a_no_op(L):
     (dict(q=0), EINVAL), (dict(q=FAKE + 2), EINVAL), (dict(out=0), EINVAL), (dict(out=FAKE + 4), EINVAL),
     (dict(scale=0.0), EINVAL), (dict(rb=-1), EINVAL), (dict(rb=50, re=40), EINVAL), (dict(re=121), EINVAL),
     (dict(hq=12), EINVAL), (dict(d=dict(v_pool=0)), EINVAL), (dict(splits=0), EINVAL), (dict(splits=65), EINVAL),
-    (dict(splits=2, lse=None), EINVAL), (dict(qps=0), EINVAL),
+    (dict(splits=2, lse=None), EINVAL), (dict(qps=0), EINVAL), (dict(logits=FAKE, ld=99), EINVAL),
+    (dict(logits=FAKE, ld=100, qps=2), EINVAL),
 ])
 def test_shared_attn_rejects(L, kw, code):
     d = desc(shared_rows=120, **kw.get("d", {}))
     r = L.kvsel_shared_attn(ctypes.byref(d), kw.get("q", FAKE), kw.get("qps", 1), kw.get("hq", 16), kw.get("scale", 0.088),
                             kw.get("rb", 0), kw.get("re", 100), kw.get("splits", 1), kw.get("out", FAKE),
-                            kw.get("lse", FAKE), None)
+                            kw.get("lse", FAKE), kw.get("logits", None), kw.get("ld", 0), None)
     assert r == code
     assert L.kvsel_last_error()
 
 
 def test_shared_attn_block_limit(L):
     d = desc(shared_rows=20000, max_blocks_per_seq=1300, max_seq_len=20000, num_blocks=3000)
-    assert L.kvsel_shared_attn(ctypes.byref(d), FAKE, 1, 16, 0.088, 0, 16385, 1, FAKE, None, None) == EUNSUP
+    assert L.kvsel_shared_attn(ctypes.byref(d), FAKE, 1, 16, 0.088, 0, 16385, 1, FAKE, None, None, 0, None) == EUNSUP
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=0), EINVAL), (dict(idx=0), EINVAL), (dict(ld_logits=99), EINVAL), (dict(norm=1), EINVAL),
+    (dict(k=0), EINVAL), (dict(scores=FAKE, ld=50), EINVAL), (dict(hq=12), EINVAL),
+])
+def test_select_logits_rejects(L, kw, code):
+    d = desc()
+    r = L.kvsel_select_logits(ctypes.byref(d), kw.get("logits", FAKE), kw.get("ld_logits", 100), kw.get("hq", 16),
+                              0.088, kw.get("norm", 0), kw.get("k", 5), None, kw.get("idx", FAKE),
+                              kw.get("scores", None), kw.get("ld", 0), None)
+    assert r == code
+    assert L.kvsel_last_error()
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -635,3 +635,35 @@ def test_merge_attention(rows, parts, inplace):
     fin = np.isfinite(rl)
     np.testing.assert_allclose(gl[fin], rl[fin], rtol=1e-6, atol=1e-5)
     assert np.all(np.isneginf(gl[~fin])) and np.all(got[~fin] == 0)
+
+
+def test_shared_attention_segment_logits():
+    """The raw dots the shared-rows kernel writes for the segment rows inside
+    its range (three parts), against the oracle's logits; entries past the
+    range stay untouched."""
+    kvsel = K()
+    rng = np.random.default_rng(3100)
+    G, batch, hkv, prefix = 2, 40, 2, 160
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 30)
+    s0, s1 = 4, 100
+    seg_b = torch.full((batch,), s0, dtype=torch.int32, device=DEV)
+    seg_e = torch.full((batch,), s1, dtype=torch.int32, device=DEV)
+    import dataclasses
+    kv = dataclasses.replace(kv, seg_begin=seg_b, seg_end=seg_e, max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    parts = torch.empty((3, batch, hq, 128), dtype=torch.float32, device=DEV)
+    plse = torch.empty((3, batch, hq), dtype=torch.float32, device=DEV)
+    ld = 128
+    logits = torch.full((batch, hq, ld), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("shared-logits", batch, s0, s1)
+    kvsel.shared_attn(kv, q, hq, SCALE, 0, 90, parts, plse, splits=3, logits=logits)   # the range ends inside the segment
+    torch.cuda.synchronize()
+    lg, qc = logits.cpu().numpy(), q.cpu()
+    for b in range(0, batch, 7):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+            ref = O.logits(O.widen(qc[b, g * G:(g + 1) * G]), Kl[s0:90], 1.0)
+            got = lg[b, g * G:(g + 1) * G, :90 - s0]
+            assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+            assert np.all(np.isnan(lg[b, g * G:(g + 1) * G, 90 - s0:]))
