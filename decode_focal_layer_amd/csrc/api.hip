@@ -343,8 +343,8 @@ kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint
 }
 
 kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq, int32_t num_q_heads,
-                               float scale, int32_t row_begin, int32_t row_end, int32_t splits, float *out,
-                               float *lse, float *logits, int64_t ld_logits, kvsel_stream stream) {
+                               float scale, int32_t row_begin, int32_t row_end, int32_t splits, int32_t accumulate,
+                               float *out, float *lse, float *logits, int64_t ld_logits, kvsel_stream stream) {
   kvsel_status st;
   int G;
   if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
@@ -360,6 +360,9 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
     return fail(KVSEL_EUNSUPPORTED, "the range touches more than %d cache blocks", kSharedMaxBlocks);
   if (splits < 1 || splits > kMaxMergeParts) return fail(KVSEL_EINVAL, "splits must be in [1, %d]", kMaxMergeParts);
   if (splits > 1 && lse == nullptr) return fail(KVSEL_EINVAL, "lse is required with splits > 1");
+  if (accumulate != 0 && accumulate != 1) return fail(KVSEL_EINVAL, "accumulate must be 0 or 1");
+  if (accumulate && (splits != 1 || lse == nullptr))
+    return fail(KVSEL_EINVAL, "accumulate needs splits = 1 and lse");
   if (q_per_seq < 1 || (int64_t)kv->batch * q_per_seq * G > 0x7fffff00ll)
     return fail(KVSEL_EINVAL, "q_per_seq must be >= 1 (and batch * q_per_seq * group < 2^31)");
   if (logits != nullptr && (q_per_seq != 1 || ld_logits < kv->max_seg_len || ld_logits < 1))
@@ -376,6 +379,7 @@ kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   a.row_begin = row_begin;
   a.row_end = row_end;
   a.splits = splits;
+  a.accumulate = accumulate;
   a.q = q;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;

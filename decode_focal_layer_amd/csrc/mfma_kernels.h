@@ -44,6 +44,7 @@ struct SharedArgs {
   int32_t hkv, hq, group, batch;
   int32_t row_begin, row_end;
   int32_t splits, chunk;         // the range in `splits` parts of `chunk` rows (a multiple of 64)
+  int32_t accumulate;            // splits = 1: out/lse hold another part on entry; the range is folded in
   const uint16_t *q;             // [batch][hq][128]
   float scale_log2;
   float *out, *lse;              // [splits][batch][hq][128], [splits][batch][hq]

@@ -309,9 +309,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // the range's end and invalid blocks.  Same tiles and tile step as the
 // prefill kernel; the output is normalised over the range, with its lse.
 // ---------------------------------------------------------------------------
-// (one wave per SIMD: each K/V load has its own paged address, and the
-// launches are small -- one work-group per 128 query rows and kv head)
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void shared_kernel(SharedArgs a) {
+// Tiles start on a cache-block boundary (keys before the part's first row are
+// masked), so each load's block is uniform: K chunk u of thread t is key
+// t0 + 16u + t/16, in block t0/16 + u; its V rows are keys t0 + 4(t/16) + u,
+// all in block t0/16 + wave.  A load is then a scalar block base plus one
+// per-thread offset.
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_kernel(SharedArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
   __shared__ int32_t s_tab[kSharedMaxBlocks];
@@ -324,7 +327,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   const int g = (int)(w / ((uint32_t)a.nblk * (uint32_t)a.splits));
   const int r0 = min(a.row_end, a.row_begin + part * a.chunk);   // this part's rows [r0, r1)
   const int r1 = min(a.row_end, r0 + a.chunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
   const int G = a.group;
   const int nrows = a.batch * G;
@@ -350,28 +354,41 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   }
   __syncthreads();   // the block ids
 
-  // a row's bytes, or the queries (valid memory) for a row outside the range
-  // or in an invalid block; those keys are masked
-  auto row_ok = [&](int key, int32_t &blk_id) {
-    if (key >= r1) return false;
-    blk_id = s_tab[(key >> 4) - first];
-    return blk_id >= 0 && (int64_t)blk_id < a.num_blocks;
+  // block id of table entry first + ti (uniform), -1 when outside the range's
+  // blocks or not a block of the pool
+  auto block_id = [&](int ti) {
+    const int32_t bi = __builtin_amdgcn_readfirstlane(ti < nb ? s_tab[ti] : -1);
+    return bi >= 0 && (int64_t)bi < a.num_blocks ? bi : -1;
   };
-  auto row_ptr = [&](const uint16_t *pool, int key) {
-    int32_t bi = 0;
-    if (!row_ok(key, bi)) return reinterpret_cast<const uint8_t *>(a.q);
-    return reinterpret_cast<const uint8_t *>(pool + ((size_t)((uint32_t)bi * (uint32_t)a.hkv + (uint32_t)g) * kBlk +
-                                                     (uint32_t)(key & 15)) * kD);
+  // this (block, kv head)'s 4 KiB run; the pool's first run for a skipped block
+  auto run_of = [&](const uint16_t *pool, int32_t bi) {
+    return reinterpret_cast<const uint8_t *>(pool) +
+           (bi < 0 ? 0 : ((size_t)((uint32_t)bi * (uint32_t)a.hkv + (uint32_t)g) << 12));
   };
-  auto fetch_tile = [&](int t0) {
-    auto kld = [&](int u) {
-      const int i = tid + kPThreads * u;
-      return *reinterpret_cast<const uint4 *>(row_ptr(a.k_pool, t0 + (i >> 4)) + (i & 15) * 16);
-    };
-    auto vld = [&](int u) {
-      return *reinterpret_cast<const uint4 *>(row_ptr(a.v_pool, t0 + (tid >> 4) * 4 + u) + (tid & 15) * 16);
-    };
-    return Stage{kld(0), kld(1), kld(2), kld(3), vld(0), vld(1), vld(2), vld(3)};
+  const uint32_t koff = (uint32_t)(tid >> 4) * 256u + (uint32_t)(tid & 15) * 16u;
+  const uint32_t voff = (uint32_t)((tid >> 4) & 3) * 1024u + (uint32_t)(tid & 15) * 16u;
+  auto ld = [](const uint8_t *p, uint32_t o) { return *reinterpret_cast<const uint4 *>(p + o); };
+  // the tile at t0 (a multiple of 16).  tmask bit i: key t0 + i is attended
+  // (inside [r0, r1) and in a pool block; uniform).  vkeep bit u: V row u of
+  // this thread is attended (the others are zeroed before the stash: p = 0
+  // must not meet a non-finite value)
+  auto fetch_tile = [&](int t0, uint64_t &tmask, int &vkeep) {
+    const int tb = (t0 >> 4) - first;
+    const int32_t b0 = block_id(tb), b1 = block_id(tb + 1), b2 = block_id(tb + 2), b3 = block_id(tb + 3);
+    const uint8_t *k0 = run_of(a.k_pool, b0), *k1 = run_of(a.k_pool, b1);
+    const uint8_t *k2 = run_of(a.k_pool, b2), *k3 = run_of(a.k_pool, b3);
+    const int lo = max(r0 - t0, 0), hi = min(r1 - t0, kBN);   // keys t0 + [lo, hi) are in the range
+    tmask = (b0 >= 0 ? 0xffffull : 0ull) | (b1 >= 0 ? 0xffffull << 16 : 0ull) | (b2 >= 0 ? 0xffffull << 32 : 0ull) |
+            (b3 >= 0 ? 0xffffull << 48 : 0ull);
+    tmask &= (hi >= kBN ? ~0ull : (1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);
+    const int32_t vb = wave == 0 ? b0 : wave == 1 ? b1 : wave == 2 ? b2 : b3;
+    const uint8_t *vr = run_of(a.v_pool, vb);
+    const int kv0 = t0 + 4 * (tid >> 4);
+    vkeep = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vkeep |= (vb >= 0 && kv0 + u >= r0 && kv0 + u < r1) ? 1 << u : 0;
+    return Stage{ld(k0, koff), ld(k1, koff), ld(k2, koff), ld(k3, koff),
+                 ld(vr, voff), ld(vr, voff + 256u), ld(vr, voff + 512u), ld(vr, voff + 768u)};
   };
 
   float mrun = -INFINITY, lsum = 0.f;
@@ -388,17 +405,29 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     lgrow = a.logits + ((size_t)b * a.hq + g * G + h) * a.ld_logits;   // entry i: segment row lg0 + i
   }
 
-  Stage st = fetch_tile(r0);
-  for (int t0 = r0; t0 < r1; t0 += kBN) {
+  const int tfirst = r0 & ~15;
+  int vkeep = 0;
+  uint64_t nmask = 0;
+  Stage st = fetch_tile(tfirst, nmask, vkeep);
+  for (int t0 = tfirst; t0 < r1; t0 += kBN) {
+    if (vkeep != 0xf) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      if (!(vkeep & 1)) st.v0 = z;
+      if (!(vkeep & 2)) st.v1 = z;
+      if (!(vkeep & 4)) st.v2 = z;
+      if (!(vkeep & 8)) st.v3 = z;
+    }
     __syncthreads();   // the previous tile's reads are done
     stash(st, s_k, s_vt, tid);
     __syncthreads();
-    if (t0 + kBN < r1) st = fetch_tile(t0 + kBN);
-    int32_t bi = 0;
-    const uint64_t vmask = __ballot(row_ok(t0 + lane, bi));   // bit i: key t0 + i is attended
+    const uint64_t vmask = nmask;   // bit i: key t0 + i is attended
+    if (t0 + kBN < r1) st = fetch_tile(t0 + kBN, nmask, vkeep);
+    // this lane half's bits: bit 8a + r of mb[bk] is key 32 bk + 8a + 4 hf + r
+    // (constant shifts below; no per-lane 64-bit masks)
+    const uint32_t mb0 = (uint32_t)(vmask >> (4 * hf)), mb1 = (uint32_t)(vmask >> (32 + 4 * hf));
     attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_live || vmask != ~0ull,
                 [&](int bk, int j) {
-                  return !live || ((vmask >> (32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3))) & 1ull) == 0ull;
+                  return !live || (((bk ? mb1 : mb0) >> (8 * (j >> 2) + (j & 3))) & 1u) == 0u;
                 },
                 [&](const f32x16 (&s)[2]) {
                   if (lgrow == nullptr || t0 + kBN <= lg0 || t0 >= lg1) return;
@@ -406,8 +435,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
                   for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                      const int key = t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3);
-                      if (key >= lg0 && key < lg1 && key < r1) lgrow[key - lg0] = s[bk][j];
+                      const int ki = 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3), key = t0 + ki;
+                      if (key >= lg0 && key < lg1 && key >= r0 && key < r1)
+                        lgrow[key - lg0] = (((bk ? mb1 : mb0) >> (8 * (j >> 2) + (j & 3))) & 1u) ? s[bk][j] : -INFINITY;
                     }
                 },
                 acc, mrun, lsum);
@@ -416,8 +446,30 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   const float lrow = half_pair_sum(lsum);
   if (!live) return;
   const size_t orow = ((size_t)part * a.batch + b) * a.hq + g * G + h;
-  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
   float *o = a.out + orow * kD;
+  const float lse_r = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;   // natural log
+  if (a.accumulate) {
+    // out/lse hold the attention over the other rows: the exact merge of the
+    // two (each lane reads the elements it then writes; both lane halves read
+    // lse before either writes it)
+    const float lo = a.lse[orow];
+    const float m = fmaxf(lo, lse_r);
+    const float wo = m == -INFINITY ? 0.f : expf(lo - m), wr = m == -INFINITY ? 0.f : expf(lse_r - m);
+    const float iz = m == -INFINITY ? 0.f : 1.f / (wo + wr);
+    const float cr = lrow > 0.f ? wr * iz / lrow : 0.f, co = wo * iz;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        float4 *p = reinterpret_cast<float4 *>(o + dt * 32 + 8 * jq + 4 * hf);
+        const float4 x = *p;
+        *p = make_float4(x.x * co + acc[dt][4 * jq] * cr, x.y * co + acc[dt][4 * jq + 1] * cr,
+                         x.z * co + acc[dt][4 * jq + 2] * cr, x.w * co + acc[dt][4 * jq + 3] * cr);
+      }
+    if (hf == 0) a.lse[orow] = m == -INFINITY ? -INFINITY : m + logf(wo + wr);
+    return;
+  }
+  const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -425,8 +477,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
       *reinterpret_cast<float4 *>(o + dt * 32 + 8 * jq + 4 * hf) =
           make_float4(acc[dt][4 * jq] * inv, acc[dt][4 * jq + 1] * inv, acc[dt][4 * jq + 2] * inv,
                       acc[dt][4 * jq + 3] * inv);
-  if (hf == 0 && a.lse != nullptr)
-    a.lse[orow] = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;
+  if (hf == 0 && a.lse != nullptr) a.lse[orow] = lse_r;
 }
 
 // eight (sequence, head) rows per work-group, 32 threads of 4 floats per row;
@@ -484,6 +535,7 @@ namespace kvsel {
 hipError_t launch_shared(const SharedArgs &a, hipStream_t s) {
   if (a.group < 1 || a.batch < 1 || a.hkv < 1 || a.row_begin < 0 || a.row_end < a.row_begin || a.splits < 1)
     return hipErrorInvalidValue;
+  if (a.accumulate && (a.splits != 1 || a.lse == nullptr)) return hipErrorInvalidValue;
   if (a.row_end > a.row_begin && ((a.row_end - 1) >> 4) - (a.row_begin >> 4) + 1 > kSharedMaxBlocks)
     return hipErrorInvalidValue;
   SharedArgs c = a;

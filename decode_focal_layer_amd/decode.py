@@ -25,10 +25,42 @@ import torch
 from . import kvsel
 
 
+def shared_parts(query_rows: int, num_kv_heads: int, rows: int) -> int:
+    """Parts to cut a shared row range into for kvsel_shared_attn: enough
+    work-groups (one per 128 query rows of a kv head, per part) for one per
+    compute unit of a 256-CU device (two fit, so a part's tail overlaps the
+    next work-group), each part at least two 64-row tiles, at most 64 parts.
+    More parts cost a write and a read of each part's output."""
+    groups = -(-query_rows // 128) * num_kv_heads
+    want = -(-256 // max(groups, 1))
+    return max(1, min(want, 64, rows // 128))
+
+
+def _cascade(L, own, kv, q, q_per_seq, hq, scale, rb, re, splits, parts_o, parts_lse, rows, out, lse_out,
+             logits=None, ld_logits=0, stream=None):
+    """One attention as the exact merge of a sequence's own rows and a shared
+    row range [rb, re).  own(o, lse) enqueues the own-rows call writing
+    there.  One part: own rows straight into out/lse_out, then the range
+    folded in by kvsel_shared_attn (accumulate).  More: own rows in part 0,
+    the range in parts 1 .. splits, one kvsel_merge_attn."""
+    vp = ctypes.c_void_p
+    lg = vp(logits.data_ptr()) if logits is not None else None
+    if splits == 1:
+        own(out, vp(lse_out.data_ptr()))
+        kvsel._check(L.kvsel_shared_attn(kv.ref(), q, q_per_seq, hq, scale, rb, re, 1, 1, out,
+                                         vp(lse_out.data_ptr()), lg, ld_logits, stream))
+        return
+    own(vp(parts_o[0].data_ptr()), vp(parts_lse[0].data_ptr()))
+    kvsel._check(L.kvsel_shared_attn(kv.ref(), q, q_per_seq, hq, scale, rb, re, splits, 0,
+                                     vp(parts_o[1].data_ptr()), vp(parts_lse[1].data_ptr()), lg, ld_logits, stream))
+    kvsel._check(L.kvsel_merge_attn(vp(parts_o.data_ptr()), vp(parts_lse.data_ptr()), 1 + splits, rows, out,
+                                    vp(lse_out.data_ptr()), stream))
+
+
 class FocalDecoder:
     def __init__(self, kvs: Sequence[kvsel.KV], num_q_heads: int, k: int, focal: Sequence[int], scale: float,
                  seg_len: int, warm_start: bool = True, device="cuda", keep_scores: bool = False,
-                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: int = 4):
+                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: Optional[int] = None):
         """shared_tail = (row_begin, row_end): every sequence's segment is
         [0, row_begin), and rows [0, row_end) are shared by all of them (the
         same cache blocks: HPD's visual and layout prefix).  Layers then attend
@@ -36,8 +68,9 @@ class FocalDecoder:
         by kvsel_gather_attn over a view whose segment reaches to row_end, and
         the shared rows once per kv head for all sequences by
         kvsel_shared_attn -- rows [row_begin, row_end) for sparse layers (in
-        shared_splits parts); the whole prefix for focal layers, whose segment
-        logits then feed kvsel_select_logits."""
+        shared_splits parts, by default shared_parts' choice); the whole
+        prefix for focal layers, whose segment logits then feed
+        kvsel_select_logits."""
         self.kvs = list(kvs)
         self.L = len(self.kvs)
         self.hq = num_q_heads
@@ -75,13 +108,15 @@ class FocalDecoder:
             self.priv = [dataclasses.replace(kv, seg_end=ext, max_seg_len=kv.max_seg_len + (re - rb),
                                              min_seg_len=kv.min_seg_len + (re - rb)) for kv in self.kvs]
             self.tail = (rb, re)
-            self.splits = int(shared_splits)
-            # the whole prefix in about as many rows per part as the tail
-            self.focal_splits = min(64, self.splits * max(1, -(-re // max(re - rb, 1))))
-            # part 0: each sequence's own rows; parts 1 ..: the shared rows
+            G = num_q_heads // hkv
+            self.splits = int(shared_splits) if shared_splits is not None else shared_parts(B * G, hkv, re - rb)
+            self.focal_splits = shared_parts(B * G, hkv, re)
+            # part 0: each sequence's own rows; parts 1 ..: the shared rows (one part is folded in place)
             np_ = 1 + max(self.splits, self.focal_splits)
-            self.parts_o = torch.empty((np_, B, num_q_heads, 128), dtype=torch.float32, device=device)
-            self.parts_lse = torch.empty((np_, B, num_q_heads), dtype=torch.float32, device=device)
+            self.parts_o = self.parts_lse = None
+            if np_ > 2:
+                self.parts_o = torch.empty((np_, B, num_q_heads, 128), dtype=torch.float32, device=device)
+                self.parts_lse = torch.empty((np_, B, num_q_heads), dtype=torch.float32, device=device)
             self.lse_out = torch.empty((B, num_q_heads), dtype=torch.float32, device=device)
             self.logits = torch.empty((B, num_q_heads, seg_len), dtype=torch.float32, device=device)
 
@@ -116,18 +151,13 @@ class FocalDecoder:
                 warm = self.idx[l][prev].data_ptr() if (self.warm_start and t > 0) else None
                 pk = self.priv[l]
                 pk.c.seq_len = sl
-                po, pl = self.parts_o, self.parts_lse
-                S = self.focal_splits
-                # own rows (after the prefix): no kept rows, the segment view covers the prefix
-                kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale, None, 0,
-                                                 ctypes.c_void_p(po[0].data_ptr()),
-                                                 ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
+
+                def own(o, ls, pk=pk):   # own rows (after the prefix): no kept rows, the segment view covers the prefix
+                    kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale, None, 0, o, ls,
+                                                     self.ws_ptr, self.ws_n, st))
+                _cascade(L, own, kv, qp, 1, self.hq, self.scale, 0, self.tail[1], self.focal_splits, self.parts_o,
+                         self.parts_lse, self.B * self.hq, op, self.lse_out, self.logits, self.seg_len, st)
                 lg = ctypes.c_void_p(self.logits.data_ptr())
-                kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, 1, self.hq, self.scale, 0, self.tail[1], S,
-                                                 ctypes.c_void_p(po[1].data_ptr()), ctypes.c_void_p(pl[1].data_ptr()),
-                                                 lg, self.seg_len, st))
-                kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()), 1 + S,
-                                                self.B * self.hq, op, ctypes.c_void_p(self.lse_out.data_ptr()), st))
                 kvsel._check(L.kvsel_select_logits(kv.ref(), lg, self.seg_len, self.hq, self.scale,
                                                    kvsel.NORM_SEGMENT, self.k, warm,
                                                    ctypes.c_void_p(self.idx[l][cur].data_ptr()), self.scores_ptr(),
@@ -151,17 +181,13 @@ class FocalDecoder:
                 else:
                     pk = self.priv[l]
                     pk.c.seq_len = sl
-                    po, pl = self.parts_o, self.parts_lse
-                    kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale,
-                                                     ctypes.c_void_p(buf.data_ptr()), self.k,
-                                                     ctypes.c_void_p(po[0].data_ptr()),
-                                                     ctypes.c_void_p(pl[0].data_ptr()), self.ws_ptr, self.ws_n, st))
-                    kvsel._check(L.kvsel_shared_attn(kv.ref(), qp, 1, self.hq, self.scale, self.tail[0],
-                                                     self.tail[1], self.splits, ctypes.c_void_p(po[1].data_ptr()),
-                                                     ctypes.c_void_p(pl[1].data_ptr()), None, 0, st))
-                    kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
-                                                    1 + self.splits, self.B * self.hq, op,
-                                                    ctypes.c_void_p(self.lse_out.data_ptr()), st))
+
+                    def own(o, ls, pk=pk, buf=buf):
+                        kvsel._check(L.kvsel_gather_attn(pk.ref(), qp, self.hq, self.scale,
+                                                         ctypes.c_void_p(buf.data_ptr()), self.k, o, ls,
+                                                         self.ws_ptr, self.ws_n, st))
+                    _cascade(L, own, kv, qp, 1, self.hq, self.scale, self.tail[0], self.tail[1], self.splits,
+                             self.parts_o, self.parts_lse, self.B * self.hq, op, self.lse_out, stream=st)
             if layer_hook is not None:
                 layer_hook(l, kind, "end")
         self.cur = prev   # this step's selection becomes "previous"
@@ -220,11 +246,13 @@ class DraftVerifier:
     row_end) are the same cache blocks in every table -- it runs as a
     cascade: each sequence's own rows (kvsel_verify_attn with the segment
     extended to row_end), the shared rows once per kv head for every draft of
-    every sequence (kvsel_shared_attn), and one exact merge
-    (kvsel_merge_attn)."""
+    every sequence (kvsel_shared_attn), merged exactly: folded into the
+    output in place when the range is one part (the default for many
+    queries), else by kvsel_merge_attn."""
 
     def __init__(self, kv: kvsel.KV, m: int, num_q_heads: int, scale: float,
-                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: int = 4, device="cuda"):
+                 shared_tail: Optional[Tuple[int, int]] = None, shared_splits: Optional[int] = None,
+                 device="cuda"):
         self.kv, self.m, self.hq, self.scale = kv, int(m), num_q_heads, float(scale)
         B = kv.batch
         self.tail = None
@@ -236,11 +264,15 @@ class DraftVerifier:
             self.priv = dataclasses.replace(kv, seg_end=ext, max_seg_len=kv.max_seg_len + (re - rb),
                                             min_seg_len=kv.min_seg_len + (re - rb))
             self.tail = (rb, re)
-            self.splits = int(shared_splits)
-            self.parts_o = torch.empty((1 + self.splits, B, self.m, num_q_heads, 128), dtype=torch.float32,
-                                       device=device)
-            self.parts_lse = torch.empty((1 + self.splits, B, self.m, num_q_heads), dtype=torch.float32,
-                                         device=device)
+            G = num_q_heads // kv.hkv
+            self.splits = (int(shared_splits) if shared_splits is not None
+                           else shared_parts(B * self.m * G, kv.hkv, re - rb))
+            self.parts_o = self.parts_lse = None   # one part is folded in place
+            if self.splits > 1:
+                self.parts_o = torch.empty((1 + self.splits, B, self.m, num_q_heads, 128), dtype=torch.float32,
+                                           device=device)
+                self.parts_lse = torch.empty((1 + self.splits, B, self.m, num_q_heads), dtype=torch.float32,
+                                             device=device)
             self.lse_out = torch.empty((B, self.m, num_q_heads), dtype=torch.float32, device=device)
 
     def verify(self, q: torch.Tensor, idx: Optional[torch.Tensor], k: int, out: torch.Tensor,
@@ -251,16 +283,13 @@ class DraftVerifier:
         L = kvsel.lib()
         st = kvsel._stream(stream)
         self.priv.c.seq_len = self.kv.c.seq_len
-        po, pl = self.parts_o, self.parts_lse
         qp = ctypes.c_void_p(q.data_ptr())
-        kvsel._check(L.kvsel_verify_attn(self.priv.ref(), qp, self.m, self.hq, self.scale,
-                                         ctypes.c_void_p(idx.data_ptr()) if idx is not None else None, k,
-                                         ctypes.c_void_p(po[0].data_ptr()), ctypes.c_void_p(pl[0].data_ptr()), st))
-        kvsel._check(L.kvsel_shared_attn(self.kv.ref(), qp, self.m, self.hq, self.scale, self.tail[0], self.tail[1],
-                                         self.splits, ctypes.c_void_p(po[1].data_ptr()),
-                                         ctypes.c_void_p(pl[1].data_ptr()), None, 0, st))
-        lo = lse if lse is not None else self.lse_out
-        kvsel._check(L.kvsel_merge_attn(ctypes.c_void_p(po.data_ptr()), ctypes.c_void_p(pl.data_ptr()),
-                                        1 + self.splits, self.kv.batch * self.m * self.hq,
-                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lo.data_ptr()), st))
+
+        def own(o, ls):
+            kvsel._check(L.kvsel_verify_attn(self.priv.ref(), qp, self.m, self.hq, self.scale,
+                                             ctypes.c_void_p(idx.data_ptr()) if idx is not None else None, k, o, ls,
+                                             st))
+        _cascade(L, own, self.kv, qp, self.m, self.hq, self.scale, self.tail[0], self.tail[1], self.splits,
+                 self.parts_o, self.parts_lse, self.kv.batch * self.m * self.hq, ctypes.c_void_p(out.data_ptr()),
+                 lse if lse is not None else self.lse_out, stream=st)
         return out

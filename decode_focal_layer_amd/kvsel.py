@@ -114,7 +114,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_verify_attn.restype = _I32
     L.kvsel_verify_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_shared_attn.restype = _I32
-    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P]
+    L.kvsel_shared_attn.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_int64,
+                                    _P]
     L.kvsel_select_logits.restype = _I32
     L.kvsel_select_logits.argtypes = [_DP, _P, ctypes.c_int64, _I32, _F32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P]
     L.kvsel_merge_attn.restype = _I32
@@ -363,10 +364,11 @@ def prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
 
 def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_begin: int, row_end: int,
                 out: torch.Tensor, lse: Optional[torch.Tensor] = None, splits: int = 1, q_per_seq: int = 1,
-                logits: Optional[torch.Tensor] = None, stream=None):
+                logits: Optional[torch.Tensor] = None, accumulate: bool = False, stream=None):
     """kvsel_shared_attn.  q: bf16 [batch][q_per_seq][hq][128]; out: fp32
     [splits][batch][q_per_seq][hq][128]; lse: fp32 [splits][batch][q_per_seq][hq];
-    logits: fp32 [batch][hq][ld] (segment rows' raw dots) or None."""
+    logits: fp32 [batch][hq][ld] (segment rows' raw dots) or None;
+    accumulate: out/lse hold another part on entry and get this range merged in."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.float32, "out")
     if lse is not None:
@@ -374,7 +376,7 @@ def shared_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, row_beg
     if logits is not None:
         _need(logits, torch.float32, "logits")
     _check(lib().kvsel_shared_attn(kv.ref(), _ptr(q), q_per_seq, num_q_heads, scale, row_begin, row_end, splits,
-                                   _ptr(out), _ptr(lse), _ptr(logits), logits.shape[-1] if logits is not None else 0,
+                                   int(bool(accumulate)), _ptr(out), _ptr(lse), _ptr(logits), logits.shape[-1] if logits is not None else 0,
                                    _stream(stream)))
     return out
 

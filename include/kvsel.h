@@ -356,19 +356,26 @@ KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, 
  * out: fp32 [splits][batch][q_per_seq][num_q_heads][128], each part
  * normalised over its rows; lse: fp32 [splits][batch][q_per_seq][num_q_heads]
  * (natural log; -inf and out =
- * 0 for an empty part), NULL allowed when splits = 1.  q and out 16-byte
+ * 0 for an empty part), NULL allowed when splits = 1.  accumulate = 1
+ * (splits = 1, lse required): out and lse hold on entry the attention of
+ * each query over other rows (normalised, with its lse, e.g. from
+ * kvsel_gather_attn or kvsel_verify_attn), and the call replaces them with
+ * the exact merge of that and this range (kvsel_merge_attn of the two, in
+ * place; -inf lse for both gives out = 0).  q and out 16-byte
  * aligned; scale > 0; the range may touch at most 1024 cache blocks
  * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to
  * +-65504).  logits: NULL, or fp32 [batch][num_q_heads][ld_logits]
  * (q_per_seq = 1, ld_logits >= max_seg_len): the raw dots q.k of each
  * sequence's segment rows that lie inside the range, entry i for segment
  * row seg_begin + i (the input of kvsel_select_logits; rows outside the
- * range are not written).  No workspace.
+ * range are not written).  A table entry of the range that is not a pool
+ * block (< 0 or >= num_blocks) is skipped: its rows are not attended and
+ * their logits are -inf.  No workspace.
  */
 KVSEL_API kvsel_status kvsel_shared_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t q_per_seq,
                                          int32_t num_q_heads, float scale, int32_t row_begin, int32_t row_end,
-                                         int32_t splits, float *out, float *lse, float *logits, int64_t ld_logits,
-                                         kvsel_stream stream);
+                                         int32_t splits, int32_t accumulate, float *out, float *lse, float *logits,
+                                         int64_t ld_logits, kvsel_stream stream);
 
 /*
  * kvsel_select_logits -- the focal selection from segment logits: per

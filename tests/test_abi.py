@@ -217,12 +217,13 @@ def test_prefill_attn_empty_is_a_no_op(L):
     (dict(scale=0.0), EINVAL), (dict(rb=-1), EINVAL), (dict(rb=50, re=40), EINVAL), (dict(re=121), EINVAL),
     (dict(hq=12), EINVAL), (dict(d=dict(v_pool=0)), EINVAL), (dict(splits=0), EINVAL), (dict(splits=65), EINVAL),
     (dict(splits=2, lse=None), EINVAL), (dict(qps=0), EINVAL), (dict(logits=FAKE, ld=99), EINVAL),
-    (dict(logits=FAKE, ld=100, qps=2), EINVAL),
+    (dict(logits=FAKE, ld=100, qps=2), EINVAL), (dict(acc=2), EINVAL), (dict(acc=1, splits=2), EINVAL),
+    (dict(acc=1, lse=None), EINVAL),
 ])
 def test_shared_attn_rejects(L, kw, code):
     d = desc(shared_rows=120, **kw.get("d", {}))
     r = L.kvsel_shared_attn(ctypes.byref(d), kw.get("q", FAKE), kw.get("qps", 1), kw.get("hq", 16), kw.get("scale", 0.088),
-                            kw.get("rb", 0), kw.get("re", 100), kw.get("splits", 1), kw.get("out", FAKE),
+                            kw.get("rb", 0), kw.get("re", 100), kw.get("splits", 1), kw.get("acc", 0), kw.get("out", FAKE),
                             kw.get("lse", FAKE), kw.get("logits", None), kw.get("ld", 0), None)
     assert r == code
     assert L.kvsel_last_error()
@@ -230,7 +231,7 @@ def test_shared_attn_rejects(L, kw, code):
 
 def test_shared_attn_block_limit(L):
     d = desc(shared_rows=20000, max_blocks_per_seq=1300, max_seq_len=20000, num_blocks=3000)
-    assert L.kvsel_shared_attn(ctypes.byref(d), FAKE, 1, 16, 0.088, 0, 16385, 1, FAKE, None, None, 0, None) == EUNSUP
+    assert L.kvsel_shared_attn(ctypes.byref(d), FAKE, 1, 16, 0.088, 0, 16385, 1, 0, FAKE, None, None, 0, None) == EUNSUP
 
 
 @pytest.mark.parametrize("kw,code", [

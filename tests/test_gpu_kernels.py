@@ -611,6 +611,107 @@ def test_shared_attention(G, batch, prefix, rng_rows, splits, qps):
             assert np.abs(gl - rl).max() < 1e-4
 
 
+@pytest.mark.parametrize("G,batch,prefix,rng_rows,qps", [(2, 5, 160, (37, 160), 1), (4, 70, 1024, (300, 1024), 1),
+                                                      (2, 9, 48, (10, 10), 1), (2, 30, 200, (16, 180), 3),
+                                                      (1, 300, 64, (0, 64), 2)])
+def test_shared_attention_accumulate(G, batch, prefix, rng_rows, qps):
+    """accumulate = 1: out/lse hold another part on entry (random values,
+    some rows empty: lse = -inf); the call leaves the exact merge of that part
+    and the range, against the oracle's merge of the two."""
+    kvsel = K()
+    rng = np.random.default_rng(3300 + G * 7 + batch)
+    hkv = 2
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 40)
+    q = torch.randn((batch, qps, hq, 128), generator=torch.Generator().manual_seed(13)).to(torch.bfloat16).to(DEV)
+    g = torch.Generator().manual_seed(batch + qps)
+    o_in = torch.randn((batch, qps, hq, 128), generator=g)
+    l_in = torch.randn((batch, qps, hq), generator=g) * 3
+    l_in.view(-1)[::5] = float("-inf")           # rows whose other part is empty
+    out, lse = o_in.to(DEV), l_in.to(DEV)
+    rb, re = rng_rows
+    log_case("shared-acc", G, batch, prefix, rb, re, qps)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, out, lse, splits=1, q_per_seq=qps, accumulate=True)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    got_o, got_l = out.cpu().numpy(), lse.cpu().numpy()
+    check = [(b, r) for b in range(batch) for r in range(qps)]
+    if len(check) > 24:
+        check = [check[i] for i in rng.choice(len(check), size=24, replace=False)]
+    for b, r in check:
+        for gi in range(hkv):
+            hs = slice(gi * G, (gi + 1) * G)
+            if re > rb:
+                Kl = O.logical_rows(kc, table[b], gi, int(lens[b]))
+                Vl = O.logical_rows(vc, table[b], gi, int(lens[b]))
+                so, sl = O.attention(O.widen(qc[b, r, hs]), Kl, Vl, np.arange(rb, re), SCALE)
+            else:
+                so, sl = np.zeros((G, 128)), np.full(G, -np.inf)
+            ref, rl = O.merge_attention(o_in[b, r, hs].numpy().astype(np.float64),
+                                        l_in[b, r, hs].numpy().astype(np.float64), so, sl)
+            assert_attn(got_o[b, r, hs], ref, f"shared-acc b{b} q{r} g{gi}")
+            fin = np.isfinite(rl)
+            assert np.abs(got_l[b, r, hs][fin] - rl[fin]).max(initial=0) < 1e-4
+            assert np.all(np.isneginf(got_l[b, r, hs][~fin])) and np.all(got_o[b, r, hs][~fin] == 0)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_shared_attention_skips_unattended_rows(splits):
+    """Rows the kernel reads but must not attend hold NaN: every pool row
+    outside [row_begin, row_end) (rows before row_begin in its first block,
+    the unused rows of the last shared block, the spare blocks, the suffixes),
+    and one block inside the range is not a pool block (-1 in every table):
+    its rows are skipped and their logits are -inf.  Output and lse against
+    the oracle over the remaining rows."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(3200 + splits)
+    G, batch, hkv, prefix = 2, 33, 2, 200
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 30)
+    rb, re, hole = 21, 200, 5                    # block 5 of the range: rows 80 .. 95
+    keep = np.zeros(kv.k_pool.shape[:2] + (16,), dtype=bool)   # [block][kv head][row]
+    for j in range(rb, re):
+        keep[table[0][j // 16], :, j % 16] = True
+    nan_rows = torch.from_numpy(~keep).to(DEV)
+    kv.k_pool[nan_rows] = float("nan")
+    kv.v_pool[nan_rows] = float("nan")
+    holed = table.copy()
+    holed[:, hole] = -1
+    s0, s1 = 4, 150
+    kvh = dataclasses.replace(kv, block_table=torch.from_numpy(holed).to(DEV),
+                              seg_begin=torch.full((batch,), s0, dtype=torch.int32, device=DEV),
+                              seg_end=torch.full((batch,), s1, dtype=torch.int32, device=DEV),
+                              max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
+    parts = torch.empty((splits, batch, hq, 128), dtype=torch.float32, device=DEV)
+    plse = torch.empty((splits, batch, hq), dtype=torch.float32, device=DEV)
+    logits = torch.full((batch, hq, 160), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("shared-skips", splits, batch, rb, re, hole)
+    kvsel.shared_attn(kvh, q, hq, SCALE, rb, re, parts, plse, splits=splits, logits=logits)
+    out = torch.empty((batch, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=DEV)
+    kvsel.merge_attn(parts, plse, out, lse)
+    torch.cuda.synchronize()
+    rows = np.array([j for j in range(rb, re) if j // 16 != hole])
+    qc, lg = q.cpu(), logits.cpu().numpy()
+    for b in range(0, batch, 4):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+            Vl = O.logical_rows(vc, table[b], g, int(lens[b]))
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref, rl = O.attention(qg, Kl, Vl, rows, SCALE)
+            assert_attn(out[b, g * G:(g + 1) * G].cpu().numpy(), ref, f"shared-skips b{b} g{g}")
+            assert np.abs(lse[b, g * G:(g + 1) * G].cpu().numpy() - rl).max() < 1e-4
+            got = lg[b, g * G:(g + 1) * G]
+            assert np.all(np.isnan(got[:, :rb - s0]))              # segment rows before the range: untouched
+            inside = np.array([j for j in range(rb, s1) if j // 16 != hole])
+            ref_l = O.logits(qg, Kl[inside], 1.0)
+            assert np.abs(got[:, inside - s0] - ref_l).max() <= 1e-5 * max(1.0, np.abs(ref_l).max())
+            assert np.all(np.isneginf(got[:, 16 * hole - s0:16 * hole + 16 - s0]))
+            assert np.all(np.isnan(got[:, s1 - s0:]))               # past the segment: untouched
+
+
 @pytest.mark.parametrize("rows,parts,inplace", [(1, 2, False), (37, 2, False), (1000, 2, True), (300, 5, True),
                                                 (9, 1, False)])
 def test_merge_attention(rows, parts, inplace):
