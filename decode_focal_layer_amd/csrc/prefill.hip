@@ -40,6 +40,7 @@ constexpr int kPWaves = kPThreads / 64;
 constexpr int kPRows = 32 * kPWaves;   // query rows per work-group
 constexpr int kBN = 64;                // keys per tile
 constexpr float kSlack = 8.f;          // log2 headroom of the running max (p <= 256 in fp16)
+constexpr int kLgStride = 65;          // floats per staged logits row (64 keys + 1: distinct banks)
 
 // byte offset of K chunk c (dims 8c .. 8c+7) of tile key r
 __device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -314,10 +315,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // t0 + 16u + t/16, in block t0/16 + u; its V rows are keys t0 + 4(t/16) + u,
 // all in block t0/16 + wave.  A load is then a scalar block base plus one
 // per-thread offset.
+//
+// Segment logits go out a query row at a time: each wave stages its tile of
+// dots (32 rows x 64 keys, rows padded to 65 floats so that the stores of a
+// key column fall in distinct banks) in dynamic LDS, then writes each row's 64
+// consecutive keys with one coalesced store.
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_kernel(SharedArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
   __shared__ int32_t s_tab[kSharedMaxBlocks];
+  extern __shared__ float s_lg[];            // logits asked for: [kPWaves][32][kLgStride]
 
   const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
   const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run: one kv head's work together
@@ -396,13 +403,30 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = {};
 
-  // raw dots of this row's segment keys inside [r0, r1), when asked for
-  int lg0 = 0, lg1 = 0;
-  float *lgrow = nullptr;
-  if (a.logits != nullptr && live) {
-    lg0 = clampi(a.seg_begin[b], 0, a.row_end);
-    lg1 = clampi(a.seg_end[b], lg0, a.row_end);
-    lgrow = a.logits + ((size_t)b * a.hq + g * G + h) * a.ld_logits;   // entry i: segment row lg0 + i
+  // raw dots of each row's segment keys inside [r0, r1), when asked for;
+  // [wlo, whi) covers the segments of this wave's rows
+  const bool want_lg = a.logits != nullptr;
+  int wlo = 0, whi = 0;
+  // this lane's row: its logits indexed by key (entry i is segment row lg0 + i)
+  // and the keys it takes, [lk0, lk1); lane c of the wave holds row c's
+  uint64_t lgb = 0;
+  int lk0 = 0, lk1 = 0;
+  if (want_lg) {
+    int lg0 = 0, lg1 = 0;
+    if (live) {
+      lg0 = clampi(a.seg_begin[b], 0, a.row_end);
+      lg1 = (int)min((int64_t)clampi(a.seg_end[b], lg0, a.row_end), (int64_t)lg0 + a.ld_logits);   // the row holds ld_logits
+      lgb = reinterpret_cast<uint64_t>(a.logits + ((size_t)b * a.hq + g * G + h) * a.ld_logits - lg0);
+    }
+    const int k0 = max(lg0, r0), k1 = max(k0, min(lg1, r1));
+    lk0 = k0;
+    lk1 = k1;
+    wlo = k1 > k0 ? k0 : 0x7fffffff;
+    whi = k1 > k0 ? k1 : 0;
+    for (int o = 32; o > 0; o >>= 1) {
+      wlo = min(wlo, __shfl_xor(wlo, o));
+      whi = max(whi, __shfl_xor(whi, o));
+    }
   }
 
   const int tfirst = r0 & ~15;
@@ -430,15 +454,29 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                   return !live || (((bk ? mb1 : mb0) >> (8 * (j >> 2) + (j & 3))) & 1u) == 0u;
                 },
                 [&](const f32x16 (&s)[2]) {
-                  if (lgrow == nullptr || t0 + kBN <= lg0 || t0 >= lg1) return;
+                  if (!want_lg || t0 + kBN <= wlo || t0 >= whi) return;
+                  float *st = s_lg + wave * (32 * kLgStride);
 #pragma unroll
                   for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                      const int ki = 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3), key = t0 + ki;
-                      if (key >= lg0 && key < lg1 && key >= r0 && key < r1)
-                        lgrow[key - lg0] = (((bk ? mb1 : mb0) >> (8 * (j >> 2) + (j & 3))) & 1u) ? s[bk][j] : -INFINITY;
-                    }
+                    for (int j = 0; j < 16; ++j)
+                      st[col * kLgStride + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3)] = s[bk][j];
+                  __builtin_amdgcn_wave_barrier();
+                  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                  const int key = t0 + lane;
+                  const bool att = ((vmask >> lane) & 1ull) != 0ull;   // a skipped block's row: -inf
+#pragma unroll
+                  for (int rw = 0; rw < 32; ++rw) {
+                    // row rw's base and range, from lane rw (uniform)
+                    const uint32_t blo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lgb, rw);
+                    const uint32_t bhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lgb >> 32), rw);
+                    const int x0 = __builtin_amdgcn_readlane(lk0, rw), x1 = __builtin_amdgcn_readlane(lk1, rw);
+                    float *base = reinterpret_cast<float *>(((uint64_t)bhi << 32) | blo);
+                    const float v = st[rw * kLgStride + lane];
+                    if (base != nullptr && key >= x0 && key < x1) base[key] = att ? v : -INFINITY;
+                  }
+                  __builtin_amdgcn_wave_barrier();
+                  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                 },
                 acc, mrun, lsum);
   }
@@ -547,7 +585,12 @@ hipError_t launch_shared(const SharedArgs &a, hipStream_t s) {
   if (items >= 0x7ffffff0ll) return hipErrorInvalidValue;
   c.items = (int32_t)items;
   const int64_t grid = (items + 7) / 8 * 8;   // a multiple of the XCD count
-  hipLaunchKernelGGL(shared_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, s, c);
+  const int dyn = a.logits != nullptr ? kPWaves * 32 * kLgStride * (int)sizeof(float) : 0;
+  if (dyn > 0) {
+    const hipError_t e = allow_dynamic_lds((const void *)shared_kernel, dyn);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(shared_kernel, dim3((unsigned)grid), dim3(kPThreads), dyn, s, c);
   return hipGetLastError();
 }
 

@@ -25,14 +25,16 @@ import torch
 from . import kvsel
 
 
-def shared_parts(query_rows: int, num_kv_heads: int, rows: int) -> int:
+def shared_parts(query_rows: int, num_kv_heads: int, rows: int, per_cu: int = 1) -> int:
     """Parts to cut a shared row range into for kvsel_shared_attn: enough
-    work-groups (one per 128 query rows of a kv head, per part) for one per
-    compute unit of a 256-CU device (two fit, so a part's tail overlaps the
-    next work-group), each part at least two 64-row tiles, at most 64 parts.
-    More parts cost a write and a read of each part's output."""
+    work-groups (one per 128 query rows of a kv head, per part) for per_cu
+    per compute unit of a 256-CU device (two fit: with one, a part's tail
+    overlaps the next work-group; the logits pass, whose stores leave the
+    matrix cores idle, wants two), each part at least two 64-row tiles, at
+    most 64 parts.  More parts cost a write and a read of each part's
+    output."""
     groups = -(-query_rows // 128) * num_kv_heads
-    want = -(-256 // max(groups, 1))
+    want = -(-256 * per_cu // max(groups, 1))
     return max(1, min(want, 64, rows // 128))
 
 
@@ -110,7 +112,7 @@ class FocalDecoder:
             self.tail = (rb, re)
             G = num_q_heads // hkv
             self.splits = int(shared_splits) if shared_splits is not None else shared_parts(B * G, hkv, re - rb)
-            self.focal_splits = shared_parts(B * G, hkv, re)
+            self.focal_splits = shared_parts(B * G, hkv, re, per_cu=2)
             # part 0: each sequence's own rows; parts 1 ..: the shared rows (one part is folded in place)
             np_ = 1 + max(self.splits, self.focal_splits)
             self.parts_o = self.parts_lse = None

@@ -167,7 +167,11 @@ def test_gather_full_budget_equals_dense_and_empty_rows():
 
 @pytest.mark.parametrize("n,k,mode", [(1, 1, "rand"), (5, 3, "ties"), (64, 64, "rand"), (3584, 179, "rand"),
                                       (6400, 320, "ties"), (3072, 154, "equal"), (12288, 600, "rand"),
-                                      (12289, 7, "ties"), (32760, 6554, "rand"), (40000, 2048, "ties")])
+                                      (12289, 7, "ties"), (32760, 6554, "rand"), (40000, 2048, "ties"),
+                                      # every score equal, a narrow band of scores, k = 1, k = n - 1,
+                                      # k = n, a row read from global memory on every pass
+                                      (40000, 5000, "equal"), (30000, 3000, "narrow"), (20000, 1, "rand"),
+                                      (20000, 19999, "ties"), (20000, 20000, "rand"), (131072, 2048, "rand")])
 def test_topk_exact(n, k, mode):
     kvsel = K()
     rng = np.random.default_rng(n + k)
@@ -176,6 +180,8 @@ def test_topk_exact(n, k, mode):
         s = rng.random((rows, n)).astype(np.float32) * 1e-3
     elif mode == "ties":
         s = (rng.integers(0, 50, size=(rows, n)) / 50).astype(np.float32)
+    elif mode == "narrow":
+        s = (1.0 + rng.random((rows, n)) * 1e-3).astype(np.float32)
     else:
         s = np.full((rows, n), 1.0 / n, dtype=np.float32)
     ld = n + 5
@@ -609,6 +615,38 @@ def test_shared_attention(G, batch, prefix, rng_rows, splits, qps):
             ref, rl = O.attention(O.widen(qc[b, r, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
             assert_attn(got, ref, f"shared b{b} q{r} g{g}")
             assert np.abs(gl - rl).max() < 1e-4
+
+
+def test_shared_attention_logits_stay_in_their_row():
+    """A device segment longer than ld_logits (a bad value) writes at most
+    ld_logits entries: the guard past the logits buffer stays NaN, and the
+    row's first ld_logits entries are its dots."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(3400)
+    G, batch, hkv, prefix = 2, 6, 2, 160
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 20)
+    s0, s1, ld = 4, 100, 96
+    seg_e = np.full(batch, s1, dtype=np.int32)
+    seg_e[-1] = 150                                   # longer than max_seg_len = ld
+    kv = dataclasses.replace(kv, seg_begin=torch.full((batch,), s0, dtype=torch.int32, device=DEV),
+                             seg_end=torch.from_numpy(seg_e).to(DEV), max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(DEV)
+    parts = torch.empty((2, batch, hq, 128), dtype=torch.float32, device=DEV)
+    plse = torch.empty((2, batch, hq), dtype=torch.float32, device=DEV)
+    buf = torch.full((batch * hq * ld + 256,), float("nan"), dtype=torch.float32, device=DEV)
+    logits = buf[:batch * hq * ld].view(batch, hq, ld)
+    log_case("shared-logits-clamp", batch, ld)
+    kvsel.shared_attn(kv, q, hq, SCALE, 0, prefix, parts, plse, splits=2, logits=logits)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(buf[batch * hq * ld:]))
+    b = batch - 1
+    lg, qc = logits.cpu().numpy(), q.cpu()
+    for g in range(hkv):
+        Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+        ref = O.logits(O.widen(qc[b, g * G:(g + 1) * G]), Kl[s0:s0 + ld], 1.0)
+        assert np.abs(lg[b, g * G:(g + 1) * G] - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
 
 
 @pytest.mark.parametrize("G,batch,prefix,rng_rows,qps", [(2, 5, 160, (37, 160), 1), (4, 70, 1024, (300, 1024), 1),
