@@ -19,6 +19,12 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kMaxHeadsPerOut = 64;
+// the fused selection: the statistics' 512 virtual threads, one each (same
+// bits for any group size); the keys in dynamic LDS sized to the longest
+// segment a row can hold (its logits row), so that four work-groups share a
+// compute unit
+constexpr int kSelectThreads = kStatThreads;
+inline __host__ __device__ int select_cap(int64_t ld_logits) { return (int)min(ld_logits, (int64_t)kSelMaxSeg); }
 
 struct FocalRow {
   int cnt, off, seg;
@@ -57,14 +63,14 @@ __global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
 }
 
 // grid (kv heads, sequences): scores + top-k of the group
-__global__ __launch_bounds__(kSelThreads) void focal_select_kernel(SelArgs a) {
-  constexpr int NT = kSelThreads;
-  __shared__ uint32_t s_keys[kSelMaxSeg];
+__global__ __launch_bounds__(kSelectThreads) void focal_select_kernel(SelArgs a) {
+  constexpr int NT = kSelectThreads;
+  extern __shared__ uint32_t s_keys[];   // select_cap(ld_logits) keys
   __shared__ RadixShared<NT> sh;
   __shared__ double s_m[8], s_iz[8];
   const int g = blockIdx.x, b = blockIdx.y;
   FocalRow r = focal_row(a, b, a.scores != nullptr ? a.ld : (int64_t)kSelMaxSeg);
-  r.seg = min(r.seg, kSelMaxSeg);
+  r.seg = min(r.seg, select_cap(a.ld_logits));
   const double c = a.scale * 1.4426950408889634;
   const float *base = a.logits + ((size_t)b * a.hq + g * a.heads_per_out) * a.ld_logits;
   auto stat_logit = [&](int hh, int i) { return base[(size_t)hh * a.ld_logits + i]; };
@@ -94,7 +100,8 @@ hipError_t launch_focal_norm(const SelArgs &a, int batch, hipStream_t s) {
 
 hipError_t launch_focal_select(const SelArgs &a, int batch, hipStream_t s) {
   if (a.heads_per_out > 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(focal_select_kernel, dim3(a.n_out, batch), dim3(kSelThreads), 0, s, a);
+  const size_t dyn = (size_t)select_cap(a.ld_logits) * sizeof(uint32_t);
+  hipLaunchKernelGGL(focal_select_kernel, dim3(a.n_out, batch), dim3(kSelectThreads), dyn, s, a);
   return hipGetLastError();
 }
 
