@@ -620,15 +620,15 @@ size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k) {
   return 0;
 }
 
-kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, int32_t n, int32_t k, const int32_t *warm_idx,
-                        int32_t *idx, void *ws, size_t ws_bytes, kvsel_stream stream) {
+kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, const int32_t *n_per_row, int32_t n, int32_t k,
+                        const int32_t *warm_idx, int32_t *idx, void *ws, size_t ws_bytes, kvsel_stream stream) {
   (void)ws;
   (void)ws_bytes;
   if (scores == nullptr || idx == nullptr) return fail(KVSEL_EINVAL, "scores and idx are required");
   if (rows < 1) return fail(KVSEL_EINVAL, "rows must be >= 1");
   if (k < 1 || k > n) return fail(KVSEL_EINVAL, "need 1 <= k <= n (k=%d, n=%d)", k, n);
   if ((int64_t)n > ld) return fail(KVSEL_EINVAL, "need n <= ld");
-  TopkArgs a{scores, ld, rows, n, k, warm_idx, idx};
+  TopkArgs a{scores, ld, rows, n, k, warm_idx, idx, n_per_row};
   return hip_status(launch_topk(a, (hipStream_t)stream), "topk launch");
 }
 

@@ -162,6 +162,7 @@ struct TopkArgs {
   int32_t rows, n, k;
   const int32_t *warm;
   int32_t *idx;
+  const int32_t *n_row;   // or null: row r ranks its first min(n_row[r], n) scores
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 

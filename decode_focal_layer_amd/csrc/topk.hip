@@ -26,28 +26,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   __shared__ RadixShared<NT> sh;
   const int row = blockIdx.x;
   const float *src = a.scores + (size_t)row * a.ld;
+  const int n = a.n_row != nullptr ? clampi(a.n_row[row], 0, a.n) : a.n;   // this row's candidates
   if (IN_LDS) {
     // eight loads in flight per thread before the LDS stores (one memory
     // latency per eight keys instead of one per key)
     constexpr int B = 8;
-    for (int base = 0; base < a.n; base += B * NT) {
+    for (int base = 0; base < n; base += B * NT) {
       float v[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const int i = base + j * NT + threadIdx.x;
-        v[j] = i < a.n ? src[i] : 0.f;
+        v[j] = i < n ? src[i] : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const int i = base + j * NT + threadIdx.x;
-        if (i < a.n) s_keys[i] = okey(v[j]);
+        if (i < n) s_keys[i] = okey(v[j]);
       }
     }
     __syncthreads();
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
   BlockSync<NT> grp;
-  radix_topk<NT, IN_LDS>(grp, key, a.n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
+  radix_topk<NT, IN_LDS>(grp, key, n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
                  a.idx + (size_t)row * a.k, sh);
 }
 

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.kvsel_score_workspace.restype = _SZ
     L.kvsel_score_workspace.argtypes = [_DP, _I32, _I32, _I32, _I32]
     L.kvsel_topk.restype = _I32
-    L.kvsel_topk.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
+    L.kvsel_topk.argtypes = [_P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]
     L.kvsel_topk_workspace.restype = _SZ
     L.kvsel_topk_workspace.argtypes = [_I32, _I32, _I32]
     L.kvsel_gather_attn.restype = _I32
@@ -277,8 +277,9 @@ def score(kv: KV, q: torch.Tensor, n_rows: int, num_q_heads: int, scale: float, 
 
 
 def topk(scores: torch.Tensor, n: int, k: int, idx: torch.Tensor, warm: Optional[torch.Tensor] = None,
-         stream=None):
-    """kvsel_topk.  scores: fp32 [..., ld] viewed as rows; idx: int32 [rows][k]."""
+         n_per_row: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_topk.  scores: fp32 [..., ld] viewed as rows; idx: int32 [rows][k];
+    n_per_row: int32 [rows] candidate counts (each clamped to n) or None."""
     _need(scores, torch.float32, "scores")
     _need(idx, torch.int32, "idx")
     ld = scores.shape[-1]
@@ -289,7 +290,12 @@ def topk(scores: torch.Tensor, n: int, k: int, idx: torch.Tensor, warm: Optional
         _need(warm, torch.int32, "warm")
         if warm.numel() != rows * k:
             raise ValueError("warm must hold rows * k entries")
-    _check(lib().kvsel_topk(_ptr(scores), ld, rows, n, k, _ptr(warm), _ptr(idx), None, 0, _stream(stream)))
+    if n_per_row is not None:
+        _need(n_per_row, torch.int32, "n_per_row")
+        if n_per_row.numel() != rows:
+            raise ValueError("n_per_row must hold one count per row")
+    _check(lib().kvsel_topk(_ptr(scores), ld, rows, _ptr(n_per_row), n, k, _ptr(warm), _ptr(idx), None, 0,
+                            _stream(stream)))
     return idx
 
 

@@ -175,6 +175,10 @@ KVSEL_API size_t kvsel_score_workspace(const kvsel_kv_desc *kv, int32_t n_rows, 
  * ascending.  Among exactly equal scores the lower index is kept.  Scores
  * must not be NaN.
  *
+ * n_per_row: NULL, or device int32 [rows]: row r's candidates are its first
+ * min(n_per_row[r], n) entries (a negative count is 0).  A row with at most k
+ * candidates gets all of them, ascending, and -1 in the remaining slots.
+ *
  * warm_idx: NULL, or int32 [rows][k], a previous selection (strictly
  * ascending, in [0, n)).  Then theta = the lowest current score among the
  * warm indices and only tokens scoring >= theta are ranked; at least k of
@@ -182,9 +186,9 @@ KVSEL_API size_t kvsel_score_workspace(const kvsel_kv_desc *kv, int32_t n_rows, 
  * indices are not strictly ascending and in range is ranked cold.
  * Requires 1 <= k <= n <= ld, rows >= 1.
  */
-KVSEL_API kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, int32_t n, int32_t k,
-                        const int32_t *warm_idx, int32_t *idx, void *ws, size_t ws_bytes,
-                        kvsel_stream stream);
+KVSEL_API kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, const int32_t *n_per_row,
+                        int32_t n, int32_t k, const int32_t *warm_idx, int32_t *idx, void *ws,
+                        size_t ws_bytes, kvsel_stream stream);
 KVSEL_API size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k);
 
 /*

@@ -135,7 +135,8 @@ def test_score_workspace_sizes(L):
 def test_topk_rejects(L, args, code):
     a = dict(scores=FAKE, ld=10, rows=4, n=10, k=3, warm=None, idx=FAKE)
     a.update(args)
-    assert L.kvsel_topk(a["scores"], a["ld"], a["rows"], a["n"], a["k"], a["warm"], a["idx"], None, 0, None) == code
+    assert L.kvsel_topk(a["scores"], a["ld"], a["rows"], None, a["n"], a["k"], a["warm"], a["idx"], None, 0,
+                        None) == code
     assert L.kvsel_topk_workspace(4, 10, 3) == 0
 
 

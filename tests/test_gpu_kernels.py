@@ -165,6 +165,40 @@ def test_gather_full_budget_equals_dense_and_empty_rows():
     assert torch.all(z == 0) and torch.all(torch.isinf(lse) & (lse < 0))
 
 
+@pytest.mark.parametrize("n,k", [(3072, 154), (40000, 2048)])
+def test_topk_rows_of_their_own_length(n, k):
+    """n_per_row: each row ranks its own first n_r scores (clamped to [0, n]);
+    a row with at most k candidates gets them all, then -1.  Rows: full,
+    shorter, exactly k, fewer than k, zero, negative, above n; warm-started
+    rows (warm indices inside the row) give the same."""
+    kvsel = K()
+    rng = np.random.default_rng(n + 17)
+    counts = np.array([n, n - 37, k, k - 3, 0, -5, n + 100, n // 2], dtype=np.int32)
+    rows = len(counts)
+    s = (rng.integers(0, 400, size=(rows, n)) / 400).astype(np.float32)   # ties included
+    st = torch.from_numpy(s).to(DEV)
+    nr = torch.from_numpy(counts).to(DEV)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    log_case("topk-rows", n, k)
+    kvsel.topk(st, n, k, idx, n_per_row=nr)
+    warm = np.zeros((rows, k), dtype=np.int32)
+    for r in range(rows):
+        nr_ = min(max(int(counts[r]), 0), n)
+        warm[r] = np.sort(rng.choice(nr_, size=k, replace=False)) if nr_ > k else np.arange(k)
+    idx_w = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    kvsel.topk(st, n, k, idx_w, warm=torch.from_numpy(warm).to(DEV), n_per_row=nr)
+    torch.cuda.synchronize()
+    got, got_w = idx.cpu().numpy(), idx_w.cpu().numpy()
+    for r in range(rows):
+        nr_ = min(max(int(counts[r]), 0), n)
+        if nr_ > k:
+            want = O.topk(s[r, :nr_], k)
+        else:
+            want = np.concatenate([np.arange(nr_), np.full(k - nr_, -1)])
+        assert np.array_equal(got[r], want), f"row {r} (n_r {counts[r]})"
+        assert np.array_equal(got_w[r], want), f"warm row {r} (n_r {counts[r]})"
+
+
 @pytest.mark.parametrize("n,k,mode", [(1, 1, "rand"), (5, 3, "ties"), (64, 64, "rand"), (3584, 179, "rand"),
                                       (6400, 320, "ties"), (3072, 154, "equal"), (12288, 600, "rand"),
                                       (12289, 7, "ties"), (32760, 6554, "rand"), (40000, 2048, "ties"),
