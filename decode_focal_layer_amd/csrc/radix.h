@@ -40,8 +40,8 @@ struct RadixShared {
   uint32_t w2[NTS / 64];
   uint32_t w3[NTS / 64];
   uint32_t misc[8];
-  uint32_t list_key[kListCap];
-  int32_t list_idx[kListCap];
+  alignas(16) uint32_t list_key[kListCap];   // read four at a time by the rank
+  alignas(16) int32_t list_idx[kListCap];
 };
 
 // All threads of the work-group take part.
@@ -288,6 +288,11 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
   } else {
     // ---- at most kListCap candidates left in the bin: collect and rank them ----
     if (t == 0) sh.misc[3] = 0;
+    // slots past the collected ones rank below every candidate (key 0, last index)
+    for (int i = t; i < kListCap; i += NTS) {
+      sh.list_key[i] = 0u;
+      sh.list_idx[i] = 0x7fffffff;
+    }
     grp.sync();
     each_key_wave<B>(key, w * ((n + NW * 64 - 1) / (NW * 64) * 64),
                      min(n, (w + 1) * ((n + NW * 64 - 1) / (NW * 64) * 64)),
@@ -307,18 +312,29 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     });
     grp.sync();
     const int nl = min((int)sh.misc[3], kListCap);
-    // rank of item j: items with a larger key, or an equal key and a lower index
-    for (int j = t; j < nl; j += NTS) {
+    const int nl4 = (nl + 3) & ~3;   // whole groups of four (the padding ranks below everything)
+    // rank of item j: items with a larger key, or an equal key and a lower
+    // index.  Four adjacent participants take item j, each a quarter of the
+    // list (four items per LDS access, several in flight), and add their
+    // counts with two lane exchanges.
+    for (int jj = t; jj < 4 * nl; jj += NTS) {
+      const int j = jj >> 2, q = jj & 3;
       const uint32_t xj = sh.list_key[j];
       const int ij = sh.list_idx[j];
       uint32_t r = 0, gt = 0;
-      for (int i = 0; i < nl; ++i) {
-        const uint32_t xi = sh.list_key[i];
-        const int ii = sh.list_idx[i];
-        gt += xi > xj ? 1u : 0u;
-        r += (xi > xj || (xi == xj && ii < ij)) ? 1u : 0u;
+#pragma unroll 2
+      for (int i = 4 * q; i < nl4; i += 16) {
+        const uint4 xi = *reinterpret_cast<const uint4 *>(&sh.list_key[i]);
+        const int4 ii = *reinterpret_cast<const int4 *>(&sh.list_idx[i]);
+        gt += (xi.x > xj ? 1u : 0u) + (xi.y > xj ? 1u : 0u) + (xi.z > xj ? 1u : 0u) + (xi.w > xj ? 1u : 0u);
+        r += ((xi.x > xj || (xi.x == xj && ii.x < ij)) ? 1u : 0u) + ((xi.y > xj || (xi.y == xj && ii.y < ij)) ? 1u : 0u) +
+             ((xi.z > xj || (xi.z == xj && ii.z < ij)) ? 1u : 0u) + ((xi.w > xj || (xi.w == xj && ii.w < ij)) ? 1u : 0u);
       }
-      if (r == krem - 1u) {
+      r += (uint32_t)__shfl_xor((int)r, 1);
+      r += (uint32_t)__shfl_xor((int)r, 2);
+      gt += (uint32_t)__shfl_xor((int)gt, 1);
+      gt += (uint32_t)__shfl_xor((int)gt, 2);
+      if (q == 0 && r == krem - 1u) {
         sh.misc[4] = xj;
         sh.misc[5] = krem - gt;
       }
