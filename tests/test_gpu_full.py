@@ -204,11 +204,15 @@ def test_c3_full_sampled():
                     assert_attn(outs[t][l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} b{b} g{g}")
 
 
-def test_c4_full_sampled():
+@pytest.mark.parametrize("cascade", [False, True])
+def test_c4_full_sampled(cascade):
     """C4 at full size (512 branches over one shared 4096-token prefix, 28
     layers, 32 steps).  Checked at steps 0, 1 and 31: the kept sets of 64
     sampled (branch, kv head) pairs at both focal layers, and all 28 layers'
-    outputs of 4 sampled pairs."""
+    outputs of 4 sampled pairs.  cascade: the configuration the benchmark
+    times -- the shared layout rows (sparse layers) and the whole prefix with
+    its logits (focal layers) once per kv head for all branches, merged with
+    each branch's own rows, the focal selection from those logits."""
     from decode_focal_layer_amd import kvsel
     from decode_focal_layer_amd.decode import FocalDecoder
     cfg = synth.C4
@@ -218,7 +222,8 @@ def test_c4_full_sampled():
                     max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
                     shared_rows=cfg.prefix_len)
            for l in range(cfg.layers)]
-    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV)
+    dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV,
+                       shared_tail=(cfg.n_visual, cfg.prefix_len) if cascade else None)
     check_steps = {0, 1, cfg.steps - 1}
     rng = np.random.default_rng(11)
     sel_pairs = [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.hkv))) for _ in range(64)]
