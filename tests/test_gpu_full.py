@@ -263,7 +263,7 @@ def test_c4_full_sampled(cascade):
                 assert_attn(outs[t][l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
 
 
-@pytest.mark.parametrize("cascade", [False, True])
+@pytest.mark.parametrize("cascade", [False, True, 3])
 def test_c4_verify_full_sampled(cascade):
     """Draft verification at the benchmark's size: 512 branches over the C4
     cache (shared 3072 + 1024 prefix, suffix U[32,1024] + 32 appended rows),
@@ -289,8 +289,10 @@ def test_c4_verify_full_sampled(cascade):
     lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device=DEV)
     log_case("c4-verify-full", cfg.batch, m, cascade)
     from decode_focal_layer_amd.decode import DraftVerifier
+    # cascade: True folds the shared rows into the output in one part; 3 cuts
+    # them into three parts merged with the own rows by kvsel_merge_attn
     ver = DraftVerifier(kv, m, cfg.hq, cfg.scale, shared_tail=(cfg.n_visual, cfg.prefix_len) if cascade else None,
-                        device=DEV)
+                        shared_splits=3 if cascade == 3 else None, device=DEV)
     ver.verify(q, idx, cfg.k, out, lse)
     torch.cuda.synchronize()
     rng = np.random.default_rng(12)
