@@ -727,6 +727,44 @@ def test_shared_attention_accumulate(G, batch, prefix, rng_rows, qps):
             assert np.all(np.isneginf(got_l[b, r, hs][~fin])) and np.all(got_o[b, r, hs][~fin] == 0)
 
 
+def test_shared_attention_accumulate_with_logits():
+    """One call that both folds the range into an existing output (accumulate)
+    and writes the segment logits -- a focal layer whose prefix is one part."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(3500)
+    G, batch, hkv, prefix = 2, 21, 2, 176
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 25)
+    s0, s1 = 0, 150
+    kv = dataclasses.replace(kv, seg_begin=torch.full((batch,), s0, dtype=torch.int32, device=DEV),
+                             seg_end=torch.full((batch,), s1, dtype=torch.int32, device=DEV),
+                             max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    g = torch.Generator().manual_seed(33)
+    o_in = torch.randn((batch, hq, 128), generator=g)
+    l_in = torch.randn((batch, hq), generator=g) * 2
+    out, lse = o_in.to(DEV), l_in.to(DEV)
+    logits = torch.full((batch, hq, s1 - s0), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("shared-acc-logits", batch, prefix)
+    kvsel.shared_attn(kv, q, hq, SCALE, 0, prefix, out, lse, splits=1, logits=logits, accumulate=True)
+    torch.cuda.synchronize()
+    qc, lg = q.cpu(), logits.cpu().numpy()
+    for b in range(0, batch, 3):
+        for gi in range(hkv):
+            hs = slice(gi * G, (gi + 1) * G)
+            Kl = O.logical_rows(kc, table[b], gi, int(lens[b]))
+            Vl = O.logical_rows(vc, table[b], gi, int(lens[b]))
+            qg = O.widen(qc[b, hs])
+            so, sl = O.attention(qg, Kl, Vl, np.arange(0, prefix), SCALE)
+            ref, rl = O.merge_attention(o_in[b, hs].numpy().astype(np.float64), l_in[b, hs].numpy().astype(np.float64),
+                                        so, sl)
+            assert_attn(out[b, hs].cpu().numpy(), ref, f"acc+logits b{b} g{gi}")
+            assert np.abs(lse[b, hs].cpu().numpy() - rl).max() < 1e-4
+            ref_l = O.logits(qg, Kl[s0:s1], 1.0)
+            assert np.abs(lg[b, hs] - ref_l).max() <= 1e-5 * max(1.0, np.abs(ref_l).max())
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_shared_attention_skips_unattended_rows(splits):
     """Rows the kernel reads but must not attend hold NaN: every pool row
