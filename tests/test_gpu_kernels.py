@@ -240,7 +240,9 @@ def test_topk_exact(n, k, mode):
         assert np.array_equal(got_w[r], want), f"warm row {r}"
 
 
-@pytest.mark.parametrize("norm,reduce,pool", [(0, 0, 1), (1, 0, 1), (0, 1, 1), (1, 0, 7), (0, 1, 7)])
+# pool widths: none, FastKV's 7, the widest staged through LDS (511) and one past it
+@pytest.mark.parametrize("norm,reduce,pool", [(0, 0, 1), (1, 0, 1), (0, 1, 1), (1, 0, 7), (0, 1, 7), (0, 0, 511),
+                                              (1, 1, 513)])
 def test_decode_scores(norm, reduce, pool):
     kvsel = K()
     rng = np.random.default_rng(norm * 10 + reduce * 3 + pool)
