@@ -287,11 +287,19 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
 
 }  // namespace
 
+// Work-groups aimed at per pass.  Measured at C2 (one 32768-token prompt,
+// 8 kv heads): 128 -> 10.4k, 256 -> 11.8k, 512 -> 10.5k, 1024 -> 10.2k
+// selections/s; each work-group's fixed costs (block ids, queries, the fp64
+// merge of its waves' statistics) are spread over more keys, one per CU.
+#ifndef KVSEL_WIN_WGS
+#define KVSEL_WIN_WGS 256
+#endif
+
 WinPlan win_plan(int batch, int hkv, int group, int n_rows, int max_seq_len, int max_seg_len) {
   WinPlan p;
   const int64_t pairs = (int64_t)batch * hkv;
-  // about two work-groups per CU (512), at least 128 keys each
-  int64_t t = ((int64_t)max_seq_len * pairs + 511) / 512;
+  // about one work-group per CU (KVSEL_WIN_WGS), at least 128 keys each
+  int64_t t = ((int64_t)max_seq_len * pairs + KVSEL_WIN_WGS - 1) / KVSEL_WIN_WGS;
   t = (t + 127) / 128 * 128;
   if (t < 128) t = 128;
   if (t > kWinMaxTileBlocks * kBlk) t = kWinMaxTileBlocks * kBlk;
