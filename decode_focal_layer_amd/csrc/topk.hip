@@ -27,10 +27,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   const int row = blockIdx.x;
   const float *src = a.scores + (size_t)row * a.ld;
   const int n = a.n_row != nullptr ? clampi(a.n_row[row], 0, a.n) : a.n;   // this row's candidates
+  // a cold row's candidate range (every key), taken while staging
+  uint32_t lo = 0xffffffffu, hi = 0u;
   if (IN_LDS) {
-    // eight loads in flight per thread before the LDS stores (one memory
-    // latency per eight keys instead of one per key)
-    constexpr int B = 8;
+    // 32 loads in flight per thread before the LDS stores (one memory latency
+    // for a whole row of up to 32768 keys)
+    constexpr int B = 32;
     for (int base = 0; base < n; base += B * NT) {
       float v[B];
 #pragma unroll
@@ -41,15 +43,40 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const int i = base + j * NT + threadIdx.x;
-        if (i < n) s_keys[i] = okey(v[j]);
+        if (i < n) {
+          const uint32_t x = okey(v[j]);
+          s_keys[i] = x;
+          lo = min(lo, x);
+          hi = max(hi, x);
+        }
       }
     }
     __syncthreads();
   }
   auto key = [&](int i) -> uint32_t { return IN_LDS ? s_keys[i] : okey(src[i]); };
   BlockSync<NT> grp;
-  radix_topk<NT, IN_LDS>(grp, key, n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr,
-                 a.idx + (size_t)row * a.k, sh);
+  int32_t *dst = a.idx + (size_t)row * a.k;
+  if (IN_LDS && a.warm == nullptr && n > a.k) {
+    // cold: the range is known, so the selection starts at the digit passes
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      sh.w1[w] = lo;
+      sh.w2[w] = hi;
+    }
+    __syncthreads();
+    lo = 0xffffffffu;
+    hi = 0u;
+    for (int i = 0; i < NT / 64; ++i) {
+      lo = min(lo, sh.w1[i]);
+      hi = max(hi, sh.w2[i]);
+    }
+    __syncthreads();
+    radix_select<NT, IN_LDS>(grp, key, n, a.k, 0u, lo, hi, (uint32_t)n, dst, sh);
+    return;
+  }
+  radix_topk<NT, IN_LDS>(grp, key, n, a.k, a.warm != nullptr ? a.warm + (size_t)row * a.k : nullptr, dst, sh);
 }
 
 }  // namespace
