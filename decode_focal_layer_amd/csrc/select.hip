@@ -19,10 +19,11 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kMaxHeadsPerOut = 64;
-// the fused selection: the statistics' 512 virtual threads, one each (same
-// bits for any group size); the keys in dynamic LDS sized to the longest
-// segment a row can hold (its logits row), so that four work-groups share a
-// compute unit
+// the fused selection: 512 threads (the statistics' virtual threads, one
+// each) when the launch has a row per CU or more, so that four work-groups
+// share a compute unit; 1024 for fewer rows (more threads per row).  Same
+// bits either way.  The keys sit in dynamic LDS sized to the longest segment
+// a row can hold (its logits row).
 constexpr int kSelectThreads = kStatThreads;
 inline __host__ __device__ int select_cap(int64_t ld_logits) { return (int)min(ld_logits, (int64_t)kSelMaxSeg); }
 
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
 }
 
 // grid (kv heads, sequences): scores + top-k of the group
-__global__ __launch_bounds__(kSelectThreads) void focal_select_kernel(SelArgs a) {
-  constexpr int NT = kSelectThreads;
+template <int NT>
+__global__ __launch_bounds__(NT) void focal_select_kernel(SelArgs a) {
   extern __shared__ uint32_t s_keys[];   // select_cap(ld_logits) keys
   __shared__ RadixShared<NT> sh;
   __shared__ double s_m[8], s_iz[8];
@@ -101,7 +102,11 @@ hipError_t launch_focal_norm(const SelArgs &a, int batch, hipStream_t s) {
 hipError_t launch_focal_select(const SelArgs &a, int batch, hipStream_t s) {
   if (a.heads_per_out > 8) return hipErrorInvalidValue;
   const size_t dyn = (size_t)select_cap(a.ld_logits) * sizeof(uint32_t);
-  hipLaunchKernelGGL(focal_select_kernel, dim3(a.n_out, batch), dim3(kSelectThreads), dyn, s, a);
+  if ((int64_t)a.n_out * batch < 256)
+    hipLaunchKernelGGL(focal_select_kernel<2 * kSelectThreads>, dim3(a.n_out, batch), dim3(2 * kSelectThreads), dyn, s,
+                       a);
+  else
+    hipLaunchKernelGGL(focal_select_kernel<kSelectThreads>, dim3(a.n_out, batch), dim3(kSelectThreads), dyn, s, a);
   return hipGetLastError();
 }
 
