@@ -307,8 +307,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // that all branches have in common, computed once per kv head for all of
 // them.  HPD-Parsing wiki, method item 2: the branches reuse the shared
 // context's KV.  Query row rr = sequence * G + head of the group; no mask but
-// the range's end and invalid blocks.  Same tiles and tile step as the
-// prefill kernel; the output is normalised over the range, with its lse.
+// the range's ends and invalid blocks.  Same tiles and tile step as the
+// prefill kernel; the output is normalised over the range, with its lse, or
+// (accumulate) folded into the attention over other rows already in out/lse.
 // ---------------------------------------------------------------------------
 // Tiles start on a cache-block boundary (keys before the part's first row are
 // masked), so each load's block is uniform: K chunk u of thread t is key

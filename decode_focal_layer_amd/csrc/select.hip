@@ -1,8 +1,9 @@
 // Focal score normalisation, alone or fused with the exact top-k, one
 // work-group per (sequence, output row), reading logits stored by the
-// attention or logits kernel (the path for shapes the fused focal attention
-// kernel does not take: split attention, context normalisation, long
-// segments).
+// attention, logits or shared-prefix kernel (the path for shapes the fused
+// focal attention kernel does not take: split attention, context
+// normalisation, long segments, and the focal layers of a shared-prefix
+// cascade).
 //
 // FastOCR (technical summary, Focal-Guided Pruning): a focal layer ranks the
 // image tokens by the attention its queries give them and keeps the top tau;
