@@ -320,7 +320,12 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // tile.  Half the accumulators of the 32-column kernel: 16 waves per CU.
 // ---------------------------------------------------------------------------
 
-constexpr int kW16Threads = 512;
+// threads per (branch, kv head) work-group: 256 ran draft verification at the
+// C4 shape (4096 pairs of ~720 rows) at 110.3 against 109.4 steps/s for 512
+#ifndef KVSEL_W16_THREADS
+#define KVSEL_W16_THREADS 256
+#endif
+constexpr int kW16Threads = KVSEL_W16_THREADS;
 constexpr int kW16Waves = kW16Threads / 64;
 constexpr int kVt16Bytes = kD * 16 * 2;   // V^T [128 dims][16 keys] bf16 per wave
 constexpr int kO16Bytes = (int)sizeof(float) * kW16Waves * 16 * kD;
