@@ -10,6 +10,10 @@ softmax and attention sum is evaluated in float64.  The one integer
 decision (which k tokens to keep) is taken on the scores rounded to
 float32, the precision the kernels decide in, with ties to the lower index.
 
+Shapes: the scoring, selection and attention functions take leading batch
+dimensions (several sequences, heads or steps at once) and apply the same
+definition to each; one call on a single group is the plain case.
+
 Sources (the pages' titles and sections; no formula for the score is
 printed there, the readings below are the plainest ones the text supports):
 
@@ -110,8 +114,8 @@ def copy_block(pool, src: int, dst: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def logits(q, K, scale) -> np.ndarray:
-    """s[..., i] = (q . K[i]) * scale, in float64."""
-    return (np.asarray(q, F64) @ np.asarray(K, F64).T) * F64(scale)
+    """s[..., j, i] = (q[..., j, :] . K[..., i, :]) * scale, in float64."""
+    return (np.asarray(q, F64) @ np.swapaxes(np.asarray(K, F64), -1, -2)) * F64(scale)
 
 
 def softmax(s) -> np.ndarray:
@@ -124,20 +128,20 @@ def softmax(s) -> np.ndarray:
 def focal_scores(qg, K, s0: int, s1: int, scale, norm: str = "segment") -> np.ndarray:
     """Decode focal score of the candidate tokens [s0, s1) for one GQA group.
 
-    qg: [G, d] the group's queries; K: [N, d] the group's logical K rows.
-    For each head: softmax of its logits over the candidate segment
+    qg: [..., G, d] the group's queries; K: [..., N, d] the group's logical
+    K rows.  For each head: softmax of its logits over the candidate segment
     ("segment") or over all N rows read off at the segment ("context"),
     then the probabilities are summed over the G heads of the group.
-    Result [s1 - s0], segment-relative (FastOCR, Focal-Guided Pruning).
+    Result [..., s1 - s0], segment-relative (FastOCR, Focal-Guided Pruning).
     """
     s = logits(qg, K, scale)
     if norm == "segment":
-        p = softmax(s[:, s0:s1])
+        p = softmax(s[..., s0:s1])
     elif norm == "context":
-        p = softmax(s)[:, s0:s1]
+        p = softmax(s)[..., s0:s1]
     else:
         raise ValueError(norm)
-    return p.sum(axis=0)
+    return p.sum(axis=-2)
 
 
 def window_scores(qw, K, s0: int, s1: int, scale, causal: bool = True) -> np.ndarray:
@@ -151,27 +155,28 @@ def window_scores(qw, K, s0: int, s1: int, scale, causal: bool = True) -> np.nda
     qw = np.asarray(qw, F64)
     K = np.asarray(K, F64)
     N = K.shape[0]
-    W = qw.shape[0]
+    W, G, d = qw.shape
+    s = logits(qw.reshape(W * G, d), K, scale).reshape(W, G, N)   # every row's logits
     acc = np.zeros(N, F64)
     for r in range(W):
         pos = N - W + r
         vis = pos + 1 if causal else N
-        p = softmax(logits(qw[r], K[:vis], scale))      # [G, vis]
+        p = softmax(s[r, :, :vis])                      # [G, vis]
         acc[:vis] += p.sum(axis=0)
     return acc[s0:s1]
 
 
 def avg_pool(x, width: int) -> np.ndarray:
-    """1-D average pool, stride 1, 'same' length, zero padding; every output
-    divides by ``width`` (padding counted), width odd."""
+    """1-D average pool along the last axis, stride 1, 'same' length, zero
+    padding; output i is the sum of the padded input over [i, i + width)
+    divided by ``width`` (padding counted), width odd."""
     assert width % 2 == 1
     x = np.asarray(x, F64)
     h = width // 2
-    pad = np.concatenate([np.zeros(h, F64), x, np.zeros(h, F64)])
-    out = np.empty_like(x)
-    for i in range(x.shape[0]):
-        out[i] = pad[i:i + width].sum() / width
-    return out
+    zeros = np.zeros(x.shape[:-1] + (h,), F64)
+    pad = np.concatenate([zeros, x, zeros], axis=-1)
+    windows = np.lib.stride_tricks.sliding_window_view(pad, width, axis=-1)   # [..., n, width]
+    return windows.sum(axis=-1) / width
 
 
 # ---------------------------------------------------------------------------
@@ -179,17 +184,18 @@ def avg_pool(x, width: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def topk(scores, k: int) -> np.ndarray:
-    """The k highest scores; among equal float32 scores the lower index wins.
+    """The k highest scores of each row (last axis); among equal float32
+    scores the lower index wins.
 
     Full sort by (score descending, index ascending), keep the first k,
     return those indices ascending.
     """
     s32 = np.asarray(scores, dtype=np.float32).astype(F64)
-    n = s32.shape[0]
+    n = s32.shape[-1]
     if not 1 <= k <= n:
         raise ValueError("need 1 <= k <= n")
-    order = np.lexsort((np.arange(n), -s32))
-    return np.sort(order[:k]).astype(np.int64)
+    order = np.lexsort((np.broadcast_to(np.arange(n), s32.shape), -s32), axis=-1)
+    return np.sort(order[..., :k], axis=-1).astype(np.int64)
 
 
 def topk_warm(scores, k: int, warm) -> np.ndarray:
@@ -218,17 +224,32 @@ def tie_band_check(gpu_idx, oracle_scores, k: int, rel: float = 1e-6):
     An index is ambiguous when its oracle score lies within ``rel`` of the
     k-th largest oracle score.  The kept set passes when it has k distinct
     in-range indices and every index in its symmetric difference with the
-    oracle's set is ambiguous.  Returns (ok, n_diff).
+    oracle's set is ambiguous.  Returns (ok, n_diff) for one row
+    (gpu_idx [k], oracle_scores [n]); for rows (gpu_idx [..., k],
+    oracle_scores [..., n]) both are arrays over the rows (n_diff -1 for a
+    row that is not k distinct in-range indices).
     """
     sc = np.asarray(oracle_scores, F64)
     g = np.asarray(gpu_idx, dtype=np.int64)
-    if g.shape[0] != k or len(np.unique(g)) != k or g.min() < 0 or g.max() >= sc.shape[0]:
-        return False, -1
-    o = topk(sc, k)
-    sk = np.sort(sc)[::-1][k - 1]
-    diff = np.setxor1d(g, o)
-    amb = np.abs(sc[diff] - sk) <= rel * abs(sk)
-    return bool(amb.all()), int(diff.shape[0])
+    n = sc.shape[-1]
+    if g.shape[:-1] != sc.shape[:-1]:
+        raise ValueError("gpu_idx must be [..., k] over the rows of oracle_scores")
+    if g.shape[-1] != k:                                             # not k indices: every row fails
+        return (False, -1) if g.ndim == 1 else (np.zeros(g.shape[:-1], bool), np.full(g.shape[:-1], -1))
+    gs = np.sort(g, axis=-1)
+    valid = (gs[..., 0] >= 0) & (gs[..., -1] < n) & np.all(gs[..., 1:] != gs[..., :-1], axis=-1)
+    in_g = np.zeros(sc.shape, dtype=bool)
+    np.put_along_axis(in_g, np.clip(g, 0, n - 1), True, axis=-1)
+    in_o = np.zeros(sc.shape, dtype=bool)
+    np.put_along_axis(in_o, topk(sc, k), True, axis=-1)
+    sk = np.take(-np.sort(-sc, axis=-1), k - 1, axis=-1)           # k-th largest oracle score
+    diff = in_g != in_o
+    amb = np.abs(sc - sk[..., None]) <= rel * np.abs(sk)[..., None]
+    ok = valid & np.all(~diff | amb, axis=-1)
+    nd = np.where(valid, diff.sum(axis=-1), -1)
+    if g.ndim == 1:
+        return bool(ok), int(nd)
+    return ok, nd
 
 
 # ---------------------------------------------------------------------------
@@ -251,6 +272,29 @@ def attention(qg, K, V, rows, scale):
     z = e.sum(axis=1, keepdims=True)
     out = (e @ Vr) / z
     return out, (m + np.log(z))[:, 0]
+
+
+def attention_masked(q, K, V, visible, scale):
+    """Softmax attention of each query over the rows it may see: the same
+    definition as ``attention`` with the row set given as a mask, so that
+    many (sequence, head, step) instances go in one call.
+
+    q [..., Q, d]; K, V [..., N, d]; visible: bool [..., Q, N] (or
+    broadcastable to it), True where query j attends row i.  Returns
+    (out [..., Q, d], lse [..., Q]); a query that sees no row gets out = 0
+    and lse = -inf (FastOCR Cross-Layer Propagation: attention over the
+    kept set only)."""
+    s = logits(q, K, scale)
+    vis = np.broadcast_to(np.asarray(visible, dtype=bool), s.shape)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    any_row = np.isfinite(m)
+    m = np.where(any_row, m, 0.0)
+    e = np.exp(s - m)                                   # exp(-inf) = 0 off the mask
+    z = e.sum(axis=-1, keepdims=True)
+    out = np.where(any_row, (e @ np.asarray(V, F64)) / np.where(any_row, z, 1.0), 0.0)
+    lse = np.where(any_row, m + np.log(np.where(any_row, z, 1.0)), -np.inf)[..., 0]
+    return out, lse
 
 
 def verify_attention(qd, K, V, rows, n: int, scale):

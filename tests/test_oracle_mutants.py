@@ -42,6 +42,25 @@ def _window_off_by_one(qw, K, s0, s1, scale, causal=True):
     return acc[s0:s1]
 
 
+def _window_always_causal(qw, K, s0, s1, scale, causal=True):
+    return _window_reference(qw, K, s0, s1, scale, lambda pos, N: pos + 1)
+
+
+def _window_noncausal_misses_last_key(qw, K, s0, s1, scale, causal=True):
+    return _window_reference(qw, K, s0, s1, scale, lambda pos, N: pos + 1 if causal else N - 1)
+
+
+def _window_reference(qw, K, s0, s1, scale, visible):
+    qw = np.asarray(qw, F64)
+    K = np.asarray(K, F64)
+    N, W = K.shape[0], qw.shape[0]
+    acc = np.zeros(N)
+    for r in range(W):
+        vis = visible(N - W + r, N)
+        acc[:vis] += O.softmax(O.logits(qw[r], K[:vis], scale)).sum(0)
+    return acc[s0:s1]
+
+
 def _attention_uses_k_for_v(qg, K, V, rows, scale):
     r = np.unique(np.asarray(rows, dtype=np.int64))
     s = O.logits(qg, np.asarray(K, F64)[r], scale)
@@ -100,11 +119,36 @@ def _pick_by_peak(ratios, n_pick):
     return np.sort(order[:n_pick])
 
 
+def _masked_ignores_mask(q, K, V, visible, scale):
+    s = O.logits(q, K, scale)
+    e = np.exp(s - s.max(-1, keepdims=True))
+    z = e.sum(-1, keepdims=True)
+    return (e @ np.asarray(V, F64)) / z, (s.max(-1, keepdims=True) + np.log(z))[..., 0]
+
+
+def _masked_shifted_mask(q, K, V, visible, scale):
+    vis = np.roll(np.broadcast_to(np.asarray(visible, bool), O.logits(q, K, scale).shape), 1, axis=-1)
+    return _masked_reference(q, K, V, vis, scale)
+
+
+def _masked_reference(q, K, V, visible, scale):
+    s = np.where(visible, O.logits(q, K, scale), -np.inf)
+    m = s.max(-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    z = e.sum(-1, keepdims=True)
+    return (e @ np.asarray(V, F64)) / np.where(z > 0, z, 1.0), (m + np.log(np.where(z > 0, z, 1.0)))[..., 0]
+
+
 MUTANTS = [
     ("logits", _no_scale, [P.test_attention_matches_sdpa, P.test_window_scores_scale_sensitive]),
     ("softmax", _softmax_axis0, [lambda: P.test_score_sums(2), lambda: P.test_golden_focal_scores("softmax_three_keys")]),
     ("topk", _topk_high_index_wins, [lambda: P.test_topk_brute_force(0), P.test_golden_topk_ties]),
     ("window_scores", _window_off_by_one, [P.test_golden_window_causal_uniform]),
+    ("window_scores", _window_always_causal, [P.test_golden_window_noncausal_uniform,
+                                              P.test_golden_window_noncausal_weighted]),
+    ("window_scores", _window_noncausal_misses_last_key, [P.test_golden_window_noncausal_uniform,
+                                                          P.test_golden_window_noncausal_weighted]),
     ("attention", _attention_uses_k_for_v, [lambda: P.test_attention_matches_sdpa(0)]),
     ("avg_pool", _pool_excluding_pad, [lambda: P.test_pool_matches_torch(8), P.test_golden_pool]),
     ("kept_rows", _kept_rows_unshifted, [P.test_full_budget_is_dense]),
@@ -113,6 +157,10 @@ MUTANTS = [
     ("visual_mass", _mass_segment_softmax, [P.test_visual_mass_closed_forms, lambda: P.test_visual_mass_matches_sdpa_indicator(0)]),
     ("pick_focal_layers", _pick_high_layer_wins, [P.test_pick_focal_layers_cases, lambda: P.test_pick_focal_layers_brute_force(0)]),
     ("pick_focal_layers", _pick_by_peak, [P.test_pick_focal_layers_cases]),
+    ("attention_masked", _masked_ignores_mask, [lambda: P.test_attention_masked_matches_sdpa(0),
+                                                P.test_attention_masked_equals_attention_over_rows]),
+    ("attention_masked", _masked_shifted_mask, [lambda: P.test_attention_masked_matches_sdpa(0),
+                                                P.test_attention_masked_equals_attention_over_rows]),
 ]
 
 

@@ -97,6 +97,30 @@ def test_golden_window_causal_uniform():
     np.testing.assert_allclose(got, c["scores"], rtol=1e-14)
 
 
+def test_golden_window_noncausal_uniform():
+    c = GOLD["window_noncausal_uniform"]
+    n, W = c["n"], c["window"]
+    qw = np.zeros((W, 1, D))
+    K = np.random.default_rng(0).standard_normal((n, D))
+    got = O.window_scores(qw, K, 0, n, SCALE, causal=False)
+    np.testing.assert_allclose(got, c["scores"], rtol=1e-14)
+
+
+def test_golden_window_noncausal_weighted():
+    """Window rows with different logits per key: K[i] is the i-th unit
+    vector and each row's query holds its logits (scaled by sqrt(d))."""
+    c = GOLD["window_noncausal_weighted"]
+    lg = np.asarray(c["logits"], dtype=np.float64)
+    W, n = lg.shape
+    K = np.zeros((n, D))
+    K[np.arange(n), np.arange(n)] = 1.0
+    qw = np.zeros((W, 1, D))
+    qw[:, 0, :n] = lg * math.sqrt(D)
+    s0, s1 = c["segment"]
+    got = O.window_scores(qw, K, s0, s1, SCALE, causal=False)
+    np.testing.assert_allclose(got, c["scores"], rtol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # library routines
 # --------------------------------------------------------------------------
@@ -537,3 +561,70 @@ def test_merge_attention_equals_union(seed):
     np.testing.assert_array_equal(le, la)
     oz, lz = O.merge_attention(empty_o, empty_l, empty_o, empty_l)
     assert np.all(oz == 0) and np.all(np.isneginf(lz))
+
+
+# --------------------------------------------------------------------------
+# many instances per call (the full-size parity checks use these forms)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_masked_matches_sdpa(seed):
+    """Masked attention against torch's scaled-dot-product attention with a
+    boolean mask, several (batch, query) instances at once; a query whose
+    mask is empty gets out = 0 and lse = -inf."""
+    rng = np.random.default_rng(100 + seed)
+    B, Q, N = 3, int(rng.integers(1, 9)), int(rng.integers(1, 200))
+    q, K, V = _rand(rng, B, Q, D), _rand(rng, B, N, D), _rand(rng, B, N, D)
+    vis = rng.random((B, Q, N)) < 0.3
+    vis[:, 0, :] = True
+    vis[1, -1, :] = False                            # nothing visible
+    out, lse = O.attention_masked(q, K, V, vis, SCALE)
+    ok = vis.any(axis=-1)
+    tq, tk, tv = (torch.from_numpy(x)[:, None] for x in (q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(vis)[:, None])[:, 0]
+    np.testing.assert_allclose(out[ok], ref.numpy()[ok], rtol=1e-12, atol=1e-12)
+    assert np.all(out[~ok] == 0) and np.all(np.isneginf(lse[~ok]))
+    s = (q @ np.swapaxes(K, 1, 2)) * SCALE
+    ref_lse = np.log(np.where(vis, np.exp(s), 0.0).sum(-1)[ok])
+    np.testing.assert_allclose(lse[ok], ref_lse, rtol=1e-12)
+
+
+def test_attention_masked_equals_attention_over_rows():
+    """Each masked instance equals attention over the rows its mask selects."""
+    rng = np.random.default_rng(7)
+    q, K, V = _rand(rng, 4, 2, D), _rand(rng, 4, 300, D), _rand(rng, 4, 300, D)
+    vis = rng.random((4, 1, 300)) < 0.1
+    out, lse = O.attention_masked(q, K, V, vis, SCALE)
+    for b in range(4):
+        ref, rl = O.attention(q[b], K[b], V[b], np.nonzero(vis[b, 0])[0], SCALE)
+        np.testing.assert_allclose(out[b], ref, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-13)
+
+
+def test_batched_scores_topk_and_tie_band_equal_per_row():
+    """Focal scores, top-k and the tie-band rule over rows equal one call
+    per row (which the pins above fix)."""
+    rng = np.random.default_rng(8)
+    q, K = _rand(rng, 5, 2, D), _rand(rng, 5, 90, D)
+    sc = O.focal_scores(q, K, 10, 80, SCALE)
+    for b in range(5):
+        np.testing.assert_array_equal(sc[b], O.focal_scores(q[b], K[b], 10, 80, SCALE))
+    k = 7
+    idx = O.topk(sc, k)
+    for b in range(5):
+        np.testing.assert_array_equal(idx[b], O.topk(sc[b], k))
+    bad = idx.copy()
+    bad[2, 0] = np.argsort(sc[2])[0] if np.argsort(sc[2])[0] not in idx[2] else np.argsort(sc[2])[1]
+    bad[2] = np.sort(bad[2])
+    bad[3, 1] = bad[3, 0]                            # a repeated index
+    ok, nd = O.tie_band_check(bad, sc, k)
+    for b in range(5):
+        assert (bool(ok[b]), int(nd[b])) == O.tie_band_check(bad[b], sc[b], k)
+    assert list(ok) == [True, True, False, False, True]
+
+
+@pytest.mark.parametrize("n", [1, 7, 50])
+def test_pool_rows_match_torch(n):
+    x = np.random.default_rng(n).random((3, n))
+    ref = torch.nn.functional.avg_pool1d(torch.from_numpy(x)[:, None], 7, 1, 3, count_include_pad=True)[:, 0].numpy()
+    np.testing.assert_allclose(O.avg_pool(x, 7), ref, rtol=1e-14, atol=1e-15)
