@@ -320,10 +320,13 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int h = 0; h < G; ++h) smax[h] = fmaxf(smax[h], dot[u][h]);
         }
-        if (ok[u] && sub < G && row >= lo && row < hi) {
+        // a segment row of this split whose block is missing is not attended:
+        // its logit is -inf (probability 0), so no stale value is ranked
+        if (sub < G && KVSEL_ROWT(base, u) < cnt && row >= lo && row < hi) {
           float dv = dot[u][0];
 #pragma unroll
           for (int h = 1; h < G; ++h) dv = sub == h ? dot[u][h] : dv;
+          if (!ok[u]) dv = -INFINITY;
           if (MODE == 2)
             s_logit[sub * a.seg_cap + (row - lo)] = dv;
           else if (row - lo < a.ld_logits)
@@ -561,8 +564,9 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 #pragma unroll
       for (int h = 1; h < G; ++h) dsel = sub == h ? dot[h] : dsel;
       const int t = base + grp + NG * u;
-      if (t < cnt && sub < G && pr[u] != kNoRow && r0 + t - lo < a.ld_logits)
-        a.logits[((size_t)b * a.hq + g * G + sub) * a.ld_logits + (r0 + t - lo)] = dsel;
+      // a row whose block is missing is not attended: logit -inf
+      if (t < cnt && sub < G && r0 + t - lo < a.ld_logits)
+        a.logits[((size_t)b * a.hq + g * G + sub) * a.ld_logits + (r0 + t - lo)] = pr[u] != kNoRow ? dsel : -INFINITY;
     }
   }
 }

@@ -28,7 +28,9 @@ constexpr int kStatThreads = 512;
 // error-free steps (TwoSum for x - m, a fused multiply-add for the product's
 // rounding error) to far below fp32 precision; its leading float goes through
 // the hardware exp2 and the small remainder r through 1 + r ln 2.  About two
-// fp32 ulps in all, with no fp64 arithmetic.
+// fp32 ulps in all, with no fp64 arithmetic.  A logit of -inf (a row that is
+// not attended, e.g. its cache block is missing) gives exactly 0: the
+// error-free steps would otherwise form -inf - (-inf).
 __device__ __forceinline__ float focal_term(float x, double m, double c) {
   const float mf = (float)m;
   const float ch = (float)c, cl = (float)(c - (double)ch);
@@ -37,7 +39,8 @@ __device__ __forceinline__ float focal_term(float x, double m, double c) {
   const float de = (x - (d - bv)) + (-mf - bv);
   const float y = d * ch;   // y + yl ~ (d + de) (ch + cl)
   const float yl = fmaf(d, ch, -y) + fmaf(d, cl, de * ch);
-  return __builtin_amdgcn_exp2f(y) * fmaf(yl, 0.6931471805599453f, 1.0f);
+  const float e = __builtin_amdgcn_exp2f(y) * fmaf(yl, 0.6931471805599453f, 1.0f);
+  return x == -INFINITY ? 0.f : e;
 }
 
 // logit(hh, i) for head hh < nh of the output row and token i < cnt.  Writes

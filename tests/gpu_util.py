@@ -57,3 +57,27 @@ def cpu_pool(t):
 
 def log_case(*parts):
     print("[case]", *parts, flush=True)
+
+
+def keep_freed_memory():
+    """Let the C heap keep freed blocks of any size instead of returning them
+    to the system, so the full-size checks, which allocate and free arrays
+    of tens of MB per (sequence, kv head), do not page-fault them in again
+    each time (mallopt M_MMAP_THRESHOLD and M_TRIM_THRESHOLD)."""
+    import ctypes
+    try:
+        libc = ctypes.CDLL("libc.so.6")
+    except OSError:
+        return
+    libc.mallopt(-3, 1 << 30)   # M_MMAP_THRESHOLD
+    libc.mallopt(-1, 1 << 30)   # M_TRIM_THRESHOLD
+
+
+def pair_rows(pool, table_row, g, rows):
+    """K or V rows at logical positions `rows` of one sequence's kv head g,
+    float64 on the host: the paged read (block table_row[j // 16], offset
+    j % 16) applied to a subset of positions."""
+    rows = np.asarray(rows, dtype=np.int64)
+    blk = torch.from_numpy(np.asarray(table_row, dtype=np.int64)[rows // 16]).to(pool.device)
+    off = torch.from_numpy(rows % 16).to(pool.device)
+    return O.widen(pool[blk, g, off, :])

@@ -880,3 +880,113 @@ def test_shared_attention_segment_logits():
             got = lg[b, g * G:(g + 1) * G, :90 - s0]
             assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
             assert np.all(np.isnan(lg[b, g * G:(g + 1) * G, 90 - s0:]))
+
+
+def _holed_reference(kc, vc, table_row, g, qg, n, s0, s1, hole):
+    """Oracle view of a sequence whose cache block `hole` is missing: its rows
+    are not attended (softmax over the remaining rows) and score 0."""
+    Kl = O.logical_rows(kc, table_row, g, n)
+    Vl = O.logical_rows(vc, table_row, g, n)
+    rows = np.array([j for j in range(n) if j // 16 != hole])
+    seg_rows = np.array([j for j in range(s0, s1) if j // 16 != hole])
+    sc = np.zeros(s1 - s0)
+    sc[seg_rows - s0] = O.focal_scores(qg, Kl[seg_rows], 0, len(seg_rows), SCALE)
+    out, _ = O.attention(qg, Kl, Vl, rows, SCALE)
+    return sc, out
+
+
+@pytest.mark.parametrize("form", ["fused", "split", "score"])
+def test_focal_selection_skips_missing_block(form):
+    """A segment block that is not a pool block (-1 in the table) is skipped:
+    its rows get logit -inf, probability 0 and score 0, and the rest of the
+    segment is normalised without them.  fused: the one-kernel focal pass
+    (256 pairs); split: split attention with the logits in the workspace and
+    the standalone selection; score: kvsel_score's logits kernel and
+    normaliser, then kvsel_topk.  The workspace is filled with NaN first, so a
+    logit that is not written would show."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(4400 + len(form))
+    G = 2
+    batch, hkv = (32, 8) if form == "fused" else (3, 4)
+    hq = hkv * G
+    n, s0, s1, hole = 700, 20, 600, 9          # block 9: rows 144 .. 159, inside the segment
+    k = 40
+    lens = [n] * batch
+    kv, kc, vc, table = make_kv(rng, batch, hkv, lens, [(s0, s1)] * batch)
+    holed = table.copy()
+    holed[:, hole] = -1
+    kvh = dataclasses.replace(kv, block_table=torch.from_numpy(holed).to(DEV))
+    ws = kvsel.Workspace(DEV, 1 << 22)
+    ws.buf.fill_(0xFF)                          # NaN in every float slot
+    ws.buf[:65536].zero_()                      # the reserved head stays zero
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(44)).to(torch.bfloat16).to(DEV)
+    out = torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV)
+    sc = torch.full((batch, hkv, s1 - s0), float("nan"), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((batch, hkv, k), dtype=torch.int32, device=DEV)
+    log_case("missing-block", form, batch, hkv)
+    if form == "score":
+        kvsel.score(kvh, q.view(batch, 1, hq, 128), 1, hq, SCALE, 0, 0, True, 1, sc, ws=ws)
+        kvsel.topk(sc, s1 - s0, k, idx)
+    else:
+        kvsel.focal_attn(kvh, q, hq, SCALE, out, k, idx, seg_scores=sc, ws=ws)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    for b in range(0, batch, max(1, batch // 4)):
+        for g in range(hkv):
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref_s, ref_o = _holed_reference(kc, vc, table[b], g, qg, n, s0, s1, hole)
+            got = sc[b, g].cpu().numpy()
+            assert np.all(got[16 * hole - s0:16 * hole + 16 - s0] == 0.0), (form, b, g)
+            kept = (np.arange(s0, s1) // 16) != hole    # segment rows outside the missing block
+            assert rel_err(got[kept], ref_s[kept]) < 2e-6, (form, b, g)
+            ok, nd = O.tie_band_check(idx[b, g].cpu().numpy(), ref_s, k, BAND)
+            assert ok, (form, b, g, nd)
+            if form != "score":
+                assert_attn(out[b, g * G:(g + 1) * G].cpu().numpy(), ref_o, f"missing-block out b{b} g{g}")
+
+
+def test_select_logits_skips_missing_block():
+    """The shared-prefix cascade's selection with one block of the shared
+    range missing from every table: kvsel_shared_attn writes -inf logits for
+    its rows, and kvsel_select_logits gives them score 0 and normalises the
+    segment over the remaining rows (against the oracle's focal scores and
+    top-k over those rows)."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(4500)
+    G, batch, hkv, prefix = 2, 33, 2, 200
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 30)
+    rb, re, hole = 16, 200, 5                    # block 5 of the range: rows 80 .. 95
+    s0, s1 = 32, 150
+    k = 12
+    holed = table.copy()
+    holed[:, hole] = -1
+    kvh = dataclasses.replace(kv, block_table=torch.from_numpy(holed).to(DEV),
+                              seg_begin=torch.full((batch,), s0, dtype=torch.int32, device=DEV),
+                              seg_end=torch.full((batch,), s1, dtype=torch.int32, device=DEV),
+                              max_seg_len=s1 - s0, min_seg_len=s1 - s0)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(45)).to(torch.bfloat16).to(DEV)
+    parts = torch.empty((1, batch, hq, 128), dtype=torch.float32, device=DEV)
+    plse = torch.empty((1, batch, hq), dtype=torch.float32, device=DEV)
+    logits = torch.full((batch, hq, s1 - s0), float("nan"), dtype=torch.float32, device=DEV)
+    sc = torch.full((batch, hkv, s1 - s0), float("nan"), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((batch, hkv, k), dtype=torch.int32, device=DEV)
+    log_case("select-logits-missing-block", batch, rb, re, hole)
+    kvsel.shared_attn(kvh, q, hq, SCALE, rb, re, parts, plse, splits=1, logits=logits)
+    kvsel.select_logits(kvh, logits, hq, SCALE, k, idx, seg_scores=sc)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    seg_rows = np.array([j for j in range(s0, s1) if j // 16 != hole])
+    for b in range(0, batch, 4):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref = np.zeros(s1 - s0)
+            ref[seg_rows - s0] = O.focal_scores(qg, Kl[seg_rows], 0, len(seg_rows), SCALE)
+            got = sc[b, g].cpu().numpy()
+            assert np.all(got[16 * hole - s0:16 * hole + 16 - s0] == 0.0), (b, g)
+            assert rel_err(got[seg_rows - s0], ref[seg_rows - s0]) < 2e-6, (b, g)
+            ok, nd = O.tie_band_check(idx[b, g].cpu().numpy(), ref, k, BAND)
+            assert ok, (b, g, nd)
