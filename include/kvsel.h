@@ -293,10 +293,12 @@ KVSEL_API size_t kvsel_mass_workspace(const kvsel_kv_desc *kv, int32_t num_q_hea
  *  layers with high concentration on image tokens.)
  *
  * ratios: fp32, device, layer l's n values at ratios[l * ld + j], j < n (for
- * instance the kvsel_visual_mass outputs of every warm-up step).  Means in
- * fp64; layers ranked by mean descending, equal means to the lower layer;
- * layers: int32 [n_pick], the chosen layers ascending.  Requires 1 <= n_pick
- * <= n_layers <= 1024, n >= 1, ld >= n.
+ * instance the kvsel_visual_mass outputs of every warm-up step).  The means
+ * are compared exactly (the sums are formed in integer arithmetic, so the
+ * result does not depend on the order of the terms; a non-finite ratio
+ * counts as 0); layers ranked by mean descending, equal means to the lower
+ * layer; layers: int32 [n_pick], the chosen layers ascending.  Requires
+ * 1 <= n_pick <= n_layers <= 1024, n >= 1, ld >= n.
  */
 KVSEL_API kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_t n_layers, int32_t n,
                                          int32_t n_pick, int32_t *layers, kvsel_stream stream);

@@ -147,8 +147,8 @@ def focal_scores(qg, K, s0: int, s1: int, scale, norm: str = "segment") -> np.nd
 def window_scores(qw, K, s0: int, s1: int, scale, causal: bool = True) -> np.ndarray:
     """FastKV window saliency of tokens [s0, s1) for one GQA group.
 
-    qw: [W, G, d], queries of the last W positions N-W .. N-1 (FastKV 2A,
-    "a recent window of queries").  Each (window row, head) is a softmax
+    qw: [W, G, d], queries of the last W positions N-W .. N-1 (FastKV 2A:
+    the queries of the most recent positions).  Each (window row, head) is a softmax
     over the keys it can see -- keys at positions <= its own when causal --
     and the probabilities are summed over the window rows and heads.
     """
@@ -393,15 +393,18 @@ def pick_focal_layers(ratios, n_pick: int) -> np.ndarray:
     with high concentration on image tokens).
 
     ratios: [n_layers, n], each layer's ratios over the warm-up steps,
-    sequences and heads.  Mean per layer in float64; layers ranked by mean
-    descending, equal means to the lower layer; the first n_pick are
-    returned ascending."""
+    sequences and heads.  The mean of each layer is taken exactly (a sum of
+    rationals, so no rounding and no dependence on the order of the terms);
+    a non-finite ratio counts as 0.  Layers ranked by mean descending, equal
+    means to the lower layer; the first n_pick are returned ascending."""
+    from fractions import Fraction
     r = np.asarray(ratios, F64)
     if not 1 <= n_pick <= r.shape[0]:
         raise ValueError("need 1 <= n_pick <= n_layers")
-    mean = r.sum(axis=1) / r.shape[1]
-    order = np.lexsort((np.arange(r.shape[0]), -mean))
-    return np.sort(order[:n_pick]).astype(np.int64)
+    n = r.shape[1]
+    mean = [sum((Fraction(float(x)) for x in row if np.isfinite(x)), Fraction(0)) / n for row in r]
+    order = sorted(range(r.shape[0]), key=lambda l: (-mean[l], l))
+    return np.sort(np.asarray(order[:n_pick], dtype=np.int64))
 
 
 # ---------------------------------------------------------------------------

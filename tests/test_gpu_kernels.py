@@ -139,6 +139,31 @@ def test_pick_layers(L, n, quant):
         assert np.array_equal(out.cpu().numpy(), O.pick_focal_layers(r.astype(np.float64), n_pick)), n_pick
 
 
+def test_pick_layers_exact_sums():
+    """Ranking by exact sums, independent of the order of the terms: layers
+    holding the same ratios in different orders tie (lower layer first); a
+    layer whose sum is larger by 2^-60 -- far below the rounding of any fp64
+    sum of 2048 ratios -- ranks first, one smaller by 2^-60 last."""
+    kvsel = K()
+    rng = np.random.default_rng(77)
+    base = rng.random(2048).astype(np.float32)
+    ratios = np.stack([base, rng.permutation(base), base[::-1], base, rng.permutation(base), base])
+    ratios = np.concatenate([ratios, np.zeros((6, 1), np.float32)], axis=1).astype(np.float32)
+    tiny = np.float32(2.0 ** -60)
+    ratios[3, -1] = tiny                   # exact sum: base's + 2^-60
+    ratios[5, -1] = -tiny                  # exact sum: base's - 2^-60
+    r64 = ratios.astype(np.float64)
+    assert list(O.pick_focal_layers(r64, 1)) == [3]
+    assert list(O.pick_focal_layers(r64, 5)) == [0, 1, 2, 3, 4]
+    rt = torch.from_numpy(np.ascontiguousarray(ratios)).to(DEV)
+    for n_pick in range(1, 7):
+        out = torch.full((n_pick,), -1, dtype=torch.int32, device=DEV)
+        kvsel.pick_layers(rt, n_pick, out)
+        torch.cuda.synchronize()
+        want = O.pick_focal_layers(r64, n_pick)
+        assert np.array_equal(out.cpu().numpy(), want), (n_pick, out.cpu().numpy(), want)
+
+
 def test_gather_full_budget_equals_dense_and_empty_rows():
     kvsel = K()
     rng = np.random.default_rng(11)

@@ -382,7 +382,8 @@ def test_visual_mass_closed_forms():
 
 
 def test_pick_focal_layers_cases():
-    r = np.array([[0.1, 0.3], [0.5, 0.5], [0.2, 0.2], [0.9, 0.1], [0.5, 0.5]])   # means .2 .5 .2 .5 .5
+    # dyadic ratios, so equal means are equal exactly: means .25 .5 .25 .5 .5
+    r = np.array([[0.125, 0.375], [0.5, 0.5], [0.25, 0.25], [0.875, 0.125], [0.5, 0.5]])
     # three layers tie at 0.5: the lower indices win
     assert list(O.pick_focal_layers(r, 2)) == [1, 3]
     assert list(O.pick_focal_layers(r, 3)) == [1, 3, 4]
@@ -391,6 +392,20 @@ def test_pick_focal_layers_cases():
     # the mean, not the peak, decides
     r2 = np.array([[0.0, 0.0, 1.0], [0.4, 0.4, 0.4]])
     assert list(O.pick_focal_layers(r2, 1)) == [1]
+
+
+def test_pick_focal_layers_exact_means():
+    """Means that fp64 summation would round together are told apart, and
+    means that are equal only as exact sums tie (to the lower layer), in
+    whatever order the terms come.  Layer 0: 2^-60 + 2^-60 + 1 (a left-to-right
+    fp64 sum rounds it to 1); layer 1: exactly 1; layer 2: 1 + 2^-59 + 0, the
+    same exact sum as layer 0; layer 3: the terms of layer 0 reversed."""
+    t = 2.0 ** -60
+    r = np.array([[t, t, 1.0], [1.0, 0.0, 0.0], [1.0, 2 * t, 0.0], [1.0, t, t]])
+    assert list(O.pick_focal_layers(r, 1)) == [0]
+    assert list(O.pick_focal_layers(r, 3)) == [0, 2, 3]
+    assert list(O.pick_focal_layers(r[[1, 0]], 1)) == [1]        # layer 1 of this pair holds the larger sum
+    assert list(O.pick_focal_layers(np.array([[np.nan, 0.5], [0.5, 0.0]]), 1)) == [0]   # NaN counts as 0: a tie
 
 
 @pytest.mark.parametrize("seed", range(3))
