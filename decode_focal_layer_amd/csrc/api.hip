@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kvsel_internal.h"
 #include "mfma_kernels.h"
@@ -234,6 +236,73 @@ kvsel_status kvsel_gather_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   AttnArgs a = attn_args(kv, q, num_q_heads, scale, idx, k, p, (char *)ws, out, lse, 0);
   a.dense = 0;   // k == 0: only the always-attended rows
   return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "gather_attn launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------
+// Gathered attention without a caller workspace: the split records live in a
+// fixed device array of this library, one per GPU (each device holds its own
+// copy of a __device__ variable).  Its address is looked up once per device,
+// with that device current, by hipGetSymbolAddress; host code only ever uses
+// that address, never the array's name (which on the host is a stand-in, not
+// a device address).
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+constexpr int kNoAllocMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kNoAllocMaxDevices];   // per device, null until looked up
+
+// this device's copy of `scratch`, looked up on the first call on the device
+kvsel_status scratch_of_current_device(char **ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVSEL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(KVSEL_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || p == nullptr)
+      return fail(KVSEL_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<char *>(g_scratch_ptr[dev]);
+  return KVSEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvsel_status kvsel_gather_attn_noalloc(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale,
+                                       const int32_t *idx, int32_t k, float *out, float *lse, kvsel_stream stream) {
+  kvsel_status st;
+  int G;
+  if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
+  if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
+  if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
+  if (out == nullptr) return fail(KVSEL_EINVAL, "out is NULL");
+  if (k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
+  if (k > 0 && idx == nullptr) return fail(KVSEL_EINVAL, "idx is NULL with k > 0");
+  if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  const AttnPlan p = attn_plan(kv->batch, kv->num_kv_heads, num_q_heads, gather_rows_bound(kv, k), 0,
+                               kv->max_seg_len, kv->max_seq_len);
+  if (p.total > kNoAllocScratchBytes)
+    return fail(KVSEL_ENOSPC, "the call needs %zu bytes of scratch; the fixed buffer holds %zu (use kvsel_gather_attn)",
+                p.total, kNoAllocScratchBytes);
+  char *ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != KVSEL_OK) return st;
+  // the split records are written before they are read, and the reserved
+  // head of the layout is not used: nothing has to start at zero
+  AttnArgs a = attn_args(kv, q, num_q_heads, scale, idx, k, p, ws, out, lse, 0);
+  a.dense = 0;
+  return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "gather_attn_noalloc launch");
 }
 
 kvsel_status kvsel_dense_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads, float scale, float *out,

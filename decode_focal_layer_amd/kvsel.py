@@ -28,7 +28,7 @@ SYMBOLS = (
     "kvsel_version", "kvsel_status_string", "kvsel_last_error",
     "kvsel_score", "kvsel_score_workspace",
     "kvsel_topk", "kvsel_topk_workspace",
-    "kvsel_gather_attn", "kvsel_attn_workspace",
+    "kvsel_gather_attn", "kvsel_attn_workspace", "kvsel_gather_attn_noalloc",
     "kvsel_dense_attn", "kvsel_focal_attn", "kvsel_gather_rows",
     "kvsel_visual_mass", "kvsel_mass_workspace", "kvsel_pick_layers",
     "kvsel_pool_create", "kvsel_pool_destroy", "kvsel_pool_free_count", "kvsel_pool_refcount",
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_topk_workspace.argtypes = [_I32, _I32, _I32]
     L.kvsel_gather_attn.restype = _I32
     L.kvsel_gather_attn.argtypes = [_DP, _P, _I32, _F32, _P, _I32, _P, _P, _P, _SZ, _P]
+    L.kvsel_gather_attn_noalloc.restype = _I32
+    L.kvsel_gather_attn_noalloc.argtypes = [_DP, _P, _I32, _F32, _P, _I32, _P, _P, _P]
     L.kvsel_attn_workspace.restype = _SZ
     L.kvsel_attn_workspace.argtypes = [_DP, _I32, _I32, _I32, _I32]
     L.kvsel_dense_attn.restype = _I32
@@ -315,6 +317,23 @@ def gather_attn(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, idx: Op
     p, n = w.ptr_and_size(attn_workspace(kv, num_q_heads, k))
     _check(lib().kvsel_gather_attn(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(idx), k, _ptr(out), _ptr(lse),
                                    p, n, _stream(stream)))
+    return out
+
+
+def gather_attn_noalloc(kv: KV, q: torch.Tensor, num_q_heads: int, scale: float, idx: Optional[torch.Tensor],
+                        k: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_gather_attn_noalloc: kvsel_gather_attn with the library's fixed
+    per-device scratch instead of a workspace (no allocation anywhere)."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.float32, "out")
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+        if idx.numel() != kv.batch * kv.hkv * k:
+            raise ValueError("idx must be [batch][num_kv_heads][k]")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(lib().kvsel_gather_attn_noalloc(kv.ref(), _ptr(q), num_q_heads, scale, _ptr(idx), k, _ptr(out),
+                                           _ptr(lse), _stream(stream)))
     return out
 
 

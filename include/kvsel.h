@@ -210,6 +210,25 @@ KVSEL_API size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k);
 KVSEL_API kvsel_status kvsel_gather_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
                                float scale, const int32_t *idx, int32_t k, float *out, float *lse,
                                void *ws, size_t ws_bytes, kvsel_stream stream);
+/*
+ * kvsel_gather_attn_noalloc -- kvsel_gather_attn without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * minus ws / ws_bytes, same result (up to summation order, as any two calls
+ * of kvsel_gather_attn).  Scratch (the split records of pairs whose rows are
+ * split over several work-groups) lives in a fixed 4 MiB device array of the
+ * library, one per GPU, held until the process ends; its address is looked
+ * up on the first call on each device.  A call that would need more scratch
+ * than that returns KVSEL_ENOSPC before anything is enqueued (use
+ * kvsel_gather_attn).  Every call on one GPU shares its array: calls that may
+ * run at the same time on one GPU (other streams, other threads) race on it
+ * and must not overlap.  The array needs no clearing: every record a call
+ * reads it has written itself.  Makes no allocation of any kind.
+ */
+KVSEL_API kvsel_status kvsel_gather_attn_noalloc(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
+                                                 float scale, const int32_t *idx, int32_t k, float *out, float *lse,
+                                                 kvsel_stream stream);
+
 /* Workspace bytes for kvsel_gather_attn with budget k (k >= 0), or for
  * kvsel_dense_attn when k < 0 (with_scores: seg_scores will be passed; norm:
  * its normalisation).  0 if the descriptor or head count is invalid. */

@@ -31,7 +31,7 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 28
+    assert len(names) == 29
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -76,6 +76,23 @@ def test_gather_attn_rejects_bad_descriptor(L, over, code):
 ])
 def test_gather_attn_rejects_bad_args(L, kw, code):
     assert gather(L, desc(), **kw) == code
+
+
+def test_gather_attn_noalloc_rejects(L):
+    """The allocation-free variant validates like kvsel_gather_attn, and a
+    call needing more split records than its fixed 4 MiB buffer holds is
+    refused with KVSEL_ENOSPC before anything is enqueued."""
+    na = lambda d, hq=16, k=5, idx=FAKE, out=FAKE: L.kvsel_gather_attn_noalloc(ctypes.byref(d), FAKE, hq, 0.088, idx, k,
+                                                                                out, None, None)
+    assert na(desc(head_dim=64)) == EUNSUP
+    assert na(desc(), hq=12) == EINVAL
+    assert na(desc(), out=0) == EINVAL
+    assert na(desc(), k=-1) == EINVAL
+    assert na(desc(), idx=0) == EINVAL
+    # 64 x 8 pairs of G = 8 split in two: 64 * 64 * 2 records of 640 B > 4 MiB
+    big = desc(batch=64, max_blocks_per_seq=100, max_seq_len=1600, max_seg_len=1000, min_seg_len=1000, num_blocks=6400)
+    assert na(big, hq=64) == ENOSPC
+    assert b"fixed buffer" in L.kvsel_last_error()
 
 
 def test_dense_attn_checks(L):
