@@ -79,10 +79,10 @@ def step_bytes(cfg, t, batch):
     return n_focal * focal + (n_pre * dense if t == 0 else 0) + n_sparse * sparse
 
 
-def cpu_baseline(w, cfg, t_sample: int, n_seq: int):
+def cpu_baseline(w, cfg, t_sample: int, n_seq: int, cores_limit=None):
     """The oracle on the host cores for the same step, on n_seq of the batch's
     sequences (all 28 layers, every kv head): returns steps/s scaled to the
-    whole batch."""
+    whole batch.  cores_limit: BLAS threads (default: every core available)."""
     import torch
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import oracle as O
@@ -97,7 +97,7 @@ def cpu_baseline(w, cfg, t_sample: int, n_seq: int):
     local_table = np.arange(n_seq * mb).reshape(n_seq, mb)
     qc = w.q[t_sample].cpu()
     plan = O.focal_layer_plan(cfg.layers, cfg.focal, t_sample)
-    with threadpool_limits(limits=cores):
+    with threadpool_limits(limits=cores_limit or cores):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         t0 = time.perf_counter()
         for b in range(n_seq):
@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="attention with KVSEL_FLAG_DETERMINISTIC (rows summed in a fixed order)")
     ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "profile", "verify", "prefill"],
                     help="c1 (default) is the metric's workload; the others print their own line")
     args = ap.parse_args()
@@ -171,7 +173,8 @@ def main():
           f"({sum(p.numel() for p in w.k_pool) * 4 / 1e9:.1f} GB of K/V)", file=sys.stderr, flush=True)
     max_len = int(w.seq_len_np.max())
     kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
-                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual)
+                    max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                    deterministic=args.deterministic)
            for l in range(cfg.layers)]
     dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, warm_start=True, device=dev)
     T = cfg.steps
@@ -196,6 +199,22 @@ def main():
     steps_per_s = 1000.0 / ms_per_step
     total_bytes = sum(step_bytes(cfg, (args.warmup + i) % T, cfg.batch) for i in range(args.steps))
     gbs = total_bytes / (ms / 1e3) / 1e9
+
+    # outside the timed region: one whole 64-step cycle (steps 0 .. 63, the
+    # first of them with its dense layers), so that the rate over the cycle's
+    # mean bytes is reported beside the rate over the timed steps' bytes
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for t in range(T):
+        dec.step(t, w.q[t], w.seq_len[t])
+    c1.record()
+    torch.cuda.synchronize()
+    cyc_ms = c0.elapsed_time(c1)
+    cyc_bytes = sum(step_bytes(cfg, t, cfg.batch) for t in range(T))
+    full_cycle = {"steps": T, "ms_per_step": round(cyc_ms / T, 4), "bytes_per_step_avg": int(cyc_bytes / T),
+                  "hbm_gbs_algorithmic": round(cyc_bytes / (cyc_ms / 1e3) / 1e9, 1),
+                  "hbm_frac_of_peak": round(cyc_bytes / (cyc_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     # roofline of the dominant kernel (gathered sparse attention, 26 of 28 layers):
     # the same K steps again, with HIP events on the decode stream at the two ends
@@ -253,6 +272,9 @@ def main():
     cpu = None
     if args.cpu_seqs > 0:
         cpu = cpu_baseline(w, cfg, 1, args.cpu_seqs)
+        # the same oracle on one core, on a smaller sample of the same step
+        one = cpu_baseline(w, cfg, 1, max(1, args.cpu_seqs // 3), cores_limit=1)
+        cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
 
     line = {
         "metric": "decode attn steps/s (score + top-k + sparse attention, 28 layers)",
@@ -270,11 +292,13 @@ def main():
         "config": {"workload": "c1_fastocr_decode: 28 layers, batch 32, 16q/8kv heads, head_dim 128, "
                                "6400 visual (80x80) + 1024 text tokens, focal layers {3,14}, top-320 per kv head, "
                                "64-step cycle, bf16 KV with fp32 accumulation",
-                   "global_batch": cfg.batch, "seq_len": cfg.prefix_len, "parallelism": "single GPU"},
+                   "global_batch": cfg.batch, "seq_len": cfg.prefix_len, "parallelism": "single GPU",
+                   "deterministic": bool(args.deterministic)},
         "tokens_per_s": round(steps_per_s * cfg.batch, 1),
         "hbm_gbs_algorithmic": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step_avg": int(total_bytes / args.steps),
+        "full_cycle": full_cycle,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -70,6 +70,7 @@ kvsel_status check_desc(const kvsel_kv_desc *kv, bool need_v) {
   if ((uint64_t)kv->num_blocks * (uint64_t)kv->num_kv_heads * kBlk >= 0xffffffffull)
     return fail(KVSEL_EUNSUPPORTED, "pool has 2^32 or more rows");
   if (kv->shared_rows < 0) return fail(KVSEL_EINVAL, "shared_rows must be >= 0");
+  if ((kv->flags & ~KVSEL_FLAG_DETERMINISTIC) != 0) return fail(KVSEL_EINVAL, "unknown flags 0x%x", kv->flags);
   if (!kv->k_pool || !kv->block_table || !kv->seq_len || !kv->seg_begin || !kv->seg_end)
     return fail(KVSEL_EINVAL, "k_pool, block_table, seq_len, seg_begin and seg_end are required");
   if (need_v && !kv->v_pool) return fail(KVSEL_EINVAL, "v_pool is required");
@@ -118,6 +119,7 @@ AttnArgs attn_args(const kvsel_kv_desc *kv, const uint16_t *q, int32_t hq, float
   a.num_blocks = kv->num_blocks;
   a.max_blocks = kv->max_blocks_per_seq;
   a.shared_rows = kv->shared_rows;
+  a.det = (kv->flags & KVSEL_FLAG_DETERMINISTIC) != 0 ? 1 : 0;
   a.hkv = kv->num_kv_heads;
   a.hq = hq;
   a.k = k;
@@ -553,7 +555,9 @@ kvsel_status kvsel_focal_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_
   if ((st = check_ws(ws, ws_bytes, p.total)) != KVSEL_OK) return st;
   AttnArgs a = attn_args(kv, q, num_q_heads, scale, nullptr, 0, p, (char *)ws, out, lse, mode);
   a.dense = 1;
-  if (p.nsplit == 1 && norm == KVSEL_NORM_SEGMENT && fused_focal_fits(G, kv->max_seg_len)) {
+  // the fused form's selecting waves leave the streaming part way: it is taken
+  // only when the rows may be summed in any order
+  if (p.nsplit == 1 && norm == KVSEL_NORM_SEGMENT && fused_focal_fits(G, kv->max_seg_len) && a.det == 0) {
     // one kernel: attention, segment logits kept in LDS, selection per (sequence, kv head)
     a.logits = nullptr;
     a.sel_idx = idx;

@@ -29,6 +29,8 @@
 //    trailing by a quarter of the loop; taking the next chunk on demand ends
 //    every wave within one chunk of the others.  The chunk a wave gets varies
 //    from run to run, so the output's rounding (not its row set) may too.
+//    Deterministic launches (a.det) give wave w the chunks w, w + waves, ...
+//    instead: the same sums in the same order on every run.
 //  * the lane-group states are merged in registers (the four groups of a
 //    wave) and in LDS (across waves).
 #include <type_traits>
@@ -384,6 +386,15 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   // has passed cend: the counter only grows, and a wave takes a new chunk
   // only after finishing one.
   auto run = [&](uint32_t *ctr, int c, int cend) {
+    if (a.det) {   // a fixed share per wave (modes 0, 1 and 3 only)
+      for (; c < cend; c += NW) {
+        uint4 kr[U], vr[U];
+        bool ok[U];
+        load_rows(c * CH, kr, vr, ok);
+        consume(c * CH, kr, vr, ok);
+      }
+      return;
+    }
     while (c < cend) {
       uint32_t nxt = 0;
       if (lane == 0) nxt = atomicAdd(ctr, 1u);   // its latency hides behind the loads
@@ -592,6 +603,7 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
   const bool stream = a.shared_rows == 0;   // rows shared across sequences stay cached
   dim3 grid(a.nsplit, a.hkv, batch);
   if (a.sel_idx != nullptr) {
+    if (a.det) return hipErrorInvalidValue;   // the fused focal pass takes rows on demand
     if constexpr (NT < kStatThreads) {
       return hipErrorInvalidValue;   // the fused selection needs kStatThreads / 64 waves
     } else {

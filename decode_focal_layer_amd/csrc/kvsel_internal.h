@@ -42,6 +42,7 @@ struct AttnArgs {
   int64_t num_blocks;
   int32_t max_blocks, hkv, hq, k;
   int32_t shared_rows;  // > 0: rows are shared across sequences, load them through the caches
+  int32_t det;          // 1: each wave takes a fixed share of the rows (bitwise reproducible)
   const uint16_t *q;
   const int32_t *idx;   // [batch][hkv][k] kept indices (gather)
   int32_t dense;        // 1: every row [0, seq_len); 0: gather

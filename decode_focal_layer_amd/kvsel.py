@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libkvsel.so")
 
 REDUCE_GROUP, REDUCE_ALL = 0, 1
 NORM_SEGMENT, NORM_CONTEXT = 0, 1
+FLAG_DETERMINISTIC = 1
 STATUS = {0: "KVSEL_OK", -1: "KVSEL_EINVAL", -2: "KVSEL_ENOSPC", -3: "KVSEL_EUNSUPPORTED", -4: "KVSEL_EHIP"}
 
 # every symbol the public header declares
@@ -53,7 +54,7 @@ class KvDescC(ctypes.Structure):
         ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
         ("seg_begin", ctypes.c_void_p), ("seg_end", ctypes.c_void_p),
-        ("shared_rows", ctypes.c_int32),
+        ("shared_rows", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -170,6 +171,7 @@ class KV:
     max_seg_len: int
     min_seg_len: int = 0
     shared_rows: int = 0   # cache hint: leading rows shared across sequences
+    deterministic: bool = False   # KVSEL_FLAG_DETERMINISTIC: bitwise reproducible attention
 
     def __post_init__(self):
         _need(self.k_pool, torch.bfloat16, "k_pool")
@@ -197,6 +199,7 @@ class KV:
         c.seg_begin = self.seg_begin.data_ptr()
         c.seg_end = self.seg_end.data_ptr()
         c.shared_rows = int(self.shared_rows)
+        c.flags = FLAG_DETERMINISTIC if self.deterministic else 0
         self.c = c
 
     @property
@@ -213,7 +216,7 @@ class KV:
     def with_seq_len(self, seq_len: torch.Tensor, max_seq_len: Optional[int] = None) -> "KV":
         return KV(self.k_pool, self.v_pool, self.block_table, seq_len, self.seg_begin, self.seg_end,
                   self.max_seq_len if max_seq_len is None else max_seq_len, self.max_seg_len, self.min_seg_len,
-                  self.shared_rows)
+                  self.shared_rows, self.deterministic)
 
 
 class Workspace:

@@ -71,13 +71,16 @@ typedef int32_t kvsel_status;
 #define KVSEL_EUNSUPPORTED (-3)  /* head_dim != 128, block_size != 16, group > 8  */
 #define KVSEL_EHIP         (-4)  /* a HIP launch failed                           */
 
-#define KVSEL_VERSION 2
+#define KVSEL_VERSION 3
 
 #define KVSEL_REDUCE_GROUP 0     /* one score per (sequence, kv head)            */
 #define KVSEL_REDUCE_ALL   1     /* one score per (sequence): summed over heads  */
 
 #define KVSEL_NORM_SEGMENT 0     /* softmax over the candidate segment only      */
 #define KVSEL_NORM_CONTEXT 1     /* softmax over every row the query can see     */
+
+/* kvsel_kv_desc.flags */
+#define KVSEL_FLAG_DETERMINISTIC 1   /* attention sums its rows in a fixed order  */
 
 typedef void *kvsel_stream;      /* hipStream_t */
 
@@ -102,6 +105,16 @@ typedef void *kvsel_stream;      /* hipStream_t */
  * not evict what is reused from call to call (block tables, indices,
  * queries); with shared_rows > 0 they load every row through the caches so
  * that the prefix stays there.  Results do not depend on it.
+ *
+ * flags: 0 or KVSEL_FLAG_DETERMINISTIC.  By default the attention calls
+ * (kvsel_gather_attn, kvsel_dense_attn, kvsel_focal_attn,
+ * kvsel_visual_mass) hand rows to waves on demand, so which wave adds which
+ * row, and with it the rounding of the output (not the row set, the scores
+ * or the kept indices), can vary from run to run.  With
+ * KVSEL_FLAG_DETERMINISTIC every wave takes a fixed share of the rows and the
+ * focal selection runs as its own kernel after the attention, so every
+ * output is bitwise reproducible, at some cost in speed.  Every other call is
+ * bitwise reproducible either way.  Other bits: KVSEL_EINVAL.
  */
 typedef struct {
   int32_t batch;               /* sequences (or branches)                        */
@@ -122,6 +135,7 @@ typedef struct {
   const int32_t *seg_begin;    /* [batch], device                                */
   const int32_t *seg_end;      /* [batch], device                                */
   int32_t shared_rows;         /* >= 0: leading rows shared across sequences      */
+  int32_t flags;               /* KVSEL_FLAG_* (0: default)                      */
 } kvsel_kv_desc;
 
 /* Version of this header's ABI (KVSEL_VERSION). */

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvsel_version() == 2
+    assert L.kvsel_version() == 3
     assert L.kvsel_status_string(-2) == b"workspace too small"
 
 
@@ -61,7 +61,7 @@ def gather(L, d, hq=16, q=FAKE, k=5, idx=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 
     (dict(k_pool=0), EINVAL), (dict(v_pool=0), EINVAL), (dict(block_table=0), EINVAL), (dict(seq_len=0), EINVAL),
     (dict(seg_begin=0), EINVAL), (dict(seg_end=0), EINVAL), (dict(k_pool=FAKE + 8), EINVAL),
     (dict(batch=4096, num_kv_heads=8), EUNSUP), (dict(num_blocks=1 << 28), EUNSUP),
-    (dict(shared_rows=-1), EINVAL),
+    (dict(shared_rows=-1), EINVAL), (dict(flags=2), EINVAL), (dict(flags=-1), EINVAL),
 ])
 def test_gather_attn_rejects_bad_descriptor(L, over, code):
     assert gather(L, desc(**over)) == code

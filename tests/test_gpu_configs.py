@@ -182,3 +182,38 @@ def test_c4_branches_small_and_shared_prefix_equals_private_copy():
     assert (dec2.out - out_shared).abs().max().item() < 1e-5   # summation order only
     for f in cfg.focal:
         assert torch.equal(dec2.selection(f), dec.selection(f))
+
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+def test_deterministic_flag_bitwise_at_full_shape(cascade):
+    """KVSEL_FLAG_DETERMINISTIC: two runs of 3 decode steps at a full shape
+    -- the FastOCR decode (28 layers, batch 32, 7424-row caches) or the
+    branched decode's cascade (512 branches over the shared prefix) -- give
+    bitwise equal outputs and kept sets, and the same outputs as the default
+    mode within the rounding of the row order."""
+    from decode_focal_layer_amd import kvsel
+    from decode_focal_layer_amd.decode import FocalDecoder
+    cfg = synth.small(synth.C4 if cascade else synth.C1, steps=3)
+    w = gen.make_focal(cfg, DEV)
+    max_len = int(w.seq_len_np.max())
+    runs = {}
+    for det, rep in ((True, 0), (True, 1), (False, 0)):
+        kvs = [kvsel.KV(w.k_pool[l], w.v_pool[l], w.block_table, w.seq_len[0], w.seg_begin, w.seg_end,
+                        max_seq_len=max_len, max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                        shared_rows=cfg.prefix_len if cascade else 0, deterministic=det)
+               for l in range(cfg.layers)]
+        dec = FocalDecoder(kvs, cfg.hq, cfg.k, cfg.focal, cfg.scale, cfg.n_visual, device=DEV,
+                           shared_tail=(cfg.n_visual, cfg.prefix_len) if cascade else None)
+        outs, sets = [], []
+        log_case("deterministic", cascade, det, rep)
+        for t in range(cfg.steps):
+            dec.step(t, w.q[t], w.seq_len[t])
+            outs.append(dec.out.clone())
+            sets.append(torch.stack([dec.selection(f).clone() for f in cfg.focal]))
+        torch.cuda.synchronize()
+        runs[(det, rep)] = (torch.stack(outs).cpu(), torch.stack(sets).cpu())
+    (o1, s1), (o2, s2), (o3, s3) = runs[(True, 0)], runs[(True, 1)], runs[(False, 0)]
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(s1, s3)
+    assert (o1 - o3).abs().max().item() < 1e-5
