@@ -687,22 +687,21 @@ kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_r
 
 // ------------------------------------------------------------------------
 size_t kvsel_topk_workspace(int32_t rows, int32_t n, int32_t k) {
-  (void)rows;
-  (void)n;
-  (void)k;
-  return 0;
+  if (rows < 1 || k < 1 || k > n) return 0;
+  return topk_workspace_bytes(rows, n);
 }
 
 kvsel_status kvsel_topk(const float *scores, int64_t ld, int32_t rows, const int32_t *n_per_row, int32_t n, int32_t k,
                         const int32_t *warm_idx, int32_t *idx, void *ws, size_t ws_bytes, kvsel_stream stream) {
-  (void)ws;
-  (void)ws_bytes;
+  kvsel_status st;
   if (scores == nullptr || idx == nullptr) return fail(KVSEL_EINVAL, "scores and idx are required");
   if (rows < 1) return fail(KVSEL_EINVAL, "rows must be >= 1");
   if (k < 1 || k > n) return fail(KVSEL_EINVAL, "need 1 <= k <= n (k=%d, n=%d)", k, n);
   if ((int64_t)n > ld) return fail(KVSEL_EINVAL, "need n <= ld");
+  if (rows > 65535) return fail(KVSEL_EINVAL, "rows must be <= 65535");
+  if ((st = check_ws(ws, ws_bytes, topk_workspace_bytes(rows, n))) != KVSEL_OK) return st;
   TopkArgs a{scores, ld, rows, n, k, warm_idx, idx, n_per_row};
-  return hip_status(launch_topk(a, (hipStream_t)stream), "topk launch");
+  return hip_status(launch_topk(a, ws, (hipStream_t)stream), "topk launch");
 }
 
 // ------------------------------------------------------------------------

@@ -290,7 +290,9 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = KVSEL_ROWT(base, u);
-      const uint32_t pr = t < cnt ? s_prow[t] : kNoRow;
+      // unbranched LDS read (a read under a branch is waited for at once)
+      const uint32_t pr_t = s_prow[max(min(t, cnt - 1), 0)];
+      const uint32_t pr = t < cnt ? pr_t : kNoRow;
       ok[u] = pr != kNoRow;
       // a row that is not attended reads this lane's query (a valid, finite
       // 16 bytes) and gets probability 0
@@ -563,7 +565,8 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + grp + NG * u;
-      pr[u] = t < cnt ? row_to_phys(a, b, g, r0 + t) : kNoRow;
+      const uint32_t pt = row_to_phys(a, b, g, r0 + min(t, cnt - 1));   // unbranched table read
+      pr[u] = t < cnt ? pt : kNoRow;
       kr[u] = pr[u] != kNoRow ? *reinterpret_cast<const uint4 *>(kbase + (size_t)pr[u] * kD)
                               : make_uint4(0, 0, 0, 0);
     }

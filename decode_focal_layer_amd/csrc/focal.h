@@ -272,7 +272,7 @@ __device__ void focal_select_fused(Grp &grp, float *s_logit, int cap, int seg, d
   }
   if (theta > lo) lo = theta;
   auto key = [&](int i) -> uint32_t { return keys[i]; };
-  radix_select<NTS>(grp, key, seg, k, theta, lo, hi, (uint32_t)seg, dst, fs.rx);
+  radix_select<NTS, true, 25>(grp, key, seg, k, theta, lo, hi, (uint32_t)seg, dst, fs.rx, keys);
 }
 
 }  // namespace kvsel

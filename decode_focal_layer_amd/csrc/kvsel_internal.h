@@ -165,7 +165,9 @@ struct TopkArgs {
   int32_t *idx;
   const int32_t *n_row;   // or null: row r ranks its first min(n_row[r], n) scores
 };
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// workspace of kvsel_topk: coarse-bin counts of the long-row path (0: none)
+size_t topk_workspace_bytes(int rows, int n);
+hipError_t launch_topk(const TopkArgs &a, void *ws, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // row gather

@@ -117,16 +117,15 @@ __device__ __forceinline__ void excl_scan2(Grp &grp, uint32_t a, uint32_t b, uin
 }
 
 // f(i, key(i)) for i = t, t + NTS, ... below n; each thread issues B key
-// reads before using them (one memory latency per B keys)
+// reads before using them (one memory latency per B keys).  The reads past n
+// read key n - 1 instead of being skipped: a read under a branch would be
+// waited for before the next one is issued.
 template <int NTS, int B, typename KeyFn, typename F>
 __device__ __forceinline__ void each_key(int t, KeyFn key, int n, F f) {
   for (int base = 0; base < n; base += B * NTS) {
     uint32_t x[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int i = base + j * NTS + t;
-      x[j] = i < n ? key(i) : 0u;
-    }
+    for (int j = 0; j < B; ++j) x[j] = key(min(base + j * NTS + t, n - 1));
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int i = base + j * NTS + t;
@@ -137,16 +136,14 @@ __device__ __forceinline__ void each_key(int t, KeyFn key, int n, F f) {
 
 // the calling wave walks [i0, i1) 64 consecutive keys at a time:
 // f(i, valid, key) in every lane, the same number of calls in each lane
+// (reads past i1 read key i1 - 1, unbranched, as in each_key)
 template <int B, typename KeyFn, typename F>
 __device__ __forceinline__ void each_key_wave(KeyFn key, int i0, int i1, F f) {
   const int lane = threadIdx.x & 63;
   for (int base = i0; base < i1; base += B * 64) {
     uint32_t x[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int i = base + j * 64 + lane;
-      x[j] = i < i1 ? key(i) : 0u;
-    }
+    for (int j = 0; j < B; ++j) x[j] = key(min(base + j * 64 + lane, i1 - 1));
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int b2 = base + j * 64;
@@ -222,13 +219,18 @@ __device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &
 // The k largest of key(i), i in [0, n), among the candidates (keys >= theta),
 // written ascending to dst; n > k >= 1.  lo <= every candidate key <= hi, and
 // nin >= the number of candidates (at least k of them).  LDS_KEYS: key(i)
-// reads LDS (the output pass then walks per-thread index ranges); otherwise
-// global memory (the output pass walks per-wave ranges 64 consecutive keys at
-// a time, so that the reads coalesce).
-template <int NTS, bool LDS_KEYS = true, typename Grp, typename KeyFn>
+// reads LDS; otherwise global memory, with more reads in flight per lane.
+// Output, keys in global memory: per-wave ranges walked 64 consecutive keys
+// at a time, so that the reads coalesce and each wave's chosen indices leave
+// in contiguous runs.  Keys in LDS: per-participant ranges of C keys (C odd:
+// the lanes of a wave read different banks); with stage (the LDS array the
+// keys live in, writable once they are read) and C <= STAGE_C, each
+// participant holds its keys in registers while the chosen indices are
+// placed in that array, which is then copied out in order (coalesced).
+template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, typename Grp, typename KeyFn>
 __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
-                             int32_t *dst, RadixShared<NTS> &sh) {
-  constexpr int B = 8;
+                             int32_t *dst, RadixShared<NTS> &sh, uint32_t *stage = nullptr) {
+  constexpr int B = LDS_KEYS ? 8 : 32;
   constexpr int NW = NTS / 64;
   const int t = grp.t(), lane = t & 63, w = t >> 6;
   const uint32_t range = hi - lo;
@@ -347,16 +349,15 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
   if constexpr (LDS_KEYS) {
     // ---- ordered output: participant t owns the indices [t*C, (t+1)*C) ----
     // It counts its keys above T and equal to T, the exclusive scans of those
-    // counts place it, and it writes its chosen indices in order: ascending
+    // counts place it, and it takes its chosen indices in order: ascending
     // output, and the equal keys taken are the lowest-indexed keq.
-    // C odd: a wave's 64 lanes read 64 different LDS banks
     const int C = ((n + NTS - 1) / NTS) | 1;
     const int i0 = min(n, t * C), i1 = min(n, i0 + C);
     uint32_t cg = 0, ce = 0;
     for (int b0 = i0; b0 < i1; b0 += B) {
       uint32_t x[B];
 #pragma unroll
-      for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+      for (int j = 0; j < B; ++j) x[j] = key(min(b0 + j, n - 1));
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         cg += (b0 + j < i1 && x[j] > T) ? 1u : 0u;
@@ -367,21 +368,42 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
     uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
     uint32_t eq_seen = eq_before;
-    for (int b0 = i0; b0 < i1; b0 += B) {
-      uint32_t x[B];
+    if (STAGE_C > 0 && stage != nullptr && C <= STAGE_C) {
+      constexpr int SC = STAGE_C > 0 ? STAGE_C : 1;
+      uint32_t x[SC];
 #pragma unroll
-      for (int j = 0; j < B; ++j) x[j] = b0 + j < i1 ? key(b0 + j) : 0u;
+      for (int j = 0; j < SC; ++j) x[j] = key(min(i0 + j, n - 1));
+      grp.sync();   // every participant holds its keys: the array is free
 #pragma unroll
-      for (int j = 0; j < B; ++j) {
-        if (b0 + j < i1) {
+      for (int j = 0; j < SC; ++j) {
+        if (i0 + j < i1) {
           bool take = x[j] > T;
           if (x[j] == T) {
             take = eq_seen < keq;
             ++eq_seen;
           }
-          if (take) {
-            if (pos < (uint32_t)k) dst[pos] = b0 + j;
-            ++pos;
+          if (take) stage[pos++] = (uint32_t)(i0 + j);
+        }
+      }
+      grp.sync();
+      for (int i = t; i < k; i += NTS) dst[i] = (int32_t)stage[i];
+    } else {
+      for (int b0 = i0; b0 < i1; b0 += B) {
+        uint32_t x[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) x[j] = key(min(b0 + j, n - 1));
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+          if (b0 + j < i1) {
+            bool take = x[j] > T;
+            if (x[j] == T) {
+              take = eq_seen < keq;
+              ++eq_seen;
+            }
+            if (take) {
+              if (pos < (uint32_t)k) dst[pos] = b0 + j;
+              ++pos;
+            }
           }
         }
       }
@@ -430,8 +452,9 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
 // Top-k of a whole row with a block of NTS threads: warm theta (optional),
 // candidate range, radix select.  When n <= k all n indices are kept,
 // followed by -1.  LDS_KEYS as for radix_select.
-template <int NTS, bool LDS_KEYS = true, typename Grp, typename KeyFn>
-__device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *warm, int32_t *dst, RadixShared<NTS> &sh) {
+template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, typename Grp, typename KeyFn>
+__device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *warm, int32_t *dst, RadixShared<NTS> &sh,
+                           uint32_t *stage = nullptr) {
   const int t = grp.t();
   if (n <= k) {
     for (int i = t; i < k; i += NTS) dst[i] = i < n ? i : -1;
@@ -440,7 +463,7 @@ __device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *war
   const uint32_t theta = warm != nullptr ? warm_theta<NTS>(grp, key, warm, n, k, sh) : 0u;
   uint32_t lo, hi, ncand;
   key_range<NTS>(grp, key, n, theta, lo, hi, ncand, sh);
-  radix_select<NTS, LDS_KEYS>(grp, key, n, k, theta, lo, hi, ncand, dst, sh);
+  radix_select<NTS, LDS_KEYS, STAGE_C>(grp, key, n, k, theta, lo, hi, ncand, dst, sh, stage);
 }
 
 }  // namespace kvsel

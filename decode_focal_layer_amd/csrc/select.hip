@@ -89,7 +89,8 @@ __global__ __launch_bounds__(NT) void focal_select_kernel(SelArgs a) {
   auto key = [&](int i) -> uint32_t { return s_keys[i]; };
   const size_t row = (size_t)b * a.n_out + g;
   BlockSync<NT> grp;
-  radix_topk<NT>(grp, key, r.seg, a.k, a.warm != nullptr ? a.warm + row * a.k : nullptr, a.idx + row * a.k, sh);
+  radix_topk<NT, true, 25>(grp, key, r.seg, a.k, a.warm != nullptr ? a.warm + row * a.k : nullptr, a.idx + row * a.k, sh,
+                           s_keys);
 }
 
 }  // namespace

@@ -164,14 +164,16 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   uint4 k0, k1, k2, k3, k4, k5, k6, k7, vv[8];
   uint32_t tile_mask = 0;   // bit i: key t0 + i of the loaded tile is attended
   auto krow_of = [&](int kr) {   // K row (16-byte pieces) of virtual row kr, or the queries
-    const uint32_t pk = kr < cnt ? s_prow[kr] : kNoRow;
+    const uint32_t pk_r = s_prow[max(min(kr, cnt - 1), 0)];   // unbranched LDS read
+    const uint32_t pk = kr < cnt ? pk_r : kNoRow;
     return reinterpret_cast<const uint4 *>(pk != kNoRow ? a.k_pool + (size_t)pk * kD : a.q);
   };
 #define KVSEL_VERIFY_LOAD_TILE(T0)                                                                   \
   do {                                                                                               \
     const int t0_ = (T0);                                                                            \
     const int key_ = t0_ + col;                                                                      \
-    const uint32_t pr_ = key_ < cnt ? s_prow[key_] : kNoRow;                                         \
+    const uint32_t prr_ = s_prow[max(min(key_, cnt - 1), 0)]; /* unbranched LDS read */              \
+    const uint32_t pr_ = key_ < cnt ? prr_ : kNoRow;                                                 \
     tile_mask = (uint32_t)__ballot(pr_ != kNoRow); /* lanes 0..31 (hf = 0) cover the 32 keys */      \
     const uint4 *vrow_ = reinterpret_cast<const uint4 *>((pr_ != kNoRow ? a.v_pool + (size_t)pr_ * kD \
                                                                         : a.q) + hf * 8);            \
@@ -430,7 +432,8 @@ __global__ __launch_bounds__(kW16Threads) __attribute__((amdgpu_waves_per_eu(4, 
 #define KVSEL_VERIFY16_LOAD(T0)                                                                      \
   do {                                                                                               \
     const int key_ = (T0) + kl;                                                                      \
-    const uint32_t pr_ = key_ < cnt ? s_prow[key_] : kNoRow;                                         \
+    const uint32_t prr_ = s_prow[max(min(key_, cnt - 1), 0)]; /* unbranched LDS read */              \
+    const uint32_t pr_ = key_ < cnt ? prr_ : kNoRow;                                                 \
     tile_mask = (uint32_t)__ballot(pr_ != kNoRow) & 0xffffu; /* lanes 0..15 cover the 16 keys */     \
     const uint4 *kr_ = reinterpret_cast<const uint4 *>((pr_ != kNoRow ? a.k_pool + (size_t)pr_ * kD  \
                                                                       : a.q) + kb * 8);              \

@@ -281,8 +281,12 @@ def score(kv: KV, q: torch.Tensor, n_rows: int, num_q_heads: int, scale: float, 
     return scores
 
 
+def topk_workspace(rows: int, n: int, k: int) -> int:
+    return lib().kvsel_topk_workspace(rows, n, k)
+
+
 def topk(scores: torch.Tensor, n: int, k: int, idx: torch.Tensor, warm: Optional[torch.Tensor] = None,
-         n_per_row: Optional[torch.Tensor] = None, stream=None):
+         n_per_row: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None, stream=None):
     """kvsel_topk.  scores: fp32 [..., ld] viewed as rows; idx: int32 [rows][k];
     n_per_row: int32 [rows] candidate counts (each clamped to n) or None."""
     _need(scores, torch.float32, "scores")
@@ -299,7 +303,9 @@ def topk(scores: torch.Tensor, n: int, k: int, idx: torch.Tensor, warm: Optional
         _need(n_per_row, torch.int32, "n_per_row")
         if n_per_row.numel() != rows:
             raise ValueError("n_per_row must hold one count per row")
-    _check(lib().kvsel_topk(_ptr(scores), ld, rows, _ptr(n_per_row), n, k, _ptr(warm), _ptr(idx), None, 0,
+    w = _ws(ws, scores.device)
+    p, nb = w.ptr_and_size(topk_workspace(rows, n, k))
+    _check(lib().kvsel_topk(_ptr(scores), ld, rows, _ptr(n_per_row), n, k, _ptr(warm), _ptr(idx), p, nb,
                             _stream(stream)))
     return idx
 

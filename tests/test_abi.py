@@ -157,6 +157,20 @@ def test_topk_rejects(L, args, code):
     assert L.kvsel_topk_workspace(4, 10, 3) == 0
 
 
+def test_topk_long_rows_need_a_workspace(L):
+    """Rows too long to stage in LDS (more than 36864 candidates) take the
+    two-kernel path, whose per-slice coarse counts (2048 per 8192-key slice
+    of each row) live in the workspace."""
+    assert L.kvsel_topk_workspace(2, 40000, 10) == 2 * 5 * 2048 * 4
+    assert L.kvsel_topk_workspace(2, 36864, 10) == 0
+    assert L.kvsel_topk_workspace(2, 40000, 0) == 0
+    t = lambda ws, nb: L.kvsel_topk(FAKE, 40000, 2, None, 40000, 10, None, FAKE, ws, nb, None)
+    assert t(None, 0) == EINVAL
+    assert t(FAKE + 64, 1 << 20) == EINVAL
+    assert t(FAKE, 1000) == ENOSPC
+    assert L.kvsel_topk(FAKE, 10, 70000, None, 10, 3, None, FAKE, None, 0, None) == EINVAL   # rows > 65535
+
+
 @pytest.mark.parametrize("args,code", [
     (dict(src=0), EINVAL), (dict(dst=0), EINVAL), (dict(src=FAKE + 4), EINVAL), (dict(row_bytes=24), EINVAL),
     (dict(row_bytes=0), EINVAL), (dict(n_idx=-1), EINVAL), (dict(n_tail=-1), EINVAL), (dict(idx=0), EINVAL),

@@ -230,7 +230,10 @@ def test_topk_rows_of_their_own_length(n, k):
                                       # every score equal, a narrow band of scores, k = 1, k = n - 1,
                                       # k = n, a row read from global memory on every pass
                                       (40000, 5000, "equal"), (30000, 3000, "narrow"), (20000, 1, "rand"),
-                                      (20000, 19999, "ties"), (20000, 20000, "rand"), (131072, 2048, "rand")])
+                                      (20000, 19999, "ties"), (20000, 20000, "rand"), (131072, 2048, "rand"),
+                                      # scores over many exponents, both signs, and a k-th score in the
+                                      # highest occupied coarse bin
+                                      (50000, 1000, "wide"), (50000, 300, "signed"), (16384, 3, "spike")])
 def test_topk_exact(n, k, mode):
     kvsel = K()
     rng = np.random.default_rng(n + k)
@@ -241,6 +244,13 @@ def test_topk_exact(n, k, mode):
         s = (rng.integers(0, 50, size=(rows, n)) / 50).astype(np.float32)
     elif mode == "narrow":
         s = (1.0 + rng.random((rows, n)) * 1e-3).astype(np.float32)
+    elif mode == "wide":
+        s = np.exp(rng.standard_normal((rows, n)) * 8.0).astype(np.float32)
+    elif mode == "signed":
+        s = rng.standard_normal((rows, n)).astype(np.float32)
+    elif mode == "spike":
+        s = (rng.random((rows, n)) * 1e-6).astype(np.float32)
+        s[:, rng.choice(n, size=5, replace=False)] = np.float32(0.5)
     else:
         s = np.full((rows, n), 1.0 / n, dtype=np.float32)
     ld = n + 5
