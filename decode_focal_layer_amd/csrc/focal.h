@@ -45,10 +45,14 @@ __device__ __forceinline__ float focal_term(float x, double m, double c) {
 
 // logit(hh, i) for head hh < nh of the output row and token i < cnt.  Writes
 // s_m[hh] = m_h and s_iz[hh] = 1 / Z_h (0 when Z_h = 0).  Run by a whole
-// block of NT >= 256 threads; up to NH heads per pass over the tokens.
+// block of NT >= 256 threads; up to NH heads per pass over the tokens.  The
+// logits are read kStatBatch tokens at a time, every read unbranched (at a
+// clamped token and head) so that they are all in flight together; the
+// normaliser still adds each thread's tokens in increasing order.
+constexpr int kStatBatch = 8;
 template <int NT, int NH, typename LF>
 __device__ void focal_stats(LF logit, int nh, int cnt, double c, double *s_m, double *s_iz) {
-  constexpr int NW = NT / 64, SW = kStatThreads / 64;
+  constexpr int NW = NT / 64, SW = kStatThreads / 64, BS = kStatBatch;
   static_assert(NT % 64 == 0 && NT >= kStatThreads, "block of at least kStatThreads threads");
   __shared__ float s_wm[NH][NW];
   __shared__ double s_wz[NH][SW];
@@ -58,10 +62,19 @@ __device__ void focal_stats(LF logit, int nh, int cnt, double c, double *s_m, do
     float mx[NH];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) mx[hh] = -INFINITY;
-    for (int i = tid; i < cnt; i += NT) {
+    for (int i0 = tid; i0 < cnt; i0 += NT * BS) {
+      float v[BS][NH];
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-        if (hh < hn) mx[hh] = fmaxf(mx[hh], logit(h0 + hh, i));
+      for (int j = 0; j < BS; ++j) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) v[j][hh] = logit(h0 + min(hh, hn - 1), min(i0 + j * NT, cnt - 1));
+      }
+#pragma unroll
+      for (int j = 0; j < BS; ++j) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          if (hh < hn && i0 + j * NT < cnt) mx[hh] = fmaxf(mx[hh], v[j][hh]);
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -80,10 +93,20 @@ __device__ void focal_stats(LF logit, int nh, int cnt, double c, double *s_m, do
       double part[NH];
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) part[hh] = 0.0;
-      for (int i = tid; i < cnt; i += kStatThreads) {
+      for (int i0 = tid; i0 < cnt; i0 += kStatThreads * BS) {
+        float v[BS][NH];
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-          if (hh < hn) part[hh] += (double)focal_term(logit(h0 + hh, i), md[hh], c);
+        for (int j = 0; j < BS; ++j) {
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh)
+            v[j][hh] = logit(h0 + min(hh, hn - 1), min(i0 + j * kStatThreads, cnt - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < BS; ++j) {   // tokens i0, i0 + kStatThreads, ... in order
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh)
+            if (hh < hn && i0 + j * kStatThreads < cnt) part[hh] += (double)focal_term(v[j][hh], md[hh], c);
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) {
@@ -102,13 +125,27 @@ __device__ void focal_stats(LF logit, int nh, int cnt, double c, double *s_m, do
   }
 }
 
-// score of token i from the statistics (fp64 sum over the heads in order)
-template <typename LF>
-__device__ __forceinline__ double focal_score(LF logit, int nh, int i, double c, const double *s_m,
-                                              const double *s_iz) {
-  double sc = 0.0;
-  for (int hh = 0; hh < nh; ++hh) sc += (double)focal_term(logit(hh, i), s_m[hh], c) * s_iz[hh];
-  return sc;
+// scores of tokens i0, i0 + stride, ... (kStatBatch of them, those below cnt)
+// from the statistics: per token the fp64 sum over the heads in order; the
+// reads of one head go out together.  f(i, score) for each token below cnt.
+template <typename LF, typename F>
+__device__ __forceinline__ void focal_scores_batch(LF logit, int nh, int i0, int stride, int cnt, double c,
+                                                   const double *s_m, const double *s_iz, F f) {
+  constexpr int BS = kStatBatch;
+  double sc[BS];
+#pragma unroll
+  for (int j = 0; j < BS; ++j) sc[j] = 0.0;
+  for (int hh = 0; hh < nh; ++hh) {
+    float v[BS];
+#pragma unroll
+    for (int j = 0; j < BS; ++j) v[j] = logit(hh, min(i0 + j * stride, cnt - 1));
+    const double m = s_m[hh], iz = s_iz[hh];
+#pragma unroll
+    for (int j = 0; j < BS; ++j) sc[j] += (double)focal_term(v[j], m, c) * iz;
+  }
+#pragma unroll
+  for (int j = 0; j < BS; ++j)
+    if (i0 + j * stride < cnt) f(i0 + j * stride, sc[j]);
 }
 
 // LDS state of the fused selection (one kv head's group of G heads)

@@ -55,13 +55,13 @@ __global__ __launch_bounds__(kSelThreads) void focal_norm_kernel(SelArgs a) {
   focal_stats<kSelThreads, 4>(stat_logit, a.heads_per_out, r.cnt, c, s_m, s_iz);
   const float *lg = base + r.off;
   auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
-  for (int i = threadIdx.x; i < r.seg; i += kSelThreads) {
-    const double sc = focal_score(seg_logit, a.heads_per_out, i, c, s_m, s_iz);
-    if (a.scores != nullptr)
-      a.scores[((size_t)b * a.n_out + o) * a.ld + i] = (float)sc;
-    else
-      a.scores64[((size_t)b * a.n_out + o) * a.ld64 + i] = sc;
-  }
+  for (int i0 = threadIdx.x; i0 < r.seg; i0 += kSelThreads * kStatBatch)
+    focal_scores_batch(seg_logit, a.heads_per_out, i0, kSelThreads, r.seg, c, s_m, s_iz, [&](int i, double sc) {
+      if (a.scores != nullptr)
+        a.scores[((size_t)b * a.n_out + o) * a.ld + i] = (float)sc;
+      else
+        a.scores64[((size_t)b * a.n_out + o) * a.ld64 + i] = sc;
+    });
 }
 
 // grid (kv heads, sequences): scores + top-k of the group
@@ -80,11 +80,12 @@ __global__ __launch_bounds__(NT) void focal_select_kernel(SelArgs a) {
   const float *lg = base + r.off;
   auto seg_logit = [&](int hh, int i) { return lg[(size_t)hh * a.ld_logits + i]; };
   float *so = a.scores != nullptr ? a.scores + ((size_t)b * a.n_out + g) * a.ld : nullptr;
-  for (int i = threadIdx.x; i < r.seg; i += NT) {
-    const float f = (float)focal_score(seg_logit, a.heads_per_out, i, c, s_m, s_iz);
-    s_keys[i] = okey(f);
-    if (so != nullptr) so[i] = f;
-  }
+  for (int i0 = threadIdx.x; i0 < r.seg; i0 += NT * kStatBatch)
+    focal_scores_batch(seg_logit, a.heads_per_out, i0, NT, r.seg, c, s_m, s_iz, [&](int i, double sc) {
+      const float f = (float)sc;
+      s_keys[i] = okey(f);
+      if (so != nullptr) so[i] = f;
+    });
   __syncthreads();
   auto key = [&](int i) -> uint32_t { return s_keys[i]; };
   const size_t row = (size_t)b * a.n_out + g;
