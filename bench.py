@@ -33,22 +33,23 @@ KERNEL_SOURCES = ["decode_focal_layer_amd/csrc/attn.hip", "decode_focal_layer_am
 
 
 def measured_traffic():
-    """HBM bytes per gathered-attention launch from the committed counter
-    summary, if it was taken on the current kernel sources; else None."""
+    """(HBM bytes per gathered-attention launch, those bytes / the algorithmic
+    bytes of the launches counted) from the committed counter summary, if it
+    was taken on the current kernel sources; else (None, None)."""
     import hashlib
     import re
     try:
         txt = open(TRAFFIC_FILE).read()
     except OSError:
-        return None
+        return None, None
     h = hashlib.sha256()
     for s in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, s), "rb").read())
     m = re.search(r"kernel-sources-sha256-16: ([0-9a-f]{16})", txt)
-    t = re.search(r"Traffic per gathered-attention launch = [0-9.]+ \+ [0-9.]+ = ([0-9.]+) MB", txt)
+    t = re.search(r"Traffic per gathered-attention launch = [0-9.]+ \+ [0-9.]+ = ([0-9.]+) MB, ([0-9.]+) x", txt)
     if not m or not t or m.group(1) != h.hexdigest()[:16]:
-        return None
-    return float(t.group(1)) * 1e6
+        return None, None
+    return float(t.group(1)) * 1e6, float(t.group(2))
 
 
 def algorithmic_bytes(cfg, t: int, batch: int):
@@ -255,10 +256,12 @@ def main():
         avg_us = tot_ms * 1e3 / launches
         bpl = nbytes / launches
         ach = bpl / (avg_us / 1e6) / 1e9
+        traffic, traffic_ratio = measured_traffic()
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, calibrated "
                                 "on a 1 GiB copy)",
+                "traffic_over_algorithmic": traffic_ratio,
                 "kernel": "attn_kernel<2,1024,4,0,true> (gathered sparse attention, streamed K/V)",
                 "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bpl), "launches_timed": launches}
 
