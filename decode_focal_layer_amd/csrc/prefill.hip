@@ -12,9 +12,20 @@
 // for any group size G.  Keys go through LDS in tiles of 64:
 //  * K row-major, bf16, the 16-byte chunks of a row XOR-swizzled by the key
 //    (conflict-free writes of whole rows and reads of one chunk per key);
-//  * V transposed, converted to fp16 (exact for bf16 values inside the fp16
-//    range), its key order permuted so that P leaves the S product already
-//    in the operand order of the P V product (no lane exchange).
+//  * V transposed, scaled by a power of two and converted to fp16, its key
+//    order permuted so that P leaves the S product already in the operand
+//    order of the P V product (no lane exchange).  The scale 2^-e is one per
+//    work-group and only grows: e is 0 while the largest V magnitude seen is
+//    in [2^-4, 2^15), else floor(log2) of it minus 14, so the scaled V stay
+//    below 2^15 (inside fp16).  Scaled V of at least 2^-14 (fp16 normal) are
+//    exact; smaller ones are off by less than 2^-20 of the largest magnitude,
+//    for V of any magnitude (bf16 values below 2^-86 aside).  The first
+//    tile's exact maximum sets e; after the P V products of each tile, each
+//    wave tests the next tile's V (already in registers) against the
+//    magnitude that would raise e and takes the exact maximum only if one
+//    reaches it; the work-group reads the waves' reports after the barrier
+//    before the stash, and when e grows O is rescaled by the exact power of
+//    two.  O is multiplied by 2^e at the end.
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as A rows, query rows as
 // B columns: each lane owns one query row and 16 keys of a 32-key block);
 // online softmax per row in fp32 whose running max is moved only when a
@@ -38,9 +49,11 @@ namespace {
 constexpr int kPThreads = 256;
 constexpr int kPWaves = kPThreads / 64;
 constexpr int kPRows = 32 * kPWaves;   // query rows per work-group
+static_assert(kPWaves == 4, "the V maxima are gathered from four waves");
 constexpr int kBN = 64;                // keys per tile
 constexpr float kSlack = 8.f;          // log2 headroom of the running max (p <= 256 in fp16)
 constexpr int kLgStride = 65;          // floats per staged logits row (64 keys + 1: distinct banks)
+constexpr int kVExpNone = -1000;       // V scale exponent before any nonzero V
 
 // byte offset of K chunk c (dims 8c .. 8c+7) of tile key r
 __device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -94,33 +107,173 @@ __device__ __forceinline__ Stage fetch(const uint8_t *kt, const uint8_t *vt, con
                ld(vt, s.o[4]), ld(vt, s.o[5]), ld(vt, s.o[6]), ld(vt, s.o[7])};
 }
 
-__device__ __forceinline__ void stash(const Stage &st, uint8_t *s_k, uint8_t *s_vt, int tid) {
+// the largest bf16 magnitude (as bits) of this thread's staged V rows
+__device__ __forceinline__ uint32_t v_max_bits(const Stage &st) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint4 vs[4] = {st.v0, st.v1, st.v2, st.v3};
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, word_of(vs[u], e) & 0x7fff7fffu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// 2^k as a float, k in [-126, 127]
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+
+// The work-group's V scale exponent after a tile whose largest V magnitude
+// has bf16 bits mx (uniform): unchanged for an all-zero tile; else at least
+// floor(log2 max) - 14 (the scaled tile stays below 2^15 = inside fp16, inf
+// and nan giving 114), 0 while the largest magnitude is in [2^-4, 2^15) (no
+// scaling for V of ordinary size), and never below -100 (2^100 is a float).
+// O is rescaled by the exact power of two when the exponent grows.
+__device__ __forceinline__ int next_v_exp(int e, uint32_t mx, f32x16 (&acc)[4]) {
+  if (mx == 0u) return e;
+  const int ex = (int)(mx >> 7) - 127;   // floor(log2 |v|); -127 for bf16 subnormals, 128 for inf and nan
+  const int want = (ex > 14 || ex < -4) ? max(ex - 14, -100) : 0;
+  if (want <= e) return e;
+  if (e != kVExpNone) {
+    const int d = e - want;   // < 0
+    const float f = d < -126 ? 0.f : pow2f(d);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[dt][j] *= f;
+  }
+  return want;
+}
+
+// bf16 bits of the smallest V magnitude that makes next_v_exp raise e: any
+// nonzero one while none is set; else 2^(e+15), for e < 0 at most 2^-4
+// (where e returns to 0); 0x8000 (above every bf16 magnitude) for none
+__device__ __forceinline__ uint32_t v_grow_bits(int e) {
+  if (e == kVExpNone) return 1u;
+  const int t = e < 0 ? min(e + 15, -4) : e + 15;   // >= -85
+  return t + 127 >= 255 ? 0x8000u : (uint32_t)(t + 127) << 7;
+}
+
+// the tile's K into LDS as it is
+__device__ __forceinline__ void stash_k(const Stage &st, uint8_t *s_k, int tid) {
   const uint4 ks[4] = {st.k0, st.k1, st.k2, st.k3};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = tid + kPThreads * u;
     *reinterpret_cast<uint4 *>(s_k + k_off(i >> 4, i & 15)) = ks[u];
   }
+}
+
+// the tile's V into LDS, transposed and converted to fp16 after scaling by
+// sc (SCALED) or as it is
+template <bool SCALED>
+__device__ __forceinline__ void stash_v_as(const Stage &st, uint8_t *s_vt, int tid, float sc) {
   const int p = quad_pos(tid >> 4), vc = tid & 15;
+  // fp16 pair of two bf16 values (as float bits)
+  auto cv = [&](uint32_t a_bits, uint32_t b_bits) {
+    return SCALED ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(a_bits) * sc,
+                                                                            __uint_as_float(b_bits) * sc))
+                  : f16_pair(a_bits, b_bits);
+  };
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {   // dims vc*8 + 2*e2 (low halves) and + 1 (high halves)
     const uint32_t w0 = word_of(st.v0, e2), w1 = word_of(st.v1, e2);
     const uint32_t w2 = word_of(st.v2, e2), w3 = word_of(st.v3, e2);
     *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + 2 * e2, p)) =
-        make_uint2(f16_pair(w0 << 16, w1 << 16), f16_pair(w2 << 16, w3 << 16));
+        make_uint2(cv(w0 << 16, w1 << 16), cv(w2 << 16, w3 << 16));
     *reinterpret_cast<uint2 *>(s_vt + vt_off(vc * 8 + 2 * e2 + 1, p)) =
-        make_uint2(f16_pair(w0 & 0xffff0000u, w1 & 0xffff0000u), f16_pair(w2 & 0xffff0000u, w3 & 0xffff0000u));
+        make_uint2(cv(w0 & 0xffff0000u, w1 & 0xffff0000u), cv(w2 & 0xffff0000u, w3 & 0xffff0000u));
   }
+}
+
+// the tile's V into LDS after scaling by 2^-e (exact; no scaling when e is 0
+// or none is set yet; e uniform)
+__device__ __forceinline__ void stash_v(const Stage &st, uint8_t *s_vt, int tid, int e) {
+  if (e == 0 || e == kVExpNone)
+    stash_v_as<false>(st, s_vt, tid, 1.f);
+  else
+    stash_v_as<true>(st, s_vt, tid, pow2f(-e));
+}
+
+// Whether one of this thread's staged V magnitudes reaches the bf16 bits t.
+// A bf16 pair read as an fp16 pair keeps the order of its values among
+// values of one sign, so the packed maximum and minimum over the raw words
+// decide it for 0 < t <= 0x7c00; an fp16 nan among them (a bf16 magnitude
+// above 0x7c00) counts as reaching.  The answer errs only towards yes: for t
+// = 1 should fp16 denormals be flushed, and for t above 0x7c00 (the fp16
+// pattern of t then a nan or -0), where every tile reaches.
+__device__ __forceinline__ bool v_reaches(const Stage &st, uint32_t t) {
+  typedef _Float16 hx2 __attribute__((ext_vector_type(2)));
+  const uint4 vs[4] = {st.v0, st.v1, st.v2, st.v3};
+  auto h = [&](int i) { return __builtin_bit_cast(hx2, word_of(vs[i >> 2], i & 3)); };
+  hx2 mx = h(0), mn = h(0);
+#pragma unroll
+  for (int i = 1; i < 16; i += 2) {
+    const hx2 x = h(i), y = i + 1 < 16 ? h(i + 1) : h(i);
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x), y);
+    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, x), y);
+  }
+  const _Float16 th = __builtin_bit_cast(_Float16, (uint16_t)t);
+  const bool r0 = !(mx.x < th), r1 = !(mx.y < th), r2 = !(mn.x > -th), r3 = !(mn.y > -th);
+  return (r0 | r1) | (r2 | r3);   // no short circuit: one straight sequence
+}
+
+// This wave's report on a fetched tile's V, for the exponent update before
+// its stash: the wave's largest magnitude (bits) when it reaches
+// v_grow_bits(e), else 0 -- the exact maximum is taken only then, and
+// whenever some wave reports one the largest report is the work-group's
+// maximum.  Lane 0 writes it to s_wmax[wave].
+__device__ __forceinline__ void report_v(const Stage &st, int e, uint32_t *s_wmax, int tid) {
+  uint32_t wm = 0u;
+  if (__ballot(v_reaches(st, v_grow_bits(e))) != 0) wm = wave_max_u32(v_max_bits(st));
+  if ((tid & 63) == 0) s_wmax[tid >> 6] = wm;
+}
+
+// the work-group's largest V magnitude from the waves' reports (uniform)
+__device__ __forceinline__ uint32_t group_v_max(const uint32_t *s_wmax) {
+  const uint4 m = *reinterpret_cast<const uint4 *>(s_wmax);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)max(max(m.x, m.y), max(m.z, m.w)));
+}
+
+// The scale exponent from the first tile's exact largest V magnitude
+__device__ __forceinline__ int first_v_exp(const Stage &st, uint32_t *s_wmax, int tid, f32x16 (&acc)[4]) {
+  const uint32_t wm = wave_max_u32(v_max_bits(st));
+  if ((tid & 63) == 0) s_wmax[tid >> 6] = wm;
+  __syncthreads();
+  return next_v_exp(kVExpNone, group_v_max(s_wmax), acc);
+}
+
+// V rows of a shared-range tile that are not attended (vkeep bit u clear:
+// row u of this thread) set to zero before the stash: p = 0 must not meet a
+// non-finite value
+__device__ __forceinline__ void zero_dropped_v(Stage &st, int vkeep) {
+  if (vkeep == 0xf) return;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  if (!(vkeep & 1)) st.v0 = z;
+  if (!(vkeep & 2)) st.v1 = z;
+  if (!(vkeep & 4)) st.v2 = z;
+  if (!(vkeep & 8)) st.v3 = z;
+}
+
+// O back from V scaled by 2^-e: O * 2^e (exact short of overflow)
+__device__ __forceinline__ void unscale_v(f32x16 (&acc)[4], int e) {
+  if (e == 0 || e == kVExpNone) return;
+  const float f = pow2f(e);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[dt][j] *= f;
 }
 
 // One 64-key tile for this lane's query row: S^T = K Q^T from the LDS K
 // tile, the online softmax, O^T += V^T P from the LDS V^T tile.  masked(bk, j)
 // drops key 32*bk + 8*(j/4) + 4*hf + j%4 of the tile; it is evaluated only
-// when need_mask.  on_dots(s) sees the raw dots before the mask.
-template <typename MaskFn, typename DotsFn>
+// when need_mask.  on_dots(s) sees the raw dots before the mask; after_pv()
+// runs once the P V products are issued (work that overlaps them).
+template <typename MaskFn, typename DotsFn, typename AfterFn>
 __device__ __forceinline__ void attend_tile(const uint8_t *s_k, const uint8_t *s_vt, const bf16x8 (&qop)[8], int col,
                                             int hf, float scale_log2, bool need_mask, MaskFn masked, DotsFn on_dots,
-                                            f32x16 (&acc)[4], float &mrun, float &lsum) {
+                                            AfterFn after_pv, f32x16 (&acc)[4], float &mrun, float &lsum) {
     // S^T, two 32-key blocks: s[bk][j] is key t0 + 32*bk + 8*(j/4) + 4*hf + j%4
     // (operands read one k-step ahead of the products that use them)
     f32x16 s[2] = {{}, {}};
@@ -213,11 +366,13 @@ __device__ __forceinline__ void attend_tile(const uint8_t *s_k, const uint8_t *s
           for (int dt = 0; dt < 4; ++dt) c[dt] = nx[dt];
       }
     }
+    after_pv();
 }
 
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wmax[kPWaves];   // each wave's report on the next tile's V
 
   const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
   const uint32_t w = (L & 7u) * per + (L >> 3);   // this XCD's run, in order
@@ -272,23 +427,35 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int wave_pos0 = wave_row0 / G;   // the wave's earliest position
 
   Stage st = fetch_tile(0);
+  int ve = first_v_exp(st, s_wmax, tid, acc);   // V scale exponent (uniform)
   for (int t0 = 0; t0 < kend; t0 += kBN) {
-    __syncthreads();   // the previous tile's reads are done
-    stash(st, s_k, s_vt, tid);
+    __syncthreads();   // the previous tile's reads are done; the waves' reports on this tile are in
+    stash_k(st, s_k, tid);
+    ve = next_v_exp(ve, group_v_max(s_wmax), acc);
+    stash_v(st, s_vt, tid, ve);
     __syncthreads();
-    if (t0 + kBN < kend) st = fetch_tile(t0 + kBN);
-    if (t0 >= wave_kend) continue;   // every row of this wave is before the tile
+    const bool more = t0 + kBN < kend;
+    if (more) st = fetch_tile(t0 + kBN);
+    // the report on the next tile (read after the next first barrier)
+    auto report = [&] {
+      if (more) report_v(st, ve, s_wmax, tid);
+    };
+    if (t0 >= wave_kend) {   // every row of this wave is before the tile
+      report();
+      continue;
+    }
 
     // the causal mask, only on tiles that reach past a row of this wave
     attend_tile(s_k, s_vt, qop, col, hf, a.scale_log2, !wave_full || t0 + kBN - 1 > wave_pos0,
                 [&](int bk, int j) { return t0 + 32 * bk + 8 * (j >> 2) + 4 * hf + (j & 3) > pos; },
-                [](const f32x16 (&)[2]) {}, acc, mrun, lsum);
+                [](const f32x16 (&)[2]) {}, report, acc, mrun, lsum);
   }
 
   const float lrow = half_pair_sum(lsum);
   if (!live) return;
   const int64_t orow = (base + pos) * a.hq + g * G + h;
   const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+  unscale_v(acc, ve);
   float *o = a.out + orow * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -325,6 +492,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
   __shared__ int32_t s_tab[kSharedMaxBlocks];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wmax[kPWaves];   // each wave's report on the next tile's V
   extern __shared__ float s_lg[];            // logits asked for: [kPWaves][32][kLgStride]
 
   const uint32_t L = blockIdx.x, per = gridDim.x >> 3;
@@ -434,19 +602,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   int vkeep = 0;
   uint64_t nmask = 0;
   Stage st = fetch_tile(tfirst, nmask, vkeep);
+  zero_dropped_v(st, vkeep);
+  int ve = first_v_exp(st, s_wmax, tid, acc);   // V scale exponent (uniform)
   for (int t0 = tfirst; t0 < r1; t0 += kBN) {
-    if (vkeep != 0xf) {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      if (!(vkeep & 1)) st.v0 = z;
-      if (!(vkeep & 2)) st.v1 = z;
-      if (!(vkeep & 4)) st.v2 = z;
-      if (!(vkeep & 8)) st.v3 = z;
-    }
-    __syncthreads();   // the previous tile's reads are done
-    stash(st, s_k, s_vt, tid);
+    __syncthreads();   // the previous tile's reads are done; the waves' reports on this tile are in
+    stash_k(st, s_k, tid);
+    ve = next_v_exp(ve, group_v_max(s_wmax), acc);
+    stash_v(st, s_vt, tid, ve);
     __syncthreads();
     const uint64_t vmask = nmask;   // bit i: key t0 + i is attended
-    if (t0 + kBN < r1) st = fetch_tile(t0 + kBN, nmask, vkeep);
+    const bool more = t0 + kBN < r1;
+    if (more) st = fetch_tile(t0 + kBN, nmask, vkeep);
     // this lane half's bits: bit 8a + r of mb[bk] is key 32 bk + 8a + 4 hf + r
     // (constant shifts below; no per-lane 64-bit masks)
     const uint32_t mb0 = (uint32_t)(vmask >> (4 * hf)), mb1 = (uint32_t)(vmask >> (32 + 4 * hf));
@@ -479,11 +645,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                   __builtin_amdgcn_wave_barrier();
                   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                 },
+                [&] {   // the next tile: dropped rows zeroed, then the report (read after the next first barrier)
+                  if (!more) return;
+                  zero_dropped_v(st, vkeep);
+                  report_v(st, ve, s_wmax, tid);
+                },
                 acc, mrun, lsum);
   }
 
   const float lrow = half_pair_sum(lsum);
   if (!live) return;
+  unscale_v(acc, ve);
   const size_t orow = ((size_t)part * a.batch + b) * a.hq + g * G + h;
   float *o = a.out + orow * kD;
   const float lse_r = lrow > 0.f ? (mrun + __log2f(lrow)) * 0.6931471805599453f : -INFINITY;   // natural log

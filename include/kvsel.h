@@ -371,8 +371,10 @@ KVSEL_API kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t
  * [total][num_kv_heads][128]; query head h reads kv head
  * h / (num_q_heads / num_kv_heads); scale > 0; out: fp32 [total][num_q_heads][128];
  * lse: NULL or fp32 [total][num_q_heads] (natural log).  q, k, v and out
- * 16-byte aligned.  P V runs in fp16: V values of magnitude above 65504
- * are clamped to it.  No workspace.
+ * 16-byte aligned.  P V runs in fp16 with V scaled by a power of two that
+ * grows with the largest V magnitude each work-group has read: V of any
+ * magnitude, each V value exact or off by less than 2^-20 of that largest
+ * magnitude.  No workspace.
  */
 KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                           const int32_t *cu_seqlens, int32_t batch, int32_t max_seqlen,
@@ -402,8 +404,8 @@ KVSEL_API kvsel_status kvsel_prefill_attn(const uint16_t *q, const uint16_t *k, 
  * the exact merge of that and this range (kvsel_merge_attn of the two, in
  * place; -inf lse for both gives out = 0).  q and out 16-byte
  * aligned; scale > 0; the range may touch at most 1024 cache blocks
- * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 (V clamped to
- * +-65504).  logits: NULL, or fp32 [batch][num_q_heads][ld_logits]
+ * (KVSEL_EUNSUPPORTED otherwise).  P V runs in fp16 with V scaled by a power
+ * of two, as in kvsel_prefill_attn (V of any magnitude).  logits: NULL, or fp32 [batch][num_q_heads][ld_logits]
  * (q_per_seq = 1, ld_logits >= max_seg_len): the raw dots q.k of each
  * sequence's segment rows that lie inside the range, entry i for segment
  * row seg_begin + i (the input of kvsel_select_logits; rows outside the

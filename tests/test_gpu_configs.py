@@ -88,8 +88,9 @@ def test_c0_full():
     print("patch tokens among the kept:", hits, "of", 8 * len(patch))
 
 
-def run_schedule(cfg, w, check_every=1, **dec_kw):
-    """Run all steps through FocalDecoder; check every layer of every step."""
+def run_schedule(cfg, w, check_every=1, v_scale=1.0, **dec_kw):
+    """Run all steps through FocalDecoder; check every layer of every step
+    (the absolute error bound taken relative to v_scale)."""
     from decode_focal_layer_amd.decode import FocalDecoder
     kv = kvsel()
     kvs = focal_kvs(w)
@@ -129,7 +130,8 @@ def run_schedule(cfg, w, check_every=1, **dec_kw):
                         _, ts, ls = e[1:]
                         rows = O.kept_rows(sets[(ts, ls)][b, g], 0, cfg.n_visual, n)
                         ref, _ = O.attention(qg, Kl, Vl, rows, cfg.scale)
-                    ma, _ = assert_attn(outs[l, b, g * G:(g + 1) * G], ref, f"t{t} l{l} {e[0]} b{b} g{g}")
+                    ma, _ = assert_attn(outs[l, b, g * G:(g + 1) * G] / v_scale, ref / v_scale,
+                                        f"t{t} l{l} {e[0]} b{b} g{g}")
                     worst = max(worst, ma)
     print(cfg.name, "worst max-abs error", worst)
     return dec, sets
@@ -150,6 +152,62 @@ def test_c4_branches_small_cascade():
                       n_always=48, suffix_range=(3, 40))
     w = gen.make_focal(cfg, DEV)
     run_schedule(cfg, w, check_every=1, shared_tail=(cfg.n_visual, cfg.prefix_len))
+
+
+def _c4_wide_shared_v(cfg, w, factor):
+    """The workload with the V rows of the shared prefix blocks (the same
+    blocks in every table) multiplied by factor in every layer."""
+    import dataclasses
+    blocks = torch.from_numpy(w.table_np[0, :-(-cfg.prefix_len // 16)].astype(np.int64)).to(DEV)
+    vp = []
+    for v in w.v_pool:
+        v = v.clone()
+        v[blocks] = (v[blocks].float() * factor).to(torch.bfloat16)
+        vp.append(v)
+    vmax = max(float(v.float().abs().max()) for v in vp)
+    return dataclasses.replace(w, v_pool=vp), vmax
+
+
+def test_c4_cascade_shared_rows_beyond_fp16():
+    """The branched decode's cascade with the shared prefix's V at 2^17 (about
+    1.3e5, beyond fp16) in every layer: every layer of every step, and the
+    draft verification cascade, against the oracle (errors relative to the
+    largest |V|)."""
+    from decode_focal_layer_amd.decode import DraftVerifier
+    kv = kvsel()
+    cfg = synth.small(synth.C4, batch=150, layers=4, steps=2, focal=(1, 2), grid_rows=8, grid_cols=32,
+                      n_always=48, suffix_range=(3, 40))
+    w, vmax = _c4_wide_shared_v(cfg, gen.make_focal(cfg, DEV), 2.0 ** 17)
+    assert vmax >= 1e5
+    run_schedule(cfg, w, check_every=1, v_scale=vmax, shared_tail=(cfg.n_visual, cfg.prefix_len))
+    # draft verification over layer 0, shared rows folded in
+    m, G, T = 4, cfg.group, cfg.steps
+    n_np = w.seq_len_np[T - 1].astype(np.int64)
+    kvd = kv.KV(w.k_pool[0], w.v_pool[0], w.block_table, w.seq_len[T - 1], w.seg_begin, w.seg_end,
+                max_seq_len=int(n_np.max()), max_seg_len=cfg.n_visual, min_seg_len=cfg.n_visual,
+                shared_rows=cfg.prefix_len)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 91)
+    keys = torch.rand((cfg.batch * cfg.hkv, cfg.n_visual), generator=g, device=DEV)
+    idx = keys.argsort(dim=1)[:, :cfg.k].sort(dim=1).values.to(torch.int32).view(cfg.batch, cfg.hkv, cfg.k)
+    q = torch.randn((cfg.batch, m, cfg.hq, 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.empty((cfg.batch, m, cfg.hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((cfg.batch, m, cfg.hq), dtype=torch.float32, device=DEV)
+    log_case("c4-verify-wide-v", cfg.batch, m)
+    DraftVerifier(kvd, m, cfg.hq, cfg.scale, shared_tail=(cfg.n_visual, cfg.prefix_len),
+                  device=DEV).verify(q, idx, cfg.k, out, lse)
+    torch.cuda.synchronize()
+    idx_c, q_c, vc = idx.cpu().numpy(), q.cpu(), w.v_pool[0].cpu()
+    rng = np.random.default_rng(93)
+    for _ in range(16):
+        b, h = int(rng.integers(cfg.batch)), int(rng.integers(cfg.hkv))
+        n = int(n_np[b])
+        Kl = O.logical_rows(w.k_pool[0].cpu(), w.table_np[b], h, n)
+        Vl = O.logical_rows(vc, w.table_np[b], h, n)
+        rows = O.kept_rows(idx_c[b, h], 0, cfg.n_visual, n)
+        ref, rl = O.verify_attention(O.widen(q_c[b, :, h * G:(h + 1) * G]), Kl, Vl, rows, n, cfg.scale)
+        got = out[b, :, h * G:(h + 1) * G].cpu().numpy()
+        assert_attn(got.reshape(-1, 128) / vmax, ref.reshape(-1, 128) / vmax, f"c4 verify wide-v b{b} g{h}")
+        assert np.abs(lse[b, :, h * G:(h + 1) * G].cpu().numpy() - rl).max() < 1e-4
 
 
 def test_c4_branches_small_and_shared_prefix_equals_private_copy():

@@ -624,6 +624,63 @@ def test_prefill_attention_propagated_tokens():
     assert np.abs(np.array([gl[i, h] for i, h in rows]) - rl).max() < 1e-4
 
 
+# V magnitudes that the fp16 staging of the prefill and shared-range kernels
+# must carry: beyond the fp16 range everywhere, far below it (fp16
+# subnormals), a few huge rows among ordinary ones, and a ramp from 2^-40 to
+# beyond fp16 along the first axis (the scale grows tile after tile).  Powers
+# of two keep the bf16 values exact.
+WIDE_V = ("huge", "tiny", "mixed", "ramp")
+
+
+def widen_v(v, kind, seed, ramp_step=1.0):
+    """v (bf16) with the vectors along its last axis scaled as kind says
+    (ramp: by 2^(floor(i * ramp_step) - 40) at index i of the first axis)."""
+    x = v.detach().cpu().float()
+    if kind == "huge":
+        x *= 2.0 ** 17
+    elif kind == "tiny":
+        x *= 2.0 ** -40
+    elif kind == "mixed":
+        pick = torch.rand(v.shape[:-1], generator=torch.Generator().manual_seed(seed)) < 0.05
+        x[pick] *= 2.0 ** 20
+    else:
+        e = np.minimum(np.floor(np.arange(x.shape[0]) * ramp_step) - 40, 60)
+        x *= torch.from_numpy(np.exp2(e)).float().view(-1, *([1] * (x.dim() - 1)))
+    return x.to(torch.bfloat16).to(v.device)
+
+
+def assert_attn_scaled(got, ref, vmax, what=""):
+    """The attention acceptance test with the absolute bound taken relative
+    to the largest |V| (the relative L2 bound is scale-free)."""
+    return assert_attn(np.asarray(got, dtype=np.float64) / vmax, np.asarray(ref, dtype=np.float64) / vmax, what)
+
+
+@pytest.mark.parametrize("kind", WIDE_V)
+def test_prefill_attention_wide_v(kind):
+    """Causal prefill with V beyond, far below, partly far beyond the fp16
+    range, or ramping across it, against the oracle (each query row's errors
+    relative to the largest |V| it sees)."""
+    kvsel = K()
+    G, hkv, lens = 2, 2, [300, 1, 77, 130]
+    hq = hkv * G
+    q, k, v, cu = _prefill_inputs(61, lens, hq, hkv)
+    v = widen_v(v, kind, 62, ramp_step=1 / 8)
+    total = sum(lens)
+    out = torch.full((total, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((total, hq), float("nan"), dtype=torch.float32, device=DEV)
+    log_case("prefill-wide-v", kind, lens)
+    kvsel.prefill_attn(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lens), SCALE, out, lse)
+    torch.cuda.synchronize()
+    got, gl = out.cpu().numpy(), lse.cpu().numpy()
+    for b, n in enumerate(lens):
+        s0 = int(cu[b])
+        ref, rl = O.causal_prefill(O.widen(q[s0:s0 + n]), O.widen(k[s0:s0 + n]), O.widen(v[s0:s0 + n]), SCALE)
+        seen = np.maximum.accumulate(v[s0:s0 + n].float().abs().amax(dim=(1, 2)).numpy().astype(np.float64))
+        sc = np.repeat(seen, hq)[:, None]                    # rows position-major, like ref
+        assert_attn(got[s0:s0 + n].reshape(n * hq, 128) / sc, ref / sc, f"prefill {kind} b{b}")
+        assert np.abs(gl[s0:s0 + n].reshape(-1) - rl).max() < 1e-4
+
+
 def _shared_prefix_kv(rng, batch, hkv, prefix_len, suffix_max):
     """A paged cache whose sequences share their first prefix_len rows (the
     same blocks, placed at random), each with a private suffix."""
@@ -686,6 +743,48 @@ def test_shared_attention(G, batch, prefix, rng_rows, splits, qps):
             ref, rl = O.attention(O.widen(qc[b, r, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
             assert_attn(got, ref, f"shared b{b} q{r} g{g}")
             assert np.abs(gl - rl).max() < 1e-4
+
+
+@pytest.mark.parametrize("kind", WIDE_V)
+def test_shared_attention_wide_v(kind):
+    """The shared-range kernel with the range's V beyond, far below, or partly
+    far beyond the fp16 range: parts and the folded (accumulate) form against
+    the oracle, errors relative to the largest |V|."""
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(3500)
+    G, batch, hkv, prefix, qps = 2, 40, 2, 400, 2
+    hq = hkv * G
+    kv, kc, vc, table, lens = _shared_prefix_kv(rng, batch, hkv, prefix, 30)
+    vp = widen_v(kv.v_pool, kind, 3501, ramp_step=2.0)
+    kv = dataclasses.replace(kv, v_pool=vp)
+    vc = cpu_pool(vp)
+    rb, re = 21, 390
+    vmax = max(float(np.abs(O.logical_rows(vc, table[0], g, re)[rb:]).max()) for g in range(hkv))
+    q = torch.randn((batch, qps, hq, 128), generator=torch.Generator().manual_seed(17)).to(torch.bfloat16).to(DEV)
+    parts = torch.empty((3, batch, qps, hq, 128), dtype=torch.float32, device=DEV)
+    plse = torch.empty((3, batch, qps, hq), dtype=torch.float32, device=DEV)
+    log_case("shared-wide-v", kind)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, parts, plse, splits=3, q_per_seq=qps)
+    out = torch.empty((batch, qps, hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((batch, qps, hq), dtype=torch.float32, device=DEV)
+    kvsel.merge_attn(parts, plse, out, lse)
+    # folded: an empty other part (lse -inf) leaves the range's own attention
+    acc_o = torch.zeros((batch, qps, hq, 128), dtype=torch.float32, device=DEV)
+    acc_l = torch.full((batch, qps, hq), float("-inf"), dtype=torch.float32, device=DEV)
+    kvsel.shared_attn(kv, q, hq, SCALE, rb, re, acc_o, acc_l, splits=1, q_per_seq=qps, accumulate=True)
+    torch.cuda.synchronize()
+    qc = q.cpu()
+    for b in rng.choice(batch, size=8, replace=False):
+        for r in range(qps):
+            for g in range(hkv):
+                Kl = O.logical_rows(kc, table[b], g, int(lens[b]))
+                Vl = O.logical_rows(vc, table[b], g, int(lens[b]))
+                ref, rl = O.attention(O.widen(qc[b, r, g * G:(g + 1) * G]), Kl, Vl, np.arange(rb, re), SCALE)
+                for name, o, l in (("parts", out, lse), ("accumulate", acc_o, acc_l)):
+                    assert_attn_scaled(o[b, r, g * G:(g + 1) * G].cpu().numpy(), ref, vmax,
+                                       f"shared {kind} {name} b{b} q{r} g{g}")
+                    assert np.abs(l[b, r, g * G:(g + 1) * G].cpu().numpy() - rl).max() < 1e-4
 
 
 def test_shared_attention_logits_stay_in_their_row():
