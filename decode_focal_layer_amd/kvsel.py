@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+# the library built in-tree; KVSEL_LIBRARY names another build of the same
+# sources (the host-sanitizer build the CPU tests load)
+LIB_PATH = os.environ.get("KVSEL_LIBRARY") or os.path.join(_HERE, "libkvsel.so")
 
 REDUCE_GROUP, REDUCE_ALL = 0, 1
 NORM_SEGMENT, NORM_CONTEXT = 0, 1
