@@ -84,8 +84,7 @@ kvsel_status check_heads(const kvsel_kv_desc *kv, int32_t hq, int *group) {
     return fail(KVSEL_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", hq,
                 kv->num_kv_heads);
   const int G = hq / kv->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(KVSEL_EUNSUPPORTED, "group size %d unsupported (1, 2, 4 or 8)", G);
+  if (G < 1 || G > 8) return fail(KVSEL_EUNSUPPORTED, "group size %d unsupported (1 .. 8)", G);
   *group = G;
   return KVSEL_OK;
 }

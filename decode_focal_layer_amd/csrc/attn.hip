@@ -595,9 +595,11 @@ __global__ __launch_bounds__(256) void logits_kernel(AttnArgs a) {
 #ifndef KVSEL_ATTN_WAVES_PER_CU4
 #define KVSEL_ATTN_WAVES_PER_CU4 8
 #endif
-constexpr int attn_threads(int G) { return G <= 2 ? KVSEL_ATTN_NT2 : (G == 4 ? KVSEL_ATTN_NT4 : 256); }
-constexpr int attn_unroll(int G) { return G == 4 ? KVSEL_ATTN_U4 : KVSEL_ATTN_U; }
-constexpr int attn_waves_per_cu(int G) { return G == 4 ? KVSEL_ATTN_WAVES_PER_CU4 : KVSEL_ATTN_WAVES_PER_CU; }
+constexpr int attn_threads(int G) { return G <= 2 ? KVSEL_ATTN_NT2 : (G <= 4 ? KVSEL_ATTN_NT4 : 256); }
+constexpr int attn_unroll(int G) { return G == 3 || G == 4 ? KVSEL_ATTN_U4 : KVSEL_ATTN_U; }
+constexpr int attn_waves_per_cu(int G) {
+  return G == 3 || G == 4 ? KVSEL_ATTN_WAVES_PER_CU4 : KVSEL_ATTN_WAVES_PER_CU;
+}
 
 template <int G>
 hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
@@ -701,7 +703,11 @@ hipError_t launch_attn(const AttnArgs &a, int batch, int group, hipStream_t s) {
   switch (group) {
     case 1: return launch_attn_g<1>(a, batch, s);
     case 2: return launch_attn_g<2>(a, batch, s);
+    case 3: return launch_attn_g<3>(a, batch, s);
     case 4: return launch_attn_g<4>(a, batch, s);
+    case 5: return launch_attn_g<5>(a, batch, s);
+    case 6: return launch_attn_g<6>(a, batch, s);
+    case 7: return launch_attn_g<7>(a, batch, s);
     case 8: return launch_attn_g<8>(a, batch, s);
     default: return hipErrorInvalidValue;
   }
@@ -713,7 +719,11 @@ hipError_t launch_logits(const AttnArgs &a, int batch, int group, int max_rows, 
   switch (group) {
     case 1: hipLaunchKernelGGL(logits_kernel<1>, grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL(logits_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(logits_kernel<3>, grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL(logits_kernel<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(logits_kernel<5>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(logits_kernel<6>, grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL(logits_kernel<7>, grid, block, 0, s, a); break;
     case 8: hipLaunchKernelGGL(logits_kernel<8>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

@@ -69,7 +69,7 @@ def test_gather_attn_rejects_bad_descriptor(L, over, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(hq=12), EINVAL), (dict(hq=24), EUNSUP), (dict(hq=0), EINVAL), (dict(q=0), EINVAL),
+    (dict(hq=12), EINVAL), (dict(hq=72), EUNSUP), (dict(hq=0), EINVAL), (dict(q=0), EINVAL),
     (dict(q=FAKE + 2), EINVAL), (dict(out=0), EINVAL), (dict(k=-1), EINVAL), (dict(idx=0), EINVAL),
     (dict(scale=float("inf")), EINVAL), (dict(ws=0), EINVAL), (dict(ws=FAKE + 64), EINVAL),
     (dict(ws_bytes=64), ENOSPC),

@@ -37,7 +37,8 @@ def make_kv(rng, batch, hkv, lens, segs, max_len=None):
 
 
 ATTN_CASES = [(1, 1, [1]), (2, 2, [15, 16]), (4, 1, [17]), (8, 2, [300, 33]), (2, 3, [4095, 1000, 2]),
-              (2, 1, [8193]), (4, 2, [1, 1000])]
+              (2, 1, [8193]), (4, 2, [1, 1000]),
+              (3, 2, [300, 33]), (5, 1, [1000]), (6, 2, [17, 4095]), (7, 1, [129])]
 
 
 @pytest.mark.parametrize("G,batch,lens", ATTN_CASES)
@@ -89,7 +90,7 @@ def test_dense_and_gather_attention(G, batch, lens):
 # ragged lengths, empty and whole segments
 MASS_CASES = [(1, 1, [1], [(0, 1)]), (2, 2, [17, 300], [(3, 15), (0, 300)]),
               (4, 3, [4095, 1000, 2], [(100, 4000), (7, 7), (1, 2)]), (8, 1, [8193], [(0, 8000)]),
-              (2, 32, None, None)]
+              (2, 32, None, None), (3, 2, [17, 300], [(3, 15), (0, 300)]), (6, 1, [1000], [(5, 900)])]
 
 
 @pytest.mark.parametrize("G,batch,lens,segs", MASS_CASES)
@@ -332,7 +333,8 @@ def test_dense_fused_scores_match_score_call():
 # (G, norm, batch, hkv, len, seg): few pairs -> split attention + separate select;
 # >= 256 (G <= 2) or 512 (G = 4) pairs -> the one-kernel fused focal pass
 FOCAL_CASES = [(2, 0, 3, 4, 3000, 2500), (4, 1, 3, 4, 3000, 2500), (1, 0, 3, 4, 3000, 2500), (8, 0, 3, 4, 3000, 2500),
-               (2, 0, 32, 8, 900, 700), (4, 0, 64, 8, 520, 400), (1, 0, 32, 8, 400, 333)]
+               (2, 0, 32, 8, 900, 700), (4, 0, 64, 8, 520, 400), (1, 0, 32, 8, 400, 333),
+               (3, 0, 3, 4, 3000, 2500), (5, 1, 3, 4, 3000, 2500), (6, 0, 8, 4, 900, 700), (7, 0, 3, 4, 400, 333)]
 
 
 @pytest.mark.parametrize("G,norm,batch,hkv,n,seg", FOCAL_CASES)
@@ -379,7 +381,8 @@ def test_focal_attn_equals_dense_then_topk(G, norm, batch, hkv, n, seg):
             assert_attn(o2[b, g * G:(g + 1) * G].cpu().numpy(), refo, f"focal out b{b} g{g}")
 
 
-@pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True)])
+@pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True),
+                                              (3, 8, 0, True), (5, 6, 1, False), (6, 5, 0, True), (7, 4, 1, True)])
 def test_window_scores(G, W, reduce, causal):
     kvsel = K()
     rng = np.random.default_rng(G * 7 + W)
@@ -523,7 +526,9 @@ def test_fork_copy_on_write(L):
 VERIFY_CASES = [(1, 1, 1, [1], [(0, 1)], 0), (2, 4, 2, [17, 300], [(3, 10), (0, 290)], 5),
                 (4, 8, 1, [4000], [(10, 3900)], 200), (8, 4, 2, [700, 129], [(64, 600), (0, 100)], 33),
                 (1, 32, 1, [96], [(0, 40)], 40), (2, 4, 1, [50], [(5, 50)], 30),
-                (2, 4, 1, [8300], [(100, 8200)], 7900), (4, 2, 3, [33, 34, 35], [(1, 30), (2, 2), (0, 33)], 0)]
+                (2, 4, 1, [8300], [(100, 8200)], 7900), (4, 2, 3, [33, 34, 35], [(1, 30), (2, 2), (0, 33)], 0),
+                (3, 4, 2, [17, 300], [(3, 10), (0, 290)], 5), (5, 6, 1, [700], [(64, 600)], 33),
+                (6, 2, 2, [50, 129], [(5, 50), (0, 100)], 20), (7, 4, 1, [400], [(10, 300)], 100)]
 
 
 @pytest.mark.parametrize("G,m,batch,lens,segs,k", VERIFY_CASES)
@@ -568,7 +573,7 @@ def test_verify_attention(G, m, batch, lens, segs, k):
 # (G, hkv, lengths): packed ragged sequences, one row, an empty sequence,
 # several 128-row blocks with a ragged tail, every group size
 PREFILL_CASES = [(1, 2, [1]), (2, 2, [31, 100]), (4, 2, [257]), (8, 1, [130, 0, 3, 64]), (4, 8, [700]),
-                 (1, 1, [129, 64])]
+                 (1, 1, [129, 64]), (3, 2, [31, 100]), (5, 1, [257]), (6, 2, [129, 3]), (7, 1, [200])]
 
 
 def _prefill_inputs(seed, lens, hq, hkv):
@@ -706,7 +711,9 @@ def _shared_prefix_kv(rng, batch, hkv, prefix_len, suffix_max):
 # parts of the range (some empty)
 SHARED_CASES = [(2, 5, 160, (37, 160), 1, 1), (1, 3, 64, (0, 64), 1, 1), (4, 70, 1024, (300, 1024), 4, 1),
                 (8, 20, 96, (5, 90), 3, 1), (2, 9, 48, (10, 10), 1, 1), (2, 600, 256, (64, 250), 2, 1),
-                (1, 4, 128, (0, 100), 5, 1), (2, 30, 200, (16, 180), 2, 3)]
+                (1, 4, 128, (0, 100), 5, 1), (2, 30, 200, (16, 180), 2, 3),
+                (3, 7, 160, (37, 160), 2, 1), (6, 9, 200, (16, 180), 1, 2), (5, 40, 96, (5, 90), 3, 1),
+                (7, 3, 64, (0, 64), 1, 4)]
 
 
 @pytest.mark.parametrize("G,batch,prefix,rng_rows,splits,qps", SHARED_CASES)
