@@ -36,6 +36,7 @@ constexpr int kListCap = 256;
 template <int NTS>
 struct RadixShared {
   uint32_t hist[2048];
+  uint32_t sink[64];   // the histogram passes' adds of keys outside the bin (never read)
   uint32_t w1[NTS / 64];
   uint32_t w2[NTS / 64];
   uint32_t w3[NTS / 64];
@@ -216,20 +217,21 @@ __device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &
   grp.sync();
 }
 
-// The k largest of key(i), i in [0, n), among the candidates (keys >= theta),
-// written ascending to dst; n > k >= 1.  lo <= every candidate key <= hi, and
-// nin >= the number of candidates (at least k of them).  LDS_KEYS: key(i)
-// reads LDS; otherwise global memory, with more reads in flight per lane.
-// Output, keys in global memory: per-wave ranges walked 64 consecutive keys
-// at a time, so that the reads coalesce and each wave's chosen indices leave
-// in contiguous runs.  Keys in LDS: per-participant ranges of C keys (C odd:
-// the lanes of a wave read different banks); with stage (the LDS array the
-// keys live in, writable once they are read) and C <= STAGE_C, each
-// participant holds its keys in registers while the chosen indices are
-// placed in that array, which is then copied out in order (coalesced).
-template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, typename Grp, typename KeyFn>
-__device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
-                             int32_t *dst, RadixShared<NTS> &sh, uint32_t *stage = nullptr) {
+// The k-th largest key T among the candidates (keys >= theta) of key(i), i in
+// [0, n), and keq, how many keys equal to T the top k hold (>= 1); n > k >= 1.
+// lo <= every candidate key <= hi, and nin >= the number of candidates (at
+// least k of them).  LDS_KEYS: key(i) reads LDS; otherwise global memory,
+// with more reads in flight per lane.  LIST: the digit passes stop once the
+// bin holding T has at most this many candidates, which are then collected
+// and ranked (0: digit passes until T is known, for keys whose passes are
+// cheap).  Ends with sh free again.
+struct RadixT {
+  uint32_t T, keq;
+};
+template <int NTS, bool LDS_KEYS = true, int LIST = kListCap, typename Grp, typename KeyFn>
+__device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
+                             RadixShared<NTS> &sh) {
+  static_assert(LIST >= 0 && LIST <= kListCap, "the candidate list holds kListCap keys");
   constexpr int B = LDS_KEYS ? 8 : 32;
   constexpr int NW = NTS / 64;
   const int t = grp.t(), lane = t & 63, w = t >> 6;
@@ -240,14 +242,21 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
   auto in_bin = [&](uint32_t x) { return x >= theta && ((x - lo) & pmask) == prefix; };
 
   // ---- digit passes until the bin holding T is small ----
-  while (top > 0 && nin > (uint32_t)kListCap) {
+  while (top > 0 && nin > (uint32_t)LIST) {
     const int bits = top < 11 ? top : 11;
     const int shift = top - bits;
     const int nb = 1 << bits;
     for (int i = t; i < nb; i += NTS) sh.hist[i] = 0;
     grp.sync();
+    // a key of the bin: x - base below 2^span (any key when span reaches 32);
+    // every key adds one, those outside the bin to this lane's sink word (no
+    // branch around the add)
+    const uint32_t base = lo + prefix;
+    const int span = shift + bits;
     each_key<NTS, B>(t, key, n, [&](int, uint32_t x) {
-      if (in_bin(x)) atomicAdd(&sh.hist[((x - lo) >> shift) & (nb - 1)], 1u);
+      const uint32_t d = x - base;
+      const bool in = x >= theta && (span >= 32 || (d >> span) == 0u);
+      atomicAdd(in ? &sh.hist[d >> shift] : &sh.sink[lane], 1u);
     });
     grp.sync();
     // participant t owns bins [t*per, (t+1)*per) (empty past nb)
@@ -283,7 +292,7 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     grp.sync();
   }
 
-  uint32_t T, keq;   // the k-th largest key; keys equal to it to keep (>= 1)
+  uint32_t T, keq;
   if (top == 0) {
     T = lo + prefix;   // every digit fixed: the bin is one key value
     keq = krem;
@@ -296,22 +305,38 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
       sh.list_idx[i] = 0x7fffffff;
     }
     grp.sync();
-    each_key_wave<B>(key, w * ((n + NW * 64 - 1) / (NW * 64) * 64),
-                     min(n, (w + 1) * ((n + NW * 64 - 1) / (NW * 64) * 64)),
-                     [&](int i, bool valid, uint32_t x) {
-      const bool m = valid && in_bin(x);
-      const uint64_t mask = __ballot(m);
-      if (mask != 0ull) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&sh.misc[3], (uint32_t)__popcll(mask));
-        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-        const uint32_t slot = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-        if (m && slot < (uint32_t)kListCap) {
-          sh.list_key[slot] = x;
-          sh.list_idx[slot] = i;
+    {
+      // wave w walks its contiguous range 64 keys at a time, B chunks per
+      // batch: the batch's matches counted from ballots, their slots taken
+      // with one add to the counter, then written
+      const int cw = (n + NW * 64 - 1) / (NW * 64) * 64;
+      const int w0 = min(n, w * cw), w1 = min(n, w0 + cw);
+      const uint64_t below = (1ull << lane) - 1ull;
+      for (int b0 = w0; b0 < w1; b0 += B * 64) {
+        uint32_t x[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) x[j] = key(min(b0 + j * 64 + lane, w1 - 1));   // unbranched reads
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < B; ++j) cnt += (uint32_t)__popcll(__ballot(b0 + j * 64 + lane < w1 && in_bin(x[j])));
+        if (cnt == 0u) continue;
+        uint32_t slot0 = 0;
+        if (lane == 0) slot0 = atomicAdd(&sh.misc[3], cnt);
+        slot0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot0);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+          const int i = b0 + j * 64 + lane;
+          const bool m = i < w1 && in_bin(x[j]);
+          const uint64_t mask = __ballot(m);
+          const uint32_t slot = slot0 + (uint32_t)__popcll(mask & below);
+          if (m && slot < (uint32_t)kListCap) {
+            sh.list_key[slot] = x[j];
+            sh.list_idx[slot] = i;
+          }
+          slot0 += (uint32_t)__popcll(mask);
         }
       }
-    });
+    }
     grp.sync();
     const int nl = min((int)sh.misc[3], kListCap);
     const int nl4 = (nl + 3) & ~3;   // whole groups of four (the padding ranks below everything)
@@ -344,8 +369,29 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     grp.sync();
     T = sh.misc[4];
     keq = sh.misc[5];
+    grp.sync();   // sh is free again
   }
+  return RadixT{T, keq};
+}
 
+// The k largest of key(i), i in [0, n), among the candidates (keys >= theta),
+// written ascending to dst; arguments as for radix_find.  Output, keys in
+// global memory: per-wave ranges walked 64 consecutive keys at a time, so
+// that the reads coalesce and each wave's chosen indices leave in contiguous
+// runs.  Keys in LDS: per-participant ranges of C keys (C odd: the lanes of a
+// wave read different banks); with stage (the LDS array the keys live in,
+// writable once they are read) and C <= STAGE_C, each participant holds its
+// keys in registers (read once for the count and the output) while the
+// chosen indices are placed in that array, which is then copied out in order
+// (coalesced).
+template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, int LIST = kListCap, typename Grp, typename KeyFn>
+__device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
+                             int32_t *dst, RadixShared<NTS> &sh, uint32_t *stage = nullptr) {
+  constexpr int B = LDS_KEYS ? 8 : 32;
+  constexpr int NW = NTS / 64;
+  const int t = grp.t(), lane = t & 63, w = t >> 6;
+  const RadixT found = radix_find<NTS, LDS_KEYS, LIST>(grp, key, n, k, theta, lo, hi, nin, sh);
+  const uint32_t T = found.T, keq = found.keq;
   if constexpr (LDS_KEYS) {
     // ---- ordered output: participant t owns the indices [t*C, (t+1)*C) ----
     // It counts its keys above T and equal to T, the exclusive scans of those
@@ -353,6 +399,39 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     // output, and the equal keys taken are the lowest-indexed keq.
     const int C = ((n + NTS - 1) / NTS) | 1;
     const int i0 = min(n, t * C), i1 = min(n, i0 + C);
+    if (STAGE_C > 0 && stage != nullptr && C <= STAGE_C) {
+      // the participant's keys read once, into registers
+      constexpr int SC = STAGE_C > 0 ? STAGE_C : 1;
+      uint32_t x[SC];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) x[j] = key(min(i0 + j, n - 1));
+      uint32_t cg = 0, ce = 0;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        cg += (i0 + j < i1 && x[j] > T) ? 1u : 0u;
+        ce += (i0 + j < i1 && x[j] == T) ? 1u : 0u;
+      }
+      uint32_t gt_before, eq_before;
+      // (its barriers also free the key array: every participant has read its keys)
+      excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
+      uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
+      uint32_t eq_seen = eq_before;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        if (i0 + j < i1) {
+          bool take = x[j] > T;
+          if (x[j] == T) {
+            take = eq_seen < keq;
+            ++eq_seen;
+          }
+          if (take) stage[pos++] = (uint32_t)(i0 + j);
+        }
+      }
+      grp.sync();
+      for (int i = t; i < k; i += NTS) dst[i] = (int32_t)stage[i];
+      grp.sync();   // sh is free again
+      return;
+    }
     uint32_t cg = 0, ce = 0;
     for (int b0 = i0; b0 < i1; b0 += B) {
       uint32_t x[B];
@@ -368,26 +447,7 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     excl_scan2<NTS>(grp, cg, ce, sh.w1, sh.w2, gt_before, eq_before);
     uint32_t pos = gt_before + (eq_before < keq ? eq_before : keq);
     uint32_t eq_seen = eq_before;
-    if (STAGE_C > 0 && stage != nullptr && C <= STAGE_C) {
-      constexpr int SC = STAGE_C > 0 ? STAGE_C : 1;
-      uint32_t x[SC];
-#pragma unroll
-      for (int j = 0; j < SC; ++j) x[j] = key(min(i0 + j, n - 1));
-      grp.sync();   // every participant holds its keys: the array is free
-#pragma unroll
-      for (int j = 0; j < SC; ++j) {
-        if (i0 + j < i1) {
-          bool take = x[j] > T;
-          if (x[j] == T) {
-            take = eq_seen < keq;
-            ++eq_seen;
-          }
-          if (take) stage[pos++] = (uint32_t)(i0 + j);
-        }
-      }
-      grp.sync();
-      for (int i = t; i < k; i += NTS) dst[i] = (int32_t)stage[i];
-    } else {
+    {
       for (int b0 = i0; b0 < i1; b0 += B) {
         uint32_t x[B];
 #pragma unroll
@@ -452,7 +512,7 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
 // Top-k of a whole row with a block of NTS threads: warm theta (optional),
 // candidate range, radix select.  When n <= k all n indices are kept,
 // followed by -1.  LDS_KEYS as for radix_select.
-template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, typename Grp, typename KeyFn>
+template <int NTS, bool LDS_KEYS = true, int STAGE_C = 0, int LIST = kListCap, typename Grp, typename KeyFn>
 __device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *warm, int32_t *dst, RadixShared<NTS> &sh,
                            uint32_t *stage = nullptr) {
   const int t = grp.t();
@@ -463,7 +523,7 @@ __device__ void radix_topk(Grp &grp, KeyFn key, int n, int k, const int32_t *war
   const uint32_t theta = warm != nullptr ? warm_theta<NTS>(grp, key, warm, n, k, sh) : 0u;
   uint32_t lo, hi, ncand;
   key_range<NTS>(grp, key, n, theta, lo, hi, ncand, sh);
-  radix_select<NTS, LDS_KEYS, STAGE_C>(grp, key, n, k, theta, lo, hi, ncand, dst, sh, stage);
+  radix_select<NTS, LDS_KEYS, STAGE_C, LIST>(grp, key, n, k, theta, lo, hi, ncand, dst, sh, stage);
 }
 
 }  // namespace kvsel

@@ -234,7 +234,9 @@ def test_topk_rows_of_their_own_length(n, k):
                                       (20000, 19999, "ties"), (20000, 20000, "rand"), (131072, 2048, "rand"),
                                       # scores over many exponents, both signs, and a k-th score in the
                                       # highest occupied coarse bin
-                                      (50000, 1000, "wide"), (50000, 300, "signed"), (16384, 3, "spike")])
+                                      (50000, 1000, "wide"), (50000, 300, "signed"), (16384, 3, "spike"),
+                                      # the coarse bin of the k-th score taken whole
+                                      (16384, 5, "spike")])
 def test_topk_exact(n, k, mode):
     kvsel = K()
     rng = np.random.default_rng(n + k)
