@@ -10,6 +10,7 @@ The binding fails loudly if libkvsel.so has not been built.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -500,7 +501,7 @@ def gather_rows(src: torch.Tensor, idx: Optional[torch.Tensor], n_idx: int, tail
     """kvsel_gather_rows: dst = src[idx[:n_idx]] ++ src[tail_begin : tail_begin + n_tail] (rows)."""
     if not src.is_contiguous() or not dst.is_contiguous():
         raise ValueError("src and dst must be contiguous")
-    row_bytes = src[0].numel() * src.element_size()
+    row_bytes = math.prod(src.shape[1:]) * src.element_size()
     if idx is not None:
         _need(idx, torch.int32, "idx")
     _check(lib().kvsel_gather_rows(_ptr(src), row_bytes, src.shape[0], _ptr(idx), n_idx, tail_begin, n_tail,

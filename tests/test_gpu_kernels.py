@@ -1,5 +1,6 @@
 """Per-entry-point parity of libkvsel against the oracle on small seeded
 shapes that span several tiles and ragged tails, with edge cases."""
+import ctypes
 import math
 
 import numpy as np
@@ -436,6 +437,38 @@ def test_gather_rows_exact():
     assert np.array_equal(d[[0, 1, 2, 3, 4]].numpy(), want[:5])
     assert np.array_equal(d[7:].numpy(), want[5:])
     assert torch.all(d[5:7] == 0)    # out-of-range indices give zero rows
+
+
+@pytest.mark.parametrize("cols,n_src,idx,tail_begin,n_tail", [
+    (296, 50, [3, 49, -2, 50, 7, 7, 0], 45, 5),     # rows of 592 bytes (fewer pieces than threads)
+    (8192, 20, [19, 0, 5], 17, 6),                  # 16 KiB rows (two passes), a tail running past the source
+    (64, 0, [0, 1], 0, 3),                          # an empty source: every row zero
+    (4096, 9, [8], 0, 0),                           # one row
+])
+def test_gather_rows_shapes(cols, n_src, idx, tail_begin, n_tail):
+    kvsel = K()
+    g = torch.Generator().manual_seed(cols + n_src)
+    src = torch.randint(-(1 << 15), 1 << 15, (max(n_src, 1), cols), generator=g, dtype=torch.int16)
+    src = src.view(torch.bfloat16).to(DEV)[:n_src]   # (an empty source still has a valid address)
+    it = torch.tensor(idx, dtype=torch.int32, device=DEV)
+    rows = len(idx) + n_tail
+    dst = torch.full((rows, cols), 3.0, dtype=torch.bfloat16, device=DEV)
+    log_case("gather-shapes", cols, n_src, len(idx), n_tail)
+    if n_src:
+        kvsel.gather_rows(src, it, len(idx), tail_begin, n_tail, dst)
+    else:   # through the C entry point: a valid buffer that holds no source row
+        buf = torch.zeros((1, cols), dtype=torch.bfloat16, device=DEV)
+        st = kvsel.lib().kvsel_gather_rows(ctypes.c_void_p(buf.data_ptr()), cols * 2, 0, ctypes.c_void_p(it.data_ptr()),
+                                           len(idx), tail_begin, n_tail, ctypes.c_void_p(dst.data_ptr()), None)
+        assert st == 0
+    torch.cuda.synchronize()
+    s_np = src.cpu().view(torch.int16).numpy() if n_src else np.zeros((0, cols), np.int16)
+    d_np = dst.cpu().view(torch.int16).numpy()
+    want = np.zeros((rows, cols), np.int16)
+    for j, r in enumerate(list(idx) + list(range(tail_begin, tail_begin + n_tail))):
+        if 0 <= r < n_src:
+            want[j] = s_np[r]
+    assert np.array_equal(d_np, want)
 
 
 def test_determinism():
