@@ -79,6 +79,20 @@ __device__ __forceinline__ SeqView seq_view_of(const AttnArgs &a, int n_raw, int
   return v;
 }
 
+// The first virtual row from which every row is this sequence's own (past the
+// rows shared across sequences, a.shared_rows > 0): those are read once and
+// may be streamed past the caches.  Virtual rows: dense, the logical rows;
+// else the kept segment rows, then [0, s0), then [s1, n).  Kept rows are
+// never counted as own here (they come first).
+__device__ __forceinline__ int own_rows_from(const AttnArgs &a, const SeqView &v, bool dense) {
+  const int sh = a.shared_rows;
+  if (dense) return min(sh, v.n);
+  if (sh >= v.n) return v.nR;                          // nothing of its own
+  if (sh > v.s1) return a.k + v.s0 + (sh - v.s1);      // [s1, sh) shared, then own
+  if (sh > v.s0) return a.k + v.s0;                    // [0, s0) shared, [s1, n) own
+  return a.k + sh;                                     // [sh, s0) and [s1, n) own
+}
+
 __device__ __forceinline__ SeqView seq_view(const AttnArgs &a, int b, bool dense) {
   return seq_view_of(a, a.seq_len[b], a.seg_begin[b], a.seg_end[b], dense);
 }
@@ -157,9 +171,11 @@ __device__ __forceinline__ void merge_records(const AttnArgs &a, int b, int g, i
 // dim 0 of that output.  STREAM: K/V rows are
 // loaded non-temporally (each is read once), so they do not evict the data
 // that is reused from launch to launch (block tables, kept indices, queries);
-// off when the rows themselves are shared by many sequences (a shared
-// prefix), which should stay cached.  Measured on MI355X: +8% for C1 decode
-// and C3, and -8% for C4 if the shared prefix were streamed too.
+// off when rows are shared by many sequences (a shared prefix), which should
+// stay cached -- then only the chunks made wholly of a sequence's own rows
+// (past the shared ones, own_rows_from) are streamed.  Measured on MI355X:
+// +8% for C1 decode and C3, and -8% for C4 if the shared prefix were streamed
+// too.
 template <int G, int NT, int U, int MODE, bool STREAM>
 __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   constexpr int NW = NT / 64;    // waves
@@ -210,6 +226,9 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   }
   const SeqView v = seq_view_of(a, n_raw, s0_raw, s1_raw, dense);
   const int cnt = max(0, min(a.rps, v.nR - start));   // rows of this split
+  // chunks starting at or past this split-local row hold only rows read once
+  // (all of them when STREAM)
+  const int own_from = STREAM ? 0 : own_rows_from(a, v, dense) - start;
   constexpr int CH = 4 * U;              // rows per chunk
   const int nch = (cnt + CH - 1) / CH;   // chunks of this split
 
@@ -285,8 +304,10 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   // rows c*CH + grp%4 + 4*u, so each load instruction of a wave covers four
   // consecutive rows.
 #define KVSEL_ROWT(base, u) ((base) + (grp & 3) + 4 * (u))
-  // K/V rows of one chunk into registers
-  auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
+  // K/V rows of one chunk into registers; NTL: loaded non-temporally (each row
+  // is read once: do not displace reused lines)
+  auto load_rows_as = [&](auto nt, int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
+    constexpr bool NTL = decltype(nt)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = KVSEL_ROWT(base, u);
@@ -299,17 +320,24 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       const uint16_t *kp = ok[u] ? kbase + (size_t)pr * kD : qbase;
       const uint16_t *vp = ok[u] ? vbase + (size_t)pr * kD : qbase;
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      if (STREAM)   // each row is read once: do not displace reused lines
+      if (NTL)
         kr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp)));
       else
         kr[u] = *reinterpret_cast<const uint4 *>(kp);
       if (MODE == 3)
         vr[u] = make_uint4(0u, 0u, 0u, 0u);   // not read
-      else if (STREAM)
+      else if (NTL)
         vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp)));
       else
         vr[u] = *reinterpret_cast<const uint4 *>(vp);
     }
+  };
+  // the chunk's rows streamed when they all lie past the shared rows (uniform)
+  auto load_rows = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
+    if (STREAM || base >= own_from)
+      load_rows_as(std::true_type{}, base, kr, vr, ok);
+    else
+      load_rows_as(std::false_type{}, base, kr, vr, ok);
   };
   // online softmax over the chunk's rows
   auto consume = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U], const bool (&ok)[U]) {
