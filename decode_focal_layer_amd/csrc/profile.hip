@@ -15,10 +15,11 @@
 // additions, and two layers tie only when their exact sums are equal; then
 // the lower layer ranks first.  A non-finite ratio counts as 0.
 //
-// One work-group of 256 threads.  Per layer: each thread adds its ratios
-// j = t, t + 256, ... into its own limbs; the limbs are summed over the
-// threads in LDS; one thread propagates the carries into normalised digits
-// (digit j in [0, 2^32), the remaining carry kept as a signed top word).
+// One work-group of 1024 threads, one wave per layer at a time (wave w takes
+// layers w, w + 16, ...): each lane adds its ratios j = lane, lane + 64, ...
+// (16 loads in flight) into its own limbs; the limbs are summed over the
+// wave's lanes; lane 0 propagates the carries into normalised digits (digit
+// j in [0, 2^32), the remaining carry kept as a signed top word).
 // Then layer l's rank is the number of layers with a larger sum, or an equal
 // sum and a lower index; the layers ranked below n_pick are written in
 // ascending order.
@@ -29,7 +30,7 @@ namespace kvsel {
 
 namespace {
 
-constexpr int kPickThreads = 256;
+constexpr int kPickThreads = 1024;
 constexpr int kLimbs = 10;   // 320 bits: 277 for any finite fp32, the rest for carries
 
 // add (sign) m << s into limbs
@@ -62,35 +63,38 @@ __global__ __launch_bounds__(kPickThreads) void pick_layers_kernel(const float *
                                                                    int n, int n_pick, int32_t *layers) {
   __shared__ uint32_t s_dig[kMaxLayers][kLimbs];
   __shared__ int32_t s_top[kMaxLayers];
-  __shared__ int64_t s_part[kLimbs][kPickThreads / 64];
   __shared__ uint8_t s_take[kMaxLayers];
+  constexpr int NW = kPickThreads / 64, B = 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int l = 0; l < n_layers; ++l) {
+  for (int l = w; l < n_layers; l += NW) {
     const float *r = ratios + (size_t)l * ld;
     int64_t acc[kLimbs];
 #pragma unroll
     for (int j = 0; j < kLimbs; ++j) acc[j] = 0;
-    for (int i = tid; i < n; i += kPickThreads) limbs_add(acc, r[i]);
-    // integer sums: exact in any order
+    for (int i0 = 0; i0 < n; i0 += B * 64) {
+      float x[B];
 #pragma unroll
-    for (int j = 0; j < kLimbs; ++j) {
-      int64_t v = acc[j];
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) s_part[j][w] = v;
+      for (int u = 0; u < B; ++u) x[u] = r[min(i0 + u * 64 + lane, n - 1)];   // unbranched reads
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (i0 + u * 64 + lane < n) limbs_add(acc, x[u]);
     }
-    __syncthreads();
-    if (tid == 0) {
+    // integer sums over the wave's lanes: exact in any order
+#pragma unroll
+    for (int j = 0; j < kLimbs; ++j)
+      for (int off = 32; off >= 1; off >>= 1) acc[j] += __shfl_xor(acc[j], off);
+    if (lane == 0) {
       int64_t carry = 0;
+#pragma unroll
       for (int j = 0; j < kLimbs; ++j) {
-        int64_t v = carry;
-        for (int i = 0; i < kPickThreads / 64; ++i) v += s_part[j][i];
+        const int64_t v = acc[j] + carry;
         carry = v >> 32;   // arithmetic shift: v = carry * 2^32 + digit, digit in [0, 2^32)
         s_dig[l][j] = (uint32_t)(v - (carry << 32));
       }
       s_top[l] = (int32_t)carry;
     }
-    __syncthreads();
   }
+  __syncthreads();
   for (int l = tid; l < n_layers; l += kPickThreads) {
     int rank = 0;
     for (int m = 0; m < n_layers; ++m)
