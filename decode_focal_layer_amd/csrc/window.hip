@@ -26,9 +26,11 @@
 //   The fp64 per-(kv head) scores feed the group-sum / pool post-pass.
 //
 // The head dimension is permuted identically in both operands (lane half hf
-// holds dims [hf*64, hf*64+64), 8 per MFMA step), so each lane reads one
-// whole 128-byte half of a key row; the dot product is independent of the
-// order of its terms.
+// holds dims [hf*64, hf*64+64), 8 per MFMA step); the dot product is
+// independent of the order of its terms.  K reaches the MFMA operands
+// through LDS: each wave streams its 32-key blocks into slices of its own by
+// direct non-temporal loads of whole rows (K is read once per pass, so it
+// need not displace anything cached), one block ahead of the one it uses.
 #include "common.h"
 #include "kvsel_internal.h"
 
@@ -78,38 +80,74 @@ __device__ __forceinline__ void stage_tile_blocks(const WinArgs &a, int b, int k
   }
 }
 
-// lane's key operand for key row `key` of the tile whose block ids start at
-// kb0.  Keys past kend or in an invalid block read `dummy` (any 256 valid
-// bytes) instead; the caller masks them.  No branch: every call issues the
-// same eight loads, so the compiler's wait counts stay exact.
-__device__ __forceinline__ bool load_k(const WinArgs &a, int g, const int *s_blk, int kb0, int key, int kend,
-                                       const uint16_t *dummy, int lane, bf16x8 (&kop)[8]) {
-  const int hf = lane >> 5;
-  const int bi = min(max((key - kb0) >> 4, 0), kWinMaxTileBlocks - 1);
-  const int blk = key < kend ? s_blk[bi] : -1;
-  const uint16_t *row = blk >= 0
-      ? a.k_pool + ((size_t)((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * kBlk + (key & 15)) * kD
-      : dummy;
-  const uint4 *p = reinterpret_cast<const uint4 *>(row + hf * 64);
+// ---- K through LDS by direct, non-temporal loads ----
+// Each wave streams its own 32-key blocks through two 8 KiB LDS slices of its
+// own (static arrays, one per slice parity: the compiler then knows a load
+// into one slice leaves the other alone and waits only for the loads of the
+// slice it reads).  A K row is read once, by whole 256-byte rows per load
+// instruction, so it can bypass the caches.
+
+typedef __attribute__((address_space(1))) void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
+constexpr int kWinWaves = kWinThreads / 64;
+constexpr int kSliceBytes = 32 * 256;   // one wave's 32-key block of K
+constexpr int kNonTemporal = 2;         // cache-policy bits of the direct loads: nt
+
+// The K rows of keys [kb, kb + 32) -- two whole cache blocks, kb a multiple of
+// 16 -- into this wave's slice: load u of half h fills keys kb + 16h + 4u ..
+// +3 (64 lanes x 16 bytes, lane L's at byte 16L of that stretch), lane L
+// taking chunk (L%16) ^ (key%16) of key kb + 16h + 4u + L/16, so that the
+// slice holds chunk c of key r at byte 256r + 16 (c ^ r%16).  Chunk (L%16) ^
+// (4u + L/16) is c0 ^ 4u, c0 = (L%16) ^ (L/16): lane L's byte offset in the
+// block's 4 KiB run is 1024u + (lo ^ 64u), lo = 256 (L/16) + 16 c0.  A block
+// that is invalid, or starts at or past t1, reads the pool's first block of
+// this kv head instead (its keys are masked by the caller), so every call
+// issues the same eight loads.
+__device__ __forceinline__ void dma_block(const WinArgs &a, int g, const int *s_blk, int kb0, int kb, int t1,
+                                          uint8_t *slice, uint32_t lo) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kop[kk] = __builtin_bit_cast(bf16x8, p[kk]);
-  return blk >= 0;
+  for (int h = 0; h < 2; ++h) {
+    const int key0 = kb + 16 * h;
+    const int bi = min(max((key0 - kb0) >> 4, 0), kWinMaxTileBlocks - 1);
+    const int sb = s_blk[bi];   // read unbranched (a read under a branch is waited for at once)
+    const int blk = __builtin_amdgcn_readfirstlane(key0 < t1 ? sb : -1);
+    const uint8_t *run = reinterpret_cast<const uint8_t *>(a.k_pool) +
+                         ((size_t)((uint32_t)max(blk, 0) * (uint32_t)a.hkv + (uint32_t)g) << 12);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_global_load_lds((gmem_t *)(run + 1024 * u + (lo ^ (64u * u))),
+                                       (lmem_t *)(slice + (16 * h + 4 * u) * 256), 16, 0, kNonTemporal);
+  }
 }
 
-// Walk a wave's 32-key blocks k0 = first, first + 128, ... < end with two
-// operand buffers: the next block's loads are in flight while one block is
-// used (loads past the end read the dummy row), and no register copy forces
-// an early wait.
-template <typename LoadF, typename UseF>
-__device__ __forceinline__ void walk_blocks(int first, int end, LoadF load, UseF use) {
-  bf16x8 ka[8], kb[8];
-  load(first, ka);
+// lane's key operand from a slice: key kl = lane % 32, dims [hf*64, hf*64+64)
+// (chunk hf*8 + kk at 16 * ((hf*8 + kk) ^ kl%16) in row kl: rb ^ 16kk)
+__device__ __forceinline__ void slice_k(const uint8_t *slice, uint32_t rb, bf16x8 (&kop)[8]) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kop[kk] = *reinterpret_cast<const bf16x8 *>(slice + (rb ^ (16u * kk)));
+}
+
+// The queries are in registers before the first direct load: the compiler
+// counts direct loads and ordinary loads as completing out of order, so an
+// ordinary load still in flight would turn every wait in the loop into a wait
+// for all loads.
+__device__ __forceinline__ void have_q(const bf16x8 (&qop)[8]) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qop[kk]));
+}
+
+// Walk a wave's 32-key blocks k0 = first, first + 128, ... < end through its
+// two slices: the next block's loads are in flight while one block is used
+// (past the end they read the dummy block).
+template <typename DmaF, typename UseF>
+__device__ __forceinline__ void walk_slices(int first, int end, uint8_t *sl0, uint8_t *sl1, DmaF dma, UseF use) {
+  dma(first, sl0);
   for (int k0 = first; k0 < end; k0 += 256) {
-    load(k0 + 128, kb);
-    use(k0, ka);
+    dma(k0 + 128, sl1);
+    use(k0, sl0);
     if (k0 + 128 >= end) break;
-    load(k0 + 256, ka);
-    use(k0 + 128, kb);
+    dma(k0 + 256, sl0);
+    use(k0 + 128, sl1);
   }
 }
 
@@ -124,6 +162,8 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
   __shared__ double s_z[8][32];
 
   __shared__ int s_blk[kWinMaxTileBlocks + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sl0[kWinWaves][kSliceBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sl1[kWinWaves][kSliceBytes];
   stage_tile_blocks(a, b, t0, t1, s_blk);
   bf16x8 qop[8];
   load_q(a, b, g, lane, qop);
@@ -135,9 +175,13 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
   float mc = -INFINITY;   // reference: the largest dot * cf so far (fp32)
   double z = 0.0;         // sum of 2^(dot * cf - mc), per element in fp32
   __syncthreads();
-  const uint16_t *dummy = a.q;
-  auto load = [&](int kb, bf16x8 (&kop)[8]) { load_k(a, g, s_blk, t0, kb + qr, t1, dummy, lane, kop); };
-  auto use = [&](int kb, const bf16x8 (&kop)[8]) {
+  const uint32_t lo = (uint32_t)(lane >> 4) * 256u + (uint32_t)(((lane & 15) ^ (lane >> 4)) << 4);
+  const uint32_t rb = (uint32_t)qr * 256u + (uint32_t)(((hf * 8) ^ (qr & 15)) << 4);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto dma = [&](int kb, uint8_t *sl) { dma_block(a, g, s_blk, t0, kb, t1, sl, lo); };
+  auto use = [&](int kb, const uint8_t *sl) {
+    bf16x8 kop[8];
+    slice_k(sl, rb, kop);
     f32x16 d = {};   // A rows: keys kb .. kb+31
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], d, 0, 0, 0);
@@ -166,7 +210,8 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
       z += (double)zs;
     }
   };
-  walk_blocks(t0 + wave * 32, t1, load, use);
+  have_q(qop);
+  walk_slices(t0 + wave * 32, t1, s_sl0[wv], s_sl1[wv], dma, use);
   s_m[wave * 2 + hf][qr] = mc;
   s_z[wave * 2 + hf][qr] = z;
   __syncthreads();
@@ -235,7 +280,8 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
 
   const int tb0 = tile * a.tile_rows;   // block-aligned base of the tile's block ids
   __shared__ int s_blk[kWinMaxTileBlocks + 1];
-  __shared__ double s_out[kWinMaxTileBlocks * kBlk];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sl0[kWinWaves][kSliceBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sl1[kWinWaves][kSliceBytes];
   stage_tile_blocks(a, b, tb0, t1, s_blk);
   bf16x8 qop[8];
   load_q(a, b, g, lane, qop);
@@ -254,9 +300,24 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
   const int R = a.n_rows * a.group;
   double *dst = a.part + ((size_t)b * a.hkv + g) * a.ld64;
   __syncthreads();
-  const uint16_t *dummy = a.q;
-  auto load = [&](int kb, bf16x8 (&kop)[8]) { load_k(a, g, s_blk, tb0, kb + kl, t1, dummy, lane, kop); };
-  auto use = [&](int kb, const bf16x8 (&kop)[8]) {
+  const uint32_t lo = (uint32_t)(lane >> 4) * 256u + (uint32_t)(((lane & 15) ^ (lane >> 4)) << 4);
+  const uint32_t rb = (uint32_t)kl * 256u + (uint32_t)(((hf * 8) ^ (kl & 15)) << 4);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto dma = [&](int kb, uint8_t *sl) { dma_block(a, g, s_blk, tb0, kb, t1, sl, lo); };
+  // A block's scores leave one block later, after the next block's loads went
+  // out: the wait at a block's start then covers that store too without
+  // holding the block up.  Keys of the segment only; invalid blocks score 0.
+  int pkey = -1;       // this lane's key of the previous block (-1: none)
+  double pval = 0.0;
+  auto flush = [&] {
+    if (hf == 0 && pkey >= t0 && pkey < t1 && pkey - v.s0 < a.ld64) dst[pkey - v.s0] = pval;
+  };
+  auto use = [&](int kb, const uint8_t *sl) {
+    bf16x8 kop[8];
+    slice_k(sl, rb, kop);
+    // the previous block's store, after this block's operands are read
+    asm volatile("" ::"v"(kop[7]) : "memory");
+    flush();
     f32x16 d = {};   // B columns: keys kb .. kb+31
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[kk], kop[kk], d, 0, 0, 0);
@@ -275,14 +336,15 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
       }
     }
     acc += __shfl_xor(acc, 32);
-    // keys in an invalid block score 0; the tile's scores leave through LDS
-    if (hf == 0 && key < t1) s_out[key - tb0] = s_blk[(key - tb0) >> 4] >= 0 ? acc : 0.0;
+    const int bi = min(max((key - tb0) >> 4, 0), kWinMaxTileBlocks - 1);
+    pval = s_blk[bi] >= 0 ? acc : 0.0;
+    pkey = key;
   };
-  // blocks aligned to the tile start so that each wave's keys are contiguous
-  walk_blocks(t0 + wave * 32, t1, load, use);
-  __syncthreads();
-  for (int key = t0 + tid; key < t1; key += kWinThreads)
-    if (key - v.s0 < a.ld64) dst[key - v.s0] = s_out[key - tb0];
+  // blocks aligned to the tile's block-aligned base (each load covers whole
+  // cache blocks); keys before t0 (before the segment) are not stored
+  have_q(qop);
+  walk_slices(tb0 + wave * 32, t1, s_sl0[wv], s_sl1[wv], dma, use);
+  flush();
 }
 
 }  // namespace
