@@ -316,6 +316,32 @@ def test_decode_scores(norm, reduce, pool):
     assert worst < 2e-6
 
 
+# Long segments, eight pooled rows: the pool then takes several positions per
+# thread (65536 positions: two; 262144: eight), at the widest halo it stages
+# through LDS.  Same scores as the oracle's pool over its focal scores.
+@pytest.mark.parametrize("n,pool", [(65536, 511), (262144, 511), (262144, 7)])
+def test_decode_scores_long_pooled(n, pool):
+    kvsel = K()
+    rng = np.random.default_rng(n + pool)
+    hkv, G = 8, 2
+    hq = hkv * G
+    kv, kc, vc, table = make_kv(rng, 1, hkv, [n], [(0, n)])
+    q = torch.randn((1, 1, hq, 128), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
+    sc = torch.full((1, hkv, n), -1.0, dtype=torch.float32, device=DEV)
+    log_case("score long pooled", n, pool)
+    kvsel.score(kv, q, 1, hq, SCALE, 0, 0, True, pool, sc)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    qc = q.cpu()
+    worst = 0.0
+    for g in range(hkv):
+        Kl = O.logical_rows(kc, table[0], g, n)
+        ref = O.avg_pool(O.focal_scores(O.widen(qc[0, 0, g * G:(g + 1) * G]), Kl, 0, n, SCALE, "segment"), pool)
+        worst = max(worst, rel_err(got[0, g], ref))
+    print("max relative score error", worst)
+    assert worst < 2e-6
+
+
 def test_dense_fused_scores_match_score_call():
     kvsel = K()
     rng = np.random.default_rng(21)
