@@ -451,6 +451,54 @@ def test_window_scores(G, W, reduce, causal):
     assert worst < 2e-6
 
 
+# Window scores of segments starting at rows that are not block aligned, with
+# one block of each segment missing from the table (-1): the missing rows take
+# no part in any softmax and score 0.  Reference: the oracle's window scores
+# over the rows with that block taken out (the window queries and every later
+# key move back by 16 together, so what each query sees is unchanged), zeros
+# put back in its place, then the pool.
+@pytest.mark.parametrize("pool", [1, 7])
+def test_window_scores_holed_unaligned(pool):
+    import dataclasses
+    kvsel = K()
+    rng = np.random.default_rng(5150 + pool)
+    G, W, hkv = 2, 8, 3
+    hq = hkv * G
+    lens = [2085, 1200]
+    segs = [(37, 2085 - W), (5, 1200 - W)]
+    holes = [20, 3]                              # rows 320 .. 335 and 48 .. 63, inside the segments
+    kv, kc, vc, table = make_kv(rng, 2, hkv, lens, segs)
+    holed = table.copy()
+    for b, hb in enumerate(holes):
+        holed[b, hb] = -1
+    kvh = dataclasses.replace(kv, block_table=torch.from_numpy(holed).to(DEV))
+    q = torch.randn((2, W, hq, 128), generator=torch.Generator().manual_seed(17)).to(torch.bfloat16).to(DEV)
+    ld = 2100
+    sc = torch.full((2, hkv, ld), -1.0, dtype=torch.float32, device=DEV)
+    log_case("window holed", pool)
+    kvsel.score(kvh, q, W, hq, SCALE, 0, 1, True, pool, sc)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    qc = q.cpu()
+    worst = 0.0
+    for b in range(2):
+        s0, s1 = segs[b]
+        h0 = 16 * holes[b]
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            Kd = np.delete(O.widen(Kl), np.arange(h0, h0 + 16), axis=0)
+            qw = O.widen(qc[b, :, g * G:(g + 1) * G])
+            part = O.window_scores(qw, Kd, s0, s1 - 16, SCALE, True)
+            full = np.concatenate([part[:h0 - s0], np.zeros(16), part[h0 - s0:]])
+            ref = O.avg_pool(full, pool) if pool > 1 else full
+            if pool == 1:
+                assert np.all(got[b, g, h0 - s0:h0 - s0 + 16] == 0.0), (b, g)
+            worst = max(worst, rel_err(got[b, g, : s1 - s0], ref))
+            assert np.all(got[b, g, s1 - s0:] == -1.0)
+    print("max relative window-score error", worst)
+    assert worst < 2e-6
+
+
 def test_gather_rows_exact():
     kvsel = K()
     src = torch.randint(-(1 << 15), 1 << 15, (300, 4096), dtype=torch.int16).view(torch.bfloat16).to(DEV)
