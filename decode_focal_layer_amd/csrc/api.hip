@@ -299,8 +299,9 @@ kvsel_status kvsel_gather_attn_noalloc(const kvsel_kv_desc *kv, const uint16_t *
                 p.total, kNoAllocScratchBytes);
   char *ws = nullptr;
   if ((st = scratch_of_current_device(&ws)) != KVSEL_OK) return st;
-  // the split records are written before they are read, and the reserved
-  // head of the layout is not used: nothing has to start at zero
+  // the split records are written before they are read; the arrival
+  // counters at the head of the layout start at zero (device memory of a
+  // loaded module is zero-filled) and every call leaves them at zero
   AttnArgs a = attn_args(kv, q, num_q_heads, scale, idx, k, p, ws, out, lse, 0);
   a.dense = 0;
   return hip_status(launch_attn(a, kv->batch, G, (hipStream_t)stream), "gather_attn_noalloc launch");

@@ -12,8 +12,8 @@
 //    writes its output directly; otherwise the pair's "virtual rows" (the kept
 //    rows, then the always-attended rows before and after the candidate
 //    segment; or every row for dense attention) are split over several
-//    work-groups whose partial (max, sum, accumulator) records are merged by a
-//    second small kernel.  No work-group waits on another.
+//    work-groups whose partial (max, sum, accumulator) records are merged by
+//    the last of them to finish.  No work-group waits on another.
 //  * prologue: the work-group resolves its rows to physical cache rows
 //    (index -> block table -> block) into LDS once, so the streaming loop
 //    issues only K/V loads.
@@ -52,6 +52,11 @@
 #endif
 #ifndef KVSEL_ATTN_WAVES_PER_CU
 #define KVSEL_ATTN_WAVES_PER_CU 16
+#endif
+// split records merged by the last work-group of each pair (1) or by a
+// second kernel (0)
+#ifndef KVSEL_ATTN_FUSED_MERGE
+#define KVSEL_ATTN_FUSED_MERGE 1
 #endif
 // minimum resident waves per SIMD the compiler must allow for (0: no bound)
 #ifndef KVSEL_ATTN_WPE
@@ -135,6 +140,17 @@ constexpr float kNegBig = -1e30f;   // finite "empty" max: 2^(kNegBig - x) == 0,
 #define KVSEL_ATTN_OCC
 #endif
 
+// A split record word, stored and loaded at agent scope: the work-group that
+// merges a pair's records may run on another XCD, whose L2 is not coherent
+// with this one's for ordinary accesses; agent-scope accesses are (stores
+// write through, loads miss a line they cannot trust).
+__device__ __forceinline__ void rec_store(float *p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float rec_load(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Combine the split records of (sequence b, kv head g) into out / lse:
 // thread x < G*128 of the caller's nt threads takes head x / 128, dim x % 128.
 template <int G>
@@ -146,13 +162,13 @@ __device__ __forceinline__ void merge_records(const AttnArgs &a, int b, int g, i
     float M = kNegBig;
     // unrolled: the records' loads go out together instead of one per latency
 #pragma unroll 8
-    for (int sp = 0; sp < nact; ++sp) M = fmaxf(M, rec0[sp * kRec + kD]);
+    for (int sp = 0; sp < nact; ++sp) M = fmaxf(M, rec_load(rec0 + sp * kRec + kD));
     float L = 0.f, A = 0.f;
 #pragma unroll 8
     for (int sp = 0; sp < nact; ++sp) {
-      const float c = fast_exp2(rec0[sp * kRec + kD] - M);
-      L += rec0[sp * kRec + kD + 1] * c;
-      A += rec0[sp * kRec + dim] * c;
+      const float c = fast_exp2(rec_load(rec0 + sp * kRec + kD) - M);
+      L += rec_load(rec0 + sp * kRec + kD + 1) * c;
+      A += rec_load(rec0 + sp * kRec + dim) * c;
     }
     if (a.mass != nullptr) {
       if (dim == 0) a.mass[hb] = L > 0.f ? A / L : 0.f;
@@ -265,23 +281,45 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   // field); only used to spread the selecting waves over the SIMDs
   const uint32_t simd = MODE == 2 ? (uint32_t)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3u : 0u;
   if (MODE == 2 && lane == 0) atomicAdd(&s_simd_n[simd], 1u);
+  // Each virtual row of this split to its physical cache row, in LDS.  The
+  // table entries of up to eight of a thread's rows are read unconditionally
+  // (a clamped, valid address for a row that is not used) before any of them
+  // is, so their latencies overlap instead of adding up.
+  constexpr int RG = RPT < 8 ? RPT : 8;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int t = tid + i * NT;
-    if (i * NT < a.rps && t < cnt) {
-      const int j = start + t;   // virtual row
-      int row;
-      if (dense) row = j;
-      else if (j < a.k) row = (iv[i] >= 0 && iv[i] < v.s1 - v.s0) ? v.s0 + iv[i] : -1;
-      else if (j < a.k + v.s0) row = j - a.k;
-      else row = v.s1 + (j - a.k - v.s0);
-      uint32_t pr = kNoRow;
-      if (row >= 0) {
-        const int blk = tab_lds ? s_tab[row >> 4] : tab[row >> 4];
-        if (blk >= 0 && (int64_t)blk < a.num_blocks)
-          pr = ((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row & 15);
+  for (int i0 = 0; i0 < RPT; i0 += RG) {
+    if (i0 * NT >= a.rps) break;
+    int rowv[RG], blkv[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      const int i = i0 + u, t = tid + i * NT;
+      int row = -1;
+      if (i * NT < a.rps && t < cnt) {
+        const int j = start + t;   // virtual row
+        if (dense) row = j;
+        else if (j < a.k) row = (iv[i] >= 0 && iv[i] < v.s1 - v.s0) ? v.s0 + iv[i] : -1;
+        else if (j < a.k + v.s0) row = j - a.k;
+        else row = v.s1 + (j - a.k - v.s0);
       }
-      s_prow[t] = pr;
+      rowv[u] = row;
+    }
+    if (tab_lds) {
+#pragma unroll
+      for (int u = 0; u < RG; ++u) blkv[u] = s_tab[max(rowv[u], 0) >> 4];
+    } else {
+#pragma unroll
+      for (int u = 0; u < RG; ++u) blkv[u] = tab[max(rowv[u], 0) >> 4];
+    }
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      const int i = i0 + u, t = tid + i * NT;
+      if (i * NT < a.rps && t < cnt) {
+        const int row = rowv[u], blk = blkv[u];
+        uint32_t pr = kNoRow;
+        if (row >= 0 && blk >= 0 && (int64_t)blk < a.num_blocks)
+          pr = ((uint32_t)blk * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row & 15);
+        s_prow[t] = pr;
+      }
     }
   }
 
@@ -553,13 +591,35 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       if (dim == 0 && a.lse != nullptr) a.lse[hb] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
     } else {
       float *rec = a.rec + (hb * a.nsplit + split) * kRec;
-      rec[dim] = A;
+      rec_store(rec + dim, A);
       if (dim == 0) {
-        rec[kD] = M;
-        rec[kD + 1] = L;
+        rec_store(rec + kD, M);
+        rec_store(rec + kD + 1, L);
       }
     }
   }
+#if KVSEL_ATTN_FUSED_MERGE
+  // Split records: the last of the pair's work-groups to finish merges them.
+  // Each thread waits until its record stores are complete (written through
+  // to the agent-coherent level), then one thread counts the work-group in;
+  // the one that brings the count to nsplit resets it to zero for the next
+  // call and reads every record with agent-scope loads.  No work-group waits
+  // for another, and no cache is written back or invalidated.
+  if (a.nsplit > 1) {
+    __shared__ uint32_t s_last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t *ctr = a.counters + (size_t)b * a.hkv + g;
+      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t last = prev == (uint32_t)a.nsplit - 1u ? 1u : 0u;
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) merge_records<G>(a, b, g, v.nR <= 0 ? 0 : min(a.nsplit, (v.nR + a.rps - 1) / a.rps), tid, NT);
+  }
+#endif
 }
 
 // merge of the split records: grid (kv heads, sequences), G*128 threads
@@ -687,7 +747,7 @@ hipError_t launch_attn_g(const AttnArgs &a, int batch, hipStream_t s) {
       hipLaunchKernelGGL((attn_kernel<G, NT, U, 0, false>), grid, dim3(NT), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (e != hipSuccess || a.nsplit == 1 || KVSEL_ATTN_FUSED_MERGE) return e;
   hipLaunchKernelGGL(attn_merge_kernel<G>, dim3(a.hkv, batch), dim3(G * kD), 0, s, a);
   return hipGetLastError();
 }

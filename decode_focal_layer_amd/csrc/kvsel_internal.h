@@ -10,9 +10,10 @@
 namespace kvsel {
 
 constexpr size_t kAlign = 256;
-// Every workspace starts with this many bytes of split counters, used only by
-// the attention kernels and always left at zero: (sequence, kv head) pairs
-// per call are limited to kCounterBytes / 4.
+// Every workspace starts with this many bytes of split counters, one per
+// (sequence, kv head) pair, used by the attention kernels to find the last
+// work-group of a pair and always left at zero when they finish: pairs per
+// call are limited to kCounterBytes / 4.
 constexpr size_t kCounterBytes = 65536;
 constexpr int kMaxPairs = (int)(kCounterBytes / 4);
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -48,7 +49,7 @@ struct AttnArgs {
   int32_t dense;        // 1: every row [0, seq_len); 0: gather
   float scale_log2;     // softmax scale * log2(e)
   int32_t rps, nsplit;
-  uint32_t *counters;   // reserved region at the start of the workspace (unused)
+  uint32_t *counters;   // per-pair arrival counters at the start of the workspace (zero between calls)
   float *rec;           // [batch][hq][nsplit][kRec]
   float *out, *lse;
   float *mass;          // non-null: the segment's attention share per head instead of out

@@ -237,7 +237,9 @@ KVSEL_API kvsel_status kvsel_gather_attn(const kvsel_kv_desc *kv, const uint16_t
  * kvsel_gather_attn).  Every call on one GPU shares its array: calls that may
  * run at the same time on one GPU (other streams, other threads) race on it
  * and must not overlap.  The array needs no clearing: every record a call
- * reads it has written itself.  Makes no allocation of any kind.
+ * reads it has written itself, and its per-pair arrival counters start at
+ * zero (the array is zero when the library loads) and are left at zero by
+ * every call.  Makes no allocation of any kind.
  */
 KVSEL_API kvsel_status kvsel_gather_attn_noalloc(const kvsel_kv_desc *kv, const uint16_t *q, int32_t num_q_heads,
                                                  float scale, const int32_t *idx, int32_t k, float *out, float *lse,
