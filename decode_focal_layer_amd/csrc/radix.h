@@ -217,6 +217,95 @@ __device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &
   grp.sync();
 }
 
+struct RadixT {
+  uint32_t T, keq;
+};
+
+// After a histogram pass over nb bins (bin nb - 1 the highest): the bin
+// holding the krem-th largest of the counted keys.  Participant t owns bins
+// [t*per, (t+1)*per); the one whose bins hold that key writes sh.misc[0] =
+// the bin, misc[1] = the keys in the bins above it, misc[2] = the keys in it,
+// which the participants read after their next sync.
+template <int NTS, typename Grp>
+__device__ __forceinline__ void pick_bin(Grp &grp, RadixShared<NTS> &sh, int nb, uint32_t krem) {
+  const int t = grp.t();
+  const int per = (nb + NTS - 1) / NTS;
+  uint32_t c = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bi = t * per + i;
+    c += bi < nb ? sh.hist[bi] : 0u;
+  }
+  uint32_t total;
+  const uint32_t below = excl_scan<NTS>(grp, c, sh.w1, total);
+  const uint32_t above = total - below - c;   // candidates in bins above this participant's
+  if (above < krem && krem <= above + c) {
+    uint32_t run = above;
+    for (int i = per - 1; i >= 0; --i) {
+      const int bi = t * per + i;
+      const uint32_t hcount = bi < nb ? sh.hist[bi] : 0u;
+      if (run + hcount >= krem) {
+        sh.misc[0] = (uint32_t)bi;
+        sh.misc[1] = run;
+        sh.misc[2] = hcount;
+        break;
+      }
+      run += hcount;
+    }
+  }
+}
+
+// An empty candidate list: its count is zero, and slots past the collected
+// ones rank below every candidate (key 0, last index).  The caller syncs
+// before collecting.
+template <int NTS, typename Grp>
+__device__ __forceinline__ void list_reset(Grp &grp, RadixShared<NTS> &sh) {
+  const int t = grp.t();
+  if (t == 0) sh.misc[3] = 0;
+  for (int i = t; i < kListCap; i += NTS) {
+    sh.list_key[i] = 0u;
+    sh.list_idx[i] = 0x7fffffff;
+  }
+}
+
+// The krem-th of the nl collected candidates in (key descending, index
+// ascending) order: its key T, and keq = krem minus the candidates with a
+// larger key (how many keys equal to T are taken).  The rank of item j is the
+// number of items with a larger key, or an equal key and a lower index.  Four
+// adjacent participants take item j, each a quarter of the list (four items
+// per LDS access, several in flight), and add their counts with two lane
+// exchanges.  Ends with sh free again.
+template <int NTS, typename Grp>
+__device__ __forceinline__ RadixT rank_list(Grp &grp, RadixShared<NTS> &sh, int nl, uint32_t krem) {
+  const int t = grp.t();
+  const int nl4 = (nl + 3) & ~3;   // whole groups of four (the padding ranks below everything)
+  for (int jj = t; jj < 4 * nl; jj += NTS) {
+    const int j = jj >> 2, q = jj & 3;
+    const uint32_t xj = sh.list_key[j];
+    const int ij = sh.list_idx[j];
+    uint32_t r = 0, gt = 0;
+#pragma unroll 2
+    for (int i = 4 * q; i < nl4; i += 16) {
+      const uint4 xi = *reinterpret_cast<const uint4 *>(&sh.list_key[i]);
+      const int4 ii = *reinterpret_cast<const int4 *>(&sh.list_idx[i]);
+      gt += (xi.x > xj ? 1u : 0u) + (xi.y > xj ? 1u : 0u) + (xi.z > xj ? 1u : 0u) + (xi.w > xj ? 1u : 0u);
+      r += ((xi.x > xj || (xi.x == xj && ii.x < ij)) ? 1u : 0u) + ((xi.y > xj || (xi.y == xj && ii.y < ij)) ? 1u : 0u) +
+           ((xi.z > xj || (xi.z == xj && ii.z < ij)) ? 1u : 0u) + ((xi.w > xj || (xi.w == xj && ii.w < ij)) ? 1u : 0u);
+    }
+    r += (uint32_t)__shfl_xor((int)r, 1);
+    r += (uint32_t)__shfl_xor((int)r, 2);
+    gt += (uint32_t)__shfl_xor((int)gt, 1);
+    gt += (uint32_t)__shfl_xor((int)gt, 2);
+    if (q == 0 && r == krem - 1u) {
+      sh.misc[4] = xj;
+      sh.misc[5] = krem - gt;
+    }
+  }
+  grp.sync();
+  const RadixT res{sh.misc[4], sh.misc[5]};
+  grp.sync();   // sh is free again
+  return res;
+}
+
 // The k-th largest key T among the candidates (keys >= theta) of key(i), i in
 // [0, n), and keq, how many keys equal to T the top k hold (>= 1); n > k >= 1.
 // lo <= every candidate key <= hi, and nin >= the number of candidates (at
@@ -225,9 +314,6 @@ __device__ void key_range(Grp &grp, KeyFn key, int n, uint32_t theta, uint32_t &
 // bin holding T has at most this many candidates, which are then collected
 // and ranked (0: digit passes until T is known, for keys whose passes are
 // cheap).  Ends with sh free again.
-struct RadixT {
-  uint32_t T, keq;
-};
 template <int NTS, bool LDS_KEYS = true, int LIST = kListCap, typename Grp, typename KeyFn>
 __device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, uint32_t lo, uint32_t hi, uint32_t nin,
                              RadixShared<NTS> &sh) {
@@ -259,30 +345,7 @@ __device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
       atomicAdd(in ? &sh.hist[d >> shift] : &sh.sink[lane], 1u);
     });
     grp.sync();
-    // participant t owns bins [t*per, (t+1)*per) (empty past nb)
-    const int per = (nb + NTS - 1) / NTS;
-    uint32_t c = 0;
-    for (int i = 0; i < per; ++i) {
-      const int bi = t * per + i;
-      c += bi < nb ? sh.hist[bi] : 0u;
-    }
-    uint32_t total;
-    const uint32_t below = excl_scan<NTS>(grp, c, sh.w1, total);
-    const uint32_t above = total - below - c;   // candidates in bins above this participant's
-    if (above < krem && krem <= above + c) {
-      uint32_t run = above;
-      for (int i = per - 1; i >= 0; --i) {
-        const int bi = t * per + i;
-        const uint32_t hcount = bi < nb ? sh.hist[bi] : 0u;
-        if (run + hcount >= krem) {
-          sh.misc[0] = (uint32_t)bi;
-          sh.misc[1] = run;
-          sh.misc[2] = hcount;
-          break;
-        }
-        run += hcount;
-      }
-    }
+    pick_bin<NTS>(grp, sh, nb, krem);
     grp.sync();
     prefix |= sh.misc[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
@@ -298,12 +361,7 @@ __device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
     keq = krem;
   } else {
     // ---- at most kListCap candidates left in the bin: collect and rank them ----
-    if (t == 0) sh.misc[3] = 0;
-    // slots past the collected ones rank below every candidate (key 0, last index)
-    for (int i = t; i < kListCap; i += NTS) {
-      sh.list_key[i] = 0u;
-      sh.list_idx[i] = 0x7fffffff;
-    }
+    list_reset<NTS>(grp, sh);
     grp.sync();
     {
       // wave w walks its contiguous range 64 keys at a time, B chunks per
@@ -338,38 +396,9 @@ __device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
       }
     }
     grp.sync();
-    const int nl = min((int)sh.misc[3], kListCap);
-    const int nl4 = (nl + 3) & ~3;   // whole groups of four (the padding ranks below everything)
-    // rank of item j: items with a larger key, or an equal key and a lower
-    // index.  Four adjacent participants take item j, each a quarter of the
-    // list (four items per LDS access, several in flight), and add their
-    // counts with two lane exchanges.
-    for (int jj = t; jj < 4 * nl; jj += NTS) {
-      const int j = jj >> 2, q = jj & 3;
-      const uint32_t xj = sh.list_key[j];
-      const int ij = sh.list_idx[j];
-      uint32_t r = 0, gt = 0;
-#pragma unroll 2
-      for (int i = 4 * q; i < nl4; i += 16) {
-        const uint4 xi = *reinterpret_cast<const uint4 *>(&sh.list_key[i]);
-        const int4 ii = *reinterpret_cast<const int4 *>(&sh.list_idx[i]);
-        gt += (xi.x > xj ? 1u : 0u) + (xi.y > xj ? 1u : 0u) + (xi.z > xj ? 1u : 0u) + (xi.w > xj ? 1u : 0u);
-        r += ((xi.x > xj || (xi.x == xj && ii.x < ij)) ? 1u : 0u) + ((xi.y > xj || (xi.y == xj && ii.y < ij)) ? 1u : 0u) +
-             ((xi.z > xj || (xi.z == xj && ii.z < ij)) ? 1u : 0u) + ((xi.w > xj || (xi.w == xj && ii.w < ij)) ? 1u : 0u);
-      }
-      r += (uint32_t)__shfl_xor((int)r, 1);
-      r += (uint32_t)__shfl_xor((int)r, 2);
-      gt += (uint32_t)__shfl_xor((int)gt, 1);
-      gt += (uint32_t)__shfl_xor((int)gt, 2);
-      if (q == 0 && r == krem - 1u) {
-        sh.misc[4] = xj;
-        sh.misc[5] = krem - gt;
-      }
-    }
-    grp.sync();
-    T = sh.misc[4];
-    keq = sh.misc[5];
-    grp.sync();   // sh is free again
+    const RadixT r = rank_list<NTS>(grp, sh, min((int)sh.misc[3], kListCap), krem);
+    T = r.T;
+    keq = r.keq;
   }
   return RadixT{T, keq};
 }

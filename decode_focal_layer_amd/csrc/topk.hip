@@ -92,6 +92,161 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                                   IN_LDS ? s_keys : nullptr);
 }
 
+// Cold rows of n <= NT * C keys (no warm start): the keys stay in registers
+// from the load to the output, so no pass reads or writes them in LDS.
+// Thread t holds keys t + j*NT (j < C): for each j the 64 lanes of a wave
+// hold 64 consecutive indices, which is what the ballot-based collection and
+// the ordered output need.  The selection is that of radix_find: digit
+// passes (11 bits, from the top of the row's key range) until the bin
+// holding the k-th largest key has at most kListCap keys, which are then
+// collected and ranked.  The output counts each 64-key chunk's keys above T
+// and equal to T, scans the counts in index order, and each wave writes its
+// chosen indices: ascending, and the equal keys taken are the lowest-indexed.
+template <int NT, int C>
+__global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs a) {
+  constexpr int NW = NT / 64;
+  static_assert(C * NW <= NT, "one chunk count per participant in the output scan");
+  __shared__ RadixShared<NT> sh;
+  __shared__ uint32_t s_cg[C * NW], s_ce[C * NW];
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float *src = a.scores + (size_t)row * a.ld;
+  const int n = a.n_row != nullptr ? clampi(a.n_row[row], 0, a.n) : a.n;
+  int32_t *dst = a.idx + (size_t)row * a.k;
+  BlockSync<NT> grp;
+  if (n <= a.k) {   // every candidate kept
+    for (int i = t; i < a.k; i += NT) dst[i] = i < n ? i : -1;
+    return;
+  }
+  uint32_t x[C];
+  {
+    float v[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) v[j] = src[min(t + j * NT, n - 1)];   // unbranched reads, all in flight
+#pragma unroll
+    for (int j = 0; j < C; ++j) x[j] = okey(v[j]);
+  }
+  auto valid = [&](int j) { return t + j * NT < n; };
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    lo = valid(j) ? min(lo, x[j]) : lo;
+    hi = valid(j) ? max(hi, x[j]) : hi;
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.w1[w] = lo;
+    sh.w2[w] = hi;
+  }
+  grp.sync();
+  lo = 0xffffffffu;
+  hi = 0u;
+  for (int i = 0; i < NW; ++i) {
+    lo = min(lo, sh.w1[i]);
+    hi = max(hi, sh.w2[i]);
+  }
+  grp.sync();
+
+  // ---- the k-th largest key T, and keq: how many keys equal to T are taken ----
+  const uint32_t range = hi - lo;
+  int top = range == 0u ? 0 : 32 - __clz(range);
+  uint32_t prefix = 0, pmask = 0;   // digits of (key - lo) fixed so far
+  uint32_t krem = (uint32_t)a.k;    // keys still to take inside the prefix's bin
+  uint32_t nin = (uint32_t)n;       // keys in the prefix's bin
+  while (top > 0 && nin > (uint32_t)kListCap) {
+    const int bits = top < 11 ? top : 11;
+    const int shift = top - bits;
+    const int nb = 1 << bits;
+    for (int i = t; i < nb; i += NT) sh.hist[i] = 0;
+    grp.sync();
+    // keys of the bin: x - base below 2^span; the others add to this lane's
+    // sink word (no branch around the add)
+    const uint32_t base = lo + prefix;
+    const int span = shift + bits;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const uint32_t d = x[j] - base;
+      const bool in = valid(j) && (span >= 32 || (d >> span) == 0u);
+      atomicAdd(in ? &sh.hist[d >> shift] : &sh.sink[lane], 1u);
+    }
+    grp.sync();
+    pick_bin<NT>(grp, sh, nb, krem);
+    grp.sync();
+    prefix |= sh.misc[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    krem -= sh.misc[1];
+    nin = sh.misc[2];
+    top -= bits;
+    grp.sync();
+  }
+  const uint64_t below = (1ull << lane) - 1ull;   // lanes below this one
+  uint32_t T, keq;
+  if (top == 0) {
+    T = lo + prefix;   // every digit fixed: the bin is one key value
+    keq = krem;
+  } else {
+    // collect the bin's keys (at most kListCap): each wave counts its matches
+    // from ballots, takes their slots with one add, then writes them
+    list_reset<NT>(grp, sh);
+    grp.sync();
+    auto in_bin = [&](int j) { return valid(j) && ((x[j] - lo) & pmask) == prefix; };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) cnt += (uint32_t)__popcll(__ballot(in_bin(j)));
+    if (cnt != 0u) {
+      uint32_t slot0 = 0;
+      if (lane == 0) slot0 = atomicAdd(&sh.misc[3], cnt);
+      slot0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot0);
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const bool m = in_bin(j);
+        const uint64_t mask = __ballot(m);
+        const uint32_t slot = slot0 + (uint32_t)__popcll(mask & below);
+        if (m && slot < (uint32_t)kListCap) {
+          sh.list_key[slot] = x[j];
+          sh.list_idx[slot] = t + j * NT;
+        }
+        slot0 += (uint32_t)__popcll(mask);
+      }
+    }
+    grp.sync();
+    const RadixT r = rank_list<NT>(grp, sh, min((int)sh.misc[3], kListCap), krem);
+    T = r.T;
+    keq = r.keq;
+  }
+
+  // ---- ordered output: chunk q = j*NW + w holds indices j*NT + 64w + [0, 64) ----
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const uint32_t g = (uint32_t)__popcll(__ballot(valid(j) && x[j] > T));
+    const uint32_t e = (uint32_t)__popcll(__ballot(valid(j) && x[j] == T));
+    if (lane == 0) {
+      s_cg[j * NW + w] = g;
+      s_ce[j * NW + w] = e;
+    }
+  }
+  grp.sync();
+  {
+    const uint32_t g = t < C * NW ? s_cg[t] : 0u, e = t < C * NW ? s_ce[t] : 0u;
+    uint32_t gb, eb;
+    excl_scan2<NT>(grp, g, e, sh.w1, sh.w2, gb, eb);
+    if (t < C * NW) {
+      s_cg[t] = gb;
+      s_ce[t] = eb;
+    }
+  }
+  grp.sync();
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const uint32_t gb = s_cg[j * NW + w], eb = s_ce[j * NW + w];   // before this chunk
+    const bool eq = valid(j) && x[j] == T;
+    const uint64_t em = __ballot(eq);
+    const bool take = valid(j) && (x[j] > T || (eq && eb + (uint32_t)__popcll(em & below) < keq));
+    const uint64_t tm = __ballot(take);
+    if (take) dst[gb + (eb < keq ? eb : keq) + (uint32_t)__popcll(tm & below)] = t + j * NT;
+  }
+}
+
 constexpr int kCoarseBins = 2048;   // key >> 21
 constexpr int kCoarseShift = 21;
 constexpr int kSliceThreads = 256;
@@ -215,6 +370,18 @@ hipError_t launch_topk(const TopkArgs &a, void *ws, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((topk_select_kernel<1024>), dim3(a.rows), dim3(1024), 0, s, a, (const uint32_t *)counts,
                        nslices);
+    return hipGetLastError();
+  }
+  if (a.warm == nullptr && a.n <= 32 * 1024) {   // cold rows: keys held in registers
+    const dim3 g(a.rows), blk(1024);
+    if (a.n <= 4 * 1024)
+      hipLaunchKernelGGL((topk_regs_kernel<1024, 4>), g, blk, 0, s, a);
+    else if (a.n <= 8 * 1024)
+      hipLaunchKernelGGL((topk_regs_kernel<1024, 8>), g, blk, 0, s, a);
+    else if (a.n <= 16 * 1024)
+      hipLaunchKernelGGL((topk_regs_kernel<1024, 16>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((topk_regs_kernel<1024, 32>), g, blk, 0, s, a);
     return hipGetLastError();
   }
   if (a.n <= kLdsKeys) {

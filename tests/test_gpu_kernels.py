@@ -237,7 +237,11 @@ def test_topk_rows_of_their_own_length(n, k):
                                       # highest occupied coarse bin
                                       (50000, 1000, "wide"), (50000, 300, "signed"), (16384, 3, "spike"),
                                       # the coarse bin of the k-th score taken whole
-                                      (16384, 5, "spike")])
+                                      (16384, 5, "spike"),
+                                      # the edges of the register-held row sizes (4, 8, 16, 32 keys per
+                                      # thread) and the first row past them
+                                      (4096, 100, "wide"), (4097, 4000, "ties"), (32768, 4000, "signed"),
+                                      (32769, 100, "wide")])
 def test_topk_exact(n, k, mode):
     kvsel = K()
     rng = np.random.default_rng(n + k)
