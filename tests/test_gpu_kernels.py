@@ -166,6 +166,58 @@ def test_pick_layers_exact_sums():
         assert np.array_equal(out.cpu().numpy(), want), (n_pick, out.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("G", [2, 4])
+def test_split_merge_repeated_launches(G):
+    """Pairs whose rows are split over many work-groups (18 here) are merged
+    by the last of their work-groups to finish.  Launches back to back on one
+    stream with the deterministic row order sum the same terms in the same
+    order, so every launch's output is bitwise equal to the first -- a merge
+    that read a record before it was complete, or a counter left non-zero by
+    an earlier launch, would break that -- and matches the oracle; the
+    workspace's arrival counters are zero afterwards."""
+    kvsel = K()
+    rng = np.random.default_rng(900 + G)
+    hkv, batch = 2, 2
+    hq = hkv * G
+    lens = [6000, 3333]
+    segs = [(100, 5900), (0, 3000)]
+    kv0, kc, vc, table = make_kv(rng, batch, hkv, lens, segs)
+    kv = kvsel.KV(kv0.k_pool, kv0.v_pool, kv0.block_table, kv0.seq_len, kv0.seg_begin, kv0.seg_end,
+                  kv0.max_seq_len, kv0.max_seg_len, kv0.min_seg_len, 0, True)
+    q = torch.randn((batch, hq, 128), generator=torch.Generator().manual_seed(31)).to(torch.bfloat16).to(DEV)
+    k = 1500
+    idx_np = np.stack([np.stack([np.sort(rng.choice(s1 - s0, size=k, replace=False)) for _ in range(hkv)])
+                       for s0, s1 in segs]).astype(np.int32)
+    idx = torch.from_numpy(idx_np).to(DEV)
+    ws = kvsel.Workspace(DEV)
+    log_case("split-merge", G)
+    gathered = [torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV) for _ in range(16)]
+    dense = [torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV) for _ in range(8)]
+    for i, o in enumerate(gathered):
+        kvsel.gather_attn(kv, q, hq, SCALE, idx, k, o, ws=ws)
+        if i % 2 == 0:
+            kvsel.dense_attn(kv, q, hq, SCALE, dense[i // 2], ws=ws)
+    torch.cuda.synchronize()
+    for o in gathered[1:]:
+        assert torch.equal(o, gathered[0])
+    for o in dense[1:]:
+        assert torch.equal(o, dense[0])
+    qc = q.cpu()
+    for b in range(batch):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[b], g, lens[b])
+            Vl = O.logical_rows(vc, table[b], g, lens[b])
+            qg = O.widen(qc[b, g * G:(g + 1) * G])
+            ref_d, _ = O.dense_attention(qg, Kl, Vl, SCALE)
+            assert_attn(dense[0][b, g * G:(g + 1) * G].cpu().numpy(), ref_d, f"dense b{b} g{g}")
+            rows = O.kept_rows(idx_np[b, g], segs[b][0], segs[b][1], lens[b])
+            ref_s, _ = O.attention(qg, Kl, Vl, rows, SCALE)
+            assert_attn(gathered[0][b, g * G:(g + 1) * G].cpu().numpy(), ref_s, f"gather b{b} g{g}")
+    addr = ws.buf.data_ptr()
+    pad = (-addr) % 256
+    assert int(ws.buf[pad:pad + 65536].count_nonzero().item()) == 0
+
+
 def test_gather_full_budget_equals_dense_and_empty_rows():
     kvsel = K()
     rng = np.random.default_rng(11)
