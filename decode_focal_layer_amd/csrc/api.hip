@@ -192,9 +192,50 @@ ScorePlan score_plan(const kvsel_kv_desc *kv, int32_t n_rows, int32_t hq, int32_
 
 }  // namespace
 
+// the debug words of every source file (debug builds register one reader per file)
+namespace {
+constexpr int kMaxDbgFiles = 64;
+kvsel::DbgTakeFn g_dbg_fns[kMaxDbgFiles];   // zero before any dynamic initialisation runs
+int g_dbg_n = 0;
+}  // namespace
+
+bool kvsel::dbg_register(DbgTakeFn f) {
+  if (g_dbg_n >= kMaxDbgFiles) return false;
+  g_dbg_fns[g_dbg_n++] = f;
+  return true;
+}
+
 extern "C" {
 
 int32_t kvsel_version(void) { return KVSEL_VERSION; }
+
+kvsel_status kvsel_debug_status(uint32_t *violations, uint32_t *first_code, uint32_t *first_detail) {
+  uint32_t total = 0, code = 0, detail = 0;
+  if (violations != nullptr) *violations = 0;
+  if (first_code != nullptr) *first_code = 0;
+  if (first_detail != nullptr) *first_detail = 0;
+#if KVSEL_DEBUG
+  for (int i = 0; i < g_dbg_n; ++i) {
+    uint32_t w[3];
+    if (!g_dbg_fns[i](w)) return fail(KVSEL_EHIP, "reading the debug words failed");
+    if (w[0] != 0u && total == 0u) {
+      code = w[1];
+      detail = w[2];
+    }
+    total += w[0];
+  }
+  if (violations != nullptr) *violations = total;
+  if (first_code != nullptr) *first_code = code;
+  if (first_detail != nullptr) *first_detail = detail;
+  if (total != 0u) return fail(KVSEL_EDEBUG, "%u device check(s) failed; first: code %u, detail %u", total, code, detail);
+  return ok();
+#else
+  (void)total;
+  (void)code;
+  (void)detail;
+  return fail(KVSEL_EUNSUPPORTED, "not a debug build (compile with KVSEL_DEBUG=1)");
+#endif
+}
 
 const char *kvsel_status_string(kvsel_status s) {
   switch (s) {
@@ -203,6 +244,7 @@ const char *kvsel_status_string(kvsel_status s) {
     case KVSEL_ENOSPC: return "workspace too small";
     case KVSEL_EUNSUPPORTED: return "unsupported shape";
     case KVSEL_EHIP: return "HIP error";
+    case KVSEL_EDEBUG: return "device check failed";
     default: return "unknown status";
   }
 }

@@ -155,6 +155,7 @@ __device__ __forceinline__ float rec_load(const float *p) {
 // thread x < G*128 of the caller's nt threads takes head x / 128, dim x % 128.
 template <int G>
 __device__ __forceinline__ void merge_records(const AttnArgs &a, int b, int g, int nact, int tid, int nt) {
+  if (tid == 0) KVSEL_CHECK(nact >= 0 && nact <= a.nsplit, kDbgCount, nact);
   for (int x = tid; x < G * kD; x += nt) {
     const int h = x / kD, dim = x % kD;
     const size_t hb = (size_t)b * a.hq + g * G + h;
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
   }
   const SeqView v = seq_view_of(a, n_raw, s0_raw, s1_raw, dense);
   const int cnt = max(0, min(a.rps, v.nR - start));   // rows of this split
+  if (tid == 0) KVSEL_CHECK(cnt <= kAttnMaxRps, kDbgLds, cnt);
   // chunks starting at or past this split-local row hold only rows read once
   // (all of them when STREAM)
   const int own_from = STREAM ? 0 : own_rows_from(a, v, dense) - start;
@@ -353,6 +355,7 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
       const uint32_t pr_t = s_prow[max(min(t, cnt - 1), 0)];
       const uint32_t pr = t < cnt ? pr_t : kNoRow;
       ok[u] = pr != kNoRow;
+      KVSEL_CHECK(!ok[u] || (uint64_t)pr < (uint64_t)a.num_blocks * (uint64_t)a.hkv * kBlk, kDbgKvRow, pr);
       // a row that is not attended reads this lane's query (a valid, finite
       // 16 bytes) and gets probability 0
       const uint16_t *kp = ok[u] ? kbase + (size_t)pr * kD : qbase;
@@ -397,8 +400,10 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int h = 1; h < G; ++h) dv = sub == h ? dot[u][h] : dv;
           if (!ok[u]) dv = -INFINITY;
-          if (MODE == 2)
+          if (MODE == 2) {
+            KVSEL_CHECK(row - lo < a.seg_cap, kDbgLds, row - lo);
             s_logit[sub * a.seg_cap + (row - lo)] = dv;
+          }
           else if (row - lo < a.ld_logits)
             a.logits[((size_t)b * a.hq + g * G + sub) * a.ld_logits + (row - lo)] = dv;
         }
@@ -612,6 +617,8 @@ __global__ __launch_bounds__(NT) KVSEL_ATTN_OCC void attn_kernel(AttnArgs a) {
     if (tid == 0) {
       uint32_t *ctr = a.counters + (size_t)b * a.hkv + g;
       const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the pair's counter started this call at zero: below nsplit at every arrival
+      KVSEL_CHECK(prev < (uint32_t)a.nsplit, kDbgCounter, prev);
       const uint32_t last = prev == (uint32_t)a.nsplit - 1u ? 1u : 0u;
       if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "debug.h"
+
 namespace kvsel {
 
 constexpr int kD = 128;        // head_dim

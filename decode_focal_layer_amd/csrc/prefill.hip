@@ -419,6 +419,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const StageOff full = stage_off(0, kBN, tid, row_bytes);   // a tile wholly inside the sequence
   auto fetch_tile = [&](int t0) {
     const size_t o = (size_t)t0 * row_bytes;
+    KVSEL_CHECK(t0 >= 0 && t0 < n, kDbgKvRow, t0);   // a tile starts inside the sequence
     return fetch(kseq + o, vseq + o, t0 + kBN <= n ? full : stage_off(t0, n, tid, row_bytes));
   };
 

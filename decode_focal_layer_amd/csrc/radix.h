@@ -396,6 +396,8 @@ __device__ RadixT radix_find(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
       }
     }
     grp.sync();
+    // the digit passes stopped at a bin of at most LIST keys: all of them collected
+    if (grp.t() == 0) KVSEL_CHECK(sh.misc[3] <= (uint32_t)kListCap, kDbgCount, sh.misc[3]);
     const RadixT r = rank_list<NTS>(grp, sh, min((int)sh.misc[3], kListCap), krem);
     T = r.T;
     keq = r.keq;
@@ -453,7 +455,10 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
             take = eq_seen < keq;
             ++eq_seen;
           }
-          if (take) stage[pos++] = (uint32_t)(i0 + j);
+          if (take) {
+            KVSEL_CHECK(pos < (uint32_t)k, kDbgOutSlot, pos);
+            stage[pos++] = (uint32_t)(i0 + j);
+          }
         }
       }
       grp.sync();
@@ -490,6 +495,7 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
               ++eq_seen;
             }
             if (take) {
+              KVSEL_CHECK(pos < (uint32_t)k, kDbgOutSlot, pos);
               if (pos < (uint32_t)k) dst[pos] = b0 + j;
               ++pos;
             }
@@ -529,6 +535,7 @@ __device__ void radix_select(Grp &grp, KeyFn key, int n, int k, uint32_t theta, 
       const uint64_t mt = __ballot(take);
       if (take) {
         const uint32_t p = pos + (uint32_t)__popcll(mt & lt);
+        KVSEL_CHECK(p < (uint32_t)k, kDbgOutSlot, p);
         if (p < (uint32_t)k) dst[p] = i;
       }
       pos += (uint32_t)__popcll(mt);

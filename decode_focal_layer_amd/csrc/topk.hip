@@ -210,6 +210,7 @@ __global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs a) {
       }
     }
     grp.sync();
+    if (t == 0) KVSEL_CHECK(sh.misc[3] <= (uint32_t)kListCap, kDbgCount, sh.misc[3]);
     const RadixT r = rank_list<NT>(grp, sh, min((int)sh.misc[3], kListCap), krem);
     T = r.T;
     keq = r.keq;
@@ -243,7 +244,9 @@ __global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs a) {
     const uint64_t em = __ballot(eq);
     const bool take = valid(j) && (x[j] > T || (eq && eb + (uint32_t)__popcll(em & below) < keq));
     const uint64_t tm = __ballot(take);
-    if (take) dst[gb + (eb < keq ? eb : keq) + (uint32_t)__popcll(tm & below)] = t + j * NT;
+    const uint32_t slot = gb + (eb < keq ? eb : keq) + (uint32_t)__popcll(tm & below);
+    KVSEL_CHECK(!take || slot < (uint32_t)a.k, kDbgOutSlot, slot);
+    if (take) dst[slot] = t + j * NT;
   }
 }
 

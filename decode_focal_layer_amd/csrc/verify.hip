@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         uint32_t pr = kNoRow;
         if (blk[u] >= 0 && (int64_t)blk[u] < a.num_blocks)
           pr = ((uint32_t)blk[u] * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row[u] & 15);
+        KVSEL_CHECK(j < a.rows_cap, kDbgLds, j);
         s_prow[j] = pr;
       }
     }
@@ -399,6 +400,7 @@ __global__ __launch_bounds__(kW16Threads) __attribute__((amdgpu_waves_per_eu(4, 
         uint32_t pr = kNoRow;
         if (blk[u] >= 0 && (int64_t)blk[u] < a.num_blocks)
           pr = ((uint32_t)blk[u] * (uint32_t)a.hkv + (uint32_t)g) * (uint32_t)kBlk + (uint32_t)(row[u] & 15);
+        KVSEL_CHECK(j < a.rows_cap, kDbgLds, j);
         s_prow[j] = pr;
       }
     }

@@ -111,6 +111,7 @@ __device__ __forceinline__ void dma_block(const WinArgs &a, int g, const int *s_
     const int bi = min(max((key0 - kb0) >> 4, 0), kWinMaxTileBlocks - 1);
     const int sb = s_blk[bi];   // read unbranched (a read under a branch is waited for at once)
     const int blk = __builtin_amdgcn_readfirstlane(key0 < t1 ? sb : -1);
+    KVSEL_CHECK((int64_t)blk < a.num_blocks, kDbgKvRow, blk);
     const uint8_t *run = reinterpret_cast<const uint8_t *>(a.k_pool) +
                          ((size_t)((uint32_t)max(blk, 0) * (uint32_t)a.hkv + (uint32_t)g) << 12);
 #pragma unroll

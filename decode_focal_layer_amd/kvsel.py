@@ -25,11 +25,12 @@ LIB_PATH = os.environ.get("KVSEL_LIBRARY") or os.path.join(_HERE, "libkvsel.so")
 REDUCE_GROUP, REDUCE_ALL = 0, 1
 NORM_SEGMENT, NORM_CONTEXT = 0, 1
 FLAG_DETERMINISTIC = 1
-STATUS = {0: "KVSEL_OK", -1: "KVSEL_EINVAL", -2: "KVSEL_ENOSPC", -3: "KVSEL_EUNSUPPORTED", -4: "KVSEL_EHIP"}
+STATUS = {0: "KVSEL_OK", -1: "KVSEL_EINVAL", -2: "KVSEL_ENOSPC", -3: "KVSEL_EUNSUPPORTED", -4: "KVSEL_EHIP",
+          -5: "KVSEL_EDEBUG"}
 
 # every symbol the public header declares
 SYMBOLS = (
-    "kvsel_version", "kvsel_status_string", "kvsel_last_error",
+    "kvsel_version", "kvsel_status_string", "kvsel_last_error", "kvsel_debug_status",
     "kvsel_score", "kvsel_score_workspace",
     "kvsel_topk", "kvsel_topk_workspace",
     "kvsel_gather_attn", "kvsel_attn_workspace", "kvsel_gather_attn_noalloc",
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_status_string.restype = ctypes.c_char_p
     L.kvsel_status_string.argtypes = [_I32]
     L.kvsel_last_error.restype = ctypes.c_char_p
+    L.kvsel_debug_status.restype = _I32
+    L.kvsel_debug_status.argtypes = [_P, _P, _P]
     L.kvsel_score.restype = _I32
     L.kvsel_score.argtypes = [_DP, _P, _I32, _I32, _F32, _I32, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]
     L.kvsel_score_workspace.restype = _SZ
@@ -262,6 +265,14 @@ def _ws(ws: Optional[Workspace], device) -> Workspace:
 
 def version() -> int:
     return lib().kvsel_version()
+
+
+def debug_status():
+    """kvsel_debug_status: (status, violations, first code, first detail).  A
+    release build gives KVSEL_EUNSUPPORTED; synchronise the device first."""
+    n, c, d = ctypes.c_uint32(0), ctypes.c_uint32(0), ctypes.c_uint32(0)
+    st = lib().kvsel_debug_status(ctypes.byref(n), ctypes.byref(c), ctypes.byref(d))
+    return st, n.value, c.value, d.value
 
 
 def score_workspace(kv: KV, n_rows: int, num_q_heads: int, reduce: int, norm: int) -> int:

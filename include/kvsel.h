@@ -70,6 +70,7 @@ typedef int32_t kvsel_status;
 #define KVSEL_ENOSPC       (-2)  /* workspace too small                           */
 #define KVSEL_EUNSUPPORTED (-3)  /* head_dim != 128, block_size != 16, group > 8  */
 #define KVSEL_EHIP         (-4)  /* a HIP launch failed                           */
+#define KVSEL_EDEBUG       (-5)  /* debug build: a device-side check failed       */
 
 #define KVSEL_VERSION 3
 
@@ -144,6 +145,30 @@ KVSEL_API int32_t kvsel_version(void);
 KVSEL_API const char *kvsel_status_string(kvsel_status s);
 /* Text of the last error on the calling thread ("" if none). */
 KVSEL_API const char *kvsel_last_error(void);
+
+/*
+ * kvsel_debug_status -- the device-side checks of a debug build.
+ *
+ * A library built with KVSEL_DEBUG=1 (libkvsel_debug.so beside the release
+ * build) checks inside its kernels the facts they rely on: every K/V row
+ * read lies inside its pool, LDS indices inside their arrays, every output
+ * slot inside its row (a top-k position below k), every split arrival
+ * counter started at zero (a workspace shared by overlapping calls, or not
+ * zeroed, breaks that), counts within their bounds.  A failed check does not
+ * trap; it is counted in device memory, with the code (KVSEL_DBG_* below) and
+ * a detail value of the first one.  This call reads and clears the counts;
+ * synchronise the device first.  violations, first_code and first_detail may
+ * each be NULL.  Returns KVSEL_OK if no check failed, KVSEL_EDEBUG if one
+ * did, KVSEL_EHIP if the counts could not be read, and KVSEL_EUNSUPPORTED
+ * (outputs 0) from a release build, whose kernels hold no checks.
+ */
+#define KVSEL_DBG_KV_ROW    1   /* detail: the physical row                       */
+#define KVSEL_DBG_LDS       2   /* detail: the index                              */
+#define KVSEL_DBG_OUT_SLOT  3   /* detail: the slot                               */
+#define KVSEL_DBG_COUNTER   4   /* detail: the counter value found                */
+#define KVSEL_DBG_SRC_ROW   5   /* detail: the row                                */
+#define KVSEL_DBG_COUNT     6   /* detail: the count                              */
+KVSEL_API kvsel_status kvsel_debug_status(uint32_t *violations, uint32_t *first_code, uint32_t *first_detail);
 
 /*
  * kvsel_score -- token saliency over the candidate segment.

@@ -31,12 +31,13 @@ def declared():
 
 def test_exports_every_declared_symbol(L):
     names = declared()
-    assert len(names) == 29
+    assert len(names) == 30
     assert sorted(kvsel.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
     assert L.kvsel_version() == 3
     assert L.kvsel_status_string(-2) == b"workspace too small"
+    assert L.kvsel_status_string(-5) == b"device check failed"
 
 
 def desc(**over):
@@ -291,3 +292,29 @@ def test_merge_attn_rejects(L, kw, code):
 
 def test_merge_attn_empty_is_a_no_op(L):
     assert L.kvsel_merge_attn(FAKE, FAKE, 3, 0, FAKE, FAKE, None) == 0
+
+
+def test_debug_status_of_the_release_and_debug_builds(L):
+    """kvsel_debug_status: the release build holds no device checks (EUNSUPPORTED,
+    outputs zeroed, no HIP call); the debug build registered every source
+    file's check counters, so it reads them -- KVSEL_EHIP without a GPU, OK on
+    one."""
+    import ctypes
+    import subprocess
+    import sys
+    n, c, d = ctypes.c_uint32(9), ctypes.c_uint32(9), ctypes.c_uint32(9)
+    if os.environ.get("KVSEL_LIBRARY", "").endswith("libkvsel_debug.so"):
+        pytest.skip("the debug build is loaded")
+    assert L.kvsel_debug_status(ctypes.byref(n), ctypes.byref(c), ctypes.byref(d)) == EUNSUP
+    assert (n.value, c.value, d.value) == (0, 0, 0)
+    assert L.kvsel_debug_status(None, None, None) == EUNSUP
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    dbg = os.path.join(root, "decode_focal_layer_amd", "libkvsel_debug.so")
+    if not os.path.exists(dbg):
+        from decode_focal_layer_amd import build
+        build.build(debug=True)
+    probe = ("import ctypes; L = ctypes.CDLL(%r); L.kvsel_last_error.restype = ctypes.c_char_p; "
+             "n = ctypes.c_uint32(9); print(L.kvsel_debug_status(ctypes.byref(n), None, None), n.value)" % dbg)
+    r = subprocess.run([sys.executable, "-c", probe], capture_output=True, text=True, timeout=120)
+    st, nv = (int(x) for x in r.stdout.split())
+    assert st in (0, -4) and nv == 0, r.stdout + r.stderr
