@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c1_hbm_traffic.md")
 KERNEL_SOURCES = ["decode_focal_layer_amd/csrc/attn.hip", "decode_focal_layer_amd/csrc/common.h",
                   "decode_focal_layer_amd/csrc/focal.h", "decode_focal_layer_amd/csrc/radix.h",
-                  "decode_focal_layer_amd/csrc/kvsel_internal.h"]
+                  "decode_focal_layer_amd/csrc/kvsel_internal.h", "decode_focal_layer_amd/csrc/debug.h"]
 
 
 def measured_traffic():
