@@ -136,6 +136,67 @@ def cpu_baseline(w, cfg, t_sample: int, n_seq: int, cores_limit=None):
                       f"full batch; {cores} host cores available"}
 
 
+def oracle_parity(dec, w, cfg, n_seq: int):
+    """The oracle leg's check of the benchmarked decoder itself: steps 0 and 1
+    of the cycle on the GPU (the launch configuration timed above), then, for
+    the first n_seq sequences, every kv head and all 28 layers of step 1
+    against the oracle on the host.  Focal layers: the kept set by the tie-band
+    rule (indices whose oracle score lies within 1e-6 of the k-th may differ)
+    and the dense output; every other layer: its output against the oracle's
+    attention over the rows the GPU's (validated) set keeps -- layers 0-2 the
+    deepest focal layer's set of step 0, the others this step's set of the
+    focal layer before them.  Tolerances: max abs 2e-3, relative L2 1e-3."""
+    import torch
+    from oracle import oracle as O
+
+    last = max(cfg.focal)
+    dec.step(0, w.q[0], w.seq_len[0])
+    prev_set = dec.selection(last)[:n_seq].cpu().numpy()
+    dec.step(1, w.q[1], w.seq_len[1])
+    torch.cuda.synchronize()
+    outs = dec.out[:, :n_seq].cpu().numpy()
+    sets = {f: dec.selection(f)[:n_seq].cpu().numpy() for f in cfg.focal}
+    n = int(w.seq_len_np[1, 0])
+    G = cfg.group
+    t0 = time.perf_counter()
+    rows = w.block_table[:n_seq].flatten().long()
+    table = np.arange(n_seq * w.max_blocks).reshape(n_seq, w.max_blocks)
+    qc = w.q[1].cpu()
+    worst_abs = worst_l2 = 0.0
+    n_out = n_sets = exact = in_band = outside = 0
+    for l, (kind, src) in enumerate(dec.plan(1)):
+        kc, vc = w.k_pool[l][rows].cpu(), w.v_pool[l][rows].cpu()
+        for b in range(n_seq):
+            for g in range(cfg.hkv):
+                K = O.logical_rows(kc, table[b], g, n)
+                V = O.logical_rows(vc, table[b], g, n)
+                qg = O.widen(qc[l, b, g * G:(g + 1) * G])
+                if kind == "focal":
+                    ref, _ = O.dense_attention(qg, K, V, cfg.scale)
+                    sc = O.focal_scores(qg, K, 0, cfg.n_visual, cfg.scale)
+                    gi = sets[l][b, g]
+                    ok, nd = O.tie_band_check(gi, sc, cfg.k)
+                    n_sets += 1
+                    exact += int(ok and nd == 0)
+                    in_band += int(ok and nd > 0)
+                    outside += int(not ok)
+                else:
+                    which, ls = src
+                    gi = prev_set[b, g] if which == "prev" else sets[ls][b, g]
+                    ref, _ = O.attention(qg, K, V, O.kept_rows(gi, 0, cfg.n_visual, n), cfg.scale)
+                got = outs[l, b, g * G:(g + 1) * G].astype(np.float64)
+                worst_abs = max(worst_abs, float(np.abs(got - ref).max()))
+                worst_l2 = max(worst_l2, float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)))
+                n_out += 1
+    ok = outside == 0 and worst_abs <= 2e-3 and worst_l2 <= 1e-3
+    return {"ok": bool(ok), "sample": f"decode step t=1 of the cycle after t=0, sequences 0-{n_seq - 1}, all "
+                                      f"{cfg.layers} layers and {cfg.hkv} kv heads",
+            "outputs_checked": n_out, "max_abs_err": float(f"{worst_abs:.3e}"),
+            "max_rel_l2": float(f"{worst_l2:.3e}"), "tolerance": {"max_abs": 2e-3, "rel_l2": 1e-3, "tie_band": 1e-6},
+            "kept_sets_checked": n_sets, "kept_sets_exact": exact, "kept_sets_within_tie_band": in_band,
+            "kept_sets_outside_tie_band": outside, "oracle_s": round(time.perf_counter() - t0, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +339,7 @@ def main():
         # the same oracle on one core, on a smaller sample of the same step
         one = cpu_baseline(w, cfg, 1, max(1, args.cpu_seqs // 3), cores_limit=1)
         cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+        cpu["parity"] = oracle_parity(dec, w, cfg, min(4, args.cpu_seqs))
 
     line = {
         "metric": "decode attn steps/s (score + top-k + sparse attention, 28 layers)",
