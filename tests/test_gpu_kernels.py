@@ -1296,3 +1296,62 @@ def test_select_logits_skips_missing_block():
             assert rel_err(got[seg_rows - s0], ref[seg_rows - s0]) < 2e-6, (b, g)
             ok, nd = O.tie_band_check(idx[b, g].cpu().numpy(), ref, k, BAND)
             assert ok, (b, g, nd)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_split_count_invariance(G):
+    """The same two sequences attended alone (few pairs: each pair's rows split
+    over many work-groups, the records merged by the last of them) and
+    replicated into a launch of 256+ (sequence, kv head) pairs (about one
+    work-group per pair): the outputs agree up to summation order, with each
+    other and with the oracle, for gathered and dense attention; with
+    KVSEL_FLAG_DETERMINISTIC the replicas of one sequence are equal bit for
+    bit.  A missing barrier in the row hand-out, the wave merge or the record
+    merge would show as a difference between the split counts or between the
+    replicas."""
+    kvsel = K()
+    rng = np.random.default_rng(4400 + G)
+    hkv, n, seg, k = 2, 3000, (100, 2100), 150
+    hq = hkv * G
+    kp, vp, table = random_paged(rng, 2, hkv, n, DEV)
+    idx_np = np.stack([np.stack([np.sort(rng.choice(seg[1] - seg[0], size=k, replace=False)) for _ in range(hkv)])
+                       for _ in range(2)]).astype(np.int32)
+    q = torch.randn((2, hq, 128), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
+    reps = 256 // (2 * hkv) + 1
+    i32 = lambda x: torch.as_tensor(np.asarray(x, dtype=np.int32)).to(DEV)
+
+    def run(R, det):
+        b = 2 * R
+        kv = kvsel.KV(kp, vp, i32(np.tile(table, (R, 1))), i32([n] * b), i32([seg[0]] * b), i32([seg[1]] * b),
+                      max_seq_len=n, max_seg_len=seg[1] - seg[0], min_seg_len=seg[1] - seg[0], deterministic=det)
+        qq = q.repeat(R, 1, 1).contiguous()
+        idx = i32(np.tile(idx_np, (R, 1, 1)))
+        og = torch.zeros((b, hq, 128), dtype=torch.float32, device=DEV)
+        lg = torch.zeros((b, hq), dtype=torch.float32, device=DEV)
+        od = torch.zeros_like(og)
+        ld = torch.zeros_like(lg)
+        kvsel.gather_attn(kv, qq, hq, SCALE, idx, k, og, lg)
+        kvsel.dense_attn(kv, qq, hq, SCALE, od, ld)
+        torch.cuda.synchronize()
+        return [x.cpu().numpy().reshape(R, 2, *x.shape[1:]) for x in (og, lg, od, ld)]
+
+    log_case("split invariance", G, reps)
+    small = run(1, False)
+    big = run(reps, False)
+    for a, bb in zip(small, big):
+        scale_ = max(float(np.abs(a).max()), 1.0)
+        assert float(np.abs(bb - a).max()) <= 1e-5 * scale_
+    det = run(reps, True)
+    for x in det:
+        assert all(np.array_equal(x[r], x[0]) for r in range(reps)), "deterministic replicas differ"
+    kc, vc, qc = cpu_pool(kp), cpu_pool(vp), q.cpu()
+    for s in range(2):
+        for g in range(hkv):
+            Kl = O.logical_rows(kc, table[s], g, n)
+            Vl = O.logical_rows(vc, table[s], g, n)
+            qg = O.widen(qc[s, g * G:(g + 1) * G])
+            ref_g, _ = O.attention(qg, Kl, Vl, O.kept_rows(idx_np[s, g], seg[0], seg[1], n), SCALE)
+            ref_d, _ = O.dense_attention(qg, Kl, Vl, SCALE)
+            for out in (small, big, det):
+                assert_attn(out[0][0, s, g * G:(g + 1) * G], ref_g, f"gather s{s} g{g}")
+                assert_attn(out[2][0, s, g * G:(g + 1) * G], ref_d, f"dense s{s} g{g}")
