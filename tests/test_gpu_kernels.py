@@ -419,7 +419,10 @@ def test_dense_fused_scores_match_score_call():
 # >= 256 (G <= 2) or 512 (G = 4) pairs -> the one-kernel fused focal pass
 FOCAL_CASES = [(2, 0, 3, 4, 3000, 2500), (4, 1, 3, 4, 3000, 2500), (1, 0, 3, 4, 3000, 2500), (8, 0, 3, 4, 3000, 2500),
                (2, 0, 32, 8, 900, 700), (4, 0, 64, 8, 520, 400), (1, 0, 32, 8, 400, 333),
-               (3, 0, 3, 4, 3000, 2500), (5, 1, 3, 4, 3000, 2500), (6, 0, 8, 4, 900, 700), (7, 0, 3, 4, 400, 333)]
+               (3, 0, 3, 4, 3000, 2500), (5, 1, 3, 4, 3000, 2500), (6, 0, 8, 4, 900, 700), (7, 0, 3, 4, 400, 333),
+               # one work-group per pair (the fused kernel): a segment whose G x 10240 logits fill the fused
+               # kernel's 80 KiB of LDS exactly, and one row more (attention with logits, then the selection)
+               (2, 0, 32, 8, 10300, 10240), (2, 0, 32, 8, 10300, 10241)]
 
 
 @pytest.mark.parametrize("G,norm,batch,hkv,n,seg", FOCAL_CASES)
