@@ -293,7 +293,9 @@ def test_topk_rows_of_their_own_length(n, k):
                                       # the edges of the register-held row sizes (4, 8, 16, 32 keys per
                                       # thread) and the first row past them
                                       (4096, 100, "wide"), (4097, 4000, "ties"), (32768, 4000, "signed"),
-                                      (32769, 100, "wide")])
+                                      (32769, 100, "wide"),
+                                      # the longest row staged in LDS and the first read from global memory
+                                      (36864, 1000, "wide"), (36865, 1000, "ties")])
 def test_topk_exact(n, k, mode):
     kvsel = K()
     rng = np.random.default_rng(n + k)
@@ -1301,8 +1303,8 @@ def test_select_logits_skips_missing_block():
             assert ok, (b, g, nd)
 
 
-@pytest.mark.parametrize("G", [1, 2, 4])
-def test_split_count_invariance(G):
+@pytest.mark.parametrize("G,n", [(1, 3000), (2, 3000), (4, 3000), (2, 8300)])
+def test_split_count_invariance(G, n):
     """The same two sequences attended alone (few pairs: each pair's rows split
     over many work-groups, the records merged by the last of them) and
     replicated into a launch of 256+ (sequence, kv head) pairs (about one
@@ -1311,10 +1313,11 @@ def test_split_count_invariance(G):
     KVSEL_FLAG_DETERMINISTIC the replicas of one sequence are equal bit for
     bit.  A missing barrier in the row hand-out, the wave merge or the record
     merge would show as a difference between the split counts or between the
-    replicas."""
+    replicas.  n = 8300: more rows per pair than one work-group's row table
+    holds, so even the replicated dense launch splits each pair in two."""
     kvsel = K()
-    rng = np.random.default_rng(4400 + G)
-    hkv, n, seg, k = 2, 3000, (100, 2100), 150
+    rng = np.random.default_rng(4400 + G + n)
+    hkv, seg, k = 2, (100, n - 900), 150
     hq = hkv * G
     kp, vp, table = random_paged(rng, 2, hkv, n, DEV)
     idx_np = np.stack([np.stack([np.sort(rng.choice(seg[1] - seg[0], size=k, replace=False)) for _ in range(hkv)])
