@@ -883,7 +883,9 @@ SHARED_CASES = [(2, 5, 160, (37, 160), 1, 1), (1, 3, 64, (0, 64), 1, 1), (4, 70,
                 (8, 20, 96, (5, 90), 3, 1), (2, 9, 48, (10, 10), 1, 1), (2, 600, 256, (64, 250), 2, 1),
                 (1, 4, 128, (0, 100), 5, 1), (2, 30, 200, (16, 180), 2, 3),
                 (3, 7, 160, (37, 160), 2, 1), (6, 9, 200, (16, 180), 1, 2), (5, 40, 96, (5, 90), 3, 1),
-                (7, 3, 64, (0, 64), 1, 4)]
+                (7, 3, 64, (0, 64), 1, 4),
+                # ranges touching the most cache blocks a call takes (1024), on and off block edges
+                (2, 6, 16384, (0, 16384), 3, 1), (2, 6, 16400, (1, 16384), 2, 1)]
 
 
 @pytest.mark.parametrize("G,batch,prefix,rng_rows,splits,qps", SHARED_CASES)
