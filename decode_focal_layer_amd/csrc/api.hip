@@ -645,8 +645,6 @@ kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_r
   if (norm != KVSEL_NORM_SEGMENT && norm != KVSEL_NORM_CONTEXT) return fail(KVSEL_EINVAL, "bad norm %d", norm);
   if (n_rows > 1 && norm != KVSEL_NORM_CONTEXT)
     return fail(KVSEL_EINVAL, "a query window (n_rows > 1) is context-normalised");
-  if (n_rows > 1 && n_rows * G > 32)
-    return fail(KVSEL_EUNSUPPORTED, "n_rows * group = %d > 32", n_rows * G);
   if (pool_width < 1 || pool_width % 2 == 0) return fail(KVSEL_EINVAL, "pool_width must be odd and >= 1");
   if (ld < kv->max_seg_len || ld < 1) return fail(KVSEL_EINVAL, "ld must be >= max_seg_len");
   if (!isfinite(scale)) return fail(KVSEL_EINVAL, "scale must be finite");

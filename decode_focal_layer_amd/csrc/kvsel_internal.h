@@ -142,6 +142,8 @@ struct WinArgs {
   float scale_log2;
   double scale;
   int32_t tile_rows, ntiles;   // keys per work-group tile, tiles per sequence
+  int32_t qr0;           // first query row (window row x group head) of this pass's block of 32
+  int32_t accumulate;    // 1: add this block's scores to the partial row (a later block)
   float *stat;           // [batch][hkv][ntiles][32] x {max dot (f32), pad, sum (f64)}
   double *rowstat;       // [batch][hkv][32] x {max dot, 1 / sum}, merged over tiles
   double *part;          // [batch][hkv][ld64] fp64 group scores

@@ -2,9 +2,11 @@
 // Propagation: the attention weights from a recent window of queries to all
 // context tokens, averaged, rank the tokens).
 //
-// For one (sequence, kv head) the window rows x group heads form R <= 32
-// query rows (row index qr = r * G + h; window row r is the query of
-// position n - W + r and, when causal, sees keys <= that position).  The
+// For one (sequence, kv head) the window rows x group heads form R query
+// rows (row index qr = r * G + h; window row r is the query of position
+// n - W + r and, when causal, sees keys <= that position), taken 32 at a time:
+// each pass below covers rows [qr0, qr0 + 32), and a pass after the first adds
+// its scores to the partial row the earlier ones wrote.  The
 // logits Q K^T are a dense (R x 128) * (128 x keys) contraction in bf16 with
 // fp32 accumulation, computed with v_mfma_f32_32x32x16_bf16.
 //
@@ -56,7 +58,7 @@ __device__ __forceinline__ WinView win_view(const WinArgs &a, int b) {
 
 // lane's query operand: row qr = lane % 32, dims [hf*64, hf*64+64)
 __device__ __forceinline__ void load_q(const WinArgs &a, int b, int g, int lane, bf16x8 (&qop)[8]) {
-  const int qr = lane & 31, hf = lane >> 5;
+  const int qr = a.qr0 + (lane & 31), hf = lane >> 5;   // this pass's block of 32 query rows
   const int R = a.n_rows * a.group;
   if (qr < R) {
     const int r = qr / a.group, h = qr % a.group;
@@ -168,10 +170,11 @@ __global__ __launch_bounds__(kWinThreads) void window_stats_kernel(WinArgs a) {
   stage_tile_blocks(a, b, t0, t1, s_blk);
   bf16x8 qop[8];
   load_q(a, b, g, lane, qop);
-  const int qr = lane & 31, hf = lane >> 5;
+  const int qr = lane & 31, hf = lane >> 5;   // this lane's query row in the block
+  const int qg = a.qr0 + qr;                   // and among all of them
   // keys [t0, kend) are visible to this lane's query row
   int kend = t0;
-  if (qr < a.n_rows * a.group) kend = a.causal ? min(t1, v.n - a.n_rows + qr / a.group + 1) : t1;
+  if (qg < a.n_rows * a.group) kend = a.causal ? min(t1, v.n - a.n_rows + qg / a.group + 1) : t1;
   const float cf = (float)(a.scale * 1.4426950408889634);
   float mc = -INFINITY;   // reference: the largest dot * cf so far (fp32)
   double z = 0.0;         // sum of 2^(dot * cf - mc), per element in fp32
@@ -311,7 +314,8 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
   int pkey = -1;       // this lane's key of the previous block (-1: none)
   double pval = 0.0;
   auto flush = [&] {
-    if (hf == 0 && pkey >= t0 && pkey < t1 && pkey - v.s0 < a.ld64) dst[pkey - v.s0] = pval;
+    if (hf == 0 && pkey >= t0 && pkey < t1 && pkey - v.s0 < a.ld64)
+      dst[pkey - v.s0] = a.accumulate ? dst[pkey - v.s0] + pval : pval;
   };
   auto use = [&](int kb, const uint8_t *sl) {
     bf16x8 kop[8];
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kWinThreads) void window_scores_kernel(WinArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int qr = 8 * (j >> 2) + 4 * hf + (j & 3);
+        const int qr = a.qr0 + 8 * (j >> 2) + 4 * hf + (j & 3);
         const bool vis = qr < R && key < v.n && (!a.causal || key <= v.n - a.n_rows + qr / a.group);
         if (vis) acc += (double)(fast_exp2(fmaf(d[j], cf, -rmc[j])) * riz[j]);
       }
@@ -382,16 +386,27 @@ WinPlan win_plan(int batch, int hkv, int group, int n_rows, int max_seq_len, int
   return p;
 }
 
-hipError_t launch_window(const WinArgs &a, const WinPlan &p, int batch, hipStream_t s) {
-  dim3 grid(p.ntiles, a.hkv, batch), block(kWinThreads);
-  hipLaunchKernelGGL(window_stats_kernel, grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(window_merge_kernel, dim3(a.hkv, batch), dim3(1024), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(window_scores_kernel, grid, block, 0, s, a);
-  return hipGetLastError();
+// The query rows of a kv head (window rows x group heads) in blocks of 32, one
+// MFMA tile each: every block has its own statistics (its rows' normalisers)
+// and adds its probabilities to the same fp64 partial scores.
+hipError_t launch_window(const WinArgs &a0, const WinPlan &p, int batch, hipStream_t s) {
+  dim3 grid(p.ntiles, a0.hkv, batch), block(kWinThreads);
+  const int R = a0.n_rows * a0.group;
+  for (int qr0 = 0; qr0 < (R > 0 ? R : 1); qr0 += 32) {
+    WinArgs a = a0;
+    a.qr0 = qr0;
+    a.accumulate = qr0 > 0 ? 1 : 0;
+    hipLaunchKernelGGL(window_stats_kernel, grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(window_merge_kernel, dim3(a.hkv, batch), dim3(1024), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(window_scores_kernel, grid, block, 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvsel

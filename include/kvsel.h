@@ -193,8 +193,8 @@ KVSEL_API kvsel_status kvsel_debug_status(uint32_t *violations, uint32_t *first_
  * seg_begin[b] + i; entries past the segment length are not written.
  * Requires ld >= max_seg_len.  n_rows in [1, 64].  NORM_SEGMENT requires
  * n_rows == 1 (a window is always context-normalised).  n_rows > 1 uses
- * MFMA on the (n_rows x group) query rows of a kv head, which must be at
- * most 32 (KVSEL_EUNSUPPORTED otherwise).  Workspace:
+ * MFMA on the (n_rows x group) query rows of a kv head, 32 at a time: each
+ * further block of 32 rows reads the keys twice more.  Workspace:
  * kvsel_score_workspace(kv, n_rows, num_q_heads, reduce, norm).
  */
 KVSEL_API kvsel_status kvsel_score(const kvsel_kv_desc *kv, const uint16_t *q, int32_t n_rows,

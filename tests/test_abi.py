@@ -131,7 +131,7 @@ def score(L, d, q=FAKE, n_rows=1, hq=16, reduce=0, norm=0, causal=1, pool=1, sco
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_rows=0), EINVAL), (dict(n_rows=65), EINVAL), (dict(reduce=2), EINVAL), (dict(norm=2), EINVAL),
-    (dict(n_rows=8, norm=0), EINVAL), (dict(n_rows=8, norm=1, hq=64), EUNSUP), (dict(pool=2), EINVAL),
+    (dict(n_rows=8, norm=0), EINVAL), (dict(n_rows=8, norm=1, hq=72), EUNSUP), (dict(pool=2), EINVAL),
     (dict(pool=0), EINVAL), (dict(ld=99), EINVAL), (dict(scores=0), EINVAL), (dict(q=0), EINVAL),
     (dict(ws_bytes=8), ENOSPC), (dict(n_rows=8, norm=1, ws_bytes=8), ENOSPC),
 ])

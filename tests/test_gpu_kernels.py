@@ -472,7 +472,9 @@ def test_focal_attn_equals_dense_then_topk(G, norm, batch, hkv, n, seg):
 
 
 @pytest.mark.parametrize("G,W,reduce,causal", [(4, 8, 1, True), (4, 8, 0, True), (2, 8, 0, False), (1, 5, 1, True),
-                                              (3, 8, 0, True), (5, 6, 1, False), (6, 5, 0, True), (7, 4, 1, True)])
+                                              (3, 8, 0, True), (5, 6, 1, False), (6, 5, 0, True), (7, 4, 1, True),
+                                              # more than 32 query rows per kv head: blocks of 32 (2, 3 and 16)
+                                              (8, 8, 1, True), (8, 8, 0, False), (5, 13, 1, True), (8, 64, 0, True)])
 def test_window_scores(G, W, reduce, causal):
     kvsel = K()
     rng = np.random.default_rng(G * 7 + W)
