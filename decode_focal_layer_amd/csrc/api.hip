@@ -386,7 +386,7 @@ kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32
   if ((st = check_desc(kv, true)) != KVSEL_OK) return st;
   if ((st = check_heads(kv, num_q_heads, &G)) != KVSEL_OK) return st;
   if (m < 1) return fail(KVSEL_EINVAL, "m must be >= 1");
-  if (m * G > 32) return fail(KVSEL_EUNSUPPORTED, "m * group = %d query rows per kv head (1 .. 32)", m * G);
+  if (m > 64) return fail(KVSEL_EUNSUPPORTED, "m = %d drafts (1 .. 64)", m);
   if (q == nullptr || !aligned(q, 16)) return fail(KVSEL_EINVAL, "q must be a 16-byte aligned pointer");
   if (out == nullptr) return fail(KVSEL_EINVAL, "out is NULL");
   if (k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");

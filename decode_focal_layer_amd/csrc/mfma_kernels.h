@@ -18,6 +18,7 @@ struct VerifyArgs {
   float scale_log2;
   float *out, *lse;      // [batch][m][hq][128], [batch][m][hq]
   int32_t rows_cap;      // attended rows per (sequence, kv head), at most kVerifyMaxRows
+  int32_t col0;          // first query column (draft x group head) of this launch's block of 32
 };
 hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s);
 

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
-  const int G = a.group, R = a.m * G;
+  const int G = a.group, R = min(a.m * G - a.col0, 32);   // this block's columns: a.col0 + [0, R)
 
   __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kTilesBytes];
   __shared__ float s_m[kVWaves][32], s_l[kVWaves][32];
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // ---- this lane's query column (B operand of k-step kk: dims kk*16 + hf*8 .. +8) ----
   bf16x8 qop[8];
-  const int qr = col / G, qh = col % G;
+  const int qr = (a.col0 + col) / G, qh = (a.col0 + col) % G;   // the column's draft and head
   if (col < R) {
     const uint4 *p = reinterpret_cast<const uint4 *>(a.q + (((size_t)b * a.m + qr) * a.hq + g * G + qh) * kD + hf * 8);
 #pragma unroll
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       L += s_l[w][c] * f;
       A += s_o[(w * 32 + c) * kD + (d ^ c)] * f;
     }
-    const int r = c / G, h = c % G;
+    const int r = (a.col0 + c) / G, h = (a.col0 + c) % G;
     const size_t ob = ((size_t)b * a.m + r) * a.hq + g * G + h;
     a.out[ob * kD + d] = L > 0.f ? A / L : 0.f;
     if (d == 0 && a.lse != nullptr) a.lse[ob] = L > 0.f ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
@@ -547,20 +547,30 @@ __global__ __launch_bounds__(kW16Threads) __attribute__((amdgpu_waves_per_eu(4, 
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyArgs &a, int batch, hipStream_t s) {
-  if (a.m < 1 || a.group < 1 || a.m * a.group > 32 || a.rows_cap < 1 || a.rows_cap > kVerifyMaxRows)
-    return hipErrorInvalidValue;
+hipError_t launch_verify(const VerifyArgs &a0, int batch, hipStream_t s) {
+  if (a0.m < 1 || a0.group < 1 || a0.rows_cap < 1 || a0.rows_cap > kVerifyMaxRows) return hipErrorInvalidValue;
   // the row table is dynamic LDS beside up to 70 KiB of static LDS (allowed once per device)
   for (const void *f : {(const void *)verify_kernel, (const void *)verify16_kernel}) {
     const hipError_t e = allow_dynamic_lds(f, kVerifyMaxRows * (int)sizeof(uint32_t));
     if (e != hipSuccess) return e;
   }
-  const size_t dyn = (size_t)a.rows_cap * sizeof(uint32_t);
-  if (a.m * a.group <= 16)
+  const size_t dyn = (size_t)a0.rows_cap * sizeof(uint32_t);
+  if (a0.m * a0.group <= 16) {
+    VerifyArgs a = a0;
+    a.col0 = 0;
     hipLaunchKernelGGL(verify16_kernel, dim3(a.hkv, batch), dim3(kW16Threads), dyn, s, a);
-  else
+    return hipGetLastError();
+  }
+  // query columns (draft x group head) 32 at a time: the columns are
+  // independent, each launch reads the branch's rows once more
+  for (int c0 = 0; c0 < a0.m * a0.group; c0 += 32) {
+    VerifyArgs a = a0;
+    a.col0 = c0;
     hipLaunchKernelGGL(verify_kernel, dim3(a.hkv, batch), dim3(kVThreads), dyn, s, a);
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvsel

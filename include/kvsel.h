@@ -376,10 +376,11 @@ KVSEL_API kvsel_status kvsel_pick_layers(const float *ratios, int64_t ld, int32_
  * is <= seq_len[b]-m+r: everything before the drafts, and the drafts up to
  * its own.  q: bf16 [batch][m][num_q_heads][128]; idx: as kvsel_gather_attn
  * (NULL when k = 0); out: fp32 [batch][m][num_q_heads][128]; lse: NULL or
- * fp32 [batch][m][num_q_heads].  Requires m * (num_q_heads / num_kv_heads)
- * <= 32 and at most 8192 attended rows per (sequence, kv head), drafts
- * included: k + max_seq_len - min_seg_len + m <= 8192 (KVSEL_EUNSUPPORTED
- * otherwise).  No workspace.
+ * fp32 [batch][m][num_q_heads].  Requires m <= 64 and at most 8192
+ * attended rows per (sequence, kv head), drafts included: k + max_seq_len -
+ * min_seg_len + m <= 8192 (KVSEL_EUNSUPPORTED otherwise).  The query columns
+ * (m x num_q_heads / num_kv_heads per kv head) run 32 at a time, each block
+ * reading the rows once more.  No workspace.
  */
 KVSEL_API kvsel_status kvsel_verify_attn(const kvsel_kv_desc *kv, const uint16_t *q, int32_t m,
                                          int32_t num_q_heads, float scale, const int32_t *idx, int32_t k,

@@ -213,7 +213,7 @@ def test_pick_layers_rejects(L, args, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(m=0), EINVAL), (dict(m=17), EUNSUP), (dict(m=33, hq=8), EUNSUP), (dict(q=0), EINVAL),
+    (dict(m=0), EINVAL), (dict(m=65), EUNSUP), (dict(m=65, hq=8), EUNSUP), (dict(q=0), EINVAL),
     (dict(q=FAKE + 2), EINVAL), (dict(out=0), EINVAL), (dict(k=-1), EINVAL), (dict(idx=0), EINVAL),
     (dict(scale=float("inf")), EINVAL), (dict(hq=12), EINVAL), (dict(k=8200), EUNSUP),
     (dict(d=dict(v_pool=0)), EINVAL),

@@ -693,14 +693,16 @@ def test_fork_copy_on_write(L):
 
 
 # (G, m, batch, lens, segments, k): the drafts are each sequence's last m rows;
-# ragged tiles, k = 0, a segment reaching into the drafts (cut at n - m), and
-# m * G at its limit of 32 query rows
+# ragged tiles, k = 0, a segment reaching into the drafts (cut at n - m), m * G
+# at one block of 32 query rows, and past it (2, 3 and 16 blocks of 32)
 VERIFY_CASES = [(1, 1, 1, [1], [(0, 1)], 0), (2, 4, 2, [17, 300], [(3, 10), (0, 290)], 5),
                 (4, 8, 1, [4000], [(10, 3900)], 200), (8, 4, 2, [700, 129], [(64, 600), (0, 100)], 33),
                 (1, 32, 1, [96], [(0, 40)], 40), (2, 4, 1, [50], [(5, 50)], 30),
                 (2, 4, 1, [8300], [(100, 8200)], 7900), (4, 2, 3, [33, 34, 35], [(1, 30), (2, 2), (0, 33)], 0),
                 (3, 4, 2, [17, 300], [(3, 10), (0, 290)], 5), (5, 6, 1, [700], [(64, 600)], 33),
-                (6, 2, 2, [50, 129], [(5, 50), (0, 100)], 20), (7, 4, 1, [400], [(10, 300)], 100)]
+                (6, 2, 2, [50, 129], [(5, 50), (0, 100)], 20), (7, 4, 1, [400], [(10, 300)], 100),
+                (8, 8, 2, [700, 129], [(64, 600), (0, 100)], 33), (3, 25, 1, [400], [(10, 300)], 60),
+                (8, 64, 1, [900], [(0, 700)], 100)]
 
 
 @pytest.mark.parametrize("G,m,batch,lens,segs,k", VERIFY_CASES)
